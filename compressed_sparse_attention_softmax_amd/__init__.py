@@ -1,0 +1,16 @@
+"""MI355X (gfx950) compressed sparse attention hot path.
+
+The work happens in ``libcsa.so`` (hand-written HIP kernels behind the C ABI
+of ``include/csa.h``); this package only loads it and marshals arguments.
+There is no CPU or PyTorch fallback: if the library is missing, ``load()``
+raises.
+"""
+from ._abi import (CSA_BF16, CSA_F32, EXPORTS, CSAError, csa_compress, csa_compress_bwd, csa_dims,
+                   csa_index_topk, csa_index_topk_workspace, csa_last_error, csa_sparse_attn_bwd,
+                   csa_sparse_attn_bwd_workspace, csa_sparse_attn_fwd, csa_version, dims_of, kprime,
+                   load, make_dims, n_compressed, LIB_PATH)
+
+__all__ = ["CSA_BF16", "CSA_F32", "EXPORTS", "CSAError", "csa_compress", "csa_compress_bwd", "csa_dims",
+           "csa_index_topk", "csa_index_topk_workspace", "csa_last_error", "csa_sparse_attn_bwd",
+           "csa_sparse_attn_bwd_workspace", "csa_sparse_attn_fwd", "csa_version", "dims_of", "kprime",
+           "load", "make_dims", "n_compressed", "LIB_PATH"]

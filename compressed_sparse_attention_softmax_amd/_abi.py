@@ -1,0 +1,215 @@
+"""Thin ctypes binding of libcsa (include/csa.h): argument marshalling only.
+
+Each function has the name of the C entry point it calls.  Tensors are torch
+tensors on the GPU; the binding checks dtype, device, contiguity and shapes,
+passes ``data_ptr()`` and the current HIP stream, and raises ``CSAError``
+with ``csa_last_error()`` on a non-zero status.  Every step of the path runs
+in the library's kernels; nothing here computes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcsa.so")
+
+CSA_F32, CSA_BF16 = 0, 1
+STATUS = {0: "CSA_OK", -1: "CSA_ERR_ARG", -2: "CSA_ERR_SHAPE", -3: "CSA_ERR_DTYPE",
+          -4: "CSA_ERR_UNSUPPORTED", -5: "CSA_ERR_WORKSPACE", -6: "CSA_ERR_HIP"}
+
+# every symbol include/csa.h declares
+EXPORTS = ["csa_compress", "csa_compress_bwd", "csa_index_topk_workspace", "csa_index_topk",
+           "csa_sparse_attn_fwd", "csa_sparse_attn_bwd_workspace", "csa_sparse_attn_bwd",
+           "csa_last_error", "csa_version"]
+
+
+class CSAError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} -> {STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class csa_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("b", "sq", "h", "d", "ratio", "span", "window", "idx_heads", "idx_dim", "topk")]
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load libcsa.so (built in-tree).  Raises if it is missing: there is no
+    fallback implementation."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libcsa.so not found at {p}; build it with "
+                           "`python -m compressed_sparse_attention_softmax_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    D = ctypes.POINTER(csa_dims)
+    lib.csa_compress.argtypes = [D, i, vp, vp, i, vp, vp, vp]
+    lib.csa_compress_bwd.argtypes = [D, i, vp, vp, i, vp, vp, vp, vp]
+    lib.csa_index_topk_workspace.argtypes = [D]
+    lib.csa_index_topk_workspace.restype = sz
+    lib.csa_index_topk.argtypes = [D, i, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.csa_sparse_attn_fwd.argtypes = [D, i, vp, vp, vp, vp, vp, f, vp, vp, vp]
+    lib.csa_sparse_attn_bwd_workspace.argtypes = [D]
+    lib.csa_sparse_attn_bwd_workspace.restype = sz
+    lib.csa_sparse_attn_bwd.argtypes = [D, i, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.csa_last_error.argtypes = []
+    lib.csa_last_error.restype = ctypes.c_char_p
+    lib.csa_version.argtypes = []
+    for fn in ("csa_compress", "csa_compress_bwd", "csa_index_topk", "csa_sparse_attn_fwd",
+               "csa_sparse_attn_bwd", "csa_version"):
+        getattr(lib, fn).restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def make_dims(b, sq, h=1, d=64, ratio=1, span=1, window=1, idx_heads=1, idx_dim=32, topk=0) -> csa_dims:
+    return csa_dims(b, sq, h, d, ratio, span, window, idx_heads, idx_dim, topk)
+
+
+def dims_of(wl) -> csa_dims:
+    """csa_dims of a workload description (any object with the csa_dims fields)."""
+    return csa_dims(wl.b, wl.sq, wl.h, wl.d, wl.ratio, wl.span, wl.window, wl.idx_heads,
+                    wl.idx_dim, wl.topk)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor], *, shape=None, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _call(fn: str, *args) -> None:
+    lib = load()
+    rc = getattr(lib, fn)(*args)
+    if rc != 0:
+        raise CSAError(fn, rc, lib.csa_last_error().decode())
+
+
+def n_compressed(dims: csa_dims) -> int:
+    return dims.sq // dims.ratio if dims.ratio >= 1 else 0
+
+
+def kprime(dims: csa_dims) -> int:
+    return min(dims.topk, n_compressed(dims))
+
+
+def csa_compress(dims: csa_dims, x, z, c, c32=None, stream=None) -> None:
+    dt = x.dtype
+    b, S, D = dims.b, dims.sq, dims.d
+    zc = z.shape[-1]
+    nc = n_compressed(dims)
+    _call("csa_compress", ctypes.byref(dims), _dtype_code(x),
+          _ptr(x, shape=(b, S, D), dtype=dt, name="x"), _ptr(z, shape=(b, S, zc), dtype=dt, name="z"),
+          zc, _ptr(c, shape=(b, nc, D), dtype=dt, name="c"),
+          _ptr(c32, shape=(b, nc, D), dtype=torch.float32, name="c32"), _stream(stream))
+
+
+def csa_compress_bwd(dims: csa_dims, x, z, dc, dx, dz, stream=None) -> None:
+    dt = x.dtype
+    b, S, D = dims.b, dims.sq, dims.d
+    zc = z.shape[-1]
+    nc = n_compressed(dims)
+    f32 = torch.float32
+    _call("csa_compress_bwd", ctypes.byref(dims), _dtype_code(x),
+          _ptr(x, shape=(b, S, D), dtype=dt, name="x"), _ptr(z, shape=(b, S, zc), dtype=dt, name="z"),
+          zc, _ptr(dc, shape=(b, nc, D), dtype=f32, name="dc"),
+          _ptr(dx, shape=(b, S, D), dtype=f32, name="dx"), _ptr(dz, shape=(b, S, zc), dtype=f32, name="dz"),
+          _stream(stream))
+
+
+def csa_index_topk_workspace(dims: csa_dims) -> int:
+    return int(load().csa_index_topk_workspace(ctypes.byref(dims)))
+
+
+def csa_index_topk(dims: csa_dims, q_i, k_i, w, idx, score=None, ws=None, stream=None) -> None:
+    dt = q_i.dtype
+    b, S = dims.b, dims.sq
+    nc, kp = n_compressed(dims), kprime(dims)
+    f32 = torch.float32
+    _call("csa_index_topk", ctypes.byref(dims), _dtype_code(q_i),
+          _ptr(q_i, shape=(b, S, dims.idx_heads, dims.idx_dim), dtype=dt, name="q_i"),
+          _ptr(k_i, shape=(b, nc, dims.idx_dim), dtype=dt, name="k_i"),
+          _ptr(w, shape=(b, S, dims.idx_heads), dtype=f32, name="w"),
+          _ptr(idx, shape=(b, S, kp), dtype=torch.int32, name="idx"),
+          _ptr(score, shape=(b, S, kp), dtype=f32, name="score"),
+          _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def _attn_ptrs(dims, q, kv, c, idx, sink):
+    dt = q.dtype
+    b, S, H, D = dims.b, dims.sq, dims.h, dims.d
+    nc = n_compressed(dims) if c is not None else 0
+    if sink is not None and sink.numel() != H:
+        raise CSAError("csa_sparse_attn", -2, f"sink has {sink.numel()} entries, h = {H}")
+    return (_ptr(q, shape=(b, S, H, D), dtype=dt, name="q"), _ptr(kv, shape=(b, S, D), dtype=dt, name="kv"),
+            _ptr(c, shape=(b, nc, D), dtype=dt, name="c"),
+            _ptr(idx, shape=(b, S, kprime(dims)), dtype=torch.int32, name="idx"),
+            _ptr(sink, shape=(H,), dtype=torch.float32, name="sink"))
+
+
+def csa_sparse_attn_fwd(dims: csa_dims, q, kv, c, idx, sink, scale: float, out, lse, stream=None) -> None:
+    b, S, H, D = dims.b, dims.sq, dims.h, dims.d
+    _call("csa_sparse_attn_fwd", ctypes.byref(dims), _dtype_code(q), *_attn_ptrs(dims, q, kv, c, idx, sink),
+          ctypes.c_float(scale), _ptr(out, shape=(b, S, H, D), dtype=q.dtype, name="out"),
+          _ptr(lse, shape=(b, S, H), dtype=torch.float32, name="lse"), _stream(stream))
+
+
+def csa_sparse_attn_bwd_workspace(dims: csa_dims) -> int:
+    return int(load().csa_sparse_attn_bwd_workspace(ctypes.byref(dims)))
+
+
+def csa_sparse_attn_bwd(dims: csa_dims, q, kv, c, idx, sink, scale: float, out, lse, dout, dq, dkv, dc,
+                        dsink=None, ws=None, stream=None) -> None:
+    b, S, H, D = dims.b, dims.sq, dims.h, dims.d
+    f32 = torch.float32
+    nc = n_compressed(dims) if c is not None else 0
+    _call("csa_sparse_attn_bwd", ctypes.byref(dims), _dtype_code(q), *_attn_ptrs(dims, q, kv, c, idx, sink),
+          ctypes.c_float(scale), _ptr(out, shape=(b, S, H, D), dtype=q.dtype, name="out"),
+          _ptr(lse, shape=(b, S, H), dtype=f32, name="lse"),
+          _ptr(dout, shape=(b, S, H, D), dtype=q.dtype, name="dout"),
+          _ptr(dq, shape=(b, S, H, D), dtype=q.dtype, name="dq"),
+          _ptr(dkv, shape=(b, S, D), dtype=f32, name="dkv"), _ptr(dc, shape=(b, nc, D), dtype=f32, name="dc"),
+          _ptr(dsink, shape=(H,), dtype=f32, name="dsink"), _ptr(ws, name="ws"),
+          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def csa_last_error() -> str:
+    return load().csa_last_error().decode()
+
+
+def csa_version() -> int:
+    return int(load().csa_version())

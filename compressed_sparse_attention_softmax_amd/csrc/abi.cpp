@@ -1,0 +1,227 @@
+// abi.cpp -- the extern "C" entry points of libcsa (declared in include/csa.h).
+//
+// Each entry point validates every argument before touching the HIP runtime,
+// records a message for csa_last_error() on failure, zero-fills accumulating
+// outputs with a fill kernel on the caller's stream (no memset nodes, so a
+// caller may capture the calls into a graph), and enqueues the kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "csa.h"
+#include "csa_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok()
+{
+    g_err.clear();
+    return CSA_OK;
+}
+
+int hip_status(hipError_t e, const char* where)
+{
+    if (e == hipSuccess) return ok();
+    return fail(CSA_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+}
+
+bool supported_d(int d) { return d == 64 || d == 128 || d == 512; }
+
+int check_common(const csa_dims* dm, int dtype, const char* fn)
+{
+    if (!dm) return fail(CSA_ERR_ARG, "%s: dims is NULL", fn);
+    if (dtype != CSA_F32 && dtype != CSA_BF16) return fail(CSA_ERR_DTYPE, "%s: unknown dtype %d", fn, dtype);
+    if (dm->b < 1 || dm->sq < 1) return fail(CSA_ERR_ARG, "%s: b=%d sq=%d must be >= 1", fn, dm->b, dm->sq);
+    return CSA_OK;
+}
+
+int check_compress_dims(const csa_dims* dm, int z_channels, const char* fn)
+{
+    if (dm->ratio < 1 || dm->span < 1)
+        return fail(CSA_ERR_ARG, "%s: ratio=%d span=%d must be >= 1", fn, dm->ratio, dm->span);
+    if (!supported_d(dm->d)) return fail(CSA_ERR_UNSUPPORTED, "%s: d=%d not in {64,128,512}", fn, dm->d);
+    if (z_channels != 1 && z_channels != dm->d)
+        return fail(CSA_ERR_SHAPE, "%s: z_channels=%d must be 1 or d=%d", fn, z_channels, dm->d);
+    return CSA_OK;
+}
+
+csa::CompressArgs compress_args(const csa_dims* dm, const void* x, const void* z, int zc)
+{
+    csa::CompressArgs a{};
+    a.x = x; a.z = z; a.zc = zc;
+    a.b = dm->b; a.S = dm->sq; a.D = dm->d; a.r = dm->ratio; a.L = dm->span;
+    a.nc = dm->sq / dm->ratio;
+    return a;
+}
+
+int kprime(const csa_dims* dm) { return dm->topk < dm->sq / dm->ratio ? dm->topk : dm->sq / dm->ratio; }
+
+int check_attn(const csa_dims* dm, int dtype, const void* q, const void* kv, const void* c,
+               const int32_t* idx, float scale, const char* fn)
+{
+    if (!q || !kv) return fail(CSA_ERR_ARG, "%s: q and kv must be non-NULL", fn);
+    if (!supported_d(dm->d)) return fail(CSA_ERR_UNSUPPORTED, "%s: d=%d not in {64,128,512}", fn, dm->d);
+    if (dm->d == 512 && dtype == CSA_F32)
+        return fail(CSA_ERR_UNSUPPORTED, "%s: fp32 with d=512 exceeds the on-chip row tile", fn);
+    if (dm->h < 1) return fail(CSA_ERR_ARG, "%s: h=%d must be >= 1", fn, dm->h);
+    if (dm->h > 64) return fail(CSA_ERR_UNSUPPORTED, "%s: h=%d > 64", fn, dm->h);
+    if (dm->window < 1) return fail(CSA_ERR_ARG, "%s: window=%d must be >= 1", fn, dm->window);
+    if (!std::isfinite(scale)) return fail(CSA_ERR_ARG, "%s: scale is not finite", fn);
+    if (c) {
+        if (dm->ratio < 1) return fail(CSA_ERR_ARG, "%s: ratio=%d must be >= 1", fn, dm->ratio);
+        if (idx && dm->topk < 1) return fail(CSA_ERR_ARG, "%s: topk=%d must be >= 1 with idx", fn, dm->topk);
+    } else if (idx) {
+        return fail(CSA_ERR_ARG, "%s: idx given without compressed rows c", fn);
+    }
+    return CSA_OK;
+}
+
+csa::AttnArgs attn_args(const csa_dims* dm, const void* q, const void* kv, const void* c,
+                        const int32_t* idx, const float* sink, float scale)
+{
+    csa::AttnArgs a{};
+    a.q = q; a.kv = kv; a.c = c; a.idx = c ? idx : nullptr; a.sink = sink; a.scale = scale;
+    a.b = dm->b; a.S = dm->sq; a.H = dm->h; a.D = dm->d; a.W = dm->window;
+    a.r = c ? dm->ratio : 1;
+    a.nc = c ? dm->sq / dm->ratio : 0;
+    a.kp = (c && idx) ? kprime(dm) : 0;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_version(void) { return CSA_ABI_VERSION; }
+
+const char* csa_last_error(void) { return g_err.c_str(); }
+
+int csa_compress(const csa_dims* dm, int dtype, const void* x, const void* z, int z_channels, void* c,
+                 float* c32, void* stream)
+{
+    int rc = check_common(dm, dtype, "csa_compress");
+    if (rc) return rc;
+    if ((rc = check_compress_dims(dm, z_channels, "csa_compress"))) return rc;
+    if (!x || !z || (!c && dm->sq / dm->ratio > 0))
+        return fail(CSA_ERR_ARG, "csa_compress: x, z and c must be non-NULL");
+    csa::CompressArgs a = compress_args(dm, x, z, z_channels);
+    a.c = c; a.c32 = c32;
+    return hip_status(csa::compress_fwd(a, dtype == CSA_BF16, (hipStream_t)stream), "csa_compress");
+}
+
+int csa_compress_bwd(const csa_dims* dm, int dtype, const void* x, const void* z, int z_channels,
+                     const float* dc, float* dx, float* dz, void* stream)
+{
+    int rc = check_common(dm, dtype, "csa_compress_bwd");
+    if (rc) return rc;
+    if ((rc = check_compress_dims(dm, z_channels, "csa_compress_bwd"))) return rc;
+    if (!x || !z || (!dc && dm->sq / dm->ratio > 0) || !dx || !dz)
+        return fail(CSA_ERR_ARG, "csa_compress_bwd: x, z, dc, dx and dz must be non-NULL");
+    csa::CompressArgs a = compress_args(dm, x, z, z_channels);
+    a.dc = dc; a.dx = dx; a.dz = dz;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = csa::zero_fill(dx, (size_t)dm->b * dm->sq * dm->d, st);
+    if (e == hipSuccess) e = csa::zero_fill(dz, (size_t)dm->b * dm->sq * z_channels, st);
+    if (e == hipSuccess) e = csa::compress_bwd(a, dtype == CSA_BF16, st);
+    return hip_status(e, "csa_compress_bwd");
+}
+
+size_t csa_index_topk_workspace(const csa_dims* dm)
+{
+    (void)dm;
+    return 0;
+}
+
+int csa_index_topk(const csa_dims* dm, int dtype, const void* q_i, const void* k_i, const float* w,
+                   int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream)
+{
+    (void)ws; (void)ws_bytes;
+    int rc = check_common(dm, dtype, "csa_index_topk");
+    if (rc) return rc;
+    if (dm->ratio < 1) return fail(CSA_ERR_ARG, "csa_index_topk: ratio=%d must be >= 1", dm->ratio);
+    if (dm->topk < 1) return fail(CSA_ERR_ARG, "csa_index_topk: topk=%d must be >= 1", dm->topk);
+    if (dm->idx_heads < 1) return fail(CSA_ERR_ARG, "csa_index_topk: idx_heads=%d must be >= 1", dm->idx_heads);
+    if (dm->idx_heads > 64) return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: idx_heads=%d > 64", dm->idx_heads);
+    if (dm->idx_dim != 32 && dm->idx_dim != 64 && dm->idx_dim != 128)
+        return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: idx_dim=%d not in {32,64,128}", dm->idx_dim);
+    if (!q_i || !k_i || !w || !idx) return fail(CSA_ERR_ARG, "csa_index_topk: q_i, k_i, w and idx must be non-NULL");
+    const int kp = kprime(dm);
+    if (kp > 2048) return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: K'=%d > 2048", kp);
+    csa::IndexArgs a{};
+    a.qi = q_i; a.ki = k_i; a.w = w; a.idx = idx; a.score = score;
+    a.b = dm->b; a.S = dm->sq; a.HI = dm->idx_heads; a.DI = dm->idx_dim; a.r = dm->ratio;
+    a.nc = dm->sq / dm->ratio; a.kp = kp;
+    if (kp > 0 && csa::index_topk_cap(a, dtype == CSA_BF16) == 0)
+        return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: K'=%d does not fit the on-chip candidate buffer", kp);
+    return hip_status(csa::index_topk(a, dtype == CSA_BF16, (hipStream_t)stream), "csa_index_topk");
+}
+
+int csa_sparse_attn_fwd(const csa_dims* dm, int dtype, const void* q, const void* kv, const void* c,
+                        const int32_t* idx, const float* sink, float scale, void* out, float* lse,
+                        void* stream)
+{
+    int rc = check_common(dm, dtype, "csa_sparse_attn_fwd");
+    if (rc) return rc;
+    if ((rc = check_attn(dm, dtype, q, kv, c, idx, scale, "csa_sparse_attn_fwd"))) return rc;
+    if (!out || !lse) return fail(CSA_ERR_ARG, "csa_sparse_attn_fwd: out and lse must be non-NULL");
+    csa::AttnArgs a = attn_args(dm, q, kv, c, idx, sink, scale);
+    a.out = out; a.lse = lse;
+    return hip_status(csa::attn_fwd(a, dtype == CSA_BF16, (hipStream_t)stream), "csa_sparse_attn_fwd");
+}
+
+size_t csa_sparse_attn_bwd_workspace(const csa_dims* dm)
+{
+    (void)dm;
+    return 0;
+}
+
+int csa_sparse_attn_bwd(const csa_dims* dm, int dtype, const void* q, const void* kv, const void* c,
+                        const int32_t* idx, const float* sink, float scale, const void* out,
+                        const float* lse, const void* dout, void* dq, float* dkv, float* dc,
+                        float* dsink, void* ws, size_t ws_bytes, void* stream)
+{
+    (void)ws; (void)ws_bytes;
+    int rc = check_common(dm, dtype, "csa_sparse_attn_bwd");
+    if (rc) return rc;
+    if ((rc = check_attn(dm, dtype, q, kv, c, idx, scale, "csa_sparse_attn_bwd"))) return rc;
+    if (!out || !lse || !dout) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: out, lse and dout must be non-NULL");
+    // all-or-nothing gradient gate
+    const bool want_c = c != nullptr;
+    const bool any = dq || dkv || dc;
+    if (!want_c && dc) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: dc given without compressed rows c");
+    if (any) {
+        if (!dq) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: gradient gate: dq is NULL while other gradients are requested");
+        if (!dkv) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: gradient gate: dkv is NULL while other gradients are requested");
+        if (want_c && !dc) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: gradient gate: dc is NULL while other gradients are requested");
+    }
+    if (dsink && !sink) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: dsink given without sink");
+    if (!any && !dsink) return ok();
+    csa::AttnArgs a = attn_args(dm, q, kv, c, idx, sink, scale);
+    a.out = const_cast<void*>(out); a.lse = const_cast<float*>(lse); a.dout = dout;
+    a.dq = dq; a.dkv = dkv; a.dc = dc; a.dsink = dsink;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (dkv) e = csa::zero_fill(dkv, (size_t)dm->b * dm->sq * dm->d, st);
+    if (e == hipSuccess && dc) e = csa::zero_fill(dc, (size_t)dm->b * a.nc * dm->d, st);
+    if (e == hipSuccess && dsink) e = csa::zero_fill(dsink, (size_t)dm->h, st);
+    if (e == hipSuccess) e = csa::attn_bwd(a, dtype == CSA_BF16, st);
+    return hip_status(e, "csa_sparse_attn_bwd");
+}
+
+}  // extern "C"

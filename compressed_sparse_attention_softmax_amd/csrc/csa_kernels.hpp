@@ -1,0 +1,59 @@
+// csa_kernels.hpp -- host-side launch interface of the gfx950 kernels (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+// dynamic LDS budget per workgroup on gfx950 (160 KiB per CU)
+constexpr int INDEX_LDS_LIMIT = 160 * 1024;
+constexpr int ATTN_LDS_LIMIT = 160 * 1024;
+
+struct CompressArgs {
+    const void* x;
+    const void* z;
+    int zc;
+    void* c;
+    float* c32;
+    const float* dc;
+    float* dx;
+    float* dz;
+    int b, S, D, r, L, nc;
+};
+
+struct IndexArgs {
+    const void* qi;
+    const void* ki;
+    const float* w;
+    int32_t* idx;
+    float* score;
+    int b, S, HI, DI, r, nc, kp;
+};
+
+struct AttnArgs {
+    const void* q;
+    const void* kv;
+    const void* c;        // nullptr: window only
+    const int32_t* idx;   // nullptr: every valid compressed row
+    const float* sink;    // nullptr: no sink
+    float scale;
+    void* out;
+    float* lse;
+    const void* dout;
+    void* dq;
+    float* dkv;
+    float* dc;
+    float* dsink;
+    int b, S, H, D, W, r, nc, kp;
+};
+
+hipError_t compress_fwd(const CompressArgs& p, bool bf16, hipStream_t st);
+hipError_t compress_bwd(const CompressArgs& p, bool bf16, hipStream_t st);
+hipError_t index_topk(const IndexArgs& p, bool bf16, hipStream_t st);
+int index_topk_cap(const IndexArgs& p, bool bf16);
+size_t topk_lds_bytes(int DI, int elem, int cap);
+hipError_t attn_fwd(const AttnArgs& p, bool bf16, hipStream_t st);
+hipError_t attn_bwd(const AttnArgs& p, bool bf16, hipStream_t st);
+hipError_t zero_fill(float* p, size_t n, hipStream_t st);
+
+}  // namespace csa

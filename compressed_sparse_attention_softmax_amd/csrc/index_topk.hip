@@ -1,0 +1,373 @@
+// index_topk.hip -- learned indexer scores + streaming top-k (gfx950).
+//
+//   I[t, j] = sum_h w[t, h] * relu(q_i[t, h] . k_i[j]),   j < n_valid(t) = (t+1)/ratio
+//
+// Megatron-LM PR #7152 (min-memory DSA kernels): scores are produced and
+// reduced tile by tile, so memory is O(tile) and the [sq, n_c] matrix never
+// exists; one full top-k (not a merge of chunked top-ks) defines the result,
+// with ties to the lower index; indices and scores leave ordered by position.
+// Megatron-LM PR #6400 (causal-mask thread): block j is invalid for t iff
+// j >= (t+1)//ratio, and rows with fewer valid blocks than K' are padded
+// with -1.
+//
+// Work split: a workgroup is 4 waves = 4 consecutive queries of one batch.
+// For each tile of 64 indexer keys the workgroup stages k_i into LDS; each
+// wave multiplies its query's q_i (all heads, held in registers as MFMA A
+// operands) against the tile: S[h, j] on 16x16x32 MFMA, ReLU, the per-head
+// weights and the sum over heads stay in registers (in-lane plus two
+// cross-lane adds), leaving lane l with the score of key j0 + l.
+//
+// Streaming top-k: each wave keeps a candidate buffer in LDS.  Keys arrive
+// in ascending index, and a key is appended (ballot + mbcnt compaction) iff
+// its score beats the current threshold tau; the buffer therefore stays
+// sorted by index.  When the next tile could overflow it, the buffer is cut
+// to exactly the K' best entries and tau becomes the K'-th score: a later key
+// with an equal score has a larger index and loses the tie, so it is rejected.
+// The cut is an exact wave-level selection: value histograms over the current
+// [lo, hi] range narrow down to one bin, which is ranked exactly; ties at the
+// threshold are kept in buffer order, i.e. lowest index first.  At the end
+// the same selection keeps min(K', n_valid) entries and the buffer is written
+// out as is: already in ascending index.
+#include <cstdlib>
+
+#include "csa_device.hpp"
+#include "csa_kernels.hpp"
+
+namespace csa {
+
+namespace {
+
+constexpr int KT = 64;          // keys per tile
+constexpr int HBINS = 256;      // histogram bins per selection level
+
+}  // namespace
+
+// LDS bytes of one workgroup: the key tile plus, per wave, the candidate
+// buffer (score + index), a histogram and a 64-entry scratch.
+size_t topk_lds_bytes(int DI, int elem, int cap)
+{
+    return (size_t)KT * (DI + 16 / elem) * elem + 4 * ((size_t)cap * 8 + HBINS * 4 + 64 * 8);
+}
+
+namespace {
+
+struct WaveBufs {
+    float* s;        // candidate scores   [cap]
+    int* j;          // candidate indices  [cap]
+    unsigned* hist;  // [HBINS]
+    float* xs;       // small-set scratch  [64]
+    int* xj;         // [64]
+};
+
+__device__ __forceinline__ int bin_of(float s, float lo, float scale)
+{
+    if (s <= lo) return 0;
+    float f = fminf((s - lo) * scale, (float)(HBINS - 1));
+    return (int)f;
+}
+
+// Keep the k best of b.s/b.j[0..n) by (score desc, index asc), preserving
+// buffer order.  Requires 1 <= k < n.  Returns the threshold score T (the
+// k-th best score).  Wave-uniform control flow.
+__device__ float select_keep(const WaveBufs& b, int n, int k)
+{
+    const int lane = lane_id();
+    float lo = INFINITY, hi = -INFINITY;
+    for (int i = lane; i < n; i += WAVE) {
+        float s = b.s[i];
+        lo = fminf(lo, s);
+        hi = fmaxf(hi, s);
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    int kk = k;          // rank sought inside [lo, hi]
+    float T = lo;
+    int need = kk;       // ties at T to keep (in buffer order)
+    for (int level = 0; level < 64; ++level) {
+        if (!(hi > lo)) { T = lo; need = kk; break; }
+        // histogram of the entries inside [lo, hi]
+        for (int i = lane; i < HBINS; i += WAVE) b.hist[i] = 0u;
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        const float scale = (float)HBINS / (hi - lo);
+        for (int i = lane; i < n; i += WAVE) {
+            float s = b.s[i];
+            if (s >= lo && s <= hi) atomicAdd(&b.hist[bin_of(s, lo, scale)], 1u);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        // suffix counts over lanes: lane l owns bins 4l..4l+3
+        unsigned c0 = b.hist[4 * lane], c1 = b.hist[4 * lane + 1], c2 = b.hist[4 * lane + 2],
+                 c3 = b.hist[4 * lane + 3];
+        int mine = (int)(c0 + c1 + c2 + c3);
+        int suf = mine;
+#pragma unroll
+        for (int o = 1; o < WAVE; o <<= 1) {
+            int v = __shfl_down(suf, o);
+            if (lane + o < WAVE) suf += v;
+        }
+        uint64_t ge = __ballot(suf >= kk);
+        int ls = 63 - __clzll((long long)ge);
+        int above_lane = __shfl(suf - mine, ls);        // entries in bins above lane ls
+        int cb[4] = {(int)__shfl((int)c0, ls), (int)__shfl((int)c1, ls), (int)__shfl((int)c2, ls),
+                     (int)__shfl((int)c3, ls)};
+        int cum = above_lane, bstar = 4 * ls, above_b = above_lane, cnt_b = cb[0];
+#pragma unroll
+        for (int q = 3; q >= 0; --q) {
+            if (cum < kk && cum + cb[q] >= kk) { bstar = 4 * ls + q; above_b = cum; cnt_b = cb[q]; }
+            cum += cb[q];
+        }
+        kk -= above_b;
+        // range of the chosen bin
+        float lo2 = INFINITY, hi2 = -INFINITY;
+        for (int i = lane; i < n; i += WAVE) {
+            float s = b.s[i];
+            if (s >= lo && s <= hi && bin_of(s, lo, scale) == bstar) {
+                lo2 = fminf(lo2, s);
+                hi2 = fmaxf(hi2, s);
+            }
+        }
+        lo2 = wave_min(lo2);
+        hi2 = wave_max(hi2);
+        if (cnt_b <= WAVE) {
+            // gather the bin's entries into lanes and rank them exactly
+            int base = 0;
+            for (int i0 = 0; i0 < n; i0 += WAVE) {
+                int i = i0 + lane;
+                float s = i < n ? b.s[i] : -INFINITY;
+                bool in = i < n && s >= lo2 && s <= hi2;
+                uint64_t m = __ballot(in);
+                if (in) {
+                    int p = base + (int)mbcnt(m);
+                    b.xs[p] = s;
+                    b.xj[p] = b.j[i];
+                }
+                base += __popcll(m);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            float ms = lane < cnt_b ? b.xs[lane] : -INFINITY;
+            int mj = lane < cnt_b ? b.xj[lane] : 0x7fffffff;
+            int rank = 0, gt = 0;
+            for (int q = 0; q < cnt_b; ++q) {
+                float os = __shfl(ms, q);
+                int oj = __shfl(mj, q);
+                rank += (os > ms || (os == ms && oj < mj)) ? 1 : 0;
+                gt += os > ms ? 1 : 0;
+            }
+            uint64_t hit = __ballot(lane < cnt_b && rank == kk - 1);
+            int lh = __ffsll((long long)hit) - 1;
+            T = __shfl(ms, lh);
+            int gtT = __shfl(gt, lh);       // entries of the bin strictly above T
+            need = kk - gtT;
+            break;
+        }
+        lo = lo2;
+        hi = hi2;
+    }
+    // in-order compaction
+    int out = 0, ties = 0;
+    for (int i0 = 0; i0 < n; i0 += WAVE) {
+        int i = i0 + lane;
+        bool in = i < n;
+        float s = in ? b.s[i] : -INFINITY;
+        int j = in ? b.j[i] : 0;
+        bool eq = in && s == T;
+        uint64_t em = __ballot(eq);
+        int tr = ties + (int)mbcnt(em);
+        ties += __popcll(em);
+        bool keep = in && (s > T || (eq && tr < need));
+        uint64_t km = __ballot(keep);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        if (keep) {
+            int p = out + (int)mbcnt(km);
+            b.s[p] = s;
+            b.j[p] = j;
+        }
+        out += __popcll(km);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return T;
+}
+
+template <typename T, int DI, int HT>
+__global__ __launch_bounds__(256, 1) void index_topk_kernel(const T* __restrict__ qi,
+                                                            const T* __restrict__ ki,
+                                                            const float* __restrict__ w,
+                                                            int32_t* __restrict__ idx,
+                                                            float* __restrict__ score, int S,
+                                                            int HI, int r, int nc, int kp, int cap)
+{
+    constexpr int KS = DI / 32;            // k-steps of 32
+    constexpr int ROW = DI + 16 / sizeof(T) * 1;   // LDS row stride (elements), one 16-B pad
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    T* ktile = reinterpret_cast<T*>(smem);
+    char* wbase = smem + (size_t)KT * ROW * sizeof(T);
+    const int wave = threadIdx.x / WAVE, lane = lane_id();
+    const int g = lane / 16, n16 = lane % 16;
+    const size_t per_wave = (size_t)cap * 8 + HBINS * 4 + 64 * 8;
+    char* mine = wbase + per_wave * wave;
+    WaveBufs bufs;
+    bufs.s = reinterpret_cast<float*>(mine);
+    bufs.j = reinterpret_cast<int*>(mine + (size_t)cap * 4);
+    bufs.hist = reinterpret_cast<unsigned*>(mine + (size_t)cap * 8);
+    bufs.xs = reinterpret_cast<float*>(mine + (size_t)cap * 8 + HBINS * 4);
+    bufs.xj = reinterpret_cast<int*>(mine + (size_t)cap * 8 + HBINS * 4 + 64 * 4);
+
+    const int bi = blockIdx.y;
+    const int t = blockIdx.x * 4 + wave;
+    const bool active = t < S;
+    const int nv = active ? min((t + 1) / r, nc) : 0;
+    const int t_last = min(blockIdx.x * 4 + 3, S - 1);
+    const int nv_max = min((t_last + 1) / r, nc);
+    const int64_t row = (int64_t)bi * S + (active ? t : 0);
+
+    // query operands (A: m = head, k = dim) and per-head weights in C-row layout
+    Frag<T> qa[HT][KS];
+    float wv[HT][4];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const int h = 16 * ht + n16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qa[ht][ks] = (active && h < HI) ? load_frag(qi + (row * HI + h) * DI + 32 * ks + 8 * g)
+                                             : zero_frag<T>();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hh = 16 * ht + 4 * g + i;
+            wv[ht][i] = (active && hh < HI) ? w[row * HI + hh] : 0.f;
+        }
+    }
+
+    const T* kb = ki + (int64_t)bi * nc * DI;
+    float tau = -INFINITY;
+    int cnt = 0;
+    constexpr int CH = 16 / sizeof(T);               // elements per 16-B chunk
+    constexpr int CHUNKS = KT * DI / CH;
+    for (int j0 = 0; j0 < nv_max; j0 += KT) {
+        __syncthreads();
+        for (int c = threadIdx.x; c < CHUNKS; c += 256) {
+            const int rr = c / (DI / CH), cc = (c % (DI / CH)) * CH;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (j0 + rr < nc) v = *reinterpret_cast<const uint4*>(kb + (int64_t)(j0 + rr) * DI + cc);
+            *reinterpret_cast<uint4*>(ktile + rr * ROW + cc) = v;
+        }
+        __syncthreads();
+        if (j0 >= nv) continue;
+        float my = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            f32x4 acc[HT];
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) acc[ht] = f4zero();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                Frag<T> bf = load_frag(ktile + (16 * st + n16) * ROW + 32 * ks + 8 * g);
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma16(qa[ht][ks], bf, acc[ht]);
+            }
+            float v = 0.f;
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v += wv[ht][i] * fmaxf(acc[ht][i], 0.f);
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            if (g == st) my = v;
+        }
+        my = my + 0.0f;                        // -0 -> +0: one value per tie class
+        const int j = j0 + lane;
+        const bool valid = j < nv;
+        const int ntile = min(KT, nv - j0);
+        if (cnt + ntile > cap) {
+            tau = select_keep(bufs, cnt, kp);
+            cnt = kp;
+        }
+        const bool take = valid && my > tau;
+        const uint64_t m = __ballot(take);
+        if (take) {
+            const int p = cnt + (int)mbcnt(m);
+            bufs.s[p] = my;
+            bufs.j[p] = j;
+        }
+        cnt += __popcll(m);
+    }
+    if (!active) return;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int kk = min(kp, nv);
+    if (cnt > kk) {
+        select_keep(bufs, cnt, kk);
+        cnt = kk;
+    }
+    int32_t* orow = idx + row * kp;
+    float* srow = score ? score + row * kp : nullptr;
+    for (int i = lane; i < kp; i += WAVE) {
+        const bool have = i < cnt;
+        orow[i] = have ? bufs.j[i] : -1;
+        if (srow) srow[i] = have ? bufs.s[i] : -INFINITY;
+    }
+}
+
+template <typename T, int DI, int HT>
+hipError_t launch_index(const IndexArgs& p, hipStream_t st)
+{
+    const int kp = p.kp;
+    const int cap = index_topk_cap(p, sizeof(T) == 2);
+    if (cap == 0) return hipErrorInvalidValue;
+    const size_t lds = topk_lds_bytes(p.DI, sizeof(T), cap);
+    auto kern = index_topk_kernel<T, DI, HT>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    dim3 grid((p.S + 3) / 4, p.b);
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const T*)p.qi, (const T*)p.ki, p.w, p.idx,
+                       p.score, p.S, p.HI, p.r, p.nc, kp, cap);
+    return hipGetLastError();
+}
+
+template <typename T, int DI>
+hipError_t launch_index_ht(const IndexArgs& p, hipStream_t st)
+{
+    if (p.HI <= 16) return launch_index<T, DI, 1>(p, st);
+    return launch_index<T, DI, 4>(p, st);
+}
+
+}  // namespace
+
+hipError_t index_topk(const IndexArgs& p, bool bf16, hipStream_t st)
+{
+    if (p.kp == 0 || p.S == 0) return hipSuccess;
+    switch (p.DI) {
+    case 32: return bf16 ? launch_index_ht<bf16_t, 32>(p, st) : launch_index_ht<float, 32>(p, st);
+    case 64: return bf16 ? launch_index_ht<bf16_t, 64>(p, st) : launch_index_ht<float, 64>(p, st);
+    case 128: return bf16 ? launch_index_ht<bf16_t, 128>(p, st) : launch_index_ht<float, 128>(p, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Candidate-buffer capacity per query (entries).  The whole valid prefix
+// when it fits on chip (no cut ever happens), else twice K' rounded up to a
+// tile, which leaves room for a full tile after every cut.  The environment
+// variable CSA_TOPK_BUFFER lowers the capacity (never below that minimum) so
+// that tests can drive the cut path at small sizes.  0 = does not fit.
+int index_topk_cap(const IndexArgs& p, bool bf16)
+{
+    const int elem = bf16 ? 2 : 4;
+    const int nc64 = (p.nc + 63) / 64 * 64, kp64 = (p.kp + 63) / 64 * 64;
+    int cap = nc64;
+    const char* env = std::getenv("CSA_TOPK_BUFFER");
+    const int env_cap = env ? std::atoi(env) : 0;
+    if (env_cap > 0 && env_cap < cap) cap = env_cap;
+    if (cap < nc64 && cap < 2 * kp64) cap = 2 * kp64;
+    cap = (cap + 63) / 64 * 64;
+    if (topk_lds_bytes(p.DI, elem, cap) > (size_t)INDEX_LDS_LIMIT) cap = 2 * kp64;
+    if (topk_lds_bytes(p.DI, elem, cap) > (size_t)INDEX_LDS_LIMIT) return 0;
+    return cap;
+}
+
+}  // namespace csa

@@ -1,0 +1,173 @@
+/*
+ * csa.h -- C ABI of libcsa, the MI355X (gfx950) HIP library for the
+ * compressed sparse attention (CSA) hot path:
+ *
+ *   compress -> index scores + streaming top-k -> sparse attention forward
+ *   (window + selected compressed rows + sink, LSE out) -> sparse attention
+ *   backward (fp32 scatter) -> compressor backward.
+ *
+ * Sources, cited by page title and review thread / commit message:
+ *  - Megatron-LM PR #6400 "Add unfused SBHD compressed sparse attention":
+ *    the compressor's fp32 softmax pooling, the gather/scatter into the compact
+ *    KV, the per-head sink and head-count checks, the compressed causal mask
+ *    (block j invalid for query t iff j >= (t+1)//ratio), the validity
+ *    re-check with -1 padding, and the ratio dispatch of the sparse core.
+ *  - torchtitan PR #4452 "Refactor Deepseek v4 to use Attention Gym's
+ *    Compressed Sparse Attention": one fused softmax over the window, the
+ *    selected compressed rows and the sink, returning the per-head LSE; an
+ *    explicit softmax scale; the backward as the sum of a probability x
+ *    grad-output product and a scaled grad-score x query product.
+ *  - Megatron-LM PR #7152 "Add the min-memory DSA attention kernels": scores
+ *    reduced tile by tile (memory O(tile), never O(sq * n_kv)); one full
+ *    top-k as the tie rule; selected indices and scores ordered by position;
+ *    selected gradients scattered back to positions in fp32; an all-or-nothing
+ *    gradient gate.
+ *
+ * CONVENTIONS (all entry points)
+ *  - Device pointers.  Every tensor argument is a device pointer to memory the
+ *    caller allocated and owns.  The library allocates nothing in these calls,
+ *    keeps no device state between calls, and never synchronises the stream;
+ *    work is enqueued on `stream` (a hipStream_t; NULL = the legacy default
+ *    stream).  Calls on different streams may run concurrently.
+ *  - Layout.  Contiguous, row-major, batch first:
+ *      q-like  [b, sq, h, d]         (q, out, dout, dq)
+ *      kv-like [b, sq, d]            (kv, x, dkv, dx)
+ *      z       [b, sq, z_channels]   (dz)
+ *      c       [b, n_c, d]           (c, c32, dc),   n_c = sq / ratio (floor)
+ *      q_i     [b, sq, idx_heads, idx_dim];  k_i [b, n_c, idx_dim]
+ *      w       [b, sq, idx_heads];   lse [b, sq, h];  sink, dsink [h]
+ *      idx, score [b, sq, K'],  K' = min(topk, n_c)
+ *    Base pointers must be 16-byte aligned.
+ *  - Dtypes.  `dtype` is CSA_F32 or CSA_BF16 and applies to q, kv, c, x, z,
+ *    q_i, k_i, out, dout, dq.  Always fp32: w, sink, lse, score, c32, dkv,
+ *    dc, dsink, dx, dz.  All arithmetic is fp32 (scores, softmax, accumulation).
+ *  - Token positions.  Query t sees the raw rows u in [max(0, t-window+1), t]
+ *    (its window, inclusive of itself) and compressed block j iff
+ *    j < n_valid(t) = (t+1) / ratio.  Block j covers tokens [j*ratio,
+ *    (j+1)*ratio); its pooling span is [(j+1)*ratio - span, (j+1)*ratio)
+ *    clipped at 0.
+ *  - Errors.  Every entry point validates its arguments before enqueuing any
+ *    work and returns CSA_OK or a negative code; csa_last_error() then returns
+ *    a message for the calling thread.  Nothing throws or aborts across the ABI.
+ *    Values of floating-point inputs are not checked (NaN/Inf give unspecified
+ *    results).
+ *  - Accumulating outputs (dkv, dc, dsink, dx, dz) are zero-filled on the
+ *    stream by the call, then accumulated (overwrite semantics).
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 };
+
+enum csa_status {
+    CSA_OK = 0,
+    CSA_ERR_ARG = -1,          /* null pointer, non-positive or inconsistent size */
+    CSA_ERR_SHAPE = -2,        /* shapes disagree (e.g. sink length != h)         */
+    CSA_ERR_DTYPE = -3,        /* unknown dtype                                   */
+    CSA_ERR_UNSUPPORTED = -4,  /* valid but outside what the kernels implement    */
+    CSA_ERR_WORKSPACE = -5,    /* workspace missing or too small                  */
+    CSA_ERR_HIP = -6           /* the HIP runtime reported an error on launch     */
+};
+
+/* Problem sizes shared by all calls.
+ *  b, sq      batch and sequence length (>= 1)
+ *  h, d       query heads on one shared KV head, head dim (key dim == value dim)
+ *  ratio      compress ratio r >= 1; span L >= 1 is the pooling span (L == r:
+ *             non-overlapping; L == 2r: overlapping)
+ *  window     sliding window W >= 1
+ *  idx_heads, idx_dim, topk   indexer heads, indexer dim and top-k (topk >= 1
+ *             when the indexer is used)
+ * Supported by the kernels: d in {64, 128, 512}; 1 <= h <= 64; idx_dim in
+ * {32, 64, 128}; 1 <= idx_heads <= 64; K' <= 2048.  Others: CSA_ERR_UNSUPPORTED. */
+typedef struct csa_dims {
+    int32_t b, sq, h, d, ratio, span, window, idx_heads, idx_dim, topk;
+} csa_dims;
+
+/* Compressor forward (Megatron-LM PR #6400, review thread on the pooling
+ * weights).  For block j < n_c and channel c:
+ *   alpha_u = softmax over u in span(j) of z[u, c]   (z[u, 0] if z_channels == 1)
+ *   c32[j, c] = sum_u alpha_u * x[u, c]               (fp32 weights and sum)
+ *   c[j, c]   = c32[j, c] rounded once to dtype.
+ * z_channels is 1 or d.  c32 may be NULL. */
+int csa_compress(const csa_dims* dims, int dtype, const void* x, const void* z, int z_channels,
+                 void* c, float* c32, void* stream);
+
+/* Compressor backward: the gradient of the pooling above given dc (fp32,
+ * [b, n_c, d]); the rounding cast is treated as the identity.
+ *   dx[u, c] = sum_j alpha_{j,u,c} dc[j, c]
+ *   dz[u, c] = sum_j alpha_{j,u,c} dc[j, c] (x[u, c] - c32[j, c])  (summed over c if z_channels == 1)
+ * Rows u >= n_c * ratio receive zero. */
+int csa_compress_bwd(const csa_dims* dims, int dtype, const void* x, const void* z,
+                     int z_channels, const float* dc, float* dx, float* dz, void* stream);
+
+/* Workspace bytes csa_index_topk needs (0: scores never leave the chip). */
+size_t csa_index_topk_workspace(const csa_dims* dims);
+
+/* Learned indexer + streaming top-k (Megatron-LM PR #6400, causal-mask thread;
+ * Megatron-LM PR #7152, routing commit messages).
+ *   I[t, j] = sum_h w[t, h] * relu(q_i[t, h] . k_i[j])   for j < n_valid(t)
+ * Scores are computed tile by tile on the chip and reduced into a running
+ * top-k; the [sq, n_c] score matrix is never written anywhere.  Row (b, t) of
+ * idx receives the K' = min(topk, n_c) largest valid scores ordered by
+ * (score desc, index asc), emitted in ascending index, then -1 for the
+ * K' - min(K', n_valid(t)) remaining slots.  score (nullable) receives the
+ * fp32 scores aligned with idx (-inf on -1 slots).  w is fp32 and already
+ * holds any softmax scale of the indexer.  ws may be NULL when
+ * csa_index_topk_workspace() returns 0. */
+int csa_index_topk(const csa_dims* dims, int dtype, const void* q_i, const void* k_i,
+                   const float* w, int32_t* idx, float* score, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* Sparse attention forward (Megatron-LM PR #6400 gather and sink threads;
+ * torchtitan PR #4452 fused operator).  For query (b, t) and head h the
+ * candidate rows are its window rows kv[b, u] and one row c[b, j] per slot
+ * of idx[b, t, :] with 0 <= j < n_valid(t) (other slots, e.g. -1, are
+ * skipped).  idx == NULL attends every valid compressed row (dense mode, the
+ * HCA layer); c == NULL attends the window only (then idx must be NULL).
+ *   l   = scale * <q[t, h], row>
+ *   lse = log(exp(sink[h]) + sum exp(l))   (no sink term if sink == NULL)
+ *   out[t, h] = sum exp(l - lse) * row     (the row is both key and value)
+ * out has dtype, lse is fp32. */
+int csa_sparse_attn_fwd(const csa_dims* dims, int dtype, const void* q, const void* kv,
+                        const void* c, const int32_t* idx, const float* sink, float scale,
+                        void* out, float* lse, void* stream);
+
+/* Workspace bytes csa_sparse_attn_bwd needs. */
+size_t csa_sparse_attn_bwd_workspace(const csa_dims* dims);
+
+/* Sparse attention backward: the gradient of csa_sparse_attn_fwd given dout,
+ * with out and lse from that forward (same inputs).  With
+ * Delta = <dout, out> and dl = P (<dout, row> - Delta):
+ *   dq[t, h] = scale * sum dl * row                          (dtype)
+ *   each candidate row gets P dout[t, h] + scale * dl q[t, h], scattered in
+ *   fp32 into dkv[b, u] (window rows) or dc[b, j] (compressed rows);
+ *   repeated indices across queries accumulate without loss of fp32 precision
+ *   dsink[h] = -sum_{b,t} exp(sink[h] - lse) Delta          (fp32)
+ * Gradient gate (Megatron-LM PR #7152): dq, dkv and dc are all non-NULL, or
+ * all NULL (no-op apart from dsink); dc must be NULL when c is NULL.  dsink
+ * may be NULL (required NULL when sink is NULL).  lse gradient is zero. */
+int csa_sparse_attn_bwd(const csa_dims* dims, int dtype, const void* q, const void* kv,
+                        const void* c, const int32_t* idx, const float* sink, float scale,
+                        const void* out, const float* lse, const void* dout, void* dq,
+                        float* dkv, float* dc, float* dsink, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* csa_last_error(void);
+
+/* CSA_ABI_VERSION of the loaded library. */
+int csa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H_ */

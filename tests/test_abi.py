@@ -1,0 +1,119 @@
+"""The C ABI boundary without a GPU: the library loads, exports every symbol
+include/csa.h declares, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_sparse_attention_softmax_amd as csa
+from compressed_sparse_attention_softmax_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+
+def _lib():
+    if not os.path.exists(csa.LIB_PATH):
+        pytest.skip("libcsa.so not built")
+    return csa.load()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_exactly_the_bound_names():
+    assert header_functions() == sorted(_abi.EXPORTS)
+
+
+def test_library_exports_every_header_symbol():
+    lib = _lib()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert lib.csa_version() == 1
+
+
+def test_dims_struct_matches_header():
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct csa_dims \{(.*?)\} csa_dims;", src, re.S).group(1)
+    names = re.findall(r"([a-z_]+)[,;]", body.replace("int32_t", ""))
+    assert names == [f[0] for f in _abi.csa_dims._fields_]
+    assert ctypes.sizeof(_abi.csa_dims) == 40
+
+
+def _d(**kw):
+    base = dict(b=1, sq=64, h=4, d=64, ratio=4, span=4, window=8, idx_heads=2, idx_dim=32, topk=8)
+    base.update(kw)
+    return _abi.csa_dims(*[base[f[0]] for f in _abi.csa_dims._fields_])
+
+
+P = ctypes.c_void_p(16)   # a non-NULL address that is never dereferenced (validation fails first)
+N = None
+
+
+@pytest.mark.parametrize("fn,args,code", [
+    ("csa_compress", lambda: (None, 0, P, P, 64, P, N, N), -1),
+    ("csa_compress", lambda: (ctypes.byref(_d()), 7, P, P, 64, P, N, N), -3),
+    ("csa_compress", lambda: (ctypes.byref(_d(ratio=0)), 0, P, P, 64, P, N, N), -1),
+    ("csa_compress", lambda: (ctypes.byref(_d(d=96)), 0, P, P, 96, P, N, N), -4),
+    ("csa_compress", lambda: (ctypes.byref(_d()), 0, P, P, 5, P, N, N), -2),
+    ("csa_compress", lambda: (ctypes.byref(_d()), 0, N, P, 64, P, N, N), -1),
+    ("csa_compress_bwd", lambda: (ctypes.byref(_d(sq=0)), 0, P, P, 64, P, P, P, N), -1),
+    ("csa_index_topk", lambda: (ctypes.byref(_d(topk=0)), 0, P, P, P, P, N, N, 0, N), -1),
+    ("csa_index_topk", lambda: (ctypes.byref(_d(idx_dim=48)), 0, P, P, P, P, N, N, 0, N), -4),
+    ("csa_index_topk", lambda: (ctypes.byref(_d(idx_heads=65)), 0, P, P, P, P, N, N, 0, N), -4),
+    ("csa_index_topk", lambda: (ctypes.byref(_d(sq=65536, topk=4096)), 1, P, P, P, P, N, N, 0, N), -4),
+    ("csa_index_topk", lambda: (ctypes.byref(_d()), 0, P, P, N, P, N, N, 0, N), -1),
+    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d(h=65)), 0, P, P, P, P, N, ctypes.c_float(1.0), P, P, N), -4),
+    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d(window=0)), 0, P, P, P, P, N, ctypes.c_float(1.0), P, P, N), -1),
+    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d()), 0, P, P, N, P, N, ctypes.c_float(1.0), P, P, N), -1),
+    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d()), 0, P, P, P, P, N, ctypes.c_float(float("nan")), P, P, N), -1),
+    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d(d=512)), 0, P, P, P, P, N, ctypes.c_float(1.0), P, P, N), -4),
+    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d()), 0, P, P, P, P, N, ctypes.c_float(1.0), N, P, N), -1),
+])
+def test_validation_errors(fn, args, code):
+    lib = _lib()
+    rc = getattr(lib, fn)(*args())
+    assert rc == code, (fn, rc, lib.csa_last_error())
+    assert lib.csa_last_error().decode().startswith(fn)
+
+
+def _bwd(dq, dkv, dc, dsink, sink=P, c=P):
+    lib = _lib()
+    return lib.csa_sparse_attn_bwd(ctypes.byref(_d()), 0, P, P, c, P, sink, ctypes.c_float(1.0), P, P, P,
+                                   dq, dkv, dc, dsink, N, 0, N)
+
+
+@pytest.mark.parametrize("missing", ["dq", "dkv", "dc"])
+def test_gradient_gate_is_all_or_nothing(missing):
+    args = dict(dq=P, dkv=P, dc=P)
+    args[missing] = N
+    rc = _bwd(args["dq"], args["dkv"], args["dc"], N)
+    assert rc == -1
+    assert missing in _lib().csa_last_error().decode()
+
+
+def test_gradient_gate_all_null_is_a_noop():
+    assert _bwd(N, N, N, N) == 0
+
+
+def test_dsink_requires_sink():
+    assert _bwd(N, N, N, P, sink=N) == -1
+
+
+def test_dc_requires_compressed_rows():
+    assert _bwd(P, P, P, N, c=N) == -1
+
+
+def test_workspace_queries_are_zero():
+    lib = _lib()
+    assert lib.csa_index_topk_workspace(ctypes.byref(_d())) == 0
+    assert lib.csa_sparse_attn_bwd_workspace(ctypes.byref(_d())) == 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="libcsa.so not found"):
+        _abi.load(str(tmp_path / "missing.so"))

@@ -1,0 +1,223 @@
+"""GPU parity of each hot-path step against the fp64 oracle, at sizes the
+oracle finishes in seconds that still span several tiles and a ragged tail.
+
+Every call goes through the C ABI (``libcsa.so``).  Inputs come from
+``csa_synth``; expected values only from ``oracle``.  Each stage is fed the
+same input values on both sides (stage isolation: the attention stage gets
+an index list drawn by the input generator or computed by the oracle, never
+one computed by the GPU).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import csa_synth
+import oracle
+from parity import check_close, check_topk_rows, f64, say, tol_of
+
+pytestmark = pytest.mark.gpu
+
+W = csa_synth.WORKLOADS
+TINY = W["tiny_f32"]
+# bf16 CSA-4 layer at reduced length: 1030 tokens (ragged vs ratio and tiles)
+CSA4_SMALL = W["csa4_s4096"].replace(sq=1030, topk=96)
+D512_SMALL = W["csa4_d512_s8192"].replace(sq=300, topk=40)
+HCA_SMALL = W["hca128_s16384"].replace(sq=1100)
+
+
+def dev(d):
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def dims(wl, **kw):
+    import compressed_sparse_attention_softmax_amd as csa
+    return csa.dims_of(wl.replace(**kw) if kw else wl)
+
+
+# ----------------------------------------------------------------- compressor
+COMPRESS_CASES = [
+    ("tiny_f32", TINY),
+    ("csa4_bf16_overlap", CSA4_SMALL),
+    ("csa4_bf16_rowscore", CSA4_SMALL.replace(z_channels=1)),
+    ("d512_bf16", D512_SMALL),
+    ("hca128_bf16", HCA_SMALL),
+    ("f32_overlap_span12", TINY.replace(sq=203, span=12)),
+    ("shorter_than_ratio", TINY.replace(sq=3)),
+]
+
+
+@pytest.mark.parametrize("name,wl", COMPRESS_CASES, ids=[c[0] for c in COMPRESS_CASES])
+def test_compress_fwd_bwd(gpu, name, wl):
+    csa = gpu
+    say(f"[compress] {name} sq={wl.sq} d={wl.d} r={wl.ratio} L={wl.span} zc={wl.z_channels} {wl.dtype}")
+    inp = csa_synth.make_inputs(wl, 11, device="cuda", parts=("compress",))
+    dm = csa.dims_of(wl)
+    b, S, D, nc = wl.b, wl.sq, wl.d, wl.n_c
+    c = torch.empty(b, nc, D, dtype=wl.torch_dtype, device="cuda")
+    c32 = torch.empty(b, nc, D, dtype=torch.float32, device="cuda")
+    csa.csa_compress(dm, inp["x"], inp["z"], c, c32)
+    g = torch.Generator(device="cuda").manual_seed(99)
+    dc = torch.randn(b, nc, D, generator=g, device="cuda")
+    dx = torch.full((b, S, D), 7.0, device="cuda")          # garbage: must be overwritten
+    dz = torch.full((b, S, wl.z_channels), 7.0, device="cuda")
+    csa.csa_compress_bwd(dm, inp["x"], inp["z"], dc, dx, dz)
+    torch.cuda.synchronize()
+    ref = oracle.compress(f64(inp["x"]), f64(inp["z"]), wl.ratio, wl.span)
+    tol = tol_of(wl.torch_dtype)
+    check_close("c32", c32, ref, tol)
+    check_close("c", c, ref, tol)
+    rdx, rdz = oracle.compress_bwd(f64(inp["x"]), f64(inp["z"]), f64(dc), wl.ratio, wl.span)
+    check_close("dx", dx, rdx, tol)
+    check_close("dz", dz, rdz, tol)
+
+
+# ------------------------------------------------------------ indexer / top-k
+def _index_case(wl, seed, rows=None, **over):
+    import compressed_sparse_attention_softmax_amd as csa
+    inp = csa_synth.make_inputs(wl, seed, device="cuda", parts=("index",))
+    inp.update({k: v for k, v in over.items()})
+    dm = csa.dims_of(wl)
+    kp = wl.kprime
+    idx = torch.full((wl.b, wl.sq, kp), -7, dtype=torch.int32, device="cuda")
+    sc = torch.empty(wl.b, wl.sq, kp, dtype=torch.float32, device="cuda")
+    assert csa.csa_index_topk_workspace(dm) == 0
+    csa.csa_index_topk(dm, inp["q_i"], inp["k_i"], inp["w"], idx, sc)
+    torch.cuda.synchronize()
+    rows = oracle.all_rows(wl.b, wl.sq) if rows is None else rows
+    qi, ki, w = f64(inp["q_i"]), f64(inp["k_i"]), f64(inp["w"])
+    oidx, osc, dense = oracle.index_topk(qi, ki, w, wl.ratio, wl.topk, rows=rows)
+    gi = idx.cpu().numpy()[rows[:, 0], rows[:, 1]]
+    gs = sc.cpu().numpy()[rows[:, 0], rows[:, 1]]
+    return gi, gs, oidx, dense, rows
+
+
+INDEX_CASES = [
+    ("tiny_f32", TINY, None),
+    ("csa4_bf16", CSA4_SMALL.replace(sq=1536), None),
+    ("csa4_bf16_b2_ragged", CSA4_SMALL.replace(b=2, sq=1027, topk=50), None),
+    ("streaming_cuts", CSA4_SMALL.replace(sq=4096, topk=100), "256"),
+    ("idx_dim64_heads40", CSA4_SMALL.replace(idx_heads=40, idx_dim=64, sq=900, topk=70), None),
+]
+
+
+@pytest.mark.parametrize("name,wl,cap", INDEX_CASES, ids=[c[0] for c in INDEX_CASES])
+def test_index_topk(gpu, name, wl, cap, monkeypatch):
+    say(f"[index_topk] {name} b={wl.b} sq={wl.sq} HI={wl.idx_heads} DI={wl.idx_dim} K={wl.topk} cap={cap}")
+    if cap:
+        monkeypatch.setenv("CSA_TOPK_BUFFER", cap)
+    gi, gs, oidx, dense, rows = _index_case(wl, 21)
+    exact = check_topk_rows(gi, gs, oidx, dense, rows[:, 1], wl.ratio, wl.n_c, wl.kprime,
+                            score_tol=tol_of(wl.torch_dtype))
+    say(f"  rows identical to the oracle: {exact}/{len(rows)}")
+
+
+def test_index_topk_exact_integer_scores_and_ties(gpu, monkeypatch):
+    # small integer inputs make every fp32 score exact, so the GPU must match
+    # the oracle bit for bit, including the lowest-index rule on exact ties
+    monkeypatch.setenv("CSA_TOPK_BUFFER", "128")
+    wl = CSA4_SMALL.replace(sq=2048, topk=40, idx_heads=8)
+    g = torch.Generator().manual_seed(5)
+    qi = torch.randint(-2, 3, (1, wl.sq, 8, 128), generator=g).to(torch.bfloat16)
+    ki = torch.randint(-1, 2, (1, wl.n_c, 128), generator=g).to(torch.bfloat16)
+    ki[0, 100:140] = ki[0, 7]                                   # many identical keys
+    w = (torch.randint(-2, 5, (1, wl.sq, 8), generator=g).float() / 4)
+    gi, gs, oidx, dense, rows = _index_case(wl, 0, q_i=qi.cuda(), k_i=ki.cuda(), w=w.cuda())
+    np.testing.assert_array_equal(gi, oidx)
+    np.testing.assert_array_equal(gs[gi >= 0], dense[np.nonzero(gi >= 0)[0], gi[gi >= 0]])
+
+
+def test_index_topk_all_zero_keys(gpu):
+    wl = CSA4_SMALL.replace(sq=600, topk=30)
+    ki = torch.zeros(1, wl.n_c, 128, dtype=torch.bfloat16, device="cuda")
+    gi, gs, oidx, dense, rows = _index_case(wl, 3, k_i=ki)
+    np.testing.assert_array_equal(gi, oidx)
+    assert np.all(gs[gi >= 0] == 0.0) and not np.any(np.signbit(gs[gi >= 0]))
+
+
+# ------------------------------------------------------------------ attention
+def _attn_case(wl, seed, idx_mode="random", with_sink=True, window_only=False, junk=False):
+    import compressed_sparse_attention_softmax_amd as csa
+    inp = csa_synth.make_inputs(wl, seed, device="cuda", parts=("attn", "compress", "bwd"),
+                                with_sink=with_sink)
+    b, S, H, D, nc = wl.b, wl.sq, wl.h, wl.d, wl.n_c
+    # compressed rows: the oracle's pooling, cast once to the working dtype
+    c = None
+    if not window_only:
+        c64 = oracle.compress(f64(inp["x"]), f64(inp["z"]), wl.ratio, wl.span)
+        c = torch.tensor(c64).to(wl.torch_dtype).cuda()
+    idx = None
+    if not window_only and idx_mode != "dense":
+        if idx_mode == "random":
+            idx = csa_synth.random_topk_indices(wl, seed + 1)
+        elif idx_mode == "block0":
+            idx = torch.full((b, S, wl.kprime), -1, dtype=torch.int32)
+            idx[:, wl.ratio - 1:, 0] = 0
+        if junk:
+            g = torch.Generator().manual_seed(seed)
+            idx = idx.clone()
+            kp = wl.kprime
+            for bi in range(b):
+                for t in range(0, S, 3):
+                    nv = (t + 1) // wl.ratio
+                    if kp >= 3 and nv >= 2:
+                        idx[bi, t, 1] = idx[bi, t, 0]               # duplicate within a row
+                        idx[bi, t, 2] = -1                          # hole in the middle
+                    if kp >= 1:
+                        idx[bi, t, kp - 1] = nv + int(torch.randint(0, 5, (1,), generator=g))  # not yet valid
+        idx = idx.cuda()
+    dm = csa.dims_of(wl)
+    dtype = wl.torch_dtype
+    out = torch.empty(b, S, H, D, dtype=dtype, device="cuda")
+    lse = torch.empty(b, S, H, dtype=torch.float32, device="cuda")
+    csa.csa_sparse_attn_fwd(dm, inp["q"], inp["kv"], c, idx, inp["sink"], wl.scale, out, lse)
+    dq = torch.empty_like(out)
+    dkv = torch.full((b, S, D), 3.0, device="cuda")
+    dc = torch.full((b, nc, D), 3.0, device="cuda") if c is not None else None
+    dsink = torch.full((H,), 3.0, device="cuda") if with_sink else None
+    csa.csa_sparse_attn_bwd(dm, inp["q"], inp["kv"], c, idx, inp["sink"], wl.scale, out, lse, inp["do"],
+                            dq, dkv, dc, dsink)
+    torch.cuda.synchronize()
+    rows = oracle.all_rows(b, S)
+    q = f64(inp["q"]).reshape(b * S, H, D)
+    kv = f64(inp["kv"])
+    cc = f64(c) if c is not None else np.zeros((b, 0, D))
+    ii = None if idx is None else idx.cpu().numpy().reshape(b * S, -1)
+    sink = None if inp["sink"] is None else f64(inp["sink"])
+    window = wl.window
+    ratio = wl.ratio
+    ro, rl = oracle.attn_fwd(q, kv, cc, ii, sink, wl.scale, window, ratio, rows)
+    rdq, rdkv, rdc, rds = oracle.attn_bwd(q, kv, cc, ii, sink, wl.scale, window, ratio, rows,
+                                          f64(inp["do"]).reshape(b * S, H, D))
+    tol = tol_of(dtype)
+    check_close("out", out.reshape(b * S, H, D), ro, tol)
+    check_close("lse", lse.reshape(b * S, H), rl, tol)
+    check_close("dq", dq.reshape(b * S, H, D), rdq, tol)
+    check_close("dkv", dkv, rdkv, tol)
+    if dc is not None:
+        check_close("dc", dc, rdc, tol)
+    if dsink is not None:
+        check_close("dsink", dsink, rds, tol)
+
+
+ATTN_CASES = [
+    ("tiny_f32", TINY, {}),
+    ("tiny_f32_nosink", TINY, dict(with_sink=False)),
+    ("tiny_f32_window1", TINY.replace(window=1), {}),
+    ("tiny_f32_junk_idx", TINY, dict(junk=True)),
+    ("csa4_bf16", CSA4_SMALL.replace(sq=640), {}),
+    ("csa4_bf16_b2_h48", CSA4_SMALL.replace(b=2, sq=333, h=48, topk=40), {}),
+    ("csa4_bf16_junk_idx", CSA4_SMALL.replace(sq=400, topk=40), dict(junk=True)),
+    ("csa4_bf16_block0_repeat", CSA4_SMALL.replace(sq=700, topk=8), dict(idx_mode="block0")),
+    ("csa4_bf16_dense", CSA4_SMALL.replace(sq=500), dict(idx_mode="dense")),
+    ("csa4_bf16_window_only", CSA4_SMALL.replace(sq=300), dict(window_only=True)),
+    ("d512_bf16", D512_SMALL, {}),
+    ("hca128_bf16_dense", HCA_SMALL, dict(idx_mode="dense")),
+]
+
+
+@pytest.mark.parametrize("name,wl,kw", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_sparse_attention_fwd_bwd(gpu, name, wl, kw):
+    say(f"[attn] {name} b={wl.b} sq={wl.sq} h={wl.h} d={wl.d} W={wl.window} r={wl.ratio} K={wl.topk} {kw}")
+    _attn_case(wl, 31, **kw)

@@ -1,0 +1,108 @@
+"""Parity at the five full workload sizes, in the launch configuration the
+benchmark times (one pass of ``pipeline.forward`` / ``pipeline.backward``).
+
+* compressor forward: every output row;
+* indexer + top-k: sampled query rows (edge positions plus random ones), with
+  the near-tie band rule;
+* attention forward: the sampled rows whose top-k list equals the oracle's;
+* attention backward: the backward is linear in dO, so a dO that is zero
+  except on the sampled rows makes every gradient (dq rows, all of dkv, dc,
+  dsink) computable by the oracle from those rows alone;
+* compressor backward: chained from each side's own dc.
+"""
+import numpy as np
+import pytest
+import torch
+
+import csa_synth
+import oracle
+from parity import check_close, check_topk_rows, f64, sample_rows, say, tol_of
+
+pytestmark = pytest.mark.gpu
+
+N_ROWS = {"tiny_f32": 256, "csa4_s4096": 96, "csa4_d512_s8192": 48, "hca128_s16384": 48,
+          "csa4_s65536_skew": 40}
+N_BWD_ROWS = {"tiny_f32": 256, "csa4_s4096": 48, "csa4_d512_s8192": 24, "hca128_s16384": 24,
+              "csa4_s65536_skew": 24}
+
+
+@pytest.mark.parametrize("name", csa_synth.WORKLOAD_ORDER)
+def test_workload_parity(gpu, name):
+    import compressed_sparse_attention_softmax_amd as csa
+    from compressed_sparse_attention_softmax_amd import pipeline
+    wl = csa_synth.WORKLOADS[name]
+    seed = csa_synth.WORKLOAD_SEEDS[name]
+    say(f"[workload] {name} seed={seed} b={wl.b} sq={wl.sq} h={wl.h} d={wl.d} r={wl.ratio} "
+        f"L={wl.span} W={wl.window} K={wl.topk} {wl.dtype}")
+    torch.cuda.empty_cache()
+    inp = csa_synth.make_inputs(wl, seed, device="cuda")
+    dm = csa.dims_of(wl)
+    buf = pipeline.allocate(dm, wl.torch_dtype, wl.z_channels)
+    pipeline.forward(dm, inp, buf, wl.scale)
+    torch.cuda.synchronize()
+    tol = tol_of(wl.torch_dtype)
+    b, S, H, D, nc, r = wl.b, wl.sq, wl.h, wl.d, wl.n_c, wl.ratio
+
+    # compressor: every row
+    c64 = oracle.compress(f64(inp["x"]), f64(inp["z"]), r, wl.span)
+    check_close("c", buf.c, c64, tol)
+    c_or = torch.tensor(c64).to(wl.torch_dtype).double().numpy()   # the single cast to dtype
+    kv = f64(inp["kv"])
+    sink = f64(inp["sink"])
+
+    must = [0, 1, r - 1, r, wl.window - 1, wl.window, S - 1, S - 2]
+    if wl.kprime:
+        must += [wl.kprime * r - 2, wl.kprime * r - 1, wl.kprime * r]
+    rows = sample_rows(b, S, N_ROWS[name], seed, must)
+    rb, rt = rows[:, 0], rows[:, 1]
+
+    if wl.topk > 0:
+        qi = f64(inp["q_i"][rb, rt])
+        w = f64(inp["w"][rb, rt])
+        dense = oracle.index_scores(qi, f64(inp["k_i"]), w, r, rows)
+        oidx, _ = oracle.topk(dense, r, wl.topk, rows)
+        gidx = buf.idx[rb, rt].cpu().numpy()
+        gsc = buf.score[rb, rt].cpu().numpy()
+        exact = check_topk_rows(gidx, gsc, oidx, dense, rt, r, nc, wl.kprime, score_tol=tol)
+        agree = np.array([np.array_equal(gidx[n], oidx[n]) for n in range(len(rows))])
+        say(f"  top-k rows identical: {exact}/{len(rows)}; used for attention: {int(agree.sum())}")
+        assert agree.sum() >= 0.75 * len(rows)
+        rows_a, idx_a = rows[agree], oidx[agree]
+    else:
+        rows_a, idx_a = rows, None
+
+    # attention forward on the agreeing rows
+    ra_b, ra_t = rows_a[:, 0], rows_a[:, 1]
+    q_rows = f64(inp["q"][ra_b, ra_t])
+    o_ref, lse_ref = oracle.attn_fwd(q_rows, kv, c_or, idx_a, sink, wl.scale, wl.window, r, rows_a)
+    check_close("out", buf.out[ra_b, ra_t], o_ref, tol)
+    check_close("lse", buf.lse[ra_b, ra_t], lse_ref, tol)
+
+    # backward with dO restricted to a subset of those rows
+    nb = min(N_BWD_ROWS[name], len(rows_a))
+    sel = np.random.default_rng(seed).choice(len(rows_a), nb, replace=False)
+    sel.sort()
+    rows_b = rows_a[sel]
+    do_m = torch.zeros_like(inp["do"])
+    bb, bt = torch.tensor(rows_b[:, 0]).cuda(), torch.tensor(rows_b[:, 1]).cuda()
+    do_m[bb, bt] = inp["do"][bb, bt]
+    inp_b = dict(inp)
+    inp_b["do"] = do_m
+    inp.pop("q_i", None)
+    pipeline.backward(dm, inp_b, buf, wl.scale)
+    torch.cuda.synchronize()
+    idx_b = None if idx_a is None else idx_a[sel]
+    rdq, rdkv, rdc, rds = oracle.attn_bwd(f64(inp["q"][bb, bt]), kv, c_or, idx_b, sink, wl.scale,
+                                          wl.window, r, rows_b, f64(inp["do"][bb, bt]))
+    check_close("dq (sampled rows)", buf.dq[bb, bt], rdq, tol)
+    other = torch.ones(b, S, dtype=torch.bool, device="cuda")
+    other[bb, bt] = False
+    assert torch.count_nonzero(buf.dq[other]) == 0
+    check_close("dkv", buf.dkv, rdkv, tol)
+    check_close("dc", buf.dc, rdc, tol)
+    check_close("dsink", buf.dsink, rds, tol)
+    rdx, rdz = oracle.compress_bwd(f64(inp["x"]), f64(inp["z"]), rdc, r, wl.span)
+    check_close("dx", buf.dx, rdx, tol)
+    check_close("dz", buf.dz, rdz, tol)
+    del buf, inp, inp_b, do_m
+    torch.cuda.empty_cache()

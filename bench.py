@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of seeded synthetic
+input already resident in HBM:
+
+    csa_compress -> csa_index_topk -> csa_sparse_attn_fwd
+                 -> csa_sparse_attn_bwd -> csa_compress_bwd
+
+all on the current HIP stream.  W untimed warm-up steps, then exactly K timed
+steps bracketed by device synchronisation.  Per-stage durations come from HIP
+events recorded on that same stream inside the timed region.
+
+Prints one JSON line (metric, tokens/s, roofline of the dominant kernel, the
+oracle's CPU baseline on a bounded sample).  ``--gpus N`` with N > 1 exits:
+this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA fwd+bwd tokens/s + TFLOPS (% MFMA peak) at sq=4096, top-k=512, bf16"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0
+STAGES = ["compress", "index_topk", "attn_fwd", "attn_bwd", "compress_bwd"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def count_work(wl, idx):
+    """Algorithmic work of one step: attention fwd = sum_{b,t} h * N_cand(t) * 2 * (d_qk + d_v),
+    bwd = 2 x fwd, indexer = sum_{b,t} n_valid(t) * idx_heads * 2 * idx_dim.  Padding (-1)
+    and not-yet-valid slots are never counted."""
+    import torch
+    dev = idx.device if idx is not None else "cuda"
+    t = torch.arange(wl.sq, device=dev)
+    nwin = torch.clamp(t + 1, max=wl.window)
+    nv = torch.clamp((t + 1) // wl.ratio, max=wl.n_c)
+    if idx is None:
+        ncomp = nv.unsqueeze(0).expand(wl.b, -1)
+    else:
+        ncomp = ((idx >= 0) & (idx < nv.view(1, -1, 1))).sum(dim=2)
+    n_cand = float((nwin.unsqueeze(0) + ncomp).sum().item())
+    fwd = n_cand * wl.h * 2 * (2 * wl.d)
+    indexer = float(nv.sum().item()) * wl.b * wl.idx_heads * 2 * wl.idx_dim if wl.topk > 0 else 0.0
+    return dict(n_cand=n_cand, attn_fwd=fwd, attn_bwd=2 * fwd, indexer=indexer,
+                avg_cand=n_cand / (wl.b * wl.sq))
+
+
+def cpu_baseline(wl, inp, seed, target_rows):
+    """The oracle (as it stands) on a bounded, stratified sample of query rows:
+    indexer scores + top-k + attention fwd + bwd for those rows, plus the
+    compressor fwd + bwd over the whole sequence scaled to the sample."""
+    import numpy as np
+    import torch
+    import oracle
+
+    def f(t):
+        return t.detach().to("cpu", torch.float64).numpy()
+
+    n = min(target_rows, wl.b * wl.sq)
+    tt = np.linspace(0, wl.sq - 1, n // wl.b).round().astype(np.int64)
+    rows = np.array([(bi, t) for bi in range(wl.b) for t in tt], dtype=np.int64)
+    rb, rt = torch.tensor(rows[:, 0]).cuda(), torch.tensor(rows[:, 1]).cuda()
+    x, z, kv = f(inp["x"]), f(inp["z"]), f(inp["kv"])
+    q, do = f(inp["q"][rb, rt]), f(inp["do"][rb, rt])
+    sink = f(inp["sink"])
+    qi = f(inp["q_i"][rb, rt]) if wl.topk > 0 else None
+    w = f(inp["w"][rb, rt]) if wl.topk > 0 else None
+    ki = f(inp["k_i"]) if wl.topk > 0 else None
+    t0 = time.perf_counter()
+    c = oracle.compress(x, z, wl.ratio, wl.span)
+    t_c = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    idx = None
+    if wl.topk > 0:
+        dense = oracle.index_scores(qi, ki, w, wl.ratio, rows)
+        idx, _ = oracle.topk(dense, wl.ratio, wl.topk, rows)
+    oracle.attn_fwd(q, kv, c, idx, sink, wl.scale, wl.window, wl.ratio, rows)
+    _, _, dc, _ = oracle.attn_bwd(q, kv, c, idx, sink, wl.scale, wl.window, wl.ratio, rows, do)
+    t_rows = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.compress_bwd(x, z, dc, wl.ratio, wl.span)
+    t_cb = time.perf_counter() - t0
+    frac = len(rows) / (wl.b * wl.sq)
+    t_total = t_rows + (t_c + t_cb) * frac
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": len(rows) / t_total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{len(rows)} query rows stratified over t (indexer + top-k + attention fwd + bwd, "
+                       f"{t_rows:.1f} s) plus compressor fwd+bwd over all rows ({t_c + t_cb:.1f} s) "
+                       f"scaled by {frac:.4f}; fp64; indexer/top-k/fwd use {cores} OpenMP threads, "
+                       f"bwd one thread")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="csa4_s4096")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=96)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this hot path runs on one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) "
+              "is not supported. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import csa_synth
+    import compressed_sparse_attention_softmax_amd as csa
+    from compressed_sparse_attention_softmax_amd import pipeline
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    csa.load()
+    wl = csa_synth.WORKLOADS[args.workload]
+    seed = csa_synth.WORKLOAD_SEEDS[args.workload]
+    dm = csa.dims_of(wl)
+    inp = csa_synth.make_inputs(wl, seed, device="cuda")
+    buf = pipeline.allocate(dm, wl.torch_dtype, wl.z_channels)
+    stream = torch.cuda.current_stream()
+    scale = wl.scale
+    sink = inp["sink"]
+
+    def stage_calls():
+        yield lambda: csa.csa_compress(dm, inp["x"], inp["z"], buf.c, None, stream=stream)
+        yield (lambda: csa.csa_index_topk(dm, inp["q_i"], inp["k_i"], inp["w"], buf.idx, buf.score,
+                                          stream=stream)) if buf.idx is not None else None
+        yield lambda: csa.csa_sparse_attn_fwd(dm, inp["q"], inp["kv"], buf.c, buf.idx, sink, scale, buf.out,
+                                              buf.lse, stream=stream)
+        yield lambda: csa.csa_sparse_attn_bwd(dm, inp["q"], inp["kv"], buf.c, buf.idx, sink, scale, buf.out,
+                                              buf.lse, inp["do"], buf.dq, buf.dkv, buf.dc, buf.dsink,
+                                              stream=stream)
+        yield lambda: csa.csa_compress_bwd(dm, inp["x"], inp["z"], buf.dc, buf.dx, buf.dz, stream=stream)
+
+    calls = list(stage_calls())
+
+    # memory contract of the indexer: nothing beyond its inputs and outputs
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    if calls[1] is not None:
+        calls[1]()
+    torch.cuda.synchronize()
+    index_peak_delta = torch.cuda.max_memory_allocated() - base
+
+    for _ in range(args.warmup):
+        for c in calls:
+            if c is not None:
+                c()
+    torch.cuda.synchronize()
+    work = count_work(wl, buf.idx)
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        e = ev[k]
+        e[0].record(stream)
+        for i, c in enumerate(calls):
+            if c is not None:
+                c()
+            e[i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {s: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(K)) / K for i, s in enumerate(STAGES)}
+    ms_step = elapsed * 1e3 / K
+    tokens = wl.b * wl.sq
+    flops_step = work["attn_fwd"] + work["attn_bwd"] + work["indexer"]
+    attn_s = (stage_ms["attn_fwd"] + stage_ms["attn_bwd"]) * 1e-3
+    attn_tflops = (work["attn_fwd"] + work["attn_bwd"]) / attn_s / 1e12
+    dom = max(("attn_fwd", "attn_bwd", "index_topk"), key=lambda s: stage_ms[s])
+    dom_flops = work["indexer"] if dom == "index_topk" else work[dom]
+    dom_tflops = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded normals, shapes and scales of the workload)",
+        "config": {"workload": wl.name, "b": wl.b, "sq": wl.sq, "h": wl.h, "d": wl.d, "ratio": wl.ratio,
+                   "span": wl.span, "window": wl.window, "idx_heads": wl.idx_heads, "idx_dim": wl.idx_dim,
+                   "topk": wl.topk, "parallelism": "single GPU"},
+        "tflops": flops_step / (ms_step * 1e-3) / 1e12,
+        "attention_tflops": attn_tflops,
+        "attention_frac_of_mfma_peak": attn_tflops / peak,
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "work": {k: v for k, v in work.items()},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": dom_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": dom_tflops / peak, "traffic": None,
+                     "timing": "HIP events on the launch stream around the entry point, mean over the timed steps"},
+        "memory": {"index_topk_workspace_bytes": csa.csa_index_topk_workspace(dm),
+                   "index_topk_peak_alloc_delta_bytes": int(index_peak_delta),
+                   "max_allocated_bytes": int(torch.cuda.max_memory_allocated())},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on a CPU sample ...")
+        result["cpu_baseline"] = cpu_baseline(wl, inp, seed, args.cpu_rows)
+    log(f"bench: {wl.name}: {ms_step:.3f} ms/step, {result['value']:.0f} tokens/s, "
+        f"{result['tflops']:.1f} TFLOP/s; stages(ms) {result['stage_ms']}; attention {attn_tflops:.1f} TFLOP/s "
+        f"({100 * attn_tflops / peak:.1f}% of peak)")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

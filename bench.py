@@ -141,7 +141,7 @@ def main():
                                               buf.lse, stream=stream)
         yield lambda: csa.csa_sparse_attn_bwd(dm, inp["q"], inp["kv"], buf.c, buf.idx, sink, scale, buf.out,
                                               buf.lse, inp["do"], buf.dq, buf.dkv, buf.dc, buf.dsink,
-                                              stream=stream)
+                                              ws=buf.ws, stream=stream)
         yield lambda: csa.csa_compress_bwd(dm, inp["x"], inp["z"], buf.dc, buf.dx, buf.dz, stream=stream)
 
     calls = list(stage_calls())

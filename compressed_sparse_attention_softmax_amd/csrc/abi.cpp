@@ -187,8 +187,18 @@ int csa_sparse_attn_fwd(const csa_dims* dm, int dtype, const void* q, const void
 
 size_t csa_sparse_attn_bwd_workspace(const csa_dims* dm)
 {
-    (void)dm;
-    return 0;
+    if (!dm || dm->b < 1 || dm->sq < 1 || dm->h < 1 || dm->window < 1 || !supported_d(dm->d)) return 0;
+    // the larger of the layouts with and without compressed rows
+    csa::AttnArgs a{};
+    a.b = dm->b; a.S = dm->sq; a.H = dm->h; a.D = dm->d; a.W = dm->window; a.r = 1; a.nc = 0;
+    size_t w0 = csa::attn_bwd_workspace_bytes(a);
+    if (dm->ratio >= 1) {
+        a.r = dm->ratio;
+        a.nc = dm->sq / dm->ratio;
+        const size_t w1 = csa::attn_bwd_workspace_bytes(a);
+        if (w1 > w0) w0 = w1;
+    }
+    return w0;
 }
 
 int csa_sparse_attn_bwd(const csa_dims* dm, int dtype, const void* q, const void* kv, const void* c,
@@ -196,7 +206,6 @@ int csa_sparse_attn_bwd(const csa_dims* dm, int dtype, const void* q, const void
                         const float* lse, const void* dout, void* dq, float* dkv, float* dc,
                         float* dsink, void* ws, size_t ws_bytes, void* stream)
 {
-    (void)ws; (void)ws_bytes;
     int rc = check_common(dm, dtype, "csa_sparse_attn_bwd");
     if (rc) return rc;
     if ((rc = check_attn(dm, dtype, q, kv, c, idx, scale, "csa_sparse_attn_bwd"))) return rc;
@@ -215,12 +224,15 @@ int csa_sparse_attn_bwd(const csa_dims* dm, int dtype, const void* q, const void
     csa::AttnArgs a = attn_args(dm, q, kv, c, idx, sink, scale);
     a.out = const_cast<void*>(out); a.lse = const_cast<float*>(lse); a.dout = dout;
     a.dq = dq; a.dkv = dkv; a.dc = dc; a.dsink = dsink;
+    const size_t need = csa::attn_bwd_workspace_bytes(a);
+    if (!ws || ws_bytes < need)
+        return fail(CSA_ERR_WORKSPACE, "csa_sparse_attn_bwd: workspace of %zu bytes needed, %zu given",
+                    need, ws ? ws_bytes : (size_t)0);
+    if (((uintptr_t)ws) & 15) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: workspace must be 16-byte aligned");
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = hipSuccess;
-    if (dkv) e = csa::zero_fill(dkv, (size_t)dm->b * dm->sq * dm->d, st);
-    if (e == hipSuccess && dc) e = csa::zero_fill(dc, (size_t)dm->b * a.nc * dm->d, st);
-    if (e == hipSuccess && dsink) e = csa::zero_fill(dsink, (size_t)dm->h, st);
-    if (e == hipSuccess) e = csa::attn_bwd(a, dtype == CSA_BF16, st);
+    if (dsink) e = csa::zero_fill(dsink, (size_t)dm->h, st);
+    if (e == hipSuccess) e = csa::attn_bwd(a, dtype == CSA_BF16, (float*)ws, st);
     return hip_status(e, "csa_sparse_attn_bwd");
 }
 

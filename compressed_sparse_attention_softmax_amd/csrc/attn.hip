@@ -12,13 +12,23 @@
 // positions in fp32 so repeated indices lose nothing.
 //
 // One KV head serves all h query heads, so the rows a query gathers are
-// shared by its heads: the natural matrix-core tile is (heads x gathered
-// rows x d).  A wave owns one query and a group of 16*HT heads and walks its
-// candidate list in chunks of 32 rows ("slots": the window rows first, then
-// the compressed slots).  Rows are loaded straight from global memory into
-// MFMA operand registers (16-byte row segments); a wave-private LDS tile
-// holds the same rows for the contractions over rows, whose operand needs 8
-// rows at one column per lane.
+// shared by its heads and the natural matrix-core tile is (heads x rows x d).
+//
+// Forward and dQ (query-major, sparse): a wave owns one query and a group of
+// 16*HT heads and walks its candidate list in chunks of 32 rows (window rows
+// first, then compressed slots).  Rows are loaded from global memory straight
+// into MFMA operand registers; a wave-private LDS tile holds the same rows
+// for the contraction over rows, read with ds_read_b64_tr_b16.
+//
+// dKV / dC (key-stationary, masked): fp32 atomics cannot absorb one add per
+// (query, row, d) -- a row is selected by hundreds of queries -- so the row
+// gradients are reduced on chip instead.  A workgroup owns a tile of key
+// rows (kept in registers as MFMA operands) and a block of consecutive
+// queries; it stages each query's q and dO in LDS and accumulates
+// P^T dO + dS'^T q over the query block in registers, masking (query, row)
+// pairs that are not candidates.  Partial sums per query block go to a
+// workspace and one reduction kernel adds them up: no atomics, and the sum
+// order is fixed.
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
 
@@ -30,7 +40,51 @@ constexpr int CHUNK = 32;
 
 template <typename T> constexpr int row_pad() { return 16 / (int)sizeof(T); }
 
-// Candidate list of one query.
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i % 4) of the 8-byte words addressed by lanes 4k + i/4, k = 0..3.
+__device__ __forceinline__ bf16x4 ds_read_tr(const bf16_t* p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+// MFMA operand whose k index runs over rows of a row-major LDS tile:
+// lane (n = lane%16, g = lane/16) gets column col0 + n of rows
+// r0 + 4g + e (e = 0..3) and r0 + 16 + 4g + (e-4) (e = 4..7).
+// This is the row order in which a 16x16 C tile pair (rows 0-15, 16-31 of a
+// 32-row chunk, lane holding rows 4g+i) feeds the k slots of one operand.
+// `stride` is the row stride in elements; with `swz` the tile is stored with
+// 8-element units permuted per row (unit u of row r at u ^ (r & 7)).
+template <typename T>
+__device__ __forceinline__ Frag<T> rows_operand(const T* tile, int stride, int r0, int col0, bool swz)
+{
+    const int lane = lane_id(), g = lane / 16, n16 = lane % 16;
+    Frag<T> f;
+    if constexpr (sizeof(T) == 2) {
+        const int r = r0 + 4 * g + (n16 >> 2);
+        const int c = col0 + 4 * (n16 & 3);
+        auto addr = [&](int rr) {
+            const int cc = swz ? ((((c >> 3) ^ (rr & 7)) << 3) | (c & 7)) : c;
+            return tile + rr * stride + cc;
+        };
+        const bf16x4 a = ds_read_tr(addr(r));
+        const bf16x4 b = ds_read_tr(addr(r + 16));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = b[e]; }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int rr = r0 + 16 * (e / 4) + 4 * g + (e % 4);
+            const int c = col0 + n16;
+            const int cc = swz ? ((((c >> 3) ^ (rr & 7)) << 3) | (c & 7)) : c;
+            f.v[e] = tile[rr * stride + cc];
+        }
+    }
+    return f;
+}
+
+// Candidate list of one query: window slots [0, nwin), then compressed slots.
 template <typename T>
 struct Cand {
     const T* kv;          // batch base of kv
@@ -51,41 +105,34 @@ struct Cand {
         const int ncs = p.c ? (p.idx ? p.kp : nv) : 0;
         nslots = nwin + ncs;
     }
-    // row of a slot: kind 0 = window row u, 1 = compressed row j, -1 = invalid
-    __device__ __forceinline__ int locate(int slot, int& where) const
+    // Row code of a slot: u (window row), j | 0x40000000 (compressed row),
+    // or -1 (invalid: padding, out of range or not yet valid).
+    __device__ __forceinline__ int code(int slot) const
     {
-        if (slot < nwin) { where = u0 + slot; return 0; }
-        if (slot >= nslots) { where = t; return -1; }
+        if (slot < nwin) return u0 + slot;
+        if (slot >= nslots) return -1;
         const int s2 = slot - nwin;
         const int j = irow ? irow[s2] : s2;
-        if (j < 0 || j >= nv) { where = t; return -1; }
-        where = j;
-        return 1;
+        return (j < 0 || j >= nv) ? -1 : (j | 0x40000000);
     }
-    __device__ __forceinline__ const T* row_ptr(int kind, int where) const
+    __device__ __forceinline__ const T* row_ptr(int code) const
     {
-        return kind == 1 ? c + (int64_t)where * D : kv + (int64_t)where * D;
-    }
-    // bit s of the result: slot c0 + s is a valid candidate (s < 32)
-    __device__ __forceinline__ uint32_t chunk_mask(int c0) const
-    {
-        int where;
-        const bool v = locate(c0 + (lane_id() & 31), where) >= 0;
-        return (uint32_t)__ballot(v);
+        if (code < 0) return kv + (int64_t)t * D;
+        if (code & 0x40000000) return c + (int64_t)(code & 0x3fffffff) * D;
+        return kv + (int64_t)code * D;
     }
 };
 
-// ---------------------------------------------------------------- forward
-// S^T[r, h] = R[r, :] . Q[h, :]        A = gathered rows (m = r, k = d),
-//                                      B = Q^T (k = d, n = h), registers
-// online softmax per column h (lane), base-2 exponentials
-// O^T[d, h] += R^T[d, r] P^T[r, h]     A = R^T from the LDS tile (8 rows at
-//                                      one column per lane), B = P^T straight
-//                                      from the S^T accumulators: lane (h, g)
-//                                      holds rows 4g+i of row tiles 0 and 1,
-//                                      i.e. k = 8g + e <-> r = 16(e/4) + 4g + e%4
-template <typename T, int D, int HT, int G>
-__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs p)
+// ------------------------------------------- forward / dQ (query-major)
+// S^T[r, h] = R[r, :] . Q[h, :]      A = gathered rows (m = r, k = d)
+//                                    B = Q^T (k = d, n = h), registers
+// forward: online softmax per column h (lane), base-2 exponentials, then
+//   O^T[d, h] += R^T P^T              A = R^T from the LDS tile, B = P^T
+//                                     straight from the S^T accumulators
+// dQ mode: dP^T = R . dO^T, P^T = exp(S^T scale - lse), dS'^T = scale P^T (dP^T - Delta),
+//   dQ^T[d, h] += R^T dS'^T           same operand shapes
+template <typename T, int D, int HT, int G, bool DQ>
+__global__ __launch_bounds__(256, 1) void attn_query_kernel(AttnArgs p, float* __restrict__ delta)
 {
     constexpr int KS = D / 32, DT = D / 16, QPW = 4 / G;
     constexpr int ROW = D + row_pad<T>();
@@ -102,18 +149,48 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs p)
     cand.init(p, bi, t);
     const int64_t qrow = (int64_t)bi * p.S + t;
     const float sl2 = p.scale * LOG2E;
+    const T* qp = (const T*)p.q + qrow * p.H * D;
 
     Frag<T> qb[HT][KS];
+    [[maybe_unused]] Frag<T> db[HT][KS];
     float m2[HT], l[HT];
+    [[maybe_unused]] float lse2[HT], dlt[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const int h = h0 + 16 * ht + n16;
         const bool hv = h < p.H;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qb[ht][ks] = hv ? load_frag((const T*)p.q + (qrow * p.H + h) * D + 32 * ks + 8 * g) : zero_frag<T>();
-        if (p.sink && hv) { m2[ht] = p.sink[h] * LOG2E; l[ht] = 1.f; }
-        else { m2[ht] = -INFINITY; l[ht] = 0.f; }
+            qb[ht][ks] = hv ? load_frag(qp + h * D + 32 * ks + 8 * g) : zero_frag<T>();
+        if constexpr (!DQ) {
+            if (p.sink && hv) { m2[ht] = p.sink[h] * LOG2E; l[ht] = 1.f; }
+            else { m2[ht] = -INFINITY; l[ht] = 0.f; }
+        } else {
+            // Delta[h] = <dO[t, h], O[t, h]>; dO kept as the B operand of dP^T
+            const T* dop = (const T*)p.dout + (qrow * p.H + h) * D;
+            const T* op = (const T*)p.out + (qrow * p.H + h) * D;
+            float part = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                db[ht][ks] = hv ? load_frag(dop + 32 * ks + 8 * g) : zero_frag<T>();
+                if (hv) {
+                    const Frag<T> of = load_frag(op + 32 * ks + 8 * g);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) part += to_f32(db[ht][ks].v[e]) * to_f32(of.v[e]);
+                }
+            }
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            dlt[ht] = part;
+            lse2[ht] = hv ? p.lse[qrow * p.H + h] * LOG2E : INFINITY;
+            if (hv && g == 0) {
+                delta[qrow * p.H + h] = part;
+                if (p.sink && p.dsink) atomicAdd(p.dsink + h, -exp2f(p.sink[h] * LOG2E - lse2[ht]) * part);
+            }
+        }
+    }
+    if constexpr (DQ) {
+        if (!p.dq) return;
     }
     f32x4 o[DT][HT];
 #pragma unroll
@@ -121,345 +198,383 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs p)
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) o[dt][ht] = f4zero();
 
-    for (int c0 = 0; c0 < cand.nslots; c0 += CHUNK) {
-        const uint32_t mask = cand.chunk_mask(c0);
-        if (mask == 0u) continue;
-        // gathered rows as A operands (m = r), copied to the LDS tile
-        Frag<T> ra[2][KS];
+    // rows of chunk c0 as A operands; lane (n16, rt) loads slot 16 rt + n16
+    auto load_chunk = [&](int c0, Frag<T> (&ra)[2][KS], uint32_t& mask) {
+        const int code = cand.code(c0 + (lane & 31));
+        mask = (uint32_t)__ballot(code >= 0);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            int where;
-            const int kind = cand.locate(c0 + 16 * rt + n16, where);
-            const T* src = cand.row_ptr(kind, where);
+            const T* src = cand.row_ptr(__shfl(code, 16 * rt + n16));
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                ra[rt][ks] = load_frag(src + 32 * ks + 8 * g);
-                store_frag(tile + (16 * rt + n16) * ROW + 32 * ks + 8 * g, ra[rt][ks]);
-            }
+            for (int ks = 0; ks < KS; ++ks) ra[rt][ks] = load_frag(src + 32 * ks + 8 * g);
         }
-        f32x4 s[2][HT];
+    };
+
+    Frag<T> ra[2][KS];
+    uint32_t mask = 0;
+    int c0 = 0;
+    // skip leading chunks that hold no candidate (e.g. all -1)
+    for (; c0 < cand.nslots; c0 += CHUNK) {
+        load_chunk(c0, ra, mask);
+        if (mask) break;
+    }
+    while (c0 < cand.nslots) {
+        // prefetch the next chunk with a candidate while this one computes
+        Frag<T> rn[2][KS];
+        uint32_t mn = 0;
+        int c1 = c0 + CHUNK;
+        for (; c1 < cand.nslots; c1 += CHUNK) {
+            load_chunk(c1, rn, mn);
+            if (mn) break;
+        }
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                f32x4 acc = f4zero();
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) acc = mfma16(ra[rt][ks], qb[ht][ks], acc);
-                s[rt][ht] = acc;
-            }
+            for (int ks = 0; ks < KS; ++ks) store_frag(tile + (16 * rt + n16) * ROW + 32 * ks + 8 * g, ra[rt][ks]);
         Frag<T> pb[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
-            float x[2][4];
-            float mx = -INFINITY;
+            f32x4 s[2];
+            [[maybe_unused]] f32x4 dp[2];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < 2; ++rt) {
+                f32x4 acc = f4zero();
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool v = (mask >> (16 * rt + 4 * g + i)) & 1u;
-                    x[rt][i] = v ? s[rt][ht][i] * sl2 : -INFINITY;
-                    mx = fmaxf(mx, x[rt][i]);
+                for (int ks = 0; ks < KS; ++ks) acc = mfma16(ra[rt][ks], qb[ht][ks], acc);
+                s[rt] = acc;
+                if constexpr (DQ) {
+                    f32x4 a2 = f4zero();
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) a2 = mfma16(ra[rt][ks], db[ht][ks], a2);
+                    dp[rt] = a2;
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(m2[ht], mx);
-            const float alpha = exp2f(m2[ht] - mnew);
-            float rs = 0.f;
+            }
+            if constexpr (!DQ) {
+                float x[2][4];
+                float mx = -INFINITY;
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+                for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float pv = exp2f(x[rt][i] - mnew);
-                    rs += pv;
-                    pb[ht].v[4 * rt + i] = from_f32<T>(pv);
+                    for (int i = 0; i < 4; ++i) {
+                        const bool v = (mask >> (16 * rt + 4 * g + i)) & 1u;
+                        x[rt][i] = v ? s[rt][i] * sl2 : -INFINITY;
+                        mx = fmaxf(mx, x[rt][i]);
+                    }
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float mnew = fmaxf(m2[ht], mx);
+                const float alpha = exp2f(m2[ht] - mnew);
+                float rs = 0.f;
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float pv = exp2f(x[rt][i] - mnew);
+                        rs += pv;
+                        pb[ht].v[4 * rt + i] = from_f32<T>(pv);
+                    }
+                rs += __shfl_xor(rs, 16);
+                rs += __shfl_xor(rs, 32);
+                l[ht] = l[ht] * alpha + rs;
+                m2[ht] = mnew;
+                if (alpha != 1.f) {
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) o[dt][ht] *= alpha;
                 }
-            rs += __shfl_xor(rs, 16);
-            rs += __shfl_xor(rs, 32);
-            l[ht] = l[ht] * alpha + rs;
-            m2[ht] = mnew;
+            } else {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o[dt][ht] *= alpha;
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool v = (mask >> (16 * rt + 4 * g + i)) & 1u;
+                        const float pv = v ? exp2f(s[rt][i] * sl2 - lse2[ht]) : 0.f;
+                        pb[ht].v[4 * rt + i] = from_f32<T>(p.scale * pv * (dp[rt][i] - dlt[ht]));
+                    }
+            }
         }
-        // O^T += R^T P^T
+        // O^T += R^T P^T   (or dQ^T += R^T dS'^T)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            Frag<T> a;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                a.v[e] = tile[(16 * (e / 4) + 4 * g + (e % 4)) * ROW + 16 * dt + n16];
+            const Frag<T> a = rows_operand<T>(tile, ROW, 0, 16 * dt, false);
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) o[dt][ht] = mfma16(a, pb[ht], o[dt][ht]);
         }
+        c0 = c1;
+        mask = mn;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) ra[rt][ks] = rn[rt][ks];
     }
-    // epilogue: O[t, h, d] = O^T[d, h] / l;  lse = (m2 + log2 l) ln 2
+    // epilogue: lane holds X^T[d = 16 dt + 4g + i][h = h0 + 16 ht + n16]
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const int h = h0 + 16 * ht + n16;
         if (h >= p.H) continue;
-        const float inv = 1.f / l[ht];
-        T* orow = (T*)p.out + (qrow * p.H + h) * D;
+        if constexpr (!DQ) {
+            const float inv = 1.f / l[ht];
+            T* orow = (T*)p.out + (qrow * p.H + h) * D;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) orow[16 * dt + 4 * g + i] = from_f32<T>(o[dt][ht][i] * inv);
+                for (int i = 0; i < 4; ++i) orow[16 * dt + 4 * g + i] = from_f32<T>(o[dt][ht][i] * inv);
+            if (g == 0) p.lse[qrow * p.H + h] = (m2[ht] + log2f(l[ht])) * LN2;
+        } else {
+            T* drow = (T*)p.dq + (qrow * p.H + h) * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) drow[16 * dt + 4 * g + i] = from_f32<T>(o[dt][ht][i]);
         }
-        if (g == 0) p.lse[qrow * p.H + h] = (m2[ht] + log2f(l[ht])) * LN2;
     }
 }
 
-// --------------------------------------------------------------- backward
-// S[h, r]  = Q[h, :] . R[r, :]       A = Q (m = h, k = d), B = R (k = d, n = r)
-// dP[h, r] = dO[h, :] . R[r, :]      same B operand
-// P = exp(scale S - lse), dS' = scale P (dP - Delta)
-// dR[r, d] = P^T dO + dS'^T Q        A = P^T / dS'^T straight from the S/dP
-//                                    accumulators (lane (r, g) holds heads 4g+i
-//                                    of head tiles 0 and 1: k = 8g + e <->
-//                                    head 16(e/4) + 4g + e%4), B = dO / Q
-//                                    gathered once per query in that head order
-//                                    -> fp32 atomics into dkv / dc
-// dQ[h, d] += dS'[h, :] R[:, d]      A = dS' through an LDS tile [h][r],
-//                                    B = R^T from the row tile
-template <typename T, int D, int HT, int G>
-__global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnArgs p)
+// ------------------------------------ dKV / dC partials (key-stationary)
+// Workgroup (tile slot x, query block y, batch z).  Tile slots [0, n_wt) are
+// window tiles: rows u = t0 - W + 1 + i of the block's band, i in
+// [x*TR, (x+1)*TR); the remaining slots are compressed tiles j in
+// [x'*TR, (x'+1)*TR).  Wave w owns RW rows of the tile.
+//   S[h, r]  = Q[h, :] . R[r, :]      A = Q from LDS (m = h), B = rows (regs)
+//   dP[h, r] = dO[h, :] . R[r, :]
+//   P = m(t, r) exp(scale S - lse), dS' = scale P (dP - Delta)   (m = multiplicity)
+//   dR[r, d] += P^T dO + dS'^T Q      A = P^T / dS'^T from the S / dP
+//                                     accumulators (lane (r, g) holds heads 4g+i
+//                                     of head tiles 2kk, 2kk+1), B = dO / Q
+//                                     from LDS through the transposing read
+struct RowsGeom {
+    int Qb, nqb, WB, n_wt, n_ct, TR;   // query block, blocks, band rows, tiles, tile rows
+    int64_t win_off, comp_off;   // float offsets of the two partial regions in the workspace
+};
+
+template <typename T, int D, int RW>
+__global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom geo,
+                                                           const float* __restrict__ delta,
+                                                           float* __restrict__ ws)
 {
-    constexpr int KS = D / 32, DT = D / 16, QPW = 4 / G;
-    constexpr int ROW = D + row_pad<T>();
-    constexpr int DSROW = CHUNK + row_pad<T>();
-    static_assert(HT <= 2, "one k-step of 32 heads per dR product");
+    constexpr int KS = D / 32, DT = D / 16, RT = RW / 16, TR = 4 * RW;
+    constexpr int HP = 64;                       // heads, padded to 4 head tiles
+    constexpr int CH = 16 / sizeof(T);           // elements per 16-byte chunk
+    constexpr int QBYTES = HP * D * sizeof(T);   // one staged q (or dO) block
     extern __shared__ __attribute__((aligned(16))) char smem[];
+    T* q_lds = reinterpret_cast<T*>(smem);
+    T* do_lds = reinterpret_cast<T*>(smem + QBYTES);
+    float* lse_lds = reinterpret_cast<float*>(smem + 2 * QBYTES);
+    float* dlt_lds = lse_lds + HP;
+    unsigned* cnt_lds = reinterpret_cast<unsigned*>(dlt_lds + HP);
+    __shared__ int any_lds;
+
     const int wave = threadIdx.x / WAVE, lane = lane_id();
     const int g = lane / 16, n16 = lane % 16;
-    const size_t wave_elems = (size_t)CHUNK * ROW + (size_t)16 * HT * DSROW;
-    T* tile = reinterpret_cast<T*>(smem) + (size_t)wave * wave_elems;
-    T* dstile = tile + (size_t)CHUNK * ROW;
+    const int bi = blockIdx.z, qb = blockIdx.y, slot = blockIdx.x;
+    const int t0 = qb * geo.Qb, t1 = min(p.S, t0 + geo.Qb);
+    const bool win = slot < geo.n_wt;
+    const int tile = win ? slot : slot - geo.n_wt;
+    const int i0 = tile * TR;                    // first partial row of the tile
+    int base_row;                                // key row of partial row 0
+    int nrows_valid;                             // partial rows [0, nrows_valid) are meaningful
+    if (win) {
+        if (i0 >= geo.WB) return;
+        base_row = t0 - p.W + 1;
+        nrows_valid = geo.WB;
+    } else {
+        const int nvmax = min(t1 / p.r, p.nc);
+        if (i0 >= nvmax) return;
+        base_row = 0;
+        nrows_valid = nvmax;
+    }
+    const T* rows = win ? (const T*)p.kv + (int64_t)bi * p.S * D : (const T*)p.c + (int64_t)bi * p.nc * D;
+    const int rmax = win ? p.S : p.nc;           // key rows that exist
 
-    const int bi = blockIdx.y;
-    const int t = blockIdx.x * QPW + wave / G;
-    if (t >= p.S) return;
-    const int h0 = (wave % G) * 16 * HT;
-    Cand<T> cand;
-    cand.init(p, bi, t);
-    const int64_t qrow = (int64_t)bi * p.S + t;
-    const T* qp = (const T*)p.q + qrow * p.H * D;
-    const T* dop = (const T*)p.dout + qrow * p.H * D;
-    const T* op = (const T*)p.out + qrow * p.H * D;
+    // this wave's rows as B operands (k = d, n = r)
+    Frag<T> rb[RT][KS];
+    int rkey[RT];                                // key row of column n16 of row tile rt (-1: none)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int i = i0 + RW * wave + 16 * rt + n16;
+        const int key = base_row + i;
+        const bool ok = i < nrows_valid && key >= 0 && key < rmax;
+        rkey[rt] = ok ? key : -1;
+        const T* src = rows + (int64_t)(ok ? key : 0) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) rb[rt][ks] = load_frag(src + 32 * ks + 8 * g);
+    }
+    f32x4 acc[RT][DT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = f4zero();
+
     const float sl2 = p.scale * LOG2E;
-
-    // Delta[h] = <dO[t, h], O[t, h]> for the wave's heads, kept in C-row layout
-    float lse2[HT][4], dlt[HT][4];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = h0 + 16 * ht + 4 * g + i;
-            lse2[ht][i] = h < p.H ? p.lse[qrow * p.H + h] * LOG2E : 0.f;
-            dlt[ht][i] = 0.f;
+    const int tile_lo = base_row + i0;           // key range of the tile
+    const int tile_hi = base_row + min(i0 + TR, nrows_valid);
+    for (int t = t0; t < t1; ++t) {
+        // does t have any candidate in this tile?
+        if (win) {
+            if (tile_hi <= t - p.W + 1 || tile_lo > t) continue;
+        } else {
+            if (tile_lo >= min((t + 1) / p.r, p.nc)) continue;
         }
-    for (int hh = 0; hh < 16 * HT; ++hh) {
-        const int h = h0 + hh;
-        if (h >= p.H) break;
-        float part = 0.f;
-        for (int d = lane; d < D; d += WAVE) part += to_f32(dop[h * D + d]) * to_f32(op[h * D + d]);
-        part = wave_sum(part);
-        const int ht = hh / 16, gg = (hh % 16) / 4, ii = hh % 4;
-#pragma unroll
-        for (int a = 0; a < HT; ++a)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (a == ht && g == gg && i == ii) dlt[a][i] = part;
-    }
-    if (p.dsink && p.sink && n16 == 0) {
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int h = h0 + 16 * ht + 4 * g + i;
-                if (h < p.H) atomicAdd(p.dsink + h, -exp2f(p.sink[h] * LOG2E - lse2[ht][i]) * dlt[ht][i]);
-            }
-    }
-    if (!p.dq) return;
-
-    Frag<T> qa[HT][KS], da[HT][KS];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const int h = h0 + 16 * ht + n16;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bool hv = h < p.H;
-            qa[ht][ks] = hv ? load_frag(qp + h * D + 32 * ks + 8 * g) : zero_frag<T>();
-            da[ht][ks] = hv ? load_frag(dop + h * D + 32 * ks + 8 * g) : zero_frag<T>();
-        }
-    }
-    // B operands of dR (k = head in the order 16(e/4) + 4g + e%4, n = d)
-    Frag<T> dob[DT], qbb[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int hk = 16 * (e / 4) + 4 * g + (e % 4);
-            const int h = h0 + hk;
-            const bool hv = hk < 16 * HT && h < p.H;
-            dob[dt].v[e] = hv ? dop[h * D + 16 * dt + n16] : from_f32<T>(0.f);
-            qbb[dt].v[e] = hv ? qp[h * D + 16 * dt + n16] : from_f32<T>(0.f);
-        }
-    f32x4 dq[HT][DT];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) dq[ht][dt] = f4zero();
-
-    float* dkv_b = p.dkv + (int64_t)bi * p.S * D;
-    float* dc_b = p.dc ? p.dc + (int64_t)bi * p.nc * D : nullptr;
-
-    for (int c0 = 0; c0 < cand.nslots; c0 += CHUNK) {
-        const uint32_t mask = cand.chunk_mask(c0);
-        if (mask == 0u) continue;
-        Frag<T> rb[2][KS];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            int where;
-            const int kind = cand.locate(c0 + 16 * rt + n16, where);
-            const T* src = cand.row_ptr(kind, where);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                rb[rt][ks] = load_frag(src + 32 * ks + 8 * g);
-                store_frag(tile + (16 * rt + n16) * ROW + 32 * ks + 8 * g, rb[rt][ks]);
-            }
-        }
-        Frag<T> pa[2], sa[2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            pa[rt] = zero_frag<T>();
-            sa[rt] = zero_frag<T>();
-            const bool rv = (mask >> (16 * rt + n16)) & 1u;
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                f32x4 sacc = f4zero(), pacc = f4zero();
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    sacc = mfma16(qa[ht][ks], rb[rt][ks], sacc);
-                    pacc = mfma16(da[ht][ks], rb[rt][ks], pacc);
+        const int64_t qrow = (int64_t)bi * p.S + t;
+        __syncthreads();
+        // stage q[t], dO[t] (8-element units permuted per row, unit u at u ^ (row & 7)),
+        // lse, Delta and the multiplicities of the tile's rows
+        {
+            const T* qsrc = (const T*)p.q + qrow * p.H * D;
+            const T* dsrc = (const T*)p.dout + qrow * p.H * D;
+            constexpr int NCHUNK = HP * D / CH;
+            for (int cidx = threadIdx.x; cidx < NCHUNK; cidx += 256) {
+                const int h = cidx / (D / CH), cc = cidx % (D / CH);
+                const int d0 = cc * CH;
+                const int dst = h * D + ((((d0 >> 3) ^ (h & 7)) << 3) | (d0 & 7));
+                uint4 vq = make_uint4(0u, 0u, 0u, 0u), vd = vq;
+                if (h < p.H) {
+                    vq = *reinterpret_cast<const uint4*>(qsrc + h * D + cc * CH);
+                    vd = *reinterpret_cast<const uint4*>(dsrc + h * D + cc * CH);
                 }
+                *reinterpret_cast<uint4*>(q_lds + dst) = vq;
+                *reinterpret_cast<uint4*>(do_lds + dst) = vd;
+            }
+            if (threadIdx.x < HP) {
+                const int h = threadIdx.x;
+                lse_lds[h] = h < p.H ? p.lse[qrow * p.H + h] * LOG2E : INFINITY;
+                dlt_lds[h] = h < p.H ? delta[qrow * p.H + h] : 0.f;
+            }
+            if (!win) {
+                for (int i = threadIdx.x; i < TR; i += 256) cnt_lds[i] = 0u;
+                if (threadIdx.x == 0) any_lds = 0;
+            }
+        }
+        if (!win) {
+            __syncthreads();
+            const int nv = min((t + 1) / p.r, p.nc);
+            int found = 0;
+            if (p.idx) {
+                const int32_t* irow = p.idx + qrow * p.kp;
+                for (int s = threadIdx.x; s < p.kp; s += 256) {
+                    const int j = irow[s];
+                    if (j >= 0 && j < nv && j >= tile_lo && j < tile_hi) {
+                        atomicAdd(&cnt_lds[j - tile_lo], 1u);
+                        found = 1;
+                    }
+                }
+            } else {
+                for (int j = tile_lo + threadIdx.x; j < min(tile_hi, nv); j += 256) {
+                    cnt_lds[j - tile_lo] = 1u;
+                    found = 1;
+                }
+            }
+            if (found) any_lds = 1;
+        }
+        __syncthreads();
+        if (!win && !any_lds) continue;
+        // multiplicity of the columns this lane holds
+        float mult[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int key = rkey[rt];
+            if (key < 0) { mult[rt] = 0.f; continue; }
+            if (win) mult[rt] = (key <= t && key > t - p.W) ? 1.f : 0.f;
+            else mult[rt] = (float)cnt_lds[key - tile_lo];
+        }
+#pragma unroll
+        for (int kk = 0; kk < HP / 32; ++kk) {
+            Frag<T> pa[RT], sa[RT];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int ht = 2 * kk + hh;
+                float ls[4], dl[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float pv = rv ? exp2f(sacc[i] * sl2 - lse2[ht][i]) : 0.f;
-                    const float dsv = p.scale * pv * (pacc[i] - dlt[ht][i]);
-                    pa[rt].v[4 * ht + i] = from_f32<T>(pv);
-                    sa[rt].v[4 * ht + i] = from_f32<T>(dsv);
-                    // dS' tile [h][r] for the dQ product
-                    dstile[(16 * ht + 4 * g + i) * DSROW + 16 * rt + n16] = from_f32<T>(dsv);
+                    ls[i] = lse_lds[16 * ht + 4 * g + i];
+                    dl[i] = dlt_lds[16 * ht + 4 * g + i];
+                }
+                Frag<T> qa[KS], da[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int hrow = 16 * ht + n16;
+                    const int off = hrow * D + (((4 * ks + g) ^ (hrow & 7)) << 3);   // d = 32 ks + 8 g
+                    qa[ks] = load_frag(q_lds + off);
+                    da[ks] = load_frag(do_lds + off);
+                }
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    f32x4 s = f4zero(), dp = f4zero();
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        s = mfma16(qa[ks], rb[rt][ks], s);
+                        dp = mfma16(da[ks], rb[rt][ks], dp);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float pv = mult[rt] * exp2f(s[i] * sl2 - ls[i]);
+                        pa[rt].v[4 * hh + i] = from_f32<T>(pv);
+                        sa[rt].v[4 * hh + i] = from_f32<T>(p.scale * pv * (dp[i] - dl[i]));
+                    }
+                }
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const Frag<T> dob = rows_operand<T>(do_lds, D, 32 * kk, 16 * dt, true);
+                const Frag<T> qbf = rows_operand<T>(q_lds, D, 32 * kk, 16 * dt, true);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    acc[rt][dt] = mfma16(pa[rt], dob, acc[rt][dt]);
+                    acc[rt][dt] = mfma16(sa[rt], qbf, acc[rt][dt]);
                 }
             }
         }
-        // dR = P^T dO + dS'^T Q, scattered with fp32 atomics
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            float* dst[4];
-            bool ok[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int where;
-                const int kind = cand.locate(c0 + 16 * rt + 4 * g + i, where);
-                ok[i] = kind >= 0;
-                dst[i] = kind == 1 ? dc_b + (int64_t)where * D : dkv_b + (int64_t)where * D;
-            }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                f32x4 acc = mfma16(pa[rt], dob[dt], f4zero());
-                acc = mfma16(sa[rt], qbb[dt], acc);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (ok[i]) atomicAdd(dst[i] + 16 * dt + n16, acc[i]);
-            }
-        }
-        // dQ += dS' R
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            const Frag<T> a = load_frag(dstile + (16 * ht + n16) * DSROW + 8 * g);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                Frag<T> bfr;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) bfr.v[e] = tile[(8 * g + e) * ROW + 16 * dt + n16];
-                dq[ht][dt] = mfma16(a, bfr, dq[ht][dt]);
-            }
-        }
     }
+    // partial rows of this wave: lane holds dR[r = 16 rt + 4g + i][d = 16 dt + n16]
+    float* part = ws + (win ? geo.win_off + (((int64_t)bi * geo.nqb + qb) * geo.WB) * D
+                            : geo.comp_off + (((int64_t)bi * geo.nqb + qb) * p.nc) * D);
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int h = h0 + 16 * ht + 4 * g + i;
-            if (h >= p.H) continue;
-            T* dqrow = (T*)p.dq + (qrow * p.H + h) * D;
+            const int pr = i0 + RW * wave + 16 * rt + 4 * g + i;
+            if (pr >= nrows_valid) continue;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) dqrow[16 * dt + n16] = from_f32<T>(dq[ht][dt][i]);
+            for (int dt = 0; dt < DT; ++dt) part[(int64_t)pr * D + 16 * dt + n16] = acc[rt][dt][i];
         }
 }
 
-template <typename T, int D, int HT>
-hipError_t launch_fwd(const AttnArgs& p, hipStream_t st)
+// dKV[b, u] = sum of the window partials of the query blocks whose band holds u;
+// dC[b, j]  = sum of the compressed partials of the query blocks that reach j.
+// One thread per (row, 4 consecutive d); the sum runs over query blocks in order.
+template <int D>
+__global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs p, RowsGeom geo, const float* __restrict__ ws)
 {
-    const int gper = (p.H + 16 * HT - 1) / (16 * HT);
-    const size_t lds = (size_t)4 * CHUNK * (D + row_pad<T>()) * sizeof(T);
-    if (lds > (size_t)ATTN_LDS_LIMIT) return hipErrorInvalidValue;
-    auto go = [&](auto kern, int qpw) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        dim3 grid((p.S + qpw - 1) / qpw, p.b);
-        hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p);
-        return hipGetLastError();
-    };
-    switch (gper) {
-    case 1: return go(attn_fwd_kernel<T, D, HT, 1>, 4);
-    case 2: return go(attn_fwd_kernel<T, D, HT, 2>, 2);
-    case 3:
-    case 4: return go(attn_fwd_kernel<T, D, HT, 4>, 1);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-template <typename T, int D, int HT>
-hipError_t launch_bwd(const AttnArgs& p, hipStream_t st)
-{
-    const int gper = (p.H + 16 * HT - 1) / (16 * HT);
-    const size_t lds = (size_t)4 * (CHUNK * (D + row_pad<T>()) + 16 * HT * (CHUNK + row_pad<T>())) * sizeof(T);
-    if (lds > (size_t)ATTN_LDS_LIMIT) return hipErrorInvalidValue;
-    auto go = [&](auto kern, int qpw) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        dim3 grid((p.S + qpw - 1) / qpw, p.b);
-        hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p);
-        return hipGetLastError();
-    };
-    switch (gper) {
-    case 1: return go(attn_bwd_kernel<T, D, HT, 1>, 4);
-    case 2: return go(attn_bwd_kernel<T, D, HT, 2>, 2);
-    case 3:
-    case 4: return go(attn_bwd_kernel<T, D, HT, 4>, 1);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-template <typename T>
-hipError_t fwd_dispatch(const AttnArgs& p, hipStream_t st)
-{
-    switch (p.D) {
-    case 64: return p.H <= 16 ? launch_fwd<T, 64, 1>(p, st) : p.H <= 32 ? launch_fwd<T, 64, 2>(p, st) : launch_fwd<T, 64, 4>(p, st);
-    case 128: return p.H <= 16 ? launch_fwd<T, 128, 1>(p, st) : p.H <= 32 ? launch_fwd<T, 128, 2>(p, st) : launch_fwd<T, 128, 4>(p, st);
-    case 512: return launch_fwd<T, 512, 1>(p, st);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-template <typename T>
-hipError_t bwd_dispatch(const AttnArgs& p, hipStream_t st)
-{
-    switch (p.D) {
-    case 64: return p.H <= 16 ? launch_bwd<T, 64, 1>(p, st) : launch_bwd<T, 64, 2>(p, st);
-    case 128: return p.H <= 16 ? launch_bwd<T, 128, 1>(p, st) : launch_bwd<T, 128, 2>(p, st);
-    case 512: return launch_bwd<T, 512, 1>(p, st);
-    default: return hipErrorInvalidValue;
+    constexpr int V = D / 4;
+    const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t nkv = (int64_t)p.b * p.S * V;
+    const int64_t nct = (int64_t)p.b * p.nc * V;
+    if (tid < nkv) {
+        const int v = tid % V;
+        const int64_t row = tid / V;
+        const int bi = (int)(row / p.S), u = (int)(row % p.S);
+        const int q_lo = u / geo.Qb;
+        const int q_hi = min(geo.nqb - 1, (u + p.W - 1) / geo.Qb);
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int q = q_lo; q <= q_hi; ++q) {
+            const int i = u - (q * geo.Qb - p.W + 1);
+            const float4 x = *reinterpret_cast<const float4*>(
+                ws + geo.win_off + (((int64_t)bi * geo.nqb + q) * geo.WB + i) * D + 4 * v);
+            s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
+        }
+        *reinterpret_cast<float4*>(p.dkv + row * D + 4 * v) = s;
+    } else if (tid < nkv + nct) {
+        const int64_t k = tid - nkv;
+        const int v = k % V;
+        const int64_t row = k / V;
+        const int bi = (int)(row / p.nc), j = (int)(row % p.nc);
+        const int q_lo = ((j + 1) * p.r + geo.Qb - 1) / geo.Qb - 1;
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int q = max(q_lo, 0); q < geo.nqb; ++q) {
+            const float4 x = *reinterpret_cast<const float4*>(
+                ws + geo.comp_off + (((int64_t)bi * geo.nqb + q) * p.nc + j) * D + 4 * v);
+            s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
+        }
+        *reinterpret_cast<float4*>(p.dc + row * D + 4 * v) = s;
     }
 }
 
@@ -472,18 +587,122 @@ __global__ void zero_fill_kernel(float* __restrict__ p, size_t n)
     }
 }
 
+// ------------------------------------------------------------------ host
+int rows_per_wave(int D) { return D <= 128 ? 64 : 16; }
+
+RowsGeom rows_geometry(const AttnArgs& p)
+{
+    RowsGeom g{};
+    g.TR = 4 * rows_per_wave(p.D);
+    const int64_t D = p.D;
+    auto part_floats = [&](int qb) {
+        const int nqb = (p.S + qb - 1) / qb;
+        return (int64_t)p.b * nqb * ((int64_t)(p.W - 1 + qb) + p.nc) * D;
+    };
+    int qb = 32;
+    while (qb < 1024 && part_floats(qb) * 4 > ((int64_t)1 << 30)) qb *= 2;
+    g.Qb = qb;
+    g.nqb = (p.S + qb - 1) / qb;
+    g.WB = p.W - 1 + qb;
+    g.n_wt = (g.WB + g.TR - 1) / g.TR;
+    g.n_ct = p.nc > 0 ? (p.nc + g.TR - 1) / g.TR : 0;
+    const int64_t delta_floats = ((int64_t)p.b * p.S * p.H + 63) / 64 * 64;
+    g.win_off = delta_floats;
+    g.comp_off = g.win_off + (int64_t)p.b * g.nqb * g.WB * D;
+    return g;
+}
+
+template <typename T, int D, int HT>
+hipError_t launch_query(const AttnArgs& p, bool dq, float* delta, hipStream_t st)
+{
+    const int gper = (p.H + 16 * HT - 1) / (16 * HT);
+    const size_t lds = (size_t)4 * CHUNK * (D + row_pad<T>()) * sizeof(T);
+    if (lds > (size_t)ATTN_LDS_LIMIT) return hipErrorInvalidValue;
+    auto go = [&](auto kern, int qpw) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        dim3 grid((p.S + qpw - 1) / qpw, p.b);
+        hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p, delta);
+        return hipGetLastError();
+    };
+    if (dq) {
+        switch (gper) {
+        case 1: return go(attn_query_kernel<T, D, HT, 1, true>, 4);
+        case 2: return go(attn_query_kernel<T, D, HT, 2, true>, 2);
+        default: return go(attn_query_kernel<T, D, HT, 4, true>, 1);
+        }
+    }
+    switch (gper) {
+    case 1: return go(attn_query_kernel<T, D, HT, 1, false>, 4);
+    case 2: return go(attn_query_kernel<T, D, HT, 2, false>, 2);
+    default: return go(attn_query_kernel<T, D, HT, 4, false>, 1);
+    }
+}
+
+template <typename T>
+hipError_t query_dispatch(const AttnArgs& p, bool dq, float* delta, hipStream_t st)
+{
+    switch (p.D) {
+    case 64: return p.H <= 16 ? launch_query<T, 64, 1>(p, dq, delta, st) : launch_query<T, 64, 4>(p, dq, delta, st);
+    case 128: return p.H <= 16 ? launch_query<T, 128, 1>(p, dq, delta, st) : launch_query<T, 128, 4>(p, dq, delta, st);
+    case 512: return launch_query<T, 512, 1>(p, dq, delta, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_rows(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStream_t st)
+{
+    constexpr int RW = D <= 128 ? 64 : 16;
+    const size_t lds = 2 * (size_t)64 * D * sizeof(T) + 2 * 64 * 4 + (size_t)4 * RW * 4;
+    if (lds > (size_t)ATTN_LDS_LIMIT) return hipErrorInvalidValue;
+    auto kern = attn_rows_kernel<T, D, RW>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    dim3 grid(geo.n_wt + (p.c ? geo.n_ct : 0), geo.nqb, p.b);
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p, geo, ws, ws);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t threads = (int64_t)p.b * (p.S + (p.c ? p.nc : 0)) * (D / 4);
+    hipLaunchKernelGGL(attn_reduce_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, p, geo,
+                       (const float*)ws);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t rows_dispatch(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStream_t st)
+{
+    switch (p.D) {
+    case 64: return launch_rows<T, 64>(p, geo, ws, st);
+    case 128: return launch_rows<T, 128>(p, geo, ws, st);
+    case 512: return launch_rows<T, 512>(p, geo, ws, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
+
+size_t attn_bwd_workspace_bytes(const AttnArgs& p)
+{
+    const RowsGeom g = rows_geometry(p);
+    const int64_t floats = g.comp_off + (int64_t)p.b * g.nqb * p.nc * p.D;
+    return (size_t)floats * 4;
+}
 
 hipError_t attn_fwd(const AttnArgs& p, bool bf16, hipStream_t st)
 {
     if (p.S == 0) return hipSuccess;
-    return bf16 ? fwd_dispatch<bf16_t>(p, st) : fwd_dispatch<float>(p, st);
+    return bf16 ? query_dispatch<bf16_t>(p, false, nullptr, st) : query_dispatch<float>(p, false, nullptr, st);
 }
 
-hipError_t attn_bwd(const AttnArgs& p, bool bf16, hipStream_t st)
+// ws: at least attn_bwd_workspace_bytes(p) bytes.  Delta (b*S*H floats) comes
+// first, then the window partials, then the compressed partials.
+hipError_t attn_bwd(const AttnArgs& p, bool bf16, float* ws, hipStream_t st)
 {
     if (p.S == 0) return hipSuccess;
-    return bf16 ? bwd_dispatch<bf16_t>(p, st) : bwd_dispatch<float>(p, st);
+    hipError_t e = bf16 ? query_dispatch<bf16_t>(p, true, ws, st) : query_dispatch<float>(p, true, ws, st);
+    if (e != hipSuccess || !p.dq) return e;
+    const RowsGeom geo = rows_geometry(p);
+    return bf16 ? rows_dispatch<bf16_t>(p, geo, ws, st) : rows_dispatch<float>(p, geo, ws, st);
 }
 
 hipError_t zero_fill(float* p, size_t n, hipStream_t st)

@@ -53,7 +53,8 @@ hipError_t index_topk(const IndexArgs& p, bool bf16, hipStream_t st);
 int index_topk_cap(const IndexArgs& p, bool bf16);
 size_t topk_lds_bytes(int DI, int elem, int cap);
 hipError_t attn_fwd(const AttnArgs& p, bool bf16, hipStream_t st);
-hipError_t attn_bwd(const AttnArgs& p, bool bf16, hipStream_t st);
+hipError_t attn_bwd(const AttnArgs& p, bool bf16, float* ws, hipStream_t st);
+size_t attn_bwd_workspace_bytes(const AttnArgs& p);
 hipError_t zero_fill(float* p, size_t n, hipStream_t st);
 
 }  // namespace csa

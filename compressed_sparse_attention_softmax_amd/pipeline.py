@@ -32,6 +32,7 @@ class Buffers:
     dsink: Optional[torch.Tensor]
     dx: torch.Tensor
     dz: torch.Tensor
+    ws: torch.Tensor        # attention-backward workspace (csa_sparse_attn_bwd_workspace bytes)
 
 
 def allocate(dims: abi.csa_dims, dtype: torch.dtype, z_channels: int, device="cuda",
@@ -54,6 +55,7 @@ def allocate(dims: abi.csa_dims, dtype: torch.dtype, z_channels: int, device="cu
         dsink=torch.empty(H, dtype=f32, **e) if with_sink else None,
         dx=torch.empty(b, S, D, dtype=f32, **e),
         dz=torch.empty(b, S, z_channels, dtype=f32, **e),
+        ws=torch.empty(max(abi.csa_sparse_attn_bwd_workspace(dims), 16), dtype=torch.uint8, **e),
     )
 
 
@@ -68,7 +70,7 @@ def forward(dims, inp, buf: Buffers, scale: float, stream=None) -> None:
 def backward(dims, inp, buf: Buffers, scale: float, stream=None) -> None:
     abi.csa_sparse_attn_bwd(dims, inp["q"], inp["kv"], buf.c, buf.idx, inp.get("sink"), scale, buf.out,
                             buf.lse, inp["do"], buf.dq, buf.dkv, buf.dc,
-                            buf.dsink if inp.get("sink") is not None else None, stream=stream)
+                            buf.dsink if inp.get("sink") is not None else None, ws=buf.ws, stream=stream)
     abi.csa_compress_bwd(dims, inp["x"], inp["z"], buf.dc, buf.dx, buf.dz, stream=stream)
 
 

@@ -108,10 +108,26 @@ def test_dc_requires_compressed_rows():
     assert _bwd(P, P, P, N, c=N) == -1
 
 
-def test_workspace_queries_are_zero():
+def test_workspace_queries():
     lib = _lib()
     assert lib.csa_index_topk_workspace(ctypes.byref(_d())) == 0
-    assert lib.csa_sparse_attn_bwd_workspace(ctypes.byref(_d())) == 0
+    d = _d()
+    need = lib.csa_sparse_attn_bwd_workspace(ctypes.byref(d))
+    # at least Delta (b*sq*h floats) plus one query block's partial rows
+    assert need >= 4 * (d.b * d.sq * d.h + (d.window - 1 + 32) * d.d + d.sq // d.ratio * d.d)
+    assert lib.csa_sparse_attn_bwd_workspace(None) == 0
+
+
+def test_workspace_too_small_is_rejected():
+    lib = _lib()
+    d = _d()
+    need = lib.csa_sparse_attn_bwd_workspace(ctypes.byref(d))
+    rc = lib.csa_sparse_attn_bwd(ctypes.byref(d), 0, P, P, P, P, P, ctypes.c_float(1.0), P, P, P,
+                                 P, P, P, N, P, need - 4, N)
+    assert rc == -5, lib.csa_last_error()
+    rc = lib.csa_sparse_attn_bwd(ctypes.byref(d), 0, P, P, P, P, P, ctypes.c_float(1.0), P, P, P,
+                                 P, P, P, N, N, 0, N)
+    assert rc == -5
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -176,8 +176,9 @@ def _attn_case(wl, seed, idx_mode="random", with_sink=True, window_only=False, j
     dkv = torch.full((b, S, D), 3.0, device="cuda")
     dc = torch.full((b, nc, D), 3.0, device="cuda") if c is not None else None
     dsink = torch.full((H,), 3.0, device="cuda") if with_sink else None
+    ws = torch.empty(csa.csa_sparse_attn_bwd_workspace(dm), dtype=torch.uint8, device="cuda")
     csa.csa_sparse_attn_bwd(dm, inp["q"], inp["kv"], c, idx, inp["sink"], wl.scale, out, lse, inp["do"],
-                            dq, dkv, dc, dsink)
+                            dq, dkv, dc, dsink, ws=ws)
     torch.cuda.synchronize()
     rows = oracle.all_rows(b, S)
     q = f64(inp["q"]).reshape(b * S, H, D)

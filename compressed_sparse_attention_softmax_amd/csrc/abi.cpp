@@ -135,11 +135,7 @@ int csa_compress_bwd(const csa_dims* dm, int dtype, const void* x, const void* z
         return fail(CSA_ERR_ARG, "csa_compress_bwd: x, z, dc, dx and dz must be non-NULL");
     csa::CompressArgs a = compress_args(dm, x, z, z_channels);
     a.dc = dc; a.dx = dx; a.dz = dz;
-    hipStream_t st = (hipStream_t)stream;
-    hipError_t e = csa::zero_fill(dx, (size_t)dm->b * dm->sq * dm->d, st);
-    if (e == hipSuccess) e = csa::zero_fill(dz, (size_t)dm->b * dm->sq * z_channels, st);
-    if (e == hipSuccess) e = csa::compress_bwd(a, dtype == CSA_BF16, st);
-    return hip_status(e, "csa_compress_bwd");
+    return hip_status(csa::compress_bwd(a, dtype == CSA_BF16, (hipStream_t)stream), "csa_compress_bwd");
 }
 
 size_t csa_index_topk_workspace(const csa_dims* dm)

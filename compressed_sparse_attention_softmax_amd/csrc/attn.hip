@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256, 1) void attn_query_kernel(AttnArgs p, float* _
             lse2[ht] = hv ? p.lse[qrow * p.H + h] * LOG2E : INFINITY;
             if (hv && g == 0) {
                 delta[qrow * p.H + h] = part;
-                if (p.sink && p.dsink) atomicAdd(p.dsink + h, -exp2f(p.sink[h] * LOG2E - lse2[ht]) * part);
+                if (p.sink && p.dsink) atomicAdd(p.dsink + h, -fast_exp2(p.sink[h] * LOG2E - lse2[ht]) * part);
             }
         }
     }
@@ -250,45 +250,49 @@ __global__ __launch_bounds__(256, 1) void attn_query_kernel(AttnArgs p, float* _
                 }
             }
             if constexpr (!DQ) {
+                // exponentials are taken against a reference m2 that moves only when
+                // some logit of the wave exceeds it by more than 2^8 (then every
+                // lane re-bases); P <= 2^8 otherwise, and O / l is unchanged.
                 float x[2][4];
                 float mx = -INFINITY;
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const bool v = (mask >> (16 * rt + 4 * g + i)) & 1u;
-                        x[rt][i] = v ? s[rt][i] * sl2 : -INFINITY;
+                        x[rt][i] = s[rt][i] * sl2;
+                        if (mask != 0xffffffffu && !((mask >> (16 * rt + 4 * g + i)) & 1u)) x[rt][i] = -INFINITY;
                         mx = fmaxf(mx, x[rt][i]);
                     }
                 mx = fmaxf(mx, __shfl_xor(mx, 16));
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float mnew = fmaxf(m2[ht], mx);
-                const float alpha = exp2f(m2[ht] - mnew);
+                if (__any(mx > m2[ht] + 8.f)) {
+                    const float mnew = fmaxf(m2[ht], mx);
+                    const float alpha = fast_exp2(m2[ht] - mnew);
+                    l[ht] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) o[dt][ht] *= alpha;
+                    m2[ht] = mnew;
+                }
                 float rs = 0.f;
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float pv = exp2f(x[rt][i] - mnew);
+                        const float pv = fast_exp2(x[rt][i] - m2[ht]);
                         rs += pv;
                         pb[ht].v[4 * rt + i] = from_f32<T>(pv);
                     }
                 rs += __shfl_xor(rs, 16);
                 rs += __shfl_xor(rs, 32);
-                l[ht] = l[ht] * alpha + rs;
-                m2[ht] = mnew;
-                if (alpha != 1.f) {
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) o[dt][ht] *= alpha;
-                }
+                l[ht] += rs;
             } else {
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const bool v = (mask >> (16 * rt + 4 * g + i)) & 1u;
-                        const float pv = v ? exp2f(s[rt][i] * sl2 - lse2[ht]) : 0.f;
-                        pb[ht].v[4 * rt + i] = from_f32<T>(p.scale * pv * (dp[rt][i] - dlt[ht]));
+                        float pv = fast_exp2(s[rt][i] * sl2 - lse2[ht]);
+                        if (mask != 0xffffffffu && !((mask >> (16 * rt + 4 * g + i)) & 1u)) pv = 0.f;
+                        pb[ht].v[4 * rt + i] = from_f32<T>((dp[rt][i] - dlt[ht]) * (p.scale * pv));
                     }
             }
         }
@@ -341,6 +345,28 @@ __global__ __launch_bounds__(256, 1) void attn_query_kernel(AttnArgs p, float* _
 //                                     accumulators (lane (r, g) holds heads 4g+i
 //                                     of head tiles 2kk, 2kk+1), B = dO / Q
 //                                     from LDS through the transposing read
+// q/dO staging buffers of the key-stationary kernel: two (the next query
+// loads while this one computes) when they fit in LDS, else one.
+template <typename T, int D> constexpr int rows_stage_buffers()
+{
+    return 4 * 64 * D * (int)sizeof(T) + 8 * 1024 <= ATTN_LDS_LIMIT ? 2 : 1;
+}
+template <typename T, int D> constexpr int rows_per_wave_t() { return D <= 128 ? 64 : 16; }
+// LDS bytes of the key-stationary kernel without / with its key-row tile
+template <typename T, int D> constexpr size_t rows_lds_base()
+{
+    return 2 * (size_t)rows_stage_buffers<T, D>() * 64 * D * sizeof(T) + 4 * 64 * 4 +
+           (size_t)3 * 4 * rows_per_wave_t<T, D>() * 4;
+}
+template <typename T, int D> constexpr size_t rows_lds_tile()
+{
+    return (size_t)4 * rows_per_wave_t<T, D>() * (D + 16 / sizeof(T)) * sizeof(T);
+}
+template <typename T, int D> constexpr bool rows_tile_in_lds()
+{
+    return rows_lds_base<T, D>() + rows_lds_tile<T, D>() <= (size_t)ATTN_LDS_LIMIT;
+}
+
 struct RowsGeom {
     int Qb, nqb, WB, n_wt, n_ct, TR;   // query block, blocks, band rows, tiles, tile rows
     int64_t win_off, comp_off;   // float offsets of the two partial regions in the workspace
@@ -353,25 +379,26 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
 {
     constexpr int KS = D / 32, DT = D / 16, RT = RW / 16, TR = 4 * RW;
     constexpr int HP = 64;                       // heads, padded to 4 head tiles
-    constexpr int CH = 16 / sizeof(T);           // elements per 16-byte chunk
-    constexpr int QBYTES = HP * D * sizeof(T);   // one staged q (or dO) block
+    constexpr int QELEMS = HP * D;               // one staged q (or dO) block
+    constexpr int NBUF = rows_stage_buffers<T, D>();
+    constexpr int L16 = QELEMS * (int)sizeof(T) / 16;   // 16-byte pieces per block
+    static_assert(L16 % 256 == 0, "staging: whole 1 KiB wave loads");
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    T* q_lds = reinterpret_cast<T*>(smem);
-    T* do_lds = reinterpret_cast<T*>(smem + QBYTES);
-    float* lse_lds = reinterpret_cast<float*>(smem + 2 * QBYTES);
-    float* dlt_lds = lse_lds + HP;
-    unsigned* cnt_lds = reinterpret_cast<unsigned*>(dlt_lds + HP);
-    __shared__ int any_lds;
+    // [buf 0: q, dO][buf 1: q, dO (double buffering only)][lse x2][Delta x2][mult x3]
+    T* stage_base = reinterpret_cast<T*>(smem);
+    float* lse_lds = reinterpret_cast<float*>(smem + 2 * NBUF * (size_t)QELEMS * sizeof(T));
+    float* dlt_lds = lse_lds + 2 * HP;
+    unsigned* cnt_lds = reinterpret_cast<unsigned*>(dlt_lds + 2 * HP);
 
     const int wave = threadIdx.x / WAVE, lane = lane_id();
     const int g = lane / 16, n16 = lane % 16;
-    const int bi = blockIdx.z, qb = blockIdx.y, slot = blockIdx.x;
+    // heaviest query blocks (latest queries: longest valid prefix) are dispatched first
+    const int bi = blockIdx.z, qb = geo.nqb - 1 - blockIdx.y, slot = blockIdx.x;
     const int t0 = qb * geo.Qb, t1 = min(p.S, t0 + geo.Qb);
     const bool win = slot < geo.n_wt;
     const int tile = win ? slot : slot - geo.n_wt;
     const int i0 = tile * TR;                    // first partial row of the tile
-    int base_row;                                // key row of partial row 0
-    int nrows_valid;                             // partial rows [0, nrows_valid) are meaningful
+    int base_row, nrows_valid;                   // key row of partial row 0; rows that are meaningful
     if (win) {
         if (i0 >= geo.WB) return;
         base_row = t0 - p.W + 1;
@@ -383,11 +410,26 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
         nrows_valid = nvmax;
     }
     const T* rows = win ? (const T*)p.kv + (int64_t)bi * p.S * D : (const T*)p.c + (int64_t)bi * p.nc * D;
-    const int rmax = win ? p.S : p.nc;           // key rows that exist
+    const int rmax = win ? p.S : p.nc;
+    const int tile_lo = base_row + i0;           // key range of the tile
+    const int tile_hi = base_row + min(i0 + TR, nrows_valid);
+    // queries of the block that can reach the tile: a contiguous range
+    int ta, tb;
+    if (win) {
+        ta = max(t0, tile_lo);
+        tb = min(t1, tile_hi + p.W - 1);
+    } else {
+        ta = max(t0, (tile_lo + 1) * p.r - 1);
+        tb = t1;
+    }
 
-    // this wave's rows as B operands (k = d, n = r)
-    Frag<T> rb[RT][KS];
-    int rkey[RT];                                // key row of column n16 of row tile rt (-1: none)
+    // this wave's rows as B operands (k = d, n = r): in registers, or (when the
+    // LDS budget allows) in a wave-private LDS tile to leave registers for S / dP
+    constexpr bool ROWS_LDS = rows_tile_in_lds<T, D>();
+    constexpr int RROW = D + row_pad<T>();
+    T* rtile = reinterpret_cast<T*>(reinterpret_cast<char*>(cnt_lds) + 3 * TR * 4) + (size_t)wave * RW * RROW;
+    Frag<T> rb[ROWS_LDS ? 1 : RT][KS];
+    int rkey[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int i = i0 + RW * wave + 16 * rt + n16;
@@ -396,7 +438,11 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
         rkey[rt] = ok ? key : -1;
         const T* src = rows + (int64_t)(ok ? key : 0) * D;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) rb[rt][ks] = load_frag(src + 32 * ks + 8 * g);
+        for (int ks = 0; ks < KS; ++ks) {
+            const Frag<T> f = load_frag(src + 32 * ks + 8 * g);
+            if constexpr (ROWS_LDS) store_frag(rtile + (16 * rt + n16) * RROW + 32 * ks + 8 * g, f);
+            else rb[rt][ks] = f;
+        }
     }
     f32x4 acc[RT][DT];
 #pragma unroll
@@ -404,78 +450,95 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = f4zero();
 
-    const float sl2 = p.scale * LOG2E;
-    const int tile_lo = base_row + i0;           // key range of the tile
-    const int tile_hi = base_row + min(i0 + TR, nrows_valid);
-    for (int t = t0; t < t1; ++t) {
-        // does t have any candidate in this tile?
-        if (win) {
-            if (tile_hi <= t - p.W + 1 || tile_lo > t) continue;
-        } else {
-            if (tile_lo >= min((t + 1) / p.r, p.nc)) continue;
-        }
+    // Stage q[t] and dO[t] into buffer `buf` with asynchronous global->LDS
+    // loads.  16-byte piece s of the block lands at LDS piece s; its source is
+    // chosen so that the LDS block holds rows of 8-element units permuted as
+    // unit u of row h at u ^ (h & 7).  Also lse, Delta (plain loads) and the
+    // multiplicities of the tile's rows for query t in cnt buffer `cb`.
+    auto stage = [&](int t, int buf, int cb) {
         const int64_t qrow = (int64_t)bi * p.S + t;
-        __syncthreads();
-        // stage q[t], dO[t] (8-element units permuted per row, unit u at u ^ (row & 7)),
-        // lse, Delta and the multiplicities of the tile's rows
-        {
-            const T* qsrc = (const T*)p.q + qrow * p.H * D;
-            const T* dsrc = (const T*)p.dout + qrow * p.H * D;
-            constexpr int NCHUNK = HP * D / CH;
-            for (int cidx = threadIdx.x; cidx < NCHUNK; cidx += 256) {
-                const int h = cidx / (D / CH), cc = cidx % (D / CH);
-                const int d0 = cc * CH;
-                const int dst = h * D + ((((d0 >> 3) ^ (h & 7)) << 3) | (d0 & 7));
-                uint4 vq = make_uint4(0u, 0u, 0u, 0u), vd = vq;
-                if (h < p.H) {
-                    vq = *reinterpret_cast<const uint4*>(qsrc + h * D + cc * CH);
-                    vd = *reinterpret_cast<const uint4*>(dsrc + h * D + cc * CH);
-                }
-                *reinterpret_cast<uint4*>(q_lds + dst) = vq;
-                *reinterpret_cast<uint4*>(do_lds + dst) = vd;
-            }
-            if (threadIdx.x < HP) {
-                const int h = threadIdx.x;
-                lse_lds[h] = h < p.H ? p.lse[qrow * p.H + h] * LOG2E : INFINITY;
-                dlt_lds[h] = h < p.H ? delta[qrow * p.H + h] : 0.f;
-            }
-            if (!win) {
-                for (int i = threadIdx.x; i < TR; i += 256) cnt_lds[i] = 0u;
-                if (threadIdx.x == 0) any_lds = 0;
-            }
+        const T* qsrc = (const T*)p.q + qrow * p.H * D;
+        const T* dsrc = (const T*)p.dout + qrow * p.H * D;
+        T* qdst = stage_base + (size_t)(2 * buf) * QELEMS;
+        T* ddst = qdst + QELEMS;
+        constexpr int PER_ROW = D * (int)sizeof(T) / 16;   // 16-byte pieces per row
+#pragma unroll
+        for (int k = 0; k < L16 / 256; ++k) {
+            const int piece = (k * 4 + wave) * WAVE + lane;
+            const int h = piece / PER_ROW, pr = piece % PER_ROW;
+            // piece pr of LDS row h holds elements [pr*E, pr*E+E) of the permuted row
+            constexpr int E = 16 / (int)sizeof(T);
+            const int pos = pr * E;                       // element position in LDS row
+            const int unit = (pos >> 3) ^ (h & 7);        // source unit
+            const int srcel = (unit << 3) | (pos & 7);
+            const int hh = h < p.H ? h : 0;               // padded heads read row 0 (masked later)
+            const size_t wbase = (size_t)(k * 4 + wave) * WAVE * 16;   // wave's 1 KiB in bytes
+            __builtin_amdgcn_global_load_lds((const void*)(qsrc + hh * D + srcel),
+                                             (__attribute__((address_space(3))) void*)((char*)qdst + wbase), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(dsrc + hh * D + srcel),
+                                             (__attribute__((address_space(3))) void*)((char*)ddst + wbase), 16, 0, 0);
+        }
+        if (threadIdx.x < HP) {
+            const int h = threadIdx.x;
+            lse_lds[buf * HP + h] = h < p.H ? p.lse[qrow * p.H + h] * LOG2E : INFINITY;
+            dlt_lds[buf * HP + h] = h < p.H ? delta[qrow * p.H + h] : 0.f;
         }
         if (!win) {
-            __syncthreads();
+            unsigned* cnt = cnt_lds + cb * TR;
             const int nv = min((t + 1) / p.r, p.nc);
-            int found = 0;
             if (p.idx) {
                 const int32_t* irow = p.idx + qrow * p.kp;
                 for (int s = threadIdx.x; s < p.kp; s += 256) {
                     const int j = irow[s];
-                    if (j >= 0 && j < nv && j >= tile_lo && j < tile_hi) {
-                        atomicAdd(&cnt_lds[j - tile_lo], 1u);
-                        found = 1;
-                    }
+                    if (j >= 0 && j < nv && j >= tile_lo && j < tile_hi) atomicAdd(&cnt[j - tile_lo], 1u);
                 }
             } else {
-                for (int j = tile_lo + threadIdx.x; j < min(tile_hi, nv); j += 256) {
-                    cnt_lds[j - tile_lo] = 1u;
-                    found = 1;
-                }
+                for (int j = tile_lo + threadIdx.x; j < min(tile_hi, nv); j += 256) cnt[j - tile_lo] = 1u;
             }
-            if (found) any_lds = 1;
         }
+    };
+
+    if (!win) {
+        for (int i = threadIdx.x; i < 3 * TR; i += 256) cnt_lds[i] = 0u;
         __syncthreads();
-        if (!win && !any_lds) continue;
-        // multiplicity of the columns this lane holds
-        float mult[RT];
+    }
+    const float sl2 = p.scale * LOG2E;
+    if (NBUF == 2 && ta < tb) stage(ta, 0, 0);
+    for (int t = ta; t < tb; ++t) {
+        const int it = t - ta, buf = NBUF == 2 ? (it & 1) : 0, cb = it % 3;
+        if constexpr (NBUF == 2) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();                               // stage(t) visible; compute(t-1) done
+            if (t + 1 < tb) stage(t + 1, buf ^ 1, (it + 1) % 3);
+        } else {
+            __syncthreads();                               // compute(t-1) done with the buffer
+            stage(t, 0, cb);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();                               // stage(t) visible
+        }
+        if (!win) {                                        // buffer of t+2: last read by compute(t-1)
+            unsigned* nxt = cnt_lds + ((it + 2) % 3) * TR;
+            for (int i = threadIdx.x; i < TR; i += 256) nxt[i] = 0u;
+        }
+        const T* q_lds = stage_base + (size_t)(2 * buf) * QELEMS;
+        const T* do_lds = q_lds + QELEMS;
+        const float* ls_b = lse_lds + buf * HP;
+        const float* dl_b = dlt_lds + buf * HP;
+        float mult[RT], msc[RT];                           // multiplicity, and times scale
+        bool any = false;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int key = rkey[rt];
-            if (key < 0) { mult[rt] = 0.f; continue; }
-            if (win) mult[rt] = (key <= t && key > t - p.W) ? 1.f : 0.f;
-            else mult[rt] = (float)cnt_lds[key - tile_lo];
+            float m = 0.f;
+            if (key >= 0) {
+                if (win) m = (key <= t && key > t - p.W) ? 1.f : 0.f;
+                else m = (float)cnt_lds[cb * TR + key - tile_lo];
+            }
+            mult[rt] = m;
+            msc[rt] = m * p.scale;
+            any |= m != 0.f;
         }
+        if (!__any(any)) continue;                         // nothing of t in this wave's rows
 #pragma unroll
         for (int kk = 0; kk < HP / 32; ++kk) {
             Frag<T> pa[RT], sa[RT];
@@ -485,32 +548,37 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
                 float ls[4], dl[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    ls[i] = lse_lds[16 * ht + 4 * g + i];
-                    dl[i] = dlt_lds[16 * ht + 4 * g + i];
+                    ls[i] = ls_b[16 * ht + 4 * g + i];
+                    dl[i] = dl_b[16 * ht + 4 * g + i];
                 }
                 Frag<T> qa[KS], da[KS];
+                const int hrow = 16 * ht + n16;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const int hrow = 16 * ht + n16;
                     const int off = hrow * D + (((4 * ks + g) ^ (hrow & 7)) << 3);   // d = 32 ks + 8 g
                     qa[ks] = load_frag(q_lds + off);
                     da[ks] = load_frag(do_lds + off);
                 }
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
-                    f32x4 s = f4zero(), dp = f4zero();
+                    f32x4 sv = f4zero(), dp = f4zero();
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
-                        s = mfma16(qa[ks], rb[rt][ks], s);
-                        dp = mfma16(da[ks], rb[rt][ks], dp);
+                        Frag<T> bk;
+                        if constexpr (ROWS_LDS) bk = load_frag(rtile + (16 * rt + n16) * RROW + 32 * ks + 8 * g);
+                        else bk = rb[rt][ks];
+                        sv = mfma16(qa[ks], bk, sv);
+                        dp = mfma16(da[ks], bk, dp);
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float pv = mult[rt] * exp2f(s[i] * sl2 - ls[i]);
-                        pa[rt].v[4 * hh + i] = from_f32<T>(pv);
-                        sa[rt].v[4 * hh + i] = from_f32<T>(p.scale * pv * (dp[i] - dl[i]));
+                        const float e = fast_exp2(sv[i] * sl2 - ls[i]);
+                        pa[rt].v[4 * hh + i] = from_f32<T>(mult[rt] * e);
+                        sa[rt].v[4 * hh + i] = from_f32<T>((dp[i] - dl[i]) * (msc[rt] * e));
                     }
                 }
+                // keep one head tile's S / dP live at a time (register pressure)
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
@@ -522,6 +590,7 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
                     acc[rt][dt] = mfma16(sa[rt], qbf, acc[rt][dt]);
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     // partial rows of this wave: lane holds dR[r = 16 rt + 4g + i][d = 16 dt + n16]
@@ -555,6 +624,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs p, RowsGeom g
         const int q_lo = u / geo.Qb;
         const int q_hi = min(geo.nqb - 1, (u + p.W - 1) / geo.Qb);
         float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
         for (int q = q_lo; q <= q_hi; ++q) {
             const int i = u - (q * geo.Qb - p.W + 1);
             const float4 x = *reinterpret_cast<const float4*>(
@@ -569,6 +639,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs p, RowsGeom g
         const int bi = (int)(row / p.nc), j = (int)(row % p.nc);
         const int q_lo = ((j + 1) * p.r + geo.Qb - 1) / geo.Qb - 1;
         float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
         for (int q = max(q_lo, 0); q < geo.nqb; ++q) {
             const float4 x = *reinterpret_cast<const float4*>(
                 ws + geo.comp_off + (((int64_t)bi * geo.nqb + q) * p.nc + j) * D + 4 * v);
@@ -653,8 +724,8 @@ hipError_t query_dispatch(const AttnArgs& p, bool dq, float* delta, hipStream_t 
 template <typename T, int D>
 hipError_t launch_rows(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStream_t st)
 {
-    constexpr int RW = D <= 128 ? 64 : 16;
-    const size_t lds = 2 * (size_t)64 * D * sizeof(T) + 2 * 64 * 4 + (size_t)4 * RW * 4;
+    constexpr int RW = rows_per_wave_t<T, D>();
+    const size_t lds = rows_lds_base<T, D>() + (rows_tile_in_lds<T, D>() ? rows_lds_tile<T, D>() : 0);
     if (lds > (size_t)ATTN_LDS_LIMIT) return hipErrorInvalidValue;
     auto kern = attn_rows_kernel<T, D, RW>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -106,6 +106,10 @@ __device__ __forceinline__ int wave_sum_i(int v)
     return v;
 }
 
+// 2^x on the transcendental unit (v_exp_f32): one instruction; results
+// below 2^-126 flush to zero, which is harmless for softmax weights.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 

@@ -41,6 +41,7 @@ constexpr int CHUNK = 32;
 template <typename T> constexpr int row_pad() { return 16 / (int)sizeof(T); }
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
 // (i % 4) of the 8-byte words addressed by lanes 4k + i/4, k = 0..3.
@@ -106,50 +107,74 @@ struct Cand {
         nslots = nwin + ncs;
     }
     // Row code of a slot: u (window row), j | 0x40000000 (compressed row),
-    // or -1 (invalid: padding, out of range or not yet valid).
-    __device__ __forceinline__ int code(int slot) const
+    // or -1 (invalid: padding, out of range or not yet valid).  With
+    // `use_ids` the index row is read from its copy `ids` in LDS.
+    __device__ __forceinline__ int code(int slot, bool use_ids, const int32_t* ids) const
     {
         if (slot < nwin) return u0 + slot;
         if (slot >= nslots) return -1;
         const int s2 = slot - nwin;
-        const int j = irow ? irow[s2] : s2;
+        const int j = use_ids ? ((const lds_i32*)ids)[s2] : (irow ? irow[s2] : s2);
         return (j < 0 || j >= nv) ? -1 : (j | 0x40000000);
     }
     __device__ __forceinline__ const T* row_ptr(int code) const
     {
-        if (code < 0) return kv + (int64_t)t * D;
-        if (code & 0x40000000) return c + (int64_t)(code & 0x3fffffff) * D;
-        return kv + (int64_t)code * D;
+        const T* base = (code >= 0 && (code & 0x40000000)) ? c : kv;
+        const int row = code < 0 ? t : (code & 0x3fffffff);
+        return base + (int64_t)row * D;
     }
 };
 
 // ------------------------------------------- forward / dQ (query-major)
-// S^T[r, h] = R[r, :] . Q[h, :]      A = gathered rows (m = r, k = d)
+// The G waves of a query (G = 1 unless head groups are split) share one
+// double-buffered LDS tile per query.  Chunk k+1's rows are gathered from
+// global memory into registers (each lane loads 16-byte pieces of its rows)
+// while chunk k computes, and written to the other buffer afterwards; rows
+// are stored with 8-element units permuted per row (unit u of row r at
+// u ^ (r & 7)) so both reads below are free of bank conflicts.
+// S^T[r, h] = R[r, :] . Q[h, :]      A = rows from LDS (m = r, k = d)
 //                                    B = Q^T (k = d, n = h), registers
 // forward: online softmax per column h (lane), base-2 exponentials, then
-//   O^T[d, h] += R^T P^T              A = R^T from the LDS tile, B = P^T
-//                                     straight from the S^T accumulators
-// dQ mode: dP^T = R . dO^T, P^T = exp(S^T scale - lse), dS'^T = scale P^T (dP^T - Delta),
+//   O^T[d, h] += R^T P^T              A = R^T through the transposing read,
+//                                     B = P^T straight from the S^T accumulators
+// dQ mode: dP^T = R . dO^T, scale*P^T = exp(S^T scale - lse), dS'^T = scale P^T (dP^T - Delta),
 //   dQ^T[d, h] += R^T dS'^T           same operand shapes
+template <typename T, int D> constexpr int chunk_bytes() { return CHUNK * D * (int)sizeof(T); }
+
 template <typename T, int D, int HT, int G, bool DQ>
-__global__ __launch_bounds__(256, 1) void attn_query_kernel(AttnArgs p, float* __restrict__ delta)
+__global__ __launch_bounds__(256, (D <= 128 && HT <= 2) ? 2 : 1)
+void attn_query_kernel(AttnArgs p, float* __restrict__ delta, int idx_lds)
 {
     constexpr int KS = D / 32, DT = D / 16, QPW = 4 / G;
-    constexpr int ROW = D + row_pad<T>();
+    constexpr int CHB = chunk_bytes<T, D>();
+    constexpr int PPR = D * (int)sizeof(T) / 16;  // 16-byte pieces per row
+    constexpr int E16 = 16 / (int)sizeof(T);      // elements per piece
+    constexpr int NPL = CHB / (16 * WAVE * G);    // pieces each lane of the query's waves carries
+    static_assert(NPL * 16 * WAVE * G == CHB, "chunk pieces split evenly over the query's waves");
+    typedef uint32_t piece_t __attribute__((ext_vector_type(4)));
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int wave = threadIdx.x / WAVE, lane = lane_id();
     const int g = lane / 16, n16 = lane % 16;
-    T* tile = reinterpret_cast<T*>(smem) + (size_t)wave * CHUNK * ROW;
+    const int qs = wave / G, sub = wave % G;      // query slot in the workgroup, wave within the query
+    char* tiles = smem + (size_t)qs * 2 * CHB;
 
     const int bi = blockIdx.y;
-    const int t = blockIdx.x * QPW + wave / G;
-    if (t >= p.S) return;
-    const int h0 = (wave % G) * 16 * HT;
+    const int t = blockIdx.x * QPW + qs;
+    const bool active = t < p.S;                  // inactive waves still join the barriers (G > 1)
+    const int h0 = sub * 16 * HT;
     Cand<T> cand;
-    cand.init(p, bi, t);
-    const int64_t qrow = (int64_t)bi * p.S + t;
+    cand.init(p, bi, active ? t : p.S - 1);
+    const int64_t qrow = (int64_t)bi * p.S + (active ? t : p.S - 1);
     const float sl2 = p.scale * LOG2E;
+    [[maybe_unused]] const float lsc = __log2f(p.scale);
     const T* qp = (const T*)p.q + qrow * p.H * D;
+    // the query's index row, read once into LDS: per-chunk slot lookups do not wait on memory
+    int32_t* ids = reinterpret_cast<int32_t*>(smem + (size_t)QPW * 2 * CHB) + (size_t)qs * p.kp;
+    const bool use_ids = idx_lds && cand.irow;
+    if (use_ids) {
+        for (int s0 = sub * WAVE + lane; s0 < p.kp; s0 += G * WAVE) ids[s0] = cand.irow[s0];
+        if constexpr (G > 1) __syncthreads();
+    }
 
     Frag<T> qb[HT][KS];
     [[maybe_unused]] Frag<T> db[HT][KS];
@@ -183,14 +208,14 @@ __global__ __launch_bounds__(256, 1) void attn_query_kernel(AttnArgs p, float* _
             part += __shfl_xor(part, 32);
             dlt[ht] = part;
             lse2[ht] = hv ? p.lse[qrow * p.H + h] * LOG2E : INFINITY;
-            if (hv && g == 0) {
+            if (active && hv && g == 0) {
                 delta[qrow * p.H + h] = part;
                 if (p.sink && p.dsink) atomicAdd(p.dsink + h, -fast_exp2(p.sink[h] * LOG2E - lse2[ht]) * part);
             }
         }
     }
     if constexpr (DQ) {
-        if (!p.dq) return;
+        if (!p.dq) return;                        // uniform over the workgroup
     }
     f32x4 o[DT][HT];
 #pragma unroll
@@ -198,118 +223,166 @@ __global__ __launch_bounds__(256, 1) void attn_query_kernel(AttnArgs p, float* _
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) o[dt][ht] = f4zero();
 
-    // rows of chunk c0 as A operands; lane (n16, rt) loads slot 16 rt + n16
-    auto load_chunk = [&](int c0, Frag<T> (&ra)[2][KS], uint32_t& mask) {
-        const int code = cand.code(c0 + (lane & 31));
-        mask = (uint32_t)__ballot(code >= 0);
+    // gather chunk c0's rows into registers; returns the chunk's candidate mask
+    piece_t rg[NPL];
+    auto fetch = [&](int c0) -> uint32_t {
+        const int code = cand.code(c0 + (lane & 31), use_ids, ids);
+        const uint32_t mask = (uint32_t)__ballot(code >= 0);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const T* src = cand.row_ptr(__shfl(code, 16 * rt + n16));
+        for (int k = 0; k < NPL; ++k) {
+            const int piece = (sub + G * k) * WAVE + lane;
+            const int r = piece / PPR, pc = piece % PPR;
+            rg[k] = *reinterpret_cast<const piece_t*>(cand.row_ptr(__shfl(code, r)) + pc * E16);
+        }
+        return mask;
+    };
+    // write the gathered rows to buffer buf, units permuted per row
+    auto stash = [&](int buf) {
+        T* dst = reinterpret_cast<T*>(tiles + (size_t)buf * CHB);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) ra[rt][ks] = load_frag(src + 32 * ks + 8 * g);
+        for (int k = 0; k < NPL; ++k) {
+            const int piece = (sub + G * k) * WAVE + lane;
+            const int r = piece / PPR, pos = (piece % PPR) * E16;
+            *reinterpret_cast<piece_t*>(dst + r * D + ((((pos >> 3) ^ (r & 7))) << 3) + (pos & 7)) = rg[k];
         }
     };
 
-    Frag<T> ra[2][KS];
-    uint32_t mask = 0;
-    int c0 = 0;
-    // skip leading chunks that hold no candidate (e.g. all -1)
-    for (; c0 < cand.nslots; c0 += CHUNK) {
-        load_chunk(c0, ra, mask);
-        if (mask) break;
-    }
-    while (c0 < cand.nslots) {
-        // prefetch the next chunk with a candidate while this one computes
-        Frag<T> rn[2][KS];
-        uint32_t mn = 0;
-        int c1 = c0 + CHUNK;
-        for (; c1 < cand.nslots; c1 += CHUNK) {
-            load_chunk(c1, rn, mn);
-            if (mn) break;
-        }
+    auto process = [&](const T* tile, uint32_t mask) {
+        // S^T (and dP^T) for every head tile first: straight-line MFMA work
+        f32x4 s[HT][2];
+        [[maybe_unused]] f32x4 dp[HT][2];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < 2; ++rt) {
+            Frag<T> ra[KS];
+            const int r = 16 * rt + n16;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) store_frag(tile + (16 * rt + n16) * ROW + 32 * ks + 8 * g, ra[rt][ks]);
-        Frag<T> pb[HT];
+            for (int ks = 0; ks < KS; ++ks) ra[ks] = load_frag(tile + r * D + (((4 * ks + g) ^ (r & 7)) << 3));
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            f32x4 s[2];
-            [[maybe_unused]] f32x4 dp[2];
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
+            for (int ht = 0; ht < HT; ++ht) {
                 f32x4 acc = f4zero();
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) acc = mfma16(ra[rt][ks], qb[ht][ks], acc);
-                s[rt] = acc;
+                for (int ks = 0; ks < KS; ++ks) acc = mfma16(ra[ks], qb[ht][ks], acc);
+                s[ht][rt] = acc;
                 if constexpr (DQ) {
                     f32x4 a2 = f4zero();
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) a2 = mfma16(ra[rt][ks], db[ht][ks], a2);
-                    dp[rt] = a2;
+                    for (int ks = 0; ks < KS; ++ks) a2 = mfma16(ra[ks], db[ht][ks], a2);
+                    dp[ht][rt] = a2;
                 }
             }
-            if constexpr (!DQ) {
-                // exponentials are taken against a reference m2 that moves only when
-                // some logit of the wave exceeds it by more than 2^8 (then every
-                // lane re-bases); P <= 2^8 otherwise, and O / l is unchanged.
-                float x[2][4];
-                float mx = -INFINITY;
+        }
+        if (mask != 0xffffffffu) {              // partial chunk (rare): non-candidates get -inf
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        x[rt][i] = s[rt][i] * sl2;
-                        if (mask != 0xffffffffu && !((mask >> (16 * rt + 4 * g + i)) & 1u)) x[rt][i] = -INFINITY;
-                        mx = fmaxf(mx, x[rt][i]);
+                for (int i = 0; i < 4; ++i)
+                    if (!((mask >> (16 * rt + 4 * g + i)) & 1u)) {
+#pragma unroll
+                        for (int ht = 0; ht < HT; ++ht) s[ht][rt][i] = -INFINITY;
                     }
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                if (__any(mx > m2[ht] + 8.f)) {
-                    const float mnew = fmaxf(m2[ht], mx);
+        }
+        Frag<T> pb[HT];
+        if constexpr (!DQ) {
+            // exponentials are taken against a reference m2 that moves only when
+            // some logit of the wave exceeds it by more than 2^8 (then every
+            // head re-bases); P <= 2^8 otherwise, and O / l is unchanged.
+            float mx[HT];
+            bool need = false;
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                float m = fmaxf(fmaxf(fmaxf(s[ht][0][0], s[ht][0][1]), fmaxf(s[ht][0][2], s[ht][0][3])),
+                                fmaxf(fmaxf(s[ht][1][0], s[ht][1][1]), fmaxf(s[ht][1][2], s[ht][1][3])));
+                m = fmaxf(m, __shfl_xor(m, 16));
+                m = fmaxf(m, __shfl_xor(m, 32));
+                mx[ht] = m * sl2;                  // scale > 0: max commutes with it
+                need |= mx[ht] > m2[ht] + 8.f;
+            }
+            if (__any(need)) {                     // rare
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) {
+                    const float mnew = fmaxf(m2[ht], mx[ht]);
                     const float alpha = fast_exp2(m2[ht] - mnew);
                     l[ht] *= alpha;
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) o[dt][ht] *= alpha;
                     m2[ht] = mnew;
                 }
+            }
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                const float negm = -m2[ht];
                 float rs = 0.f;
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float pv = fast_exp2(x[rt][i] - m2[ht]);
+                        const float pv = fast_exp2(fmaf(s[ht][rt][i], sl2, negm));
                         rs += pv;
                         pb[ht].v[4 * rt + i] = from_f32<T>(pv);
                     }
                 rs += __shfl_xor(rs, 16);
                 rs += __shfl_xor(rs, 32);
                 l[ht] += rs;
-            } else {
+            }
+        } else {
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                // scale * P in one exponential: 2^(s*scale*log2e + log2(scale) - lse*log2e)
+                const float off = lsc - lse2[ht];
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        float pv = fast_exp2(s[rt][i] * sl2 - lse2[ht]);
-                        if (mask != 0xffffffffu && !((mask >> (16 * rt + 4 * g + i)) & 1u)) pv = 0.f;
-                        pb[ht].v[4 * rt + i] = from_f32<T>((dp[rt][i] - dlt[ht]) * (p.scale * pv));
+                        const float ps = fast_exp2(fmaf(s[ht][rt][i], sl2, off));
+                        pb[ht].v[4 * rt + i] = from_f32<T>((dp[ht][rt][i] - dlt[ht]) * ps);
                     }
             }
         }
         // O^T += R^T P^T   (or dQ^T += R^T dS'^T)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const Frag<T> a = rows_operand<T>(tile, ROW, 0, 16 * dt, false);
+            const Frag<T> a = rows_operand<T>(tile, D, 0, 16 * dt, true);
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) o[dt][ht] = mfma16(a, pb[ht], o[dt][ht]);
         }
-        c0 = c1;
-        mask = mn;
+    };
+
+    // slots past the last candidate need no chunk (index rows usually end in -1 padding)
+    int last = -1;
+    for (int s0 = 0; s0 < cand.nslots; s0 += WAVE)
+        if (cand.code(s0 + lane, use_ids, ids) >= 0) last = s0 + lane;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+    for (int o2 = 32; o2 >= 1; o2 >>= 1) last = max(last, __shfl_xor(last, o2));
+    const int nch = active ? (last + CHUNK) / CHUNK : 0;
+    int nloop = nch;
+    if constexpr (G > 1) {
+        // every wave of the workgroup runs the same number of barrier rounds:
+        // the longest candidate list among its queries
+        __shared__ int nch_s[4];
+        if (lane == 0 && sub == 0) nch_s[qs] = nch;
+        __syncthreads();
+        nloop = 0;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) ra[rt][ks] = rn[rt][ks];
+        for (int i = 0; i < QPW; ++i) nloop = max(nloop, nch_s[i]);
     }
+    // every load so far (Q, dO, O, the index row) has landed: the loop below
+    // then waits only on its own row gathers
+    __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)
+    uint32_t mcur = 0u, mnext = 0u;
+    if (nch > 0) { mcur = fetch(0); stash(0); }
+    if (nch > 1) mnext = fetch(CHUNK);
+    if constexpr (G > 1) __syncthreads();
+    for (int k = 0; k < nloop; ++k) {
+        if (G == 1 || k < nch) process(reinterpret_cast<const T*>(tiles + (size_t)(k & 1) * CHB), mcur);
+        if (k + 1 < nch) { stash((k + 1) & 1); mcur = mnext; }
+        if (k + 2 < nch) mnext = fetch(CHUNK * (k + 2));
+        // G > 1: chunk k+1 fully written, chunk k read by every wave, before
+        // the next round reads k+1 and refills k's buffer.  G == 1: a wave's
+        // LDS accesses run in order, so its own reads of a buffer finish
+        // before its later writes to it.
+        if constexpr (G > 1) __syncthreads();
+    }
+    if (!active) return;
     // epilogue: lane holds X^T[d = 16 dt + 4g + i][h = h0 + 16 ht + n16]
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -455,6 +528,8 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
     // chosen so that the LDS block holds rows of 8-element units permuted as
     // unit u of row h at u ^ (h & 7).  Also lse, Delta (plain loads) and the
     // multiplicities of the tile's rows for query t in cnt buffer `cb`.
+    constexpr int IDX_REGS = 2048 / 256;          // K' <= 2048
+    int jreg[IDX_REGS];
     auto stage = [&](int t, int buf, int cb) {
         const int64_t qrow = (int64_t)bi * p.S + t;
         const T* qsrc = (const T*)p.q + qrow * p.H * D;
@@ -484,17 +559,30 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
             dlt_lds[buf * HP + h] = h < p.H ? delta[qrow * p.H + h] : 0.f;
         }
         if (!win) {
-            unsigned* cnt = cnt_lds + cb * TR;
-            const int nv = min((t + 1) / p.r, p.nc);
             if (p.idx) {
+                // index entries are only loaded here; count() consumes them later
                 const int32_t* irow = p.idx + qrow * p.kp;
-                for (int s = threadIdx.x; s < p.kp; s += 256) {
-                    const int j = irow[s];
-                    if (j >= 0 && j < nv && j >= tile_lo && j < tile_hi) atomicAdd(&cnt[j - tile_lo], 1u);
+#pragma unroll
+                for (int k = 0; k < IDX_REGS; ++k) {
+                    const int s = threadIdx.x + 256 * k;
+                    jreg[k] = s < p.kp ? irow[s] : -1;
                 }
             } else {
+                unsigned* cnt = cnt_lds + cb * TR;
+                const int nv = min((t + 1) / p.r, p.nc);
                 for (int j = tile_lo + threadIdx.x; j < min(tile_hi, nv); j += 256) cnt[j - tile_lo] = 1u;
             }
+        }
+    };
+    // multiplicities of the tile's rows for query t from the staged index entries
+    auto count = [&](int t, int cb) {
+        if (win || !p.idx) return;
+        unsigned* cnt = cnt_lds + cb * TR;
+        const int nv = min((t + 1) / p.r, p.nc);
+#pragma unroll
+        for (int k = 0; k < IDX_REGS; ++k) {
+            const int j = jreg[k];
+            if (j >= 0 && j < nv && j >= tile_lo && j < tile_hi) atomicAdd(&cnt[j - tile_lo], 1u);
         }
     };
 
@@ -503,7 +591,10 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
         __syncthreads();
     }
     const float sl2 = p.scale * LOG2E;
-    if (NBUF == 2 && ta < tb) stage(ta, 0, 0);
+    if (NBUF == 2 && ta < tb) {
+        stage(ta, 0, 0);
+        count(ta, 0);
+    }
     for (int t = ta; t < tb; ++t) {
         const int it = t - ta, buf = NBUF == 2 ? (it & 1) : 0, cb = it % 3;
         if constexpr (NBUF == 2) {
@@ -513,6 +604,7 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
         } else {
             __syncthreads();                               // compute(t-1) done with the buffer
             stage(t, 0, cb);
+            count(t, cb);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();                               // stage(t) visible
         }
@@ -538,7 +630,7 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
             msc[rt] = m * p.scale;
             any |= m != 0.f;
         }
-        if (!__any(any)) continue;                         // nothing of t in this wave's rows
+        if (__any(any)) {                                  // anything of t in this wave's rows?
 #pragma unroll
         for (int kk = 0; kk < HP / 32; ++kk) {
             Frag<T> pa[RT], sa[RT];
@@ -591,6 +683,10 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
+        }
+        }
+        if constexpr (NBUF == 2) {
+            if (t + 1 < tb) count(t + 1, (it + 1) % 3);     // its index loads had compute(t) to land
         }
     }
     // partial rows of this wave: lane holds dR[r = 16 rt + 4g + i][d = 16 dt + n16]
@@ -687,13 +783,19 @@ template <typename T, int D, int HT>
 hipError_t launch_query(const AttnArgs& p, bool dq, float* delta, hipStream_t st)
 {
     const int gper = (p.H + 16 * HT - 1) / (16 * HT);
-    const size_t lds = (size_t)4 * CHUNK * (D + row_pad<T>()) * sizeof(T);
+    const int G = gper <= 1 ? 1 : (gper <= 2 ? 2 : 4);
+    const int qpw = 4 / G;
+    // two chunk tiles per query of the workgroup, then (when they fit) the index rows
+    size_t lds = (size_t)qpw * 2 * chunk_bytes<T, D>();
     if (lds > (size_t)ATTN_LDS_LIMIT) return hipErrorInvalidValue;
-    auto go = [&](auto kern, int qpw) {
+    const size_t with_ids = lds + (size_t)qpw * p.kp * sizeof(int32_t);
+    const int idx_lds = (p.idx && p.kp > 0 && with_ids <= (size_t)ATTN_LDS_LIMIT) ? 1 : 0;
+    if (idx_lds) lds = with_ids;
+    auto go = [&](auto kern, int qpw_) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        dim3 grid((p.S + qpw - 1) / qpw, p.b);
-        hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p, delta);
+        dim3 grid((p.S + qpw_ - 1) / qpw_, p.b);
+        hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p, delta, idx_lds);
         return hipGetLastError();
     };
     if (dq) {
@@ -714,8 +816,8 @@ template <typename T>
 hipError_t query_dispatch(const AttnArgs& p, bool dq, float* delta, hipStream_t st)
 {
     switch (p.D) {
-    case 64: return p.H <= 16 ? launch_query<T, 64, 1>(p, dq, delta, st) : launch_query<T, 64, 4>(p, dq, delta, st);
-    case 128: return p.H <= 16 ? launch_query<T, 128, 1>(p, dq, delta, st) : launch_query<T, 128, 4>(p, dq, delta, st);
+    case 64: return p.H <= 16 ? launch_query<T, 64, 1>(p, dq, delta, st) : launch_query<T, 64, 2>(p, dq, delta, st);
+    case 128: return p.H <= 16 ? launch_query<T, 128, 1>(p, dq, delta, st) : launch_query<T, 128, 2>(p, dq, delta, st);
     case 512: return launch_query<T, 512, 1>(p, dq, delta, st);
     default: return hipErrorInvalidValue;
     }

@@ -57,6 +57,43 @@ def count_work(wl, idx):
                 avg_cand=n_cand / (wl.b * wl.sq))
 
 
+def kernel_work(wl, work):
+    """Algorithmic work of one launch of each kernel: (amount, unit, bound).
+
+    The attention work splits by product: the forward kernel does Q.row and
+    P.row; the dq kernel the dP and dQ products; the key-stationary kernel the
+    dK and dV products (P^T dO and dS'^T Q).  Recomputed logits are not
+    counted.  Memory-bound kernels count the bytes they must move."""
+    e = 2 if wl.dtype == "bf16" else 4
+    tok = wl.b * wl.sq
+    nc_rows = wl.b * wl.n_c
+    fl = work["attn_fwd"]
+    return {
+        "attn_query_fwd": (fl, "flop", "mfma"),
+        "attn_query_dq": (fl, "flop", "mfma"),
+        "attn_rows": (fl, "flop", "mfma"),
+        "index_topk": (work["indexer"], "flop", "mfma"),
+        "compress_fwd": (tok * (wl.d + wl.z_channels) * e + nc_rows * wl.d * e, "byte", "hbm"),
+        "compress_bwd": (tok * (wl.d + wl.z_channels) * (e + 4) + nc_rows * wl.d * 4, "byte", "hbm"),
+        "attn_reduce": ((tok + nc_rows) * wl.d * 4, "byte", "hbm"),
+    }
+
+
+def load_traffic(kernel, workload):
+    """HBM traffic of `kernel` from the committed PMC summary, if it was taken
+    on the current source of that kernel (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "compressed_sparse_attention_softmax_amd", "csrc", rec["source"])
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if digest != rec["source_sha256"]:
+        return None
+    return rec["traffic_bytes"]
+
+
 def cpu_baseline(wl, inp, seed, target_rows):
     """The oracle (as it stands) on a bounded, stratified sample of query rows:
     indexer scores + top-k + attention fwd + bwd for those rows, plus the
@@ -110,6 +147,8 @@ def main():
     ap.add_argument("--workload", default="csa4_s4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB 3 times (HBM counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -155,15 +194,34 @@ def main():
     torch.cuda.synchronize()
     index_peak_delta = torch.cuda.max_memory_allocated() - base
 
-    for _ in range(args.warmup):
+    def one_step():
         for c in calls:
             if c is not None:
                 c()
+
+    for _ in range(args.warmup):
+        one_step()
     torch.cuda.synchronize()
     work = count_work(wl, buf.idx)
+    kwork = kernel_work(wl, work)
+
+    # per-kernel durations (HIP events around each launch, two steps per
+    # kernel, outside the timed region): picks the dominant kernel
+    kernel_ms = {}
+    for k in range(7):
+        csa.csa_timing_enable(k)
+        one_step()
+        one_step()
+        n, ms = csa.csa_timing_read()
+        if n:
+            kernel_ms[csa.csa_kernel_name(k)] = ms / n
+    csa.csa_timing_enable(-1)
+    dom_k = max(kernel_ms, key=kernel_ms.get)
+    dom_id = [csa.csa_kernel_name(k) for k in range(7)].index(dom_k)
 
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(K)]
+    csa.csa_timing_enable(dom_id)          # the dominant kernel, timed live in the timed region
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
@@ -175,6 +233,9 @@ def main():
             e[i + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    csa.csa_timing_enable(-1)
+    n_dom, ms_dom = csa.csa_timing_read()
+    dom_ms = ms_dom / max(n_dom, 1)
 
     stage_ms = {s: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(K)) / K for i, s in enumerate(STAGES)}
     ms_step = elapsed * 1e3 / K
@@ -182,10 +243,17 @@ def main():
     flops_step = work["attn_fwd"] + work["attn_bwd"] + work["indexer"]
     attn_s = (stage_ms["attn_fwd"] + stage_ms["attn_bwd"]) * 1e-3
     attn_tflops = (work["attn_fwd"] + work["attn_bwd"]) / attn_s / 1e12
-    dom = max(("attn_fwd", "attn_bwd", "index_topk"), key=lambda s: stage_ms[s])
-    dom_flops = work["indexer"] if dom == "index_topk" else work[dom]
-    dom_tflops = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    amount, unit, bound = kwork[dom_k]
+    if unit == "flop":
+        achieved, r_unit, r_peak = amount / (dom_ms * 1e-3) / 1e12, "TFLOP/s", peak
+    else:
+        achieved, r_unit, r_peak = amount / (dom_ms * 1e-3) / 1e9, "GB/s", PEAK_HBM_GBS
+    roofline = {"bound": bound, "achieved": achieved, "peak": r_peak, "unit": r_unit, "frac": achieved / r_peak,
+                "traffic": load_traffic(dom_k, wl.name), "kernel": dom_k, "launches": n_dom,
+                "avg_launch_ms": dom_ms, "algorithmic_per_launch": amount,
+                "timing": "HIP events recorded on the launch stream around every launch of the kernel "
+                          "inside the timed region"}
     result = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -207,9 +275,8 @@ def main():
         "attention_frac_of_mfma_peak": attn_tflops / peak,
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "work": {k: v for k, v in work.items()},
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": dom_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": dom_tflops / peak, "traffic": None,
-                     "timing": "HIP events on the launch stream around the entry point, mean over the timed steps"},
+        "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
+        "roofline": roofline,
         "memory": {"index_topk_workspace_bytes": csa.csa_index_topk_workspace(dm),
                    "index_topk_peak_alloc_delta_bytes": int(index_peak_delta),
                    "max_allocated_bytes": int(torch.cuda.max_memory_allocated())},
@@ -220,8 +287,19 @@ def main():
         result["cpu_baseline"] = cpu_baseline(wl, inp, seed, args.cpu_rows)
     log(f"bench: {wl.name}: {ms_step:.3f} ms/step, {result['value']:.0f} tokens/s, "
         f"{result['tflops']:.1f} TFLOP/s; stages(ms) {result['stage_ms']}; attention {attn_tflops:.1f} TFLOP/s "
-        f"({100 * attn_tflops / peak:.1f}% of peak)")
+        f"({100 * attn_tflops / peak:.1f}% of peak); kernels(ms) {result['kernel_ms']}; "
+        f"roofline {dom_k}: {achieved:.1f} {r_unit} ({100 * roofline['frac']:.1f}% of peak)")
     print(json.dumps(result), flush=True)
+    if args.copy_mib > 0:
+        # a plain device copy of known size: its FETCH_SIZE / WRITE_SIZE under
+        # rocprofv3 calibrate the HBM byte counters of the kernels above
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copied {args.copy_mib} MiB x3 for counter calibration")
 
 
 if __name__ == "__main__":

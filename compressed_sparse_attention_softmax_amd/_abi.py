@@ -24,7 +24,11 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_ARG", -2: "CSA_ERR_SHAPE", -3: "CSA_ERR_DTYP
 # every symbol include/csa.h declares
 EXPORTS = ["csa_compress", "csa_compress_bwd", "csa_index_topk_workspace", "csa_index_topk",
            "csa_sparse_attn_fwd", "csa_sparse_attn_bwd_workspace", "csa_sparse_attn_bwd",
-           "csa_last_error", "csa_version"]
+           "csa_last_error", "csa_version", "csa_timing_enable", "csa_timing_read", "csa_kernel_name"]
+
+# kernel ids of the timing hook (enum csa_kernel_id)
+CSA_K_COMPRESS_FWD, CSA_K_COMPRESS_BWD, CSA_K_INDEX_TOPK, CSA_K_ATTN_FWD = 0, 1, 2, 3
+CSA_K_ATTN_DQ, CSA_K_ATTN_ROWS, CSA_K_ATTN_REDUCE = 4, 5, 6
 
 
 class CSAError(RuntimeError):
@@ -66,8 +70,12 @@ def load(path: Optional[str] = None):
     lib.csa_last_error.argtypes = []
     lib.csa_last_error.restype = ctypes.c_char_p
     lib.csa_version.argtypes = []
+    lib.csa_timing_enable.argtypes = [i]
+    lib.csa_timing_read.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
+    lib.csa_kernel_name.argtypes = [i]
+    lib.csa_kernel_name.restype = ctypes.c_char_p
     for fn in ("csa_compress", "csa_compress_bwd", "csa_index_topk", "csa_sparse_attn_fwd",
-               "csa_sparse_attn_bwd", "csa_version"):
+               "csa_sparse_attn_bwd", "csa_version", "csa_timing_enable", "csa_timing_read"):
         getattr(lib, fn).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -213,3 +221,21 @@ def csa_last_error() -> str:
 
 def csa_version() -> int:
     return int(load().csa_version())
+
+
+def csa_timing_enable(kernel: int) -> None:
+    """Bracket every later launch of kernel ``kernel`` (a CSA_K_* id) with HIP
+    events on its stream; -1 switches timing off."""
+    _call("csa_timing_enable", int(kernel))
+
+
+def csa_timing_read():
+    """(launches, total_ms) of the launches timed since the last read."""
+    n = ctypes.c_int(0)
+    ms = ctypes.c_double(0.0)
+    _call("csa_timing_read", ctypes.byref(n), ctypes.byref(ms))
+    return n.value, ms.value
+
+
+def csa_kernel_name(kernel: int) -> str:
+    return load().csa_kernel_name(int(kernel)).decode()

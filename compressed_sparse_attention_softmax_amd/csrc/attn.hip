@@ -29,8 +29,11 @@
 // pairs that are not candidates.  Partial sums per query block go to a
 // workspace and one reduction kernel adds them up: no atomics, and the sum
 // order is fixed.
+#include <type_traits>
+
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
+#include "timing.hpp"
 
 namespace csa {
 
@@ -465,8 +468,15 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
 
     const int wave = threadIdx.x / WAVE, lane = lane_id();
     const int g = lane / 16, n16 = lane % 16;
-    // heaviest query blocks (latest queries: longest valid prefix) are dispatched first
-    const int bi = blockIdx.z, qb = geo.nqb - 1 - blockIdx.y, slot = blockIdx.x;
+    // Workgroups go to the 8 XCDs round-robin by linear id.  All tiles of one
+    // query block are mapped to the same XCD, so its staged q / dO rows are
+    // fetched from HBM once into that XCD's L2; query blocks are dealt to the
+    // XCDs in turn, heaviest (latest queries: longest valid prefix) first.
+    const int ntiles = geo.n_wt + (p.c ? geo.n_ct : 0);
+    const int lin = blockIdx.x, xcd = lin & 7, kx = lin >> 3;
+    const int qbi = (kx / ntiles) * 8 + xcd;     // index over (batch, query block)
+    if (qbi >= p.b * geo.nqb) return;
+    const int bi = qbi / geo.nqb, qb = geo.nqb - 1 - qbi % geo.nqb, slot = kx % ntiles;
     const int t0 = qb * geo.Qb, t1 = min(p.S, t0 + geo.Qb);
     const bool win = slot < geo.n_wt;
     const int tile = win ? slot : slot - geo.n_wt;
@@ -521,7 +531,7 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = f4zero();
+        for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = sizeof(T) == 2 ? agpr_zero() : f4zero();
 
     // Stage q[t] and dO[t] into buffer `buf` with asynchronous global->LDS
     // loads.  16-byte piece s of the block lands at LDS piece s; its source is
@@ -555,8 +565,10 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
         }
         if (threadIdx.x < HP) {
             const int h = threadIdx.x;
-            lse_lds[buf * HP + h] = h < p.H ? p.lse[qrow * p.H + h] * LOG2E : INFINITY;
-            dlt_lds[buf * HP + h] = h < p.H ? delta[qrow * p.H + h] : 0.f;
+            // initial values of the S and dP accumulators of head h: the logit
+            // offset -lse/scale (so that scale*log2e*S' = log2 P) and -Delta
+            lse_lds[buf * HP + h] = h < p.H ? -p.lse[qrow * p.H + h] / p.scale : -INFINITY;
+            dlt_lds[buf * HP + h] = h < p.H ? -delta[qrow * p.H + h] : 0.f;
         }
         if (!win) {
             if (p.idx) {
@@ -595,6 +607,15 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
         stage(ta, 0, 0);
         count(ta, 0);
     }
+    // waves none of whose rows is a key of this tile only stage and synchronise
+    // (their own loop copy: no branch around the accumulators inside the loop;
+    // their partial rows are past the tile or at negative keys, never read)
+    bool live = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) live |= rkey[rt] >= 0;
+    live = __any(live);
+    auto query_loop = [&](auto compute_tag) {
+    constexpr bool COMPUTE = decltype(compute_tag)::value;
     for (int t = ta; t < tb; ++t) {
         const int it = t - ta, buf = NBUF == 2 ? (it & 1) : 0, cb = it % 3;
         if constexpr (NBUF == 2) {
@@ -616,8 +637,11 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
         const T* do_lds = q_lds + QELEMS;
         const float* ls_b = lse_lds + buf * HP;
         const float* dl_b = dlt_lds + buf * HP;
-        float mult[RT], msc[RT];                           // multiplicity, and times scale
-        bool any = false;
+        if constexpr (COMPUTE) {
+        // every (head, row) pair is computed; rows that are not candidates of t
+        // get multiplicity 0 (no branch, so the accumulators stay put).  The
+        // multiplicity enters the exponent: m P = 2^(scale log2e S' + log2 m).
+        float lm[RT];                                      // log2 of the multiplicity, -inf for 0
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int key = rkey[rt];
@@ -626,22 +650,19 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
                 if (win) m = (key <= t && key > t - p.W) ? 1.f : 0.f;
                 else m = (float)cnt_lds[cb * TR + key - tile_lo];
             }
-            mult[rt] = m;
-            msc[rt] = m * p.scale;
-            any |= m != 0.f;
+            lm[rt] = m > 0.f ? __log2f(m) : -INFINITY;
         }
-        if (__any(any)) {                                  // anything of t in this wave's rows?
 #pragma unroll
         for (int kk = 0; kk < HP / 32; ++kk) {
             Frag<T> pa[RT], sa[RT];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int ht = 2 * kk + hh;
-                float ls[4], dl[4];
+                f32x4 s0, d0;                              // accumulator starts: -lse/scale, -Delta
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    ls[i] = ls_b[16 * ht + 4 * g + i];
-                    dl[i] = dl_b[16 * ht + 4 * g + i];
+                    s0[i] = ls_b[16 * ht + 4 * g + i];
+                    d0[i] = dl_b[16 * ht + 4 * g + i];
                 }
                 Frag<T> qa[KS], da[KS];
                 const int hrow = 16 * ht + n16;
@@ -653,7 +674,7 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
                 }
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
-                    f32x4 sv = f4zero(), dp = f4zero();
+                    f32x4 sv = s0, dp = d0;
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
                         Frag<T> bk;
@@ -662,11 +683,13 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
                         sv = mfma16(qa[ks], bk, sv);
                         dp = mfma16(da[ks], bk, dp);
                     }
+                    // sv = S - lse/scale, dp = dP - Delta:  m P = 2^(sv sl2 + lm),
+                    // scaled dS = scale (m P) (dP - Delta)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float e = fast_exp2(sv[i] * sl2 - ls[i]);
-                        pa[rt].v[4 * hh + i] = from_f32<T>(mult[rt] * e);
-                        sa[rt].v[4 * hh + i] = from_f32<T>((dp[i] - dl[i]) * (msc[rt] * e));
+                        const float e = fast_exp2(fmaf(sv[i], sl2, lm[rt]));
+                        pa[rt].v[4 * hh + i] = from_f32<T>(e);
+                        sa[rt].v[4 * hh + i] = from_f32<T>((dp[i] * p.scale) * e);
                     }
                 }
                 // keep one head tile's S / dP live at a time (register pressure)
@@ -676,10 +699,14 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
             for (int dt = 0; dt < DT; ++dt) {
                 const Frag<T> dob = rows_operand<T>(do_lds, D, 32 * kk, 16 * dt, true);
                 const Frag<T> qbf = rows_operand<T>(q_lds, D, 32 * kk, 16 * dt, true);
+                if constexpr (sizeof(T) == 2 && RT == 4) {
+                    mfma16x8_acc(acc[0][dt], acc[1][dt], acc[2][dt], acc[3][dt], pa, sa, dob, qbf);
+                } else {
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    acc[rt][dt] = mfma16(pa[rt], dob, acc[rt][dt]);
-                    acc[rt][dt] = mfma16(sa[rt], qbf, acc[rt][dt]);
+                    for (int rt = 0; rt < RT; ++rt) {
+                        mfma16_acc(acc[rt][dt], pa[rt], dob);
+                        mfma16_acc(acc[rt][dt], sa[rt], qbf);
+                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -689,6 +716,13 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
             if (t + 1 < tb) count(t + 1, (it + 1) % 3);     // its index loads had compute(t) to land
         }
     }
+    };
+    if (!live) {                                           // no partial row of this wave is ever read
+        query_loop(std::false_type{});
+        return;
+    }
+    query_loop(std::true_type{});
+    if constexpr (sizeof(T) == 2) agpr_drain<RT * DT>(&acc[0][0]);
     // partial rows of this wave: lane holds dR[r = 16 rt + 4g + i][d = 16 dt + n16]
     float* part = ws + (win ? geo.win_off + (((int64_t)bi * geo.nqb + qb) * geo.WB) * D
                             : geo.comp_off + (((int64_t)bi * geo.nqb + qb) * p.nc) * D);
@@ -795,6 +829,7 @@ hipError_t launch_query(const AttnArgs& p, bool dq, float* delta, hipStream_t st
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         dim3 grid((p.S + qpw_ - 1) / qpw_, p.b);
+        TimedLaunch tl(dq ? K_ATTN_DQ : K_ATTN_FWD, st);
         hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p, delta, idx_lds);
         return hipGetLastError();
     };
@@ -832,10 +867,16 @@ hipError_t launch_rows(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStr
     auto kern = attn_rows_kernel<T, D, RW>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    dim3 grid(geo.n_wt + (p.c ? geo.n_ct : 0), geo.nqb, p.b);
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p, geo, ws, ws);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int ntiles = geo.n_wt + (p.c ? geo.n_ct : 0);
+    const int64_t groups = ((int64_t)p.b * geo.nqb + 7) / 8;     // rounds of 8 query blocks
+    dim3 grid((unsigned)(groups * 8 * ntiles));
+    {
+        TimedLaunch tl(K_ATTN_ROWS, st);
+        hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p, geo, ws, ws);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const int64_t threads = (int64_t)p.b * (p.S + (p.c ? p.nc : 0)) * (D / 4);
+    TimedLaunch tl(K_ATTN_REDUCE, st);
     hipLaunchKernelGGL(attn_reduce_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, p, geo,
                        (const float*)ws);
     return hipGetLastError();

@@ -14,6 +14,7 @@
 // states are merged through LDS.
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
+#include "timing.hpp"
 
 namespace csa {
 
@@ -227,6 +228,7 @@ template <typename T, int D>
 hipError_t launch_compress_fwd(const CompressArgs& p, hipStream_t st)
 {
     dim3 grid(p.nc, p.b);
+    TimedLaunch tl(K_COMPRESS_FWD, st);
     hipLaunchKernelGGL((compress_fwd_kernel<T, D>), grid, dim3(256), 0, st,
                        (const T*)p.x, (const T*)p.z, p.zc, (T*)p.c, p.c32, p.S, p.r, p.L, p.nc);
     return hipGetLastError();
@@ -246,6 +248,7 @@ hipError_t launch_compress_bwd(const CompressArgs& p, hipStream_t st)
         if (e != hipSuccess) return e;
     }
     dim3 grid((p.nc + jb - 1) / jb, p.b);
+    TimedLaunch tl(K_COMPRESS_BWD, st);
     hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const T*)p.x, (const T*)p.z, p.zc, p.dc, p.dx,
                        p.dz, p.S, p.r, p.L, p.nc, jb);
     return hipGetLastError();

@@ -39,6 +39,65 @@ __device__ __forceinline__ f32x4 mfma16(const Frag<float>& a, const Frag<float>&
     return c;
 }
 
+// Accumulating MFMA with the accumulator pinned to the AGPR file ("+a"): a
+// loop-carried accumulator then never moves between register files.  The
+// compiler's hazard checks do not look inside inline asm, so the asm carries
+// its own: s_nop 1 provides the two wait states an MFMA needs after a VALU
+// write of any of its source registers, and agpr_drain() must separate the
+// last of these MFMAs from every other read of the accumulators.  Back-to-back
+// accumulation into the same registers needs no wait states.
+__device__ __forceinline__ void mfma16_acc(f32x4& acc, const Frag<bf16_t>& a, const Frag<bf16_t>& b)
+{
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a.v), "v"(b.v));
+}
+__device__ __forceinline__ void mfma16_acc(f32x4& acc, const Frag<float>& a, const Frag<float>& b)
+{
+    acc = mfma16(a, b, acc);
+}
+// Eight accumulating MFMAs in one asm block (one set of wait states):
+// c_r += pa[r] * b0, then c_r += sa[r] * b1, r = 0..3; consecutive MFMAs use
+// different accumulators.
+__device__ __forceinline__ void mfma16x8_acc(f32x4& c0, f32x4& c1, f32x4& c2, f32x4& c3, const Frag<bf16_t>* pa,
+                                             const Frag<bf16_t>* sa, const Frag<bf16_t>& b0, const Frag<bf16_t>& b1)
+{
+    asm("s_nop 1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %0, %4, %12, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %5, %12, %1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %2, %6, %12, %2\n\t"
+        "v_mfma_f32_16x16x32_bf16 %3, %7, %12, %3\n\t"
+        "v_mfma_f32_16x16x32_bf16 %0, %8, %13, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %9, %13, %1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %2, %10, %13, %2\n\t"
+        "v_mfma_f32_16x16x32_bf16 %3, %11, %13, %3"
+        : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3)
+        : "v"(pa[0].v), "v"(pa[1].v), "v"(pa[2].v), "v"(pa[3].v), "v"(sa[0].v), "v"(sa[1].v), "v"(sa[2].v),
+          "v"(sa[3].v), "v"(b0.v), "v"(b1.v));
+}
+
+// Zero accumulator created in the AGPR file (an MFMA of zero operands), so
+// that a loop-carried accumulator is an AGPR value from its first definition.
+// The trailing 32 wait states let the compiler copy the result right away.
+__device__ __forceinline__ f32x4 agpr_zero()
+{
+    f32x4 acc;
+    const bf16x8 z = {};
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0\n\ts_nop 15\n\ts_nop 15" : "=a"(acc) : "v"(z));
+    return acc;
+}
+
+// 32 wait states after the last mfma16_acc on accumulators a[0..N) (more than
+// the latest read-after-MFMA-write requirement), ordered after every one of
+// them because the asm reads and writes all N.
+template <int N> __device__ __forceinline__ void agpr_drain(f32x4* a);
+template <> __device__ __forceinline__ void agpr_drain<16>(f32x4* a)
+{
+    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(a[4]), "+a"(a[5]), "+a"(a[6]), "+a"(a[7]), "+a"(a[8]), "+a"(a[9]), "+a"(a[10]), "+a"(a[11]), "+a"(a[12]), "+a"(a[13]), "+a"(a[14]), "+a"(a[15]));
+}
+template <> __device__ __forceinline__ void agpr_drain<32>(f32x4* a)
+{
+    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(a[4]), "+a"(a[5]), "+a"(a[6]), "+a"(a[7]), "+a"(a[8]), "+a"(a[9]), "+a"(a[10]), "+a"(a[11]), "+a"(a[12]), "+a"(a[13]), "+a"(a[14]), "+a"(a[15]), "+a"(a[16]), "+a"(a[17]), "+a"(a[18]), "+a"(a[19]), "+a"(a[20]), "+a"(a[21]), "+a"(a[22]), "+a"(a[23]), "+a"(a[24]), "+a"(a[25]), "+a"(a[26]), "+a"(a[27]), "+a"(a[28]), "+a"(a[29]), "+a"(a[30]), "+a"(a[31]));
+}
+
 template <typename T> __device__ __forceinline__ Frag<T> zero_frag()
 {
     Frag<T> f;

@@ -32,6 +32,7 @@
 
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
+#include "timing.hpp"
 
 namespace csa {
 
@@ -325,6 +326,7 @@ hipError_t launch_index(const IndexArgs& p, hipStream_t st)
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     dim3 grid((p.S + 3) / 4, p.b);
+    TimedLaunch tl(K_INDEX_TOPK, st);
     hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const T*)p.qi, (const T*)p.ki, p.w, p.idx,
                        p.score, p.S, p.HI, p.r, p.nc, kp, cap);
     return hipGetLastError();

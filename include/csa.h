@@ -167,6 +167,31 @@ const char* csa_last_error(void);
 /* CSA_ABI_VERSION of the loaded library. */
 int csa_version(void);
 
+/* ---------------------------------------------------------------- timing
+ * Benchmark hook, not part of the computation.  Kernel ids of the entry
+ * points above (one entry point may launch several kernels):
+ *   csa_compress          -> CSA_K_COMPRESS_FWD
+ *   csa_compress_bwd      -> CSA_K_COMPRESS_BWD
+ *   csa_index_topk        -> CSA_K_INDEX_TOPK
+ *   csa_sparse_attn_fwd   -> CSA_K_ATTN_FWD
+ *   csa_sparse_attn_bwd   -> CSA_K_ATTN_DQ (dq, Delta, dsink), CSA_K_ATTN_ROWS
+ *                            (per-query-block dkv / dc partials), CSA_K_ATTN_REDUCE
+ * csa_timing_enable(k) makes every later launch of kernel k, from any thread,
+ * record one hipEvent before and one after it on the launch stream; -1
+ * switches timing off.  Returns CSA_ERR_ARG for an unknown id.
+ * csa_timing_read() waits for the recorded events, returns the number of
+ * timed launches and the sum of their durations in milliseconds, and forgets
+ * them; CSA_ERR_HIP if an event could not be read.  The events are created by
+ * the library on first use and reused; they are the only resource it keeps. */
+enum csa_kernel_id {
+    CSA_K_COMPRESS_FWD = 0, CSA_K_COMPRESS_BWD = 1, CSA_K_INDEX_TOPK = 2, CSA_K_ATTN_FWD = 3,
+    CSA_K_ATTN_DQ = 4, CSA_K_ATTN_ROWS = 5, CSA_K_ATTN_REDUCE = 6
+};
+int csa_timing_enable(int kernel);
+int csa_timing_read(int* launches, double* total_ms);
+/* Short name of a kernel id ("" if unknown). */
+const char* csa_kernel_name(int kernel);
+
 #ifdef __cplusplus
 }
 #endif

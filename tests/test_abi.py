@@ -133,3 +133,17 @@ def test_workspace_too_small_is_rejected():
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="libcsa.so not found"):
         _abi.load(str(tmp_path / "missing.so"))
+
+
+def test_timing_hook_without_launches():
+    # host-only paths: enabling, reading with nothing recorded, names, bad ids
+    lib = _lib()
+    assert lib.csa_timing_enable(7) == -1
+    assert lib.csa_timing_enable(-2) == -1
+    assert lib.csa_timing_enable(csa.CSA_K_ATTN_ROWS) == 0
+    assert csa.csa_timing_read() == (0, 0.0)
+    assert lib.csa_timing_enable(-1) == 0
+    names = [csa.csa_kernel_name(k) for k in range(7)]
+    assert names == ["compress_fwd", "compress_bwd", "index_topk", "attn_query_fwd", "attn_query_dq",
+                     "attn_rows", "attn_reduce"]
+    assert csa.csa_kernel_name(99) == ""

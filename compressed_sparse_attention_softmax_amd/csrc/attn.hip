@@ -438,9 +438,11 @@ template <typename T, int D> constexpr size_t rows_lds_tile()
 {
     return (size_t)4 * rows_per_wave_t<T, D>() * (D + 16 / sizeof(T)) * sizeof(T);
 }
+// bf16 rows at d <= 128 stay in registers (64 VGPRs next to the AGPR
+// accumulators): the tile would be re-read from LDS for every head tile.
 template <typename T, int D> constexpr bool rows_tile_in_lds()
 {
-    return rows_lds_base<T, D>() + rows_lds_tile<T, D>() <= (size_t)ATTN_LDS_LIMIT;
+    return !(sizeof(T) == 2 && D <= 128) && rows_lds_base<T, D>() + rows_lds_tile<T, D>() <= (size_t)ATTN_LDS_LIMIT;
 }
 
 struct RowsGeom {
@@ -692,8 +694,8 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
                         sa[rt].v[4 * hh + i] = from_f32<T>((dp[i] * p.scale) * e);
                     }
                 }
-                // keep one head tile's S / dP live at a time (register pressure)
-                __builtin_amdgcn_sched_barrier(0);
+                // (no scheduling barrier: the S / dP MFMAs of the next head tile
+                // interleave with this tile's exponentials)
             }
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {

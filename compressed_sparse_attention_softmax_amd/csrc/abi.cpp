@@ -1,9 +1,10 @@
 // abi.cpp -- the extern "C" entry points of libcsa (declared in include/csa.h).
 //
 // Each entry point validates every argument before touching the HIP runtime,
-// records a message for csa_last_error() on failure, zero-fills accumulating
-// outputs with a fill kernel on the caller's stream (no memset nodes, so a
-// caller may capture the calls into a graph), and enqueues the kernels.
+// records a message for csa_last_error() on failure, and enqueues the kernels
+// on the caller's stream.  Every element of a gradient output is written by a
+// kernel (a fill kernel where nothing else writes it; no memset nodes, so a
+// caller may capture the calls into a graph).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -226,10 +227,7 @@ int csa_sparse_attn_bwd(const csa_dims* dm, int dtype, const void* q, const void
                     need, ws ? ws_bytes : (size_t)0);
     if (((uintptr_t)ws) & 15) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: workspace must be 16-byte aligned");
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = hipSuccess;
-    if (dsink) e = csa::zero_fill(dsink, (size_t)dm->h, st);
-    if (e == hipSuccess) e = csa::attn_bwd(a, dtype == CSA_BF16, (float*)ws, st);
-    return hip_status(e, "csa_sparse_attn_bwd");
+    return hip_status(csa::attn_bwd(a, dtype == CSA_BF16, (float*)ws, st), "csa_sparse_attn_bwd");
 }
 
 }  // extern "C"

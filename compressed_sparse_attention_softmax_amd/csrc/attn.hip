@@ -146,7 +146,7 @@ template <typename T, int D> constexpr int chunk_bytes() { return CHUNK * D * (i
 
 template <typename T, int D, int HT, int G, bool DQ>
 __global__ __launch_bounds__(256, (D <= 128 && HT <= 2) ? 2 : 1)
-void attn_query_kernel(AttnArgs p, float* __restrict__ delta, int idx_lds)
+void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict__ csink, int idx_lds)
 {
     constexpr int KS = D / 32, DT = D / 16, QPW = 4 / G;
     constexpr int CHB = chunk_bytes<T, D>();
@@ -154,6 +154,8 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, int idx_lds)
     constexpr int E16 = 16 / (int)sizeof(T);      // elements per piece
     constexpr int NPL = CHB / (16 * WAVE * G);    // pieces each lane of the query's waves carries
     static_assert(NPL * 16 * WAVE * G == CHB, "chunk pieces split evenly over the query's waves");
+    constexpr int LPR = WAVE * G / CHUNK;         // lanes sharing one row of a chunk
+    static_assert(LPR * NPL == PPR, "a row's pieces split evenly over its lanes");
     typedef uint32_t piece_t __attribute__((ext_vector_type(4)));
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int wave = threadIdx.x / WAVE, lane = lane_id();
@@ -181,7 +183,8 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, int idx_lds)
 
     Frag<T> qb[HT][KS];
     [[maybe_unused]] Frag<T> db[HT][KS];
-    float m2[HT], l[HT];
+    float m2[HT];
+    [[maybe_unused]] f32x4 lsum[HT];              // softmax denominators (every element holds the head's)
     [[maybe_unused]] float lse2[HT], dlt[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -191,8 +194,10 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, int idx_lds)
         for (int ks = 0; ks < KS; ++ks)
             qb[ht][ks] = hv ? load_frag(qp + h * D + 32 * ks + 8 * g) : zero_frag<T>();
         if constexpr (!DQ) {
-            if (p.sink && hv) { m2[ht] = p.sink[h] * LOG2E; l[ht] = 1.f; }
-            else { m2[ht] = -INFINITY; l[ht] = 0.f; }
+            const bool sk = p.sink && hv;
+            m2[ht] = sk ? p.sink[h] * LOG2E : -INFINITY;
+            const float l0 = sk ? 1.f : 0.f;
+            lsum[ht] = f32x4{l0, l0, l0, l0};
         } else {
             // Delta[h] = <dO[t, h], O[t, h]>; dO kept as the B operand of dP^T
             const T* dop = (const T*)p.dout + (qrow * p.H + h) * D;
@@ -213,40 +218,43 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, int idx_lds)
             lse2[ht] = hv ? p.lse[qrow * p.H + h] * LOG2E : INFINITY;
             if (active && hv && g == 0) {
                 delta[qrow * p.H + h] = part;
-                if (p.sink && p.dsink) atomicAdd(p.dsink + h, -fast_exp2(p.sink[h] * LOG2E - lse2[ht]) * part);
+                // this query's term of dsink[h], head-major; summed in a fixed order later
+                if (csink) csink[(int64_t)h * p.b * p.S + qrow] = -fast_exp2(p.sink[h] * LOG2E - lse2[ht]) * part;
             }
         }
     }
     if constexpr (DQ) {
         if (!p.dq) return;                        // uniform over the workgroup
     }
+    [[maybe_unused]] Frag<T> ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones.v[e] = (T)1.0f;
     f32x4 o[DT][HT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) o[dt][ht] = f4zero();
 
-    // gather chunk c0's rows into registers; returns the chunk's candidate mask
+    // Gather chunk c0's rows into registers; returns the chunk's candidate
+    // mask.  Lane q = 64 sub + lane of the query's waves owns row q / LPR of the
+    // chunk and its pieces (q % LPR) + LPR k, k < NPL: it resolves that row's
+    // address itself, and its loads differ by immediate offsets only.
+    const int my_r = (sub * WAVE + lane) / LPR, my_j = (sub * WAVE + lane) % LPR;
     piece_t rg[NPL];
     auto fetch = [&](int c0) -> uint32_t {
-        const int code = cand.code(c0 + (lane & 31), use_ids, ids);
-        const uint32_t mask = (uint32_t)__ballot(code >= 0);
+        const uint32_t mask = (uint32_t)__ballot(cand.code(c0 + (lane & 31), use_ids, ids) >= 0);
+        const T* rp = cand.row_ptr(cand.code(c0 + my_r, use_ids, ids)) + my_j * E16;
 #pragma unroll
-        for (int k = 0; k < NPL; ++k) {
-            const int piece = (sub + G * k) * WAVE + lane;
-            const int r = piece / PPR, pc = piece % PPR;
-            rg[k] = *reinterpret_cast<const piece_t*>(cand.row_ptr(__shfl(code, r)) + pc * E16);
-        }
+        for (int k = 0; k < NPL; ++k) rg[k] = *reinterpret_cast<const piece_t*>(rp + k * LPR * E16);
         return mask;
     };
     // write the gathered rows to buffer buf, units permuted per row
     auto stash = [&](int buf) {
-        T* dst = reinterpret_cast<T*>(tiles + (size_t)buf * CHB);
+        T* dst = reinterpret_cast<T*>(tiles + (size_t)buf * CHB) + my_r * D;
 #pragma unroll
         for (int k = 0; k < NPL; ++k) {
-            const int piece = (sub + G * k) * WAVE + lane;
-            const int r = piece / PPR, pos = (piece % PPR) * E16;
-            *reinterpret_cast<piece_t*>(dst + r * D + ((((pos >> 3) ^ (r & 7))) << 3) + (pos & 7)) = rg[k];
+            const int pos = (my_j + LPR * k) * E16;
+            *reinterpret_cast<piece_t*>(dst + ((((pos >> 3) ^ (my_r & 7))) << 3) + (pos & 7)) = rg[k];
         }
     };
 
@@ -267,7 +275,7 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, int idx_lds)
                 for (int ks = 0; ks < KS; ++ks) acc = mfma16(ra[ks], qb[ht][ks], acc);
                 s[ht][rt] = acc;
                 if constexpr (DQ) {
-                    f32x4 a2 = f4zero();
+                    f32x4 a2 = f32x4{-dlt[ht], -dlt[ht], -dlt[ht], -dlt[ht]};
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) a2 = mfma16(ra[ks], db[ht][ks], a2);
                     dp[ht][rt] = a2;
@@ -288,24 +296,26 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, int idx_lds)
         if constexpr (!DQ) {
             // exponentials are taken against a reference m2 that moves only when
             // some logit of the wave exceeds it by more than 2^8 (then every
-            // head re-bases); P <= 2^8 otherwise, and O / l is unchanged.
-            float mx[HT];
+            // head re-bases); P <= 2^8 otherwise, and O / l is unchanged.  The
+            // test needs only each lane's own maximum; the per-head maximum
+            // (a cross-lane reduction) is formed on the rare re-base.
+            float mloc[HT];
             bool need = false;
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
-                float m = fmaxf(fmaxf(fmaxf(s[ht][0][0], s[ht][0][1]), fmaxf(s[ht][0][2], s[ht][0][3])),
-                                fmaxf(fmaxf(s[ht][1][0], s[ht][1][1]), fmaxf(s[ht][1][2], s[ht][1][3])));
-                m = fmaxf(m, __shfl_xor(m, 16));
-                m = fmaxf(m, __shfl_xor(m, 32));
-                mx[ht] = m * sl2;                  // scale > 0: max commutes with it
-                need |= mx[ht] > m2[ht] + 8.f;
+                mloc[ht] = fmaxf(fmaxf(fmaxf(s[ht][0][0], s[ht][0][1]), fmaxf(s[ht][0][2], s[ht][0][3])),
+                                 fmaxf(fmaxf(s[ht][1][0], s[ht][1][1]), fmaxf(s[ht][1][2], s[ht][1][3])));
+                need |= mloc[ht] * sl2 > m2[ht] + 8.f;   // scale > 0: max commutes with it
             }
             if (__any(need)) {                     // rare
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) {
-                    const float mnew = fmaxf(m2[ht], mx[ht]);
+                    float m = mloc[ht];
+                    m = fmaxf(m, __shfl_xor(m, 16));
+                    m = fmaxf(m, __shfl_xor(m, 32));
+                    const float mnew = fmaxf(m2[ht], m * sl2);
                     const float alpha = fast_exp2(m2[ht] - mnew);
-                    l[ht] *= alpha;
+                    lsum[ht] *= alpha;
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) o[dt][ht] *= alpha;
                     m2[ht] = mnew;
@@ -314,30 +324,27 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, int idx_lds)
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
                 const float negm = -m2[ht];
-                float rs = 0.f;
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float pv = fast_exp2(fmaf(s[ht][rt][i], sl2, negm));
-                        rs += pv;
-                        pb[ht].v[4 * rt + i] = from_f32<T>(pv);
-                    }
-                rs += __shfl_xor(rs, 16);
-                rs += __shfl_xor(rs, 32);
-                l[ht] += rs;
+                    for (int i = 0; i < 4; ++i)
+                        pb[ht].v[4 * rt + i] = from_f32<T>(fast_exp2(fmaf(s[ht][rt][i], sl2, negm)));
+                // row sums on the matrix core: a ones row against P^T sums the
+                // chunk's (rounded) P of head n in every row of the result
+                lsum[ht] = mfma16(ones, pb[ht], lsum[ht]);
             }
         } else {
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
-                // scale * P in one exponential: 2^(s*scale*log2e + log2(scale) - lse*log2e)
+                // scale * P in one exponential: 2^(s*scale*log2e + log2(scale) - lse*log2e);
+                // dp started at -Delta, so dp = dP - Delta
                 const float off = lsc - lse2[ht];
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float ps = fast_exp2(fmaf(s[ht][rt][i], sl2, off));
-                        pb[ht].v[4 * rt + i] = from_f32<T>((dp[ht][rt][i] - dlt[ht]) * ps);
+                        pb[ht].v[4 * rt + i] = from_f32<T>(dp[ht][rt][i] * ps);
                     }
             }
         }
@@ -392,13 +399,14 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, int idx_lds)
         const int h = h0 + 16 * ht + n16;
         if (h >= p.H) continue;
         if constexpr (!DQ) {
-            const float inv = 1.f / l[ht];
+            const float lt = lsum[ht][0];
+            const float inv = 1.f / lt;
             T* orow = (T*)p.out + (qrow * p.H + h) * D;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) orow[16 * dt + 4 * g + i] = from_f32<T>(o[dt][ht][i] * inv);
-            if (g == 0) p.lse[qrow * p.H + h] = (m2[ht] + log2f(l[ht])) * LN2;
+            if (g == 0) p.lse[qrow * p.H + h] = (m2[ht] + log2f(lt)) * LN2;
         } else {
             T* drow = (T*)p.dq + (qrow * p.H + h) * D;
 #pragma unroll
@@ -447,7 +455,8 @@ template <typename T, int D> constexpr bool rows_tile_in_lds()
 
 struct RowsGeom {
     int Qb, nqb, WB, n_wt, n_ct, TR;   // query block, blocks, band rows, tiles, tile rows
-    int64_t win_off, comp_off;   // float offsets of the two partial regions in the workspace
+    int64_t sink_off;                  // float offset of the per-query dsink terms [H, b*S]
+    int64_t win_off, comp_off;         // float offsets of the two partial regions in the workspace
 };
 
 template <typename T, int D, int RW>
@@ -742,10 +751,30 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
 // dKV[b, u] = sum of the window partials of the query blocks whose band holds u;
 // dC[b, j]  = sum of the compressed partials of the query blocks that reach j.
 // One thread per (row, 4 consecutive d); the sum runs over query blocks in order.
+// Blocks from `row_blocks` on: dsink[h] = sum over all queries of their terms
+// (one block per head, a fixed summation order).
 template <int D>
-__global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs p, RowsGeom geo, const float* __restrict__ ws)
+__global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs p, RowsGeom geo, const float* __restrict__ ws,
+                                                          int row_blocks)
 {
     constexpr int V = D / 4;
+    if ((int)blockIdx.x >= row_blocks) {
+        __shared__ float part[256];
+        const int h = blockIdx.x - row_blocks;
+        const int64_t n = (int64_t)p.b * p.S;
+        const float* src = ws + geo.sink_off + (int64_t)h * n;
+        float acc = 0.f;
+        for (int64_t i = threadIdx.x; i < n; i += 256) acc += src[i];
+        part[threadIdx.x] = acc;
+        __syncthreads();
+#pragma unroll
+        for (int w = 128; w >= 1; w >>= 1) {
+            if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) p.dsink[h] = part[0];
+        return;
+    }
     const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t nkv = (int64_t)p.b * p.S * V;
     const int64_t nct = (int64_t)p.b * p.nc * V;
@@ -810,13 +839,14 @@ RowsGeom rows_geometry(const AttnArgs& p)
     g.n_wt = (g.WB + g.TR - 1) / g.TR;
     g.n_ct = p.nc > 0 ? (p.nc + g.TR - 1) / g.TR : 0;
     const int64_t delta_floats = ((int64_t)p.b * p.S * p.H + 63) / 64 * 64;
-    g.win_off = delta_floats;
+    g.sink_off = delta_floats;
+    g.win_off = g.sink_off + delta_floats;
     g.comp_off = g.win_off + (int64_t)p.b * g.nqb * g.WB * D;
     return g;
 }
 
 template <typename T, int D, int HT>
-hipError_t launch_query(const AttnArgs& p, bool dq, float* delta, hipStream_t st)
+hipError_t launch_query(const AttnArgs& p, bool dq, float* delta, float* csink, hipStream_t st)
 {
     const int gper = (p.H + 16 * HT - 1) / (16 * HT);
     const int G = gper <= 1 ? 1 : (gper <= 2 ? 2 : 4);
@@ -832,7 +862,7 @@ hipError_t launch_query(const AttnArgs& p, bool dq, float* delta, hipStream_t st
         if (e != hipSuccess) return e;
         dim3 grid((p.S + qpw_ - 1) / qpw_, p.b);
         TimedLaunch tl(dq ? K_ATTN_DQ : K_ATTN_FWD, st);
-        hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p, delta, idx_lds);
+        hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p, delta, csink, idx_lds);
         return hipGetLastError();
     };
     if (dq) {
@@ -850,14 +880,31 @@ hipError_t launch_query(const AttnArgs& p, bool dq, float* delta, hipStream_t st
 }
 
 template <typename T>
-hipError_t query_dispatch(const AttnArgs& p, bool dq, float* delta, hipStream_t st)
+hipError_t query_dispatch(const AttnArgs& p, bool dq, float* delta, float* csink, hipStream_t st)
 {
     switch (p.D) {
-    case 64: return p.H <= 16 ? launch_query<T, 64, 1>(p, dq, delta, st) : launch_query<T, 64, 2>(p, dq, delta, st);
-    case 128: return p.H <= 16 ? launch_query<T, 128, 1>(p, dq, delta, st) : launch_query<T, 128, 2>(p, dq, delta, st);
-    case 512: return launch_query<T, 512, 1>(p, dq, delta, st);
+    case 64:
+        return p.H <= 16 ? launch_query<T, 64, 1>(p, dq, delta, csink, st) : launch_query<T, 64, 2>(p, dq, delta, csink, st);
+    case 128:
+        return p.H <= 16 ? launch_query<T, 128, 1>(p, dq, delta, csink, st)
+                         : launch_query<T, 128, 2>(p, dq, delta, csink, st);
+    case 512: return launch_query<T, 512, 1>(p, dq, delta, csink, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+// the fixed-order reductions: dkv / dc rows (when gradients are requested) and dsink
+template <int D>
+hipError_t launch_reduce(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStream_t st)
+{
+    const int64_t threads = p.dq ? (int64_t)p.b * (p.S + (p.c ? p.nc : 0)) * (D / 4) : 0;
+    const int row_blocks = (int)((threads + 255) / 256);
+    const int blocks = row_blocks + (p.sink && p.dsink ? p.H : 0);
+    if (blocks == 0) return hipSuccess;
+    TimedLaunch tl(K_ATTN_REDUCE, st);
+    hipLaunchKernelGGL(attn_reduce_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, st, p, geo, (const float*)ws,
+                       row_blocks);
+    return hipGetLastError();
 }
 
 template <typename T, int D>
@@ -877,11 +924,7 @@ hipError_t launch_rows(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStr
         hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p, geo, ws, ws);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int64_t threads = (int64_t)p.b * (p.S + (p.c ? p.nc : 0)) * (D / 4);
-    TimedLaunch tl(K_ATTN_REDUCE, st);
-    hipLaunchKernelGGL(attn_reduce_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, p, geo,
-                       (const float*)ws);
-    return hipGetLastError();
+    return launch_reduce<D>(p, geo, ws, st);
 }
 
 template <typename T>
@@ -907,7 +950,8 @@ size_t attn_bwd_workspace_bytes(const AttnArgs& p)
 hipError_t attn_fwd(const AttnArgs& p, bool bf16, hipStream_t st)
 {
     if (p.S == 0) return hipSuccess;
-    return bf16 ? query_dispatch<bf16_t>(p, false, nullptr, st) : query_dispatch<float>(p, false, nullptr, st);
+    return bf16 ? query_dispatch<bf16_t>(p, false, nullptr, nullptr, st)
+                : query_dispatch<float>(p, false, nullptr, nullptr, st);
 }
 
 // ws: at least attn_bwd_workspace_bytes(p) bytes.  Delta (b*S*H floats) comes
@@ -915,9 +959,17 @@ hipError_t attn_fwd(const AttnArgs& p, bool bf16, hipStream_t st)
 hipError_t attn_bwd(const AttnArgs& p, bool bf16, float* ws, hipStream_t st)
 {
     if (p.S == 0) return hipSuccess;
-    hipError_t e = bf16 ? query_dispatch<bf16_t>(p, true, ws, st) : query_dispatch<float>(p, true, ws, st);
-    if (e != hipSuccess || !p.dq) return e;
     const RowsGeom geo = rows_geometry(p);
+    float* csink = (p.sink && p.dsink) ? ws + geo.sink_off : nullptr;
+    hipError_t e = bf16 ? query_dispatch<bf16_t>(p, true, ws, csink, st) : query_dispatch<float>(p, true, ws, csink, st);
+    if (e != hipSuccess) return e;
+    if (!p.dq) {                                   // dsink only
+        switch (p.D) {
+        case 64: return launch_reduce<64>(p, geo, ws, st);
+        case 128: return launch_reduce<128>(p, geo, ws, st);
+        default: return launch_reduce<512>(p, geo, ws, st);
+        }
+    }
     return bf16 ? rows_dispatch<bf16_t>(p, geo, ws, st) : rows_dispatch<float>(p, geo, ws, st);
 }
 

@@ -51,8 +51,8 @@
  *    a message for the calling thread.  Nothing throws or aborts across the ABI.
  *    Values of floating-point inputs are not checked (NaN/Inf give unspecified
  *    results).
- *  - Accumulating outputs (dkv, dc, dsink, dx, dz) are zero-filled on the
- *    stream by the call, then accumulated (overwrite semantics).
+ *  - Gradient outputs that sum contributions (dkv, dc, dsink, dx, dz) are
+ *    overwritten, not added to: every element is written by the call.
  */
 #ifndef CSA_H_
 #define CSA_H_
@@ -141,7 +141,11 @@ int csa_sparse_attn_fwd(const csa_dims* dims, int dtype, const void* q, const vo
                         const void* c, const int32_t* idx, const float* sink, float scale,
                         void* out, float* lse, void* stream);
 
-/* Workspace bytes csa_sparse_attn_bwd needs. */
+/* Workspace bytes csa_sparse_attn_bwd needs (device memory, 16-byte aligned,
+ * owned by the caller, contents on entry irrelevant): Delta and the per-query
+ * dsink terms ([b, sq, h] fp32 each) and fp32 partial rows of dkv and dc per
+ * block of consecutive queries, which the call reduces in a fixed order (the
+ * results do not depend on scheduling).  0 for invalid dims. */
 size_t csa_sparse_attn_bwd_workspace(const csa_dims* dims);
 
 /* Sparse attention backward: the gradient of csa_sparse_attn_fwd given dout,
@@ -154,7 +158,9 @@ size_t csa_sparse_attn_bwd_workspace(const csa_dims* dims);
  *   dsink[h] = -sum_{b,t} exp(sink[h] - lse) Delta          (fp32)
  * Gradient gate (Megatron-LM PR #7152): dq, dkv and dc are all non-NULL, or
  * all NULL (no-op apart from dsink); dc must be NULL when c is NULL.  dsink
- * may be NULL (required NULL when sink is NULL).  lse gradient is zero. */
+ * may be NULL (required NULL when sink is NULL).  lse gradient is zero.
+ * ws / ws_bytes: the workspace (CSA_ERR_WORKSPACE if NULL or smaller than
+ * csa_sparse_attn_bwd_workspace(dims)). */
 int csa_sparse_attn_bwd(const csa_dims* dims, int dtype, const void* q, const void* kv,
                         const void* c, const int32_t* idx, const float* sink, float scale,
                         const void* out, const float* lse, const void* dout, void* dq,

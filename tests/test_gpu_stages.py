@@ -137,7 +137,7 @@ def test_index_topk_all_zero_keys(gpu):
 
 
 # ------------------------------------------------------------------ attention
-def _attn_case(wl, seed, idx_mode="random", with_sink=True, window_only=False, junk=False):
+def _attn_case(wl, seed, idx_mode="random", with_sink=True, window_only=False, junk=False, dsink_only=False):
     import compressed_sparse_attention_softmax_amd as csa
     inp = csa_synth.make_inputs(wl, seed, device="cuda", parts=("attn", "compress", "bwd"),
                                 with_sink=with_sink)
@@ -177,6 +177,8 @@ def _attn_case(wl, seed, idx_mode="random", with_sink=True, window_only=False, j
     dc = torch.full((b, nc, D), 3.0, device="cuda") if c is not None else None
     dsink = torch.full((H,), 3.0, device="cuda") if with_sink else None
     ws = torch.empty(csa.csa_sparse_attn_bwd_workspace(dm), dtype=torch.uint8, device="cuda")
+    if dsink_only:       # gradient gate closed: only dsink is produced
+        dq = dkv = dc = None
     csa.csa_sparse_attn_bwd(dm, inp["q"], inp["kv"], c, idx, inp["sink"], wl.scale, out, lse, inp["do"],
                             dq, dkv, dc, dsink, ws=ws)
     torch.cuda.synchronize()
@@ -194,8 +196,9 @@ def _attn_case(wl, seed, idx_mode="random", with_sink=True, window_only=False, j
     tol = tol_of(dtype)
     check_close("out", out.reshape(b * S, H, D), ro, tol)
     check_close("lse", lse.reshape(b * S, H), rl, tol)
-    check_close("dq", dq.reshape(b * S, H, D), rdq, tol)
-    check_close("dkv", dkv, rdkv, tol)
+    if not dsink_only:
+        check_close("dq", dq.reshape(b * S, H, D), rdq, tol)
+        check_close("dkv", dkv, rdkv, tol)
     if dc is not None:
         check_close("dc", dc, rdc, tol)
     if dsink is not None:
@@ -213,6 +216,7 @@ ATTN_CASES = [
     ("csa4_bf16_block0_repeat", CSA4_SMALL.replace(sq=700, topk=8), dict(idx_mode="block0")),
     ("csa4_bf16_dense", CSA4_SMALL.replace(sq=500), dict(idx_mode="dense")),
     ("csa4_bf16_window_only", CSA4_SMALL.replace(sq=300), dict(window_only=True)),
+    ("csa4_bf16_dsink_only", CSA4_SMALL.replace(sq=300), dict(dsink_only=True)),
     ("d512_bf16", D512_SMALL, {}),
     ("hca128_bf16_dense", HCA_SMALL, dict(idx_mode="dense")),
 ]

@@ -173,12 +173,20 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
     const float sl2 = p.scale * LOG2E;
     [[maybe_unused]] const float lsc = __log2f(p.scale);
     const T* qp = (const T*)p.q + qrow * p.H * D;
-    // the query's index row, read once into LDS: per-chunk slot lookups do not wait on memory
+    // The query's index row goes to LDS once (per-chunk slot lookups then do
+    // not wait on memory).  Its loads are issued first, into registers, so
+    // that they overlap the loads of Q (dO, O) below.
     int32_t* ids = reinterpret_cast<int32_t*>(smem + (size_t)QPW * 2 * CHB) + (size_t)qs * p.kp;
     const bool use_ids = idx_lds && cand.irow;
+    constexpr int IPL = 2048 / (WAVE * G);        // index entries per lane, K' <= 2048
+    const int qlane = sub * WAVE + lane;
+    int iv[IPL];
     if (use_ids) {
-        for (int s0 = sub * WAVE + lane; s0 < p.kp; s0 += G * WAVE) ids[s0] = cand.irow[s0];
-        if constexpr (G > 1) __syncthreads();
+#pragma unroll
+        for (int k = 0; k < IPL; ++k) {
+            const int s0 = qlane + k * WAVE * G;
+            iv[k] = s0 < p.kp ? cand.irow[s0] : -1;
+        }
     }
 
     Frag<T> qb[HT][KS];
@@ -357,24 +365,50 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
         }
     };
 
-    // slots past the last candidate need no chunk (index rows usually end in -1 padding)
-    int last = -1;
-    for (int s0 = 0; s0 < cand.nslots; s0 += WAVE)
-        if (cand.code(s0 + lane, use_ids, ids) >= 0) last = s0 + lane;
+    // Slots past the last candidate need no chunk (index rows usually end in
+    // -1 padding).  The last valid index slot comes from the entries each lane
+    // loaded, which it also writes to LDS.
+    int lastc = -1;                               // last valid compressed slot (index into the row)
+    if (use_ids) {
 #pragma unroll
-    for (int o2 = 32; o2 >= 1; o2 >>= 1) last = max(last, __shfl_xor(last, o2));
-    const int nch = active ? (last + CHUNK) / CHUNK : 0;
-    int nloop = nch;
+        for (int k = 0; k < IPL; ++k) {
+            const int s0 = qlane + k * WAVE * G;
+            if (s0 < p.kp) {
+                ids[s0] = iv[k];
+                if (iv[k] >= 0 && iv[k] < cand.nv) lastc = max(lastc, s0);
+            }
+        }
+    } else if (cand.irow) {                       // index row left in global memory
+        for (int s0 = qlane; s0 < p.kp; s0 += WAVE * G) {
+            const int j = cand.irow[s0];
+            if (j >= 0 && j < cand.nv) lastc = max(lastc, s0);
+        }
+    } else {
+        lastc = cand.nslots - cand.nwin - 1;      // dense mode: every valid block; window only: none
+    }
+#pragma unroll
+    for (int o2 = 32; o2 >= 1; o2 >>= 1) lastc = max(lastc, __shfl_xor(lastc, o2));
+    int last = active ? max(cand.nwin - 1, lastc >= 0 ? cand.nwin + lastc : -1) : -1;
+    int nloop;
     if constexpr (G > 1) {
-        // every wave of the workgroup runs the same number of barrier rounds:
-        // the longest candidate list among its queries
-        __shared__ int nch_s[4];
-        if (lane == 0 && sub == 0) nch_s[qs] = nch;
+        // one barrier: the index row is in LDS, and every wave sees every
+        // query's last slot; all waves of the workgroup run the same number of
+        // barrier rounds, for the longest candidate list among its queries
+        __shared__ int last_s[4];
+        if (lane == 0) last_s[wave] = last;
         __syncthreads();
         nloop = 0;
 #pragma unroll
-        for (int i = 0; i < QPW; ++i) nloop = max(nloop, nch_s[i]);
+        for (int q = 0; q < QPW; ++q) {
+            int lq = -1;
+#pragma unroll
+            for (int w = 0; w < G; ++w) lq = max(lq, last_s[q * G + w]);
+            if (q == qs) last = lq;
+            nloop = max(nloop, (lq + CHUNK) / CHUNK);
+        }
     }
+    const int nch = (last + CHUNK) / CHUNK;
+    if constexpr (G == 1) nloop = nch;
     // every load so far (Q, dO, O, the index row) has landed: the loop below
     // then waits only on its own row gathers
     __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)

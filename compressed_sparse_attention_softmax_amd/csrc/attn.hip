@@ -53,13 +53,25 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const bf16_t* p)
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
+// Row-dependent permutation of the 8-element units of an LDS row: unit u of
+// row r is stored at u ^ unit_swz(r, units).  Within any 16 consecutive rows
+// (aligned) the XOR values are all different, so 16 lanes reading the same
+// unit of 16 rows hit 16 different bank groups; within any 8 consecutive
+// rows (aligned) they differ in more than the lowest bit, so 32 lanes reading
+// a unit pair {2m, 2m+1} of 8 rows (the transposing read) hit 16 different
+// bank groups.  `units` (a power of two) is the number of units per row.
+__device__ __forceinline__ int unit_swz(int r, int units)
+{
+    return (((r & 7) << 1) | ((r >> 3) & 1)) & (units - 1);
+}
+
 // MFMA operand whose k index runs over rows of a row-major LDS tile:
 // lane (n = lane%16, g = lane/16) gets column col0 + n of rows
 // r0 + 4g + e (e = 0..3) and r0 + 16 + 4g + (e-4) (e = 4..7).
 // This is the row order in which a 16x16 C tile pair (rows 0-15, 16-31 of a
 // 32-row chunk, lane holding rows 4g+i) feeds the k slots of one operand.
 // `stride` is the row stride in elements; with `swz` the tile is stored with
-// 8-element units permuted per row (unit u of row r at u ^ (r & 7)).
+// 8-element units permuted per row (unit u of row r at u ^ unit_swz(r)).
 template <typename T>
 __device__ __forceinline__ Frag<T> rows_operand(const T* tile, int stride, int r0, int col0, bool swz)
 {
@@ -69,7 +81,7 @@ __device__ __forceinline__ Frag<T> rows_operand(const T* tile, int stride, int r
         const int r = r0 + 4 * g + (n16 >> 2);
         const int c = col0 + 4 * (n16 & 3);
         auto addr = [&](int rr) {
-            const int cc = swz ? ((((c >> 3) ^ (rr & 7)) << 3) | (c & 7)) : c;
+            const int cc = swz ? ((((c >> 3) ^ unit_swz(rr, stride >> 3)) << 3) | (c & 7)) : c;
             return tile + rr * stride + cc;
         };
         const bf16x4 a = ds_read_tr(addr(r));
@@ -81,7 +93,7 @@ __device__ __forceinline__ Frag<T> rows_operand(const T* tile, int stride, int r
         for (int e = 0; e < 8; ++e) {
             const int rr = r0 + 16 * (e / 4) + 4 * g + (e % 4);
             const int c = col0 + n16;
-            const int cc = swz ? ((((c >> 3) ^ (rr & 7)) << 3) | (c & 7)) : c;
+            const int cc = swz ? ((((c >> 3) ^ unit_swz(rr, stride >> 3)) << 3) | (c & 7)) : c;
             f.v[e] = tile[rr * stride + cc];
         }
     }
@@ -134,7 +146,7 @@ struct Cand {
 // global memory into registers (each lane loads 16-byte pieces of its rows)
 // while chunk k computes, and written to the other buffer afterwards; rows
 // are stored with 8-element units permuted per row (unit u of row r at
-// u ^ (r & 7)) so both reads below are free of bank conflicts.
+// u ^ unit_swz(r)) so both reads below are free of bank conflicts.
 // S^T[r, h] = R[r, :] . Q[h, :]      A = rows from LDS (m = r, k = d)
 //                                    B = Q^T (k = d, n = h), registers
 // forward: online softmax per column h (lane), base-2 exponentials, then
@@ -262,7 +274,7 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
 #pragma unroll
         for (int k = 0; k < NPL; ++k) {
             const int pos = (my_j + LPR * k) * E16;
-            *reinterpret_cast<piece_t*>(dst + ((((pos >> 3) ^ (my_r & 7))) << 3) + (pos & 7)) = rg[k];
+            *reinterpret_cast<piece_t*>(dst + ((((pos >> 3) ^ unit_swz(my_r, D / 8))) << 3) + (pos & 7)) = rg[k];
         }
     };
 
@@ -275,7 +287,7 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
             Frag<T> ra[KS];
             const int r = 16 * rt + n16;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) ra[ks] = load_frag(tile + r * D + (((4 * ks + g) ^ (r & 7)) << 3));
+            for (int ks = 0; ks < KS; ++ks) ra[ks] = load_frag(tile + r * D + (((4 * ks + g) ^ unit_swz(r, D / 8)) << 3));
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
                 f32x4 acc = f4zero();
@@ -581,7 +593,7 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
     // Stage q[t] and dO[t] into buffer `buf` with asynchronous global->LDS
     // loads.  16-byte piece s of the block lands at LDS piece s; its source is
     // chosen so that the LDS block holds rows of 8-element units permuted as
-    // unit u of row h at u ^ (h & 7).  Also lse, Delta (plain loads) and the
+    // unit u of row h at u ^ unit_swz(h).  Also lse, Delta (plain loads) and the
     // multiplicities of the tile's rows for query t in cnt buffer `cb`.
     constexpr int IDX_REGS = 2048 / 256;          // K' <= 2048
     int jreg[IDX_REGS];
@@ -599,7 +611,7 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
             // piece pr of LDS row h holds elements [pr*E, pr*E+E) of the permuted row
             constexpr int E = 16 / (int)sizeof(T);
             const int pos = pr * E;                       // element position in LDS row
-            const int unit = (pos >> 3) ^ (h & 7);        // source unit
+            const int unit = (pos >> 3) ^ unit_swz(h, D / 8);   // source unit
             const int srcel = (unit << 3) | (pos & 7);
             const int hh = h < p.H ? h : 0;               // padded heads read row 0 (masked later)
             const size_t wbase = (size_t)(k * 4 + wave) * WAVE * 16;   // wave's 1 KiB in bytes
@@ -713,7 +725,7 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
                 const int hrow = 16 * ht + n16;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const int off = hrow * D + (((4 * ks + g) ^ (hrow & 7)) << 3);   // d = 32 ks + 8 g
+                    const int off = hrow * D + (((4 * ks + g) ^ unit_swz(hrow, D / 8)) << 3);   // d = 32 ks + 8 g
                     qa[ks] = load_frag(q_lds + off);
                     da[ks] = load_frag(do_lds + off);
                 }

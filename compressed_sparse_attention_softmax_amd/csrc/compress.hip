@@ -7,11 +7,12 @@
 // (z_channels == d) or with one score per row (z_channels == 1).
 //
 // HBM-bound: every element of x and z is read once (twice when spans
-// overlap).  One workgroup of 256 threads owns block (b, j): the d channels
-// are split in chunks of 8 (one 16-byte load per row for bf16) and the rows of
-// the span are split over the remaining threads, each keeping an online
-// softmax (running max, denominator, weighted sum) per channel; the partial
-// states are merged through LDS.
+// overlap).  A group of NS consecutive lanes owns one (block, 8 channels)
+// pair: lane split sp takes the span rows lo + sp, lo + sp + NS, ... in groups
+// of 8 (one 16-byte load per row for bf16), keeping a running max, denominator
+// and weighted sum per channel, and the NS partial states are merged with
+// lane shuffles.  NS never exceeds the ratio, so every split owns at least one
+// row of every span (spans are clipped at 0 but keep at least `ratio` rows).
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
 #include "timing.hpp"
@@ -27,89 +28,92 @@ template <typename T> __device__ __forceinline__ void load8(const T* p, float* o
     for (int e = 0; e < 8; ++e) out[e] = to_f32(f.v[e]);
 }
 
-template <typename T, int D>
-struct PoolState {
-    static constexpr int NCH = D / 8;
-    static constexpr int NSPLIT = 256 / NCH;
-};
+// e^x on the transcendental unit (v_exp_f32 after a multiply by log2 e)
+__device__ __forceinline__ float fexp(float x) { return fast_exp2(x * LOG2E); }
 
-// Per-thread online softmax over its share of the span's rows, then a merge
-// over the row splits.  On return the threads with split 0 hold the block's
-// (max, denominator, weighted sum) for their 8 channels.
-template <typename T, int D>
-__device__ __forceinline__ void pool_block(const T* __restrict__ x, const T* __restrict__ z,
-                                           int zc, int64_t rowbase, int lo, int hi, int q, int sp,
-                                           float* m, float* s, float* a, float* lds)
+// Softmax state (max m, denominator s, weighted sum a) of the 8 channels
+// [8q, 8q+8) over the rows [lo, hi) of one span, split NS ways over
+// consecutive lanes; every lane of the group returns the merged state.
+template <typename T, int D, int NS>
+__device__ __forceinline__ void span_state(const T* __restrict__ x, const T* __restrict__ z, int zc,
+                                           int64_t rowbase, int lo, int hi, int q, int sp,
+                                           float* m, float* s, float* a)
 {
-    constexpr int NCH = PoolState<T, D>::NCH;
-    constexpr int NSPLIT = PoolState<T, D>::NSPLIT;
 #pragma unroll
     for (int e = 0; e < 8; ++e) { m[e] = -INFINITY; s[e] = 0.f; a[e] = 0.f; }
-    for (int u = lo + sp; u < hi; u += NSPLIT) {
-        float xv[8], zv[8];
-        load8(x + (rowbase + u) * D + 8 * q, xv);
-        if (zc == 1) {
-            float zz = to_f32(z[rowbase + u]);
+    for (int u0 = lo + sp; u0 < hi; u0 += 8 * NS) {
+        float xv[8][8], zv[8][8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) zv[e] = zz;
-        } else {
-            load8(z + (rowbase + u) * D + 8 * q, zv);
-        }
+        for (int k = 0; k < 8; ++k) {
+            const int u = u0 + k * NS;
+            if (u < hi) {
+                load8(x + (rowbase + u) * D + 8 * q, xv[k]);
+                if (zc == 1) {
+                    const float zz = to_f32(z[rowbase + u]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if (zv[e] > m[e]) {
-                float f = expf(m[e] - zv[e]);
-                s[e] = s[e] * f + 1.f;
-                a[e] = a[e] * f + xv[e];
-                m[e] = zv[e];
+                    for (int e = 0; e < 8; ++e) zv[k][e] = zz;
+                } else {
+                    load8(z + (rowbase + u) * D + 8 * q, zv[k]);
+                }
             } else {
-                float f = expf(zv[e] - m[e]);
-                s[e] += f;
-                a[e] += f * xv[e];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { xv[k][e] = 0.f; zv[k][e] = -INFINITY; }
             }
         }
-    }
-    // merge the row splits: lds holds [3][256][8] floats
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        lds[(0 * 256 + tid) * 8 + e] = m[e];
-        lds[(1 * 256 + tid) * 8 + e] = s[e];
-        lds[(2 * 256 + tid) * 8 + e] = a[e];
-    }
-    __syncthreads();
-    if (sp == 0) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            float M = -INFINITY;
-            for (int k = 0; k < NSPLIT; ++k) M = fmaxf(M, lds[(0 * 256 + k * NCH + q) * 8 + e]);
-            float S = 0.f, A = 0.f;
-            for (int k = 0; k < NSPLIT; ++k) {
-                float mk = lds[(0 * 256 + k * NCH + q) * 8 + e];
-                float f = mk == -INFINITY ? 0.f : expf(mk - M);
-                S += lds[(1 * 256 + k * NCH + q) * 8 + e] * f;
-                A += lds[(2 * 256 + k * NCH + q) * 8 + e] * f;
+            float gm = zv[0][e];
+#pragma unroll
+            for (int k = 1; k < 8; ++k) gm = fmaxf(gm, zv[k][e]);
+            const float mn = fmaxf(m[e], gm);      // finite: the first group of a split has a row
+            const float f = fexp(m[e] - mn);
+            float ss = 0.f, aa = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float w = fexp(zv[k][e] - mn);
+                ss += w;
+                aa += w * xv[k][e];
             }
-            m[e] = M; s[e] = S; a[e] = A;
+            s[e] = s[e] * f + ss;
+            a[e] = a[e] * f + aa;
+            m[e] = mn;
+        }
+    }
+#pragma unroll
+    for (int o = 1; o < NS; o <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float mo = __shfl_xor(m[e], o), so = __shfl_xor(s[e], o), ao = __shfl_xor(a[e], o);
+            const float mn = fmaxf(m[e], mo);
+            const float f0 = fexp(m[e] - mn), f1 = fexp(mo - mn);
+            s[e] = s[e] * f0 + so * f1;
+            a[e] = a[e] * f0 + ao * f1;
+            m[e] = mn;
         }
     }
 }
 
-template <typename T, int D>
+// one lane group per (batch, block, 8 channels)
+template <typename T, int D, int NS>
 __global__ __launch_bounds__(256) void compress_fwd_kernel(const T* __restrict__ x,
                                                            const T* __restrict__ z, int zc,
                                                            T* __restrict__ c, float* __restrict__ c32,
-                                                           int S, int r, int L, int nc)
+                                                           int b, int S, int r, int L, int nc)
 {
-    constexpr int NCH = PoolState<T, D>::NCH;
-    __shared__ float lds[3 * 256 * 8];
-    const int j = blockIdx.x, bi = blockIdx.y;
-    const int q = threadIdx.x % NCH, sp = threadIdx.x / NCH;
+    constexpr int NCH = D / 8;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)b * nc * NCH * NS;
+    const bool live = gid < total;                 // whole lane groups share liveness
+    const int64_t gg = live ? gid : 0;
+    const int sp = (int)(gg % NS);
+    const int q = (int)(gg / NS % NCH);
+    const int64_t bj = gg / NS / NCH;
+    const int j = (int)(bj % nc), bi = (int)(bj / nc);
     const int hi = (j + 1) * r, lo = max(0, hi - L);
     float m[8], s[8], a[8];
-    pool_block<T, D>(x, z, zc, (int64_t)bi * S, lo, hi, q, sp, m, s, a, lds);
-    if (sp == 0) {
-        const int64_t o = ((int64_t)bi * nc + j) * D + 8 * q;
+    span_state<T, D, NS>(x, z, zc, (int64_t)bi * S, lo, hi, q, sp, m, s, a);
+    if (live && sp == 0) {
+        const int64_t o = bj * D + 8 * q;
         Frag<T> f;
         float v[8];
 #pragma unroll
@@ -130,10 +134,10 @@ __global__ __launch_bounds__(256) void compress_fwd_kernel(const T* __restrict__
 // [j0*ratio, (j0+JB)*ratio) exclusively (no atomics): it first recomputes the
 // softmax state (max, 1/den, c32) and stages dc for every block whose span
 // reaches those rows -- its own blocks plus the halo of later blocks when
-// spans overlap -- then each thread gathers, for a (row, 8 channels) pair,
-// the contributions of the blocks covering the row.  Rows past n_c*ratio are
-// covered by no block and get zeros.
-template <typename T, int D>
+// spans overlap -- all blocks at once, then each thread gathers, for a
+// (row, 8 channels) pair, the contributions of the blocks covering the row.
+// Rows past n_c*ratio are covered by no block and get zeros.
+template <typename T, int D, int NS>
 __global__ __launch_bounds__(256) void compress_bwd_kernel(const T* __restrict__ x,
                                                            const T* __restrict__ z, int zc,
                                                            const float* __restrict__ dc,
@@ -141,32 +145,37 @@ __global__ __launch_bounds__(256) void compress_bwd_kernel(const T* __restrict__
                                                            float* __restrict__ dz, int S, int r,
                                                            int L, int nc, int JB)
 {
-    constexpr int NCH = PoolState<T, D>::NCH;
-    __shared__ float lds[3 * 256 * 8];
+    constexpr int NCH = D / 8;
     extern __shared__ float st[];             // [block][4][D]: max, 1/den, c32, dc
     const int bi = blockIdx.y;
     const int j0 = blockIdx.x * JB;
     const int halo = (L + r - 1) / r - 1;
     const int jhi = min(nc, j0 + JB + halo);
-    const int q = threadIdx.x % NCH, sp = threadIdx.x / NCH;
     const int64_t rowbase = (int64_t)bi * S;
-    for (int j = j0; j < jhi; ++j) {
+    // softmax state of every block the workgroup needs, NS lanes per (block, chunk)
+    const int nst = (jhi - j0) * NCH * NS;
+    for (int i0 = 0; i0 < nst; i0 += 256) {       // uniform trip count: groups stay whole
+        const int i = i0 + (int)threadIdx.x;
+        const bool live = i < nst;
+        const int ii = live ? i : 0;
+        const int sp = ii % NS, q = ii / NS % NCH, j = j0 + ii / NS / NCH;
         const int hi = (j + 1) * r, lo = max(0, hi - L);
         float m[8], s[8], a[8];
-        pool_block<T, D>(x, z, zc, rowbase, lo, hi, q, sp, m, s, a, lds);
-        if (sp == 0) {
+        span_state<T, D, NS>(x, z, zc, rowbase, lo, hi, q, sp, m, s, a);
+        if (live && sp == 0) {
             float* sj = st + (size_t)(j - j0) * 4 * D;
             const Frag<float> gf = load_frag(dc + ((int64_t)bi * nc + j) * D + 8 * q);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
+                const float inv = 1.f / s[e];
                 sj[8 * q + e] = m[e];
-                sj[D + 8 * q + e] = 1.f / s[e];
-                sj[2 * D + 8 * q + e] = a[e] / s[e];
+                sj[D + 8 * q + e] = inv;
+                sj[2 * D + 8 * q + e] = a[e] * inv;
                 sj[3 * D + 8 * q + e] = gf.v[e];
             }
         }
-        __syncthreads();     // the pooling scratch is reused by the next block
     }
+    __syncthreads();
     const int u_lo = j0 * r, u_hi = min(j0 + JB, nc) * r;
     const int npairs = (u_hi - u_lo) * NCH;
     const int nloop = (npairs + 255) / 256 * 256;     // whole waves stay together for the row sums
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(256) void compress_bwd_kernel(const T* __restrict__
                 const float* sj = st + (size_t)(j - j0) * 4 * D + 8 * qq;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float ag = expf(zv[e] - sj[e]) * sj[D + e] * sj[3 * D + e];
+                    const float ag = fexp(zv[e] - sj[e]) * sj[D + e] * sj[3 * D + e];
                     gx[e] += ag;
                     gz[e] += ag * (xv[e] - sj[2 * D + e]);
                 }
@@ -224,25 +233,46 @@ __global__ __launch_bounds__(256) void compress_bwd_kernel(const T* __restrict__
     }
 }
 
-template <typename T, int D>
-hipError_t launch_compress_fwd(const CompressArgs& p, hipStream_t st)
+// lanes per span: a power of two, at most the ratio (every split keeps a row)
+// and about one group of 8 rows per lane, at most 8
+inline int span_splits(int r, int L)
 {
-    dim3 grid(p.nc, p.b);
+    int ns = 1;
+    while (ns * 2 <= 8 && ns * 2 <= r && ns * 2 * 8 <= L) ns *= 2;
+    return ns;
+}
+
+template <typename T, int D, int NS>
+hipError_t launch_compress_fwd_ns(const CompressArgs& p, hipStream_t st)
+{
+    const int64_t threads = (int64_t)p.b * p.nc * (D / 8) * NS;
+    dim3 grid((unsigned)((threads + 255) / 256));
     TimedLaunch tl(K_COMPRESS_FWD, st);
-    hipLaunchKernelGGL((compress_fwd_kernel<T, D>), grid, dim3(256), 0, st,
-                       (const T*)p.x, (const T*)p.z, p.zc, (T*)p.c, p.c32, p.S, p.r, p.L, p.nc);
+    hipLaunchKernelGGL((compress_fwd_kernel<T, D, NS>), grid, dim3(256), 0, st, (const T*)p.x, (const T*)p.z, p.zc,
+                       (T*)p.c, p.c32, p.b, p.S, p.r, p.L, p.nc);
     return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_compress_bwd(const CompressArgs& p, hipStream_t st)
+hipError_t launch_compress_fwd(const CompressArgs& p, hipStream_t st)
+{
+    switch (span_splits(p.r, p.L)) {
+    case 1: return launch_compress_fwd_ns<T, D, 1>(p, st);
+    case 2: return launch_compress_fwd_ns<T, D, 2>(p, st);
+    case 4: return launch_compress_fwd_ns<T, D, 4>(p, st);
+    default: return launch_compress_fwd_ns<T, D, 8>(p, st);
+    }
+}
+
+template <typename T, int D, int NS>
+hipError_t launch_compress_bwd_ns(const CompressArgs& p, hipStream_t st)
 {
     // about 512 workgroups, at most 16 blocks each
     int jb = (int)(((int64_t)p.nc * p.b) / 512);
     jb = jb < 1 ? 1 : (jb > 16 ? 16 : jb);
     const int halo = (p.L + p.r - 1) / p.r - 1;
     const size_t lds = (size_t)(jb + halo) * 4 * D * sizeof(float);
-    auto kern = compress_bwd_kernel<T, D>;
+    auto kern = compress_bwd_kernel<T, D, NS>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -252,6 +282,17 @@ hipError_t launch_compress_bwd(const CompressArgs& p, hipStream_t st)
     hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const T*)p.x, (const T*)p.z, p.zc, p.dc, p.dx,
                        p.dz, p.S, p.r, p.L, p.nc, jb);
     return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_compress_bwd(const CompressArgs& p, hipStream_t st)
+{
+    switch (span_splits(p.r, p.L)) {
+    case 1: return launch_compress_bwd_ns<T, D, 1>(p, st);
+    case 2: return launch_compress_bwd_ns<T, D, 2>(p, st);
+    case 4: return launch_compress_bwd_ns<T, D, 4>(p, st);
+    default: return launch_compress_bwd_ns<T, D, 8>(p, st);
+    }
 }
 
 }  // namespace

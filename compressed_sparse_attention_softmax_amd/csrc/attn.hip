@@ -176,7 +176,8 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
     char* tiles = smem + (size_t)qs * 2 * CHB;
 
     const int bi = blockIdx.y;
-    const int t = blockIdx.x * QPW + qs;
+    // latest queries (longest candidate lists) first: short ones fill the tail
+    const int t = ((int)gridDim.x - 1 - (int)blockIdx.x) * QPW + qs;
     const bool active = t < p.S;                  // inactive waves still join the barriers (G > 1)
     const int h0 = sub * 16 * HT;
     Cand<T> cand;

@@ -249,14 +249,29 @@ __global__ __launch_bounds__(256, 1) void index_topk_kernel(const T* __restrict_
     int cnt = 0;
     constexpr int CH = 16 / sizeof(T);               // elements per 16-B chunk
     constexpr int CHUNKS = KT * DI / CH;
-    for (int j0 = 0; j0 < nv_max; j0 += KT) {
-        __syncthreads();
-        for (int c = threadIdx.x; c < CHUNKS; c += 256) {
+    constexpr int CPT = CHUNKS / 256;                // chunks per thread
+    static_assert(CPT * 256 == CHUNKS, "a key tile splits evenly over the workgroup");
+    // the next key tile is loaded into registers while the current one computes
+    uint4 pre[CPT];
+    auto load_tile = [&](int j0) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int c = (int)threadIdx.x + 256 * k;
             const int rr = c / (DI / CH), cc = (c % (DI / CH)) * CH;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (j0 + rr < nc) v = *reinterpret_cast<const uint4*>(kb + (int64_t)(j0 + rr) * DI + cc);
-            *reinterpret_cast<uint4*>(ktile + rr * ROW + cc) = v;
+            pre[k] = j0 + rr < nc ? *reinterpret_cast<const uint4*>(kb + (int64_t)(j0 + rr) * DI + cc)
+                                  : make_uint4(0u, 0u, 0u, 0u);
         }
+    };
+    if (nv_max > 0) load_tile(0);
+    for (int j0 = 0; j0 < nv_max; j0 += KT) {
+        __syncthreads();                              // every wave is done with the previous tile
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int c = (int)threadIdx.x + 256 * k;
+            const int rr = c / (DI / CH), cc = (c % (DI / CH)) * CH;
+            *reinterpret_cast<uint4*>(ktile + rr * ROW + cc) = pre[k];
+        }
+        if (j0 + KT < nv_max) load_tile(j0 + KT);
         __syncthreads();
         if (j0 >= nv) continue;
         float my = -INFINITY;

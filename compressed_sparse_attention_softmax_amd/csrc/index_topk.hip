@@ -220,10 +220,12 @@ __global__ __launch_bounds__(256, 1) void index_topk_kernel(const T* __restrict_
     bufs.xj = reinterpret_cast<int*>(mine + (size_t)cap * 8 + HBINS * 4 + 64 * 4);
 
     const int bi = blockIdx.y;
-    const int t = blockIdx.x * 4 + wave;
+    // latest queries (most valid blocks) first: short ones fill the tail
+    const int qblk = (int)gridDim.x - 1 - (int)blockIdx.x;
+    const int t = qblk * 4 + wave;
     const bool active = t < S;
     const int nv = active ? min((t + 1) / r, nc) : 0;
-    const int t_last = min(blockIdx.x * 4 + 3, S - 1);
+    const int t_last = min(qblk * 4 + 3, S - 1);
     const int nv_max = min((t_last + 1) / r, nc);
     const int64_t row = (int64_t)bi * S + (active ? t : 0);
 

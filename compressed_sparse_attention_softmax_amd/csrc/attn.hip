@@ -233,8 +233,7 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
                     for (int e = 0; e < 8; ++e) part += to_f32(db[ht][ks].v[e]) * to_f32(of.v[e]);
                 }
             }
-            part += __shfl_xor(part, 16);
-            part += __shfl_xor(part, 32);
+            part = rows_sum(part);
             dlt[ht] = part;
             lse2[ht] = hv ? p.lse[qrow * p.H + h] * LOG2E : INFINITY;
             if (active && hv && g == 0) {
@@ -331,9 +330,7 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
             if (__any(need)) {                     // rare
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) {
-                    float m = mloc[ht];
-                    m = fmaxf(m, __shfl_xor(m, 16));
-                    m = fmaxf(m, __shfl_xor(m, 32));
+                    const float m = rows_max(mloc[ht]);
                     const float mnew = fmaxf(m2[ht], m * sl2);
                     const float alpha = fast_exp2(m2[ht] - mnew);
                     lsum[ht] *= alpha;

@@ -165,6 +165,25 @@ __device__ __forceinline__ int wave_sum_i(int v)
     return v;
 }
 
+// Sums / maxima over the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48) with the gfx950 row-swap moves: v_permlane16_swap exchanges odd and
+// even rows between its two operands, v_permlane32_swap the two halves, so
+// combining both results of each swap reduces across rows without LDS.
+__device__ __forceinline__ float rows_sum(float v)
+{
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows_max(float v)
+{
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // 2^x on the transcendental unit (v_exp_f32): one instruction; results
 // below 2^-126 flush to zero, which is harmless for softmax weights.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -196,7 +196,7 @@ __device__ float select_keep(const WaveBufs& b, int n, int k)
 }
 
 template <typename T, int DI, int HT>
-__global__ __launch_bounds__(256, 1) void index_topk_kernel(const T* __restrict__ qi,
+__global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict__ qi,
                                                             const T* __restrict__ ki,
                                                             const float* __restrict__ w,
                                                             int32_t* __restrict__ idx,
@@ -292,9 +292,9 @@ __global__ __launch_bounds__(256, 1) void index_topk_kernel(const T* __restrict_
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v += wv[ht][i] * fmaxf(acc[ht][i], 0.f);
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
+                for (int i = 0; i < 4; ++i)      // ReLU on the bit pattern: negative floats are negative ints
+                    v += wv[ht][i] * __int_as_float(max(__float_as_int(acc[ht][i]), 0));
+            v = rows_sum(v);
             if (g == st) my = v;
         }
         my = my + 0.0f;                        // -0 -> +0: one value per tie class

@@ -184,6 +184,7 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
     cand.init(p, bi, active ? t : p.S - 1);
     const int64_t qrow = (int64_t)bi * p.S + (active ? t : p.S - 1);
     const float sl2 = p.scale * LOG2E;
+    [[maybe_unused]] const float isl2 = 1.f / sl2;
     [[maybe_unused]] const float lsc = __log2f(p.scale);
     const T* qp = (const T*)p.q + qrow * p.H * D;
     // The query's index row goes to LDS once (per-chunk slot lookups then do
@@ -319,18 +320,21 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
             // head re-bases); P <= 2^8 otherwise, and O / l is unchanged.  The
             // test needs only each lane's own maximum; the per-head maximum
             // (a cross-lane reduction) is formed on the rare re-base.
-            float mloc[HT];
             bool need = false;
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
-                mloc[ht] = fmaxf(fmaxf(fmaxf(s[ht][0][0], s[ht][0][1]), fmaxf(s[ht][0][2], s[ht][0][3])),
-                                 fmaxf(fmaxf(s[ht][1][0], s[ht][1][1]), fmaxf(s[ht][1][2], s[ht][1][3])));
-                need |= mloc[ht] * sl2 > m2[ht] + 8.f;   // scale > 0: max commutes with it
+                const float thr = fmaf(m2[ht] + 8.f, isl2, 0.f);   // scale > 0: compare logits directly
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) need |= s[ht][rt][i] > thr;
             }
             if (__any(need)) {                     // rare
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) {
-                    const float m = rows_max(mloc[ht]);
+                    const float mloc = fmaxf(fmaxf(fmaxf(s[ht][0][0], s[ht][0][1]), fmaxf(s[ht][0][2], s[ht][0][3])),
+                                             fmaxf(fmaxf(s[ht][1][0], s[ht][1][1]), fmaxf(s[ht][1][2], s[ht][1][3])));
+                    const float m = rows_max(mloc);
                     const float mnew = fmaxf(m2[ht], m * sl2);
                     const float alpha = fast_exp2(m2[ht] - mnew);
                     lsum[ht] *= alpha;

@@ -483,16 +483,20 @@ template <typename T, int D> constexpr int rows_stage_buffers()
 {
     return 4 * 64 * D * (int)sizeof(T) + 8 * 1024 <= ATTN_LDS_LIMIT ? 2 : 1;
 }
-template <typename T, int D> constexpr int rows_per_wave_t() { return D <= 128 ? 64 : 16; }
+// waves per workgroup and key rows per wave: a workgroup's tile is 256 rows at
+// d <= 128 (64 at d = 512).  bf16 uses 8 waves of 32 rows: two waves per SIMD,
+// so one wave's exponentials overlap the other's matrix work.
+template <typename T, int D> constexpr int rows_waves_t() { return (sizeof(T) == 2 && D <= 128) ? 8 : 4; }
+template <typename T, int D> constexpr int rows_per_wave_t() { return D <= 128 ? 256 / rows_waves_t<T, D>() : 16; }
 // LDS bytes of the key-stationary kernel without / with its key-row tile
 template <typename T, int D> constexpr size_t rows_lds_base()
 {
     return 2 * (size_t)rows_stage_buffers<T, D>() * 64 * D * sizeof(T) + 4 * 64 * 4 +
-           (size_t)3 * 4 * rows_per_wave_t<T, D>() * 4;
+           (size_t)3 * rows_waves_t<T, D>() * rows_per_wave_t<T, D>() * 4;
 }
 template <typename T, int D> constexpr size_t rows_lds_tile()
 {
-    return (size_t)4 * rows_per_wave_t<T, D>() * (D + 16 / sizeof(T)) * sizeof(T);
+    return (size_t)rows_waves_t<T, D>() * rows_per_wave_t<T, D>() * (D + 16 / sizeof(T)) * sizeof(T);
 }
 // bf16 rows at d <= 128 stay in registers (64 VGPRs next to the AGPR
 // accumulators): the tile would be re-read from LDS for every head tile.
@@ -507,17 +511,17 @@ struct RowsGeom {
     int64_t win_off, comp_off;         // float offsets of the two partial regions in the workspace
 };
 
-template <typename T, int D, int RW>
-__global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom geo,
+template <typename T, int D, int RW, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsGeom geo,
                                                            const float* __restrict__ delta,
                                                            float* __restrict__ ws)
 {
-    constexpr int KS = D / 32, DT = D / 16, RT = RW / 16, TR = 4 * RW;
+    constexpr int KS = D / 32, DT = D / 16, RT = RW / 16, TR = NW * RW, NT = 64 * NW;
     constexpr int HP = 64;                       // heads, padded to 4 head tiles
     constexpr int QELEMS = HP * D;               // one staged q (or dO) block
     constexpr int NBUF = rows_stage_buffers<T, D>();
     constexpr int L16 = QELEMS * (int)sizeof(T) / 16;   // 16-byte pieces per block
-    static_assert(L16 % 256 == 0, "staging: whole 1 KiB wave loads");
+    static_assert(L16 % NT == 0, "staging: whole 1 KiB wave loads");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     // [buf 0: q, dO][buf 1: q, dO (double buffering only)][lse x2][Delta x2][mult x3]
     T* stage_base = reinterpret_cast<T*>(smem);
@@ -597,7 +601,7 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
     // chosen so that the LDS block holds rows of 8-element units permuted as
     // unit u of row h at u ^ unit_swz(h).  Also lse, Delta (plain loads) and the
     // multiplicities of the tile's rows for query t in cnt buffer `cb`.
-    constexpr int IDX_REGS = 2048 / 256;          // K' <= 2048
+    constexpr int IDX_REGS = 2048 / NT;           // K' <= 2048
     int jreg[IDX_REGS];
     auto stage = [&](int t, int buf, int cb) {
         const int64_t qrow = (int64_t)bi * p.S + t;
@@ -607,8 +611,8 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
         T* ddst = qdst + QELEMS;
         constexpr int PER_ROW = D * (int)sizeof(T) / 16;   // 16-byte pieces per row
 #pragma unroll
-        for (int k = 0; k < L16 / 256; ++k) {
-            const int piece = (k * 4 + wave) * WAVE + lane;
+        for (int k = 0; k < L16 / NT; ++k) {
+            const int piece = (k * NW + wave) * WAVE + lane;
             const int h = piece / PER_ROW, pr = piece % PER_ROW;
             // piece pr of LDS row h holds elements [pr*E, pr*E+E) of the permuted row
             constexpr int E = 16 / (int)sizeof(T);
@@ -616,7 +620,7 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
             const int unit = (pos >> 3) ^ unit_swz(h, D / 8);   // source unit
             const int srcel = (unit << 3) | (pos & 7);
             const int hh = h < p.H ? h : 0;               // padded heads read row 0 (masked later)
-            const size_t wbase = (size_t)(k * 4 + wave) * WAVE * 16;   // wave's 1 KiB in bytes
+            const size_t wbase = (size_t)(k * NW + wave) * WAVE * 16;  // wave's 1 KiB in bytes
             __builtin_amdgcn_global_load_lds((const void*)(qsrc + hh * D + srcel),
                                              (__attribute__((address_space(3))) void*)((char*)qdst + wbase), 16, 0, 0);
             __builtin_amdgcn_global_load_lds((const void*)(dsrc + hh * D + srcel),
@@ -635,13 +639,13 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
                 const int32_t* irow = p.idx + qrow * p.kp;
 #pragma unroll
                 for (int k = 0; k < IDX_REGS; ++k) {
-                    const int s = threadIdx.x + 256 * k;
+                    const int s = threadIdx.x + NT * k;
                     jreg[k] = s < p.kp ? irow[s] : -1;
                 }
             } else {
                 unsigned* cnt = cnt_lds + cb * TR;
                 const int nv = min((t + 1) / p.r, p.nc);
-                for (int j = tile_lo + threadIdx.x; j < min(tile_hi, nv); j += 256) cnt[j - tile_lo] = 1u;
+                for (int j = tile_lo + threadIdx.x; j < min(tile_hi, nv); j += NT) cnt[j - tile_lo] = 1u;
             }
         }
     };
@@ -658,7 +662,7 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
     };
 
     if (!win) {
-        for (int i = threadIdx.x; i < 3 * TR; i += 256) cnt_lds[i] = 0u;
+        for (int i = threadIdx.x; i < 3 * TR; i += NT) cnt_lds[i] = 0u;
         __syncthreads();
     }
     const float sl2 = p.scale * LOG2E;
@@ -690,7 +694,7 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
         }
         if (!win) {                                        // buffer of t+2: last read by compute(t-1)
             unsigned* nxt = cnt_lds + ((it + 2) % 3) * TR;
-            for (int i = threadIdx.x; i < TR; i += 256) nxt[i] = 0u;
+            for (int i = threadIdx.x; i < TR; i += NT) nxt[i] = 0u;
         }
         const T* q_lds = stage_base + (size_t)(2 * buf) * QELEMS;
         const T* do_lds = q_lds + QELEMS;
@@ -760,6 +764,8 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs p, RowsGeom 
                 const Frag<T> qbf = rows_operand<T>(q_lds, D, 32 * kk, 16 * dt, true);
                 if constexpr (sizeof(T) == 2 && RT == 4) {
                     mfma16x8_acc(acc[0][dt], acc[1][dt], acc[2][dt], acc[3][dt], pa, sa, dob, qbf);
+                } else if constexpr (sizeof(T) == 2 && RT == 2) {
+                    mfma16x4_acc(acc[0][dt], acc[1][dt], pa, sa, dob, qbf);
                 } else {
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) {
@@ -958,10 +964,10 @@ hipError_t launch_reduce(const AttnArgs& p, const RowsGeom& geo, float* ws, hipS
 template <typename T, int D>
 hipError_t launch_rows(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStream_t st)
 {
-    constexpr int RW = rows_per_wave_t<T, D>();
+    constexpr int RW = rows_per_wave_t<T, D>(), NW = rows_waves_t<T, D>();
     const size_t lds = rows_lds_base<T, D>() + (rows_tile_in_lds<T, D>() ? rows_lds_tile<T, D>() : 0);
     if (lds > (size_t)ATTN_LDS_LIMIT) return hipErrorInvalidValue;
-    auto kern = attn_rows_kernel<T, D, RW>;
+    auto kern = attn_rows_kernel<T, D, RW, NW>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int ntiles = geo.n_wt + (p.c ? geo.n_ct : 0);
@@ -969,7 +975,7 @@ hipError_t launch_rows(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStr
     dim3 grid((unsigned)(groups * 8 * ntiles));
     {
         TimedLaunch tl(K_ATTN_ROWS, st);
-        hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p, geo, ws, ws);
+        hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, st, p, geo, ws, ws);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return launch_reduce<D>(p, geo, ws, st);

@@ -74,6 +74,20 @@ __device__ __forceinline__ void mfma16x8_acc(f32x4& c0, f32x4& c1, f32x4& c2, f3
           "v"(sa[3].v), "v"(b0.v), "v"(b1.v));
 }
 
+// Four accumulating MFMAs in one asm block: c_r += pa[r] * b0, then
+// c_r += sa[r] * b1, r = 0..1.
+__device__ __forceinline__ void mfma16x4_acc(f32x4& c0, f32x4& c1, const Frag<bf16_t>* pa, const Frag<bf16_t>* sa,
+                                             const Frag<bf16_t>& b0, const Frag<bf16_t>& b1)
+{
+    asm("s_nop 1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %0, %2, %6, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %3, %6, %1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %0, %4, %7, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %5, %7, %1"
+        : "+a"(c0), "+a"(c1)
+        : "v"(pa[0].v), "v"(pa[1].v), "v"(sa[0].v), "v"(sa[1].v), "v"(b0.v), "v"(b1.v));
+}
+
 // Zero accumulator created in the AGPR file (an MFMA of zero operands), so
 // that a loop-carried accumulator is an AGPR value from its first definition.
 // The trailing 32 wait states let the compiler copy the result right away.
@@ -89,6 +103,10 @@ __device__ __forceinline__ f32x4 agpr_zero()
 // the latest read-after-MFMA-write requirement), ordered after every one of
 // them because the asm reads and writes all N.
 template <int N> __device__ __forceinline__ void agpr_drain(f32x4* a);
+template <> __device__ __forceinline__ void agpr_drain<8>(f32x4* a)
+{
+    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(a[4]), "+a"(a[5]), "+a"(a[6]), "+a"(a[7]));
+}
 template <> __device__ __forceinline__ void agpr_drain<16>(f32x4* a)
 {
     asm volatile("s_nop 15\n\ts_nop 15" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(a[4]), "+a"(a[5]), "+a"(a[6]), "+a"(a[7]), "+a"(a[8]), "+a"(a[9]), "+a"(a[10]), "+a"(a[11]), "+a"(a[12]), "+a"(a[13]), "+a"(a[14]), "+a"(a[15]));

@@ -50,12 +50,12 @@ def _load():
             i64, dp, ip = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
             lib.csa_oracle_compress.argtypes = [i64] * 6 + [dp] * 3
             lib.csa_oracle_compress_bwd.argtypes = [i64] * 6 + [dp] * 5
-            lib.csa_oracle_index_scores.argtypes = [i64] * 4 + [dp] * 3 + [i64, ip, ip, dp]
-            lib.csa_oracle_topk.argtypes = [i64] * 4 + [ip, dp, ip, dp]
+            lib.csa_oracle_index_scores.argtypes = [i64] * 4 + [dp] * 3 + [i64, ip, ip, i64, ip, dp]
+            lib.csa_oracle_topk.argtypes = [i64] * 4 + [ip, ip, i64, ip, dp, ip, dp]
             lib.csa_oracle_attn_fwd.argtypes = ([i64] * 7 + [dp] * 3 + [ip, dp, ctypes.c_double,
-                                                 i64, ip, ip, dp, dp])
+                                                 i64, ip, ip, ip, dp, dp])
             lib.csa_oracle_attn_bwd.argtypes = ([i64] * 7 + [dp] * 3 + [ip, dp, ctypes.c_double,
-                                                 i64, ip, ip, dp, dp, dp, dp, dp])
+                                                 i64, ip, ip, ip, dp, dp, dp, dp, dp])
             for f in (lib.csa_oracle_compress, lib.csa_oracle_compress_bwd,
                       lib.csa_oracle_index_scores, lib.csa_oracle_topk,
                       lib.csa_oracle_attn_fwd, lib.csa_oracle_attn_bwd):
@@ -71,6 +71,14 @@ def _f64(a) -> np.ndarray:
 
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _doc(doc):
+    """doc_ids [b, S] as contiguous int32 (or None) and the row length S."""
+    if doc is None:
+        return None, 0
+    d = np.ascontiguousarray(np.asarray(doc, dtype=np.int32))
+    return d, d.shape[1]
 
 
 def _check(rc, name):
@@ -110,23 +118,24 @@ def compress_bwd(x, z, dc, ratio, span):
     return dx, dz
 
 
-def index_scores(q_i_rows, k_i, w_rows, ratio, rows):
+def index_scores(q_i_rows, k_i, w_rows, ratio, rows, doc=None):
     """Dense indexer scores of the listed rows.
 
     q_i_rows [n,HI,DI], w_rows [n,HI] hold the listed query rows; k_i is
-    [b,n_c,DI]; rows [n,2] lists (batch, t).  Returns I [n, n_c] (-inf where
-    block j is not yet valid for t)."""
+    [b,n_c,DI]; rows [n,2] lists (batch, t); doc [b,S] optional document ids.
+    Returns I [n, n_c] (-inf where block j is not valid for t)."""
     q, k, w = _f64(q_i_rows), _f64(k_i), _f64(w_rows)
     rows, rb, rt = _rows(rows, None, None)
     n, HI, DI = q.shape
     nc = k.shape[1]
     out = np.zeros((n, nc))
+    d, S = _doc(doc)
     _check(_load().csa_oracle_index_scores(nc, ratio, HI, DI, _ptr(q), _ptr(k), _ptr(w), n,
-                                           _ptr(rb), _ptr(rt), _ptr(out)), "index_scores")
+                                           _ptr(rb), _ptr(rt), S, _ptr(d), _ptr(out)), "index_scores")
     return out
 
 
-def topk(scores, ratio, k, rows):
+def topk(scores, ratio, k, rows, doc=None):
     """One full top-k per row; returns (idx int32 [n,K'], score fp64 [n,K'])."""
     s = _f64(scores)
     rows, rb, rt = _rows(rows, None, None)
@@ -134,22 +143,23 @@ def topk(scores, ratio, k, rows):
     kp = min(k, nc)
     idx = np.zeros((n, kp), dtype=np.int32)
     sc = np.zeros((n, kp))
-    _check(_load().csa_oracle_topk(nc, ratio, k, n, _ptr(rt), _ptr(s), _ptr(idx), _ptr(sc)),
-           "topk")
+    d, S = _doc(doc)
+    _check(_load().csa_oracle_topk(nc, ratio, k, n, _ptr(rb), _ptr(rt), S, _ptr(d), _ptr(s), _ptr(idx),
+                                   _ptr(sc)), "topk")
     return idx, sc
 
 
-def index_topk(q_i, k_i, w, ratio, k, rows=None):
+def index_topk(q_i, k_i, w, ratio, k, rows=None, doc=None):
     """Scores + top-k for rows of full tensors q_i [b,S,HI,DI], w [b,S,HI]."""
     q_i, w = np.asarray(q_i), np.asarray(w)
     b, S = q_i.shape[:2]
     rows, rb, rt = _rows(rows, b, S)
-    scores = index_scores(q_i[rb, rt], k_i, w[rb, rt], ratio, rows)
-    idx, sc = topk(scores, ratio, k, rows)
+    scores = index_scores(q_i[rb, rt], k_i, w[rb, rt], ratio, rows, doc)
+    idx, sc = topk(scores, ratio, k, rows, doc)
     return idx, sc, scores
 
 
-def attn_fwd(q_rows, kv, c, idx_rows, sink, scale, window, ratio, rows):
+def attn_fwd(q_rows, kv, c, idx_rows, sink, scale, window, ratio, rows, doc=None):
     """Forward for listed rows.  q_rows [n,H,D]; idx_rows [n,K'] int32 or None.
 
     Returns (O [n,H,D], LSE [n,H])."""
@@ -166,13 +176,14 @@ def attn_fwd(q_rows, kv, c, idx_rows, sink, scale, window, ratio, rows):
     snk = None if sink is None else _f64(sink)
     o = np.zeros((n, H, D))
     lse = np.zeros((n, H))
+    d, _ = _doc(doc)
     _check(_load().csa_oracle_attn_fwd(S, H, D, window, ratio, nc, kp, _ptr(q), _ptr(kv), _ptr(c),
                                        _ptr(idx_rows), _ptr(snk), float(scale), n, _ptr(rb),
-                                       _ptr(rt), _ptr(o), _ptr(lse)), "attn_fwd")
+                                       _ptr(rt), _ptr(d), _ptr(o), _ptr(lse)), "attn_fwd")
     return o, lse
 
 
-def attn_bwd(q_rows, kv, c, idx_rows, sink, scale, window, ratio, rows, do_rows):
+def attn_bwd(q_rows, kv, c, idx_rows, sink, scale, window, ratio, rows, do_rows, doc=None):
     """Backward for listed rows.  Returns (dQ [n,H,D], dKV [b,S,D], dC [b,n_c,D], dsink [H])."""
     q, kv, c, do = _f64(q_rows), _f64(kv), _f64(c), _f64(do_rows)
     rows, rb, rt = _rows(rows, None, None)
@@ -189,9 +200,10 @@ def attn_bwd(q_rows, kv, c, idx_rows, sink, scale, window, ratio, rows, do_rows)
     dkv = np.zeros((b, S, D))
     dc = np.zeros((b, nc, D))
     dsink = np.zeros((H,))
+    d, _ = _doc(doc)
     _check(_load().csa_oracle_attn_bwd(S, H, D, window, ratio, nc, kp, _ptr(q), _ptr(kv), _ptr(c),
                                        _ptr(idx_rows), _ptr(snk), float(scale), n, _ptr(rb),
-                                       _ptr(rt), _ptr(do), _ptr(dq), _ptr(dkv), _ptr(dc),
+                                       _ptr(rt), _ptr(d), _ptr(do), _ptr(dq), _ptr(dkv), _ptr(dc),
                                        _ptr(dsink)), "attn_bwd")
     return dq, dkv, dc, dsink
 

@@ -17,6 +17,10 @@ candidate lists it builds dense masked matrices.
   softmax).  Multiplicity matrices count how many slots select each key, so a
   repeated index in one row counts once per slot.
 * Backward: the matrix form of the softmax-with-sink gradient.
+* Packed documents (``doc`` [b, S]): equality masks ``doc[t] == doc[u]`` on the
+  window and ``doc[t] == doc[j*ratio]`` on the indexer's blocks (torchtitan
+  PR #4452, its description of packed documents); dense mode (no index rows)
+  uses the indexer's block rule, given index rows are taken as they are.
 """
 from __future__ import annotations
 
@@ -67,25 +71,35 @@ def compressed_valid(S: int, ratio: int) -> np.ndarray:
     return j < (t + 1) // ratio
 
 
-def index_scores(q_i, k_i, w, ratio):
+def block_valid(b, S, ratio, doc=None):
+    """V[b, t, j]: block j is valid for query t (causal, and with doc in t's document)."""
+    V = np.broadcast_to(compressed_valid(S, ratio)[None], (b, S, S // ratio))
+    if doc is None:
+        return V
+    doc = np.asarray(doc)
+    nc = S // ratio
+    return V & (doc[:, :, None] == doc[:, None, np.arange(nc) * ratio])
+
+
+def index_scores(q_i, k_i, w, ratio, doc=None):
     q_i = np.asarray(q_i, np.float64)   # [b,S,HI,DI]
     k_i = np.asarray(k_i, np.float64)   # [b,nc,DI]
     w = np.asarray(w, np.float64)       # [b,S,HI]
-    S = q_i.shape[1]
+    b, S = q_i.shape[:2]
     dots = np.einsum("bthe,bje->bthj", q_i, k_i)
     I = np.einsum("bth,bthj->btj", w, np.maximum(dots, 0.0))
-    return np.where(compressed_valid(S, ratio)[None], I, -np.inf)
+    return np.where(block_valid(b, S, ratio, doc), I, -np.inf)
 
 
-def topk(I, ratio, k):
+def topk(I, ratio, k, doc=None):
     b, S, nc = I.shape
     kp = min(k, nc)
-    V = compressed_valid(S, ratio)
+    V = block_valid(b, S, ratio, doc)
     idx = np.full((b, S, kp), -1, dtype=np.int32)
     sc = np.full((b, S, kp), -np.inf)
     for bi in range(b):
         for t in range(S):
-            js = np.nonzero(V[t])[0]
+            js = np.nonzero(V[bi, t])[0]
             order = np.lexsort((js, -I[bi, t, js]))     # primary: score desc, then index asc
             sel = np.sort(js[order[:kp]])
             idx[bi, t, :len(sel)] = sel
@@ -93,17 +107,21 @@ def topk(I, ratio, k):
     return idx, sc
 
 
-def key_multiplicity(S, nc, window, ratio, idx):
+def key_multiplicity(S, nc, window, ratio, idx, doc=None):
     """N[b, t, key] over the unified axis [S + nc]: how many candidates of
     query t point at each key (window rows once, compressed rows once per
     valid slot; idx None = every valid compressed row once)."""
     t = np.arange(S)[:, None]
     u = np.arange(S)[None, :]
-    win = ((u <= t) & (u > t - window)).astype(np.float64)          # [S, S]
+    win = ((u <= t) & (u > t - window)).astype(np.float64)[None]    # [1, S, S]
+    if doc is not None:
+        d = np.asarray(doc)
+        win = win * (d[:, :, None] == d[:, None, :])                 # [b, S, S]
     V = compressed_valid(S, ratio)
     if idx is None:
-        comp = V.astype(np.float64)[None]                            # [1, S, nc]
-        b = 1
+        bd = 1 if doc is None else np.asarray(doc).shape[0]
+        comp = block_valid(bd, S, ratio, doc).astype(np.float64)     # [bd, S, nc]
+        b = bd
     else:
         idx = np.asarray(idx)
         b = idx.shape[0]
@@ -113,17 +131,18 @@ def key_multiplicity(S, nc, window, ratio, idx):
                 for j in idx[bi, tt]:
                     if 0 <= j < nc and V[tt, j]:
                         comp[bi, tt, j] += 1.0
-    return np.concatenate([np.broadcast_to(win, (comp.shape[0], S, S)), comp], axis=2), b
+    bb = max(comp.shape[0], win.shape[0])
+    return np.concatenate([np.broadcast_to(win, (bb, S, S)), np.broadcast_to(comp, (bb, S, nc))], axis=2), b
 
 
-def attn_fwd(q, kv, c, idx, sink, scale, window, ratio):
+def attn_fwd(q, kv, c, idx, sink, scale, window, ratio, doc=None):
     """Returns (O [b,S,H,D], LSE [b,S,H], P [b,S,H,S+nc], Psink [b,S,H])."""
     q = np.asarray(q, np.float64)
     kv = np.asarray(kv, np.float64)
     c = np.asarray(c, np.float64)
     b, S, H, D = q.shape
     nc = c.shape[1]
-    N, _ = key_multiplicity(S, nc, window, ratio, idx)
+    N, _ = key_multiplicity(S, nc, window, ratio, idx, doc)
     N = np.broadcast_to(N, (b, S, S + nc))
     keys = np.concatenate([kv, c], axis=1)                           # [b, S+nc, D]
     logits = scale * np.einsum("bthd,bkd->bthk", q, keys)
@@ -141,14 +160,14 @@ def attn_fwd(q, kv, c, idx, sink, scale, window, ratio):
     return o, lse, P, psink
 
 
-def attn_bwd(q, kv, c, idx, sink, scale, window, ratio, do):
+def attn_bwd(q, kv, c, idx, sink, scale, window, ratio, do, doc=None):
     """Returns (dQ, dKV, dC, dsink)."""
     q = np.asarray(q, np.float64)
     kv = np.asarray(kv, np.float64)
     c = np.asarray(c, np.float64)
     do = np.asarray(do, np.float64)
     S = q.shape[1]
-    o, lse, P, psink = attn_fwd(q, kv, c, idx, sink, scale, window, ratio)
+    o, lse, P, psink = attn_fwd(q, kv, c, idx, sink, scale, window, ratio, doc)
     keys = np.concatenate([kv, c], axis=1)
     delta = np.einsum("bthd,bthd->bth", do, o)
     dP = np.einsum("bthd,bkd->bthk", do, keys)

@@ -29,6 +29,11 @@
  *                  Gym's CSA": the fused operator (window + selected compressed
  *                  rows + sink in one softmax, per-head LSE returned) and the
  *                  comment on its backward as a sum of two products.
+ *  [TT4452-docs]   same PR, its description of packed documents: with
+ *                  doc_ids [b, S], the window keeps only keys of the query's
+ *                  document, and indexer entry j (tokens [j*r, (j+1)*r)) belongs
+ *                  to the document of token j*r and is selectable by t iff that
+ *                  document is t's and j < (t+1)//r.
  *  [PR7152-route]  Megatron-LM PR #7152 "Add the min-memory DSA attention
  *                  kernels", commit messages on routing: one full top-k (not
  *                  chunked) is the tie rule; indices/scores ordered by position.
@@ -46,7 +51,11 @@
  *  - indexer score I[t,j] = sum_h w[t,h] * relu(q_i[t,h] . k_i[j]);
  *    top-k order is (score desc, index asc); output ascending index, then -1;
  *  - every slot of an index row is one candidate (a repeated index in one row
- *    counts once per slot); slots outside [0, n_valid(t)) are ignored.
+ *    counts once per slot); slots outside [0, n_valid(t)) are ignored;
+ *  - packed documents (doc != NULL): the window and the indexer follow
+ *    [TT4452-docs]; entries of a given index row are taken as given (the
+ *    attention leaves the selected branch to the indexer), while the dense
+ *    mode (no index rows) applies the indexer's document rule to every block.
  */
 #include <math.h>
 #include <stdint.h>
@@ -57,6 +66,13 @@
 #define ORACLE_ERR (-1)
 
 static int64_t n_valid_blocks(int64_t t, int64_t r) { return (t + 1) / r; }
+
+/* Tokens t and u of batch row bi are in the same packed document [TT4452-docs]
+ * (always, without document ids). */
+static int same_doc(const int32_t* doc, int64_t S, int64_t bi, int64_t t, int64_t u)
+{
+    return !doc || doc[bi * S + t] == doc[bi * S + u];
+}
 
 /* ------------------------------------------------------------------ a1 --- */
 /* Softmax pooling [PR6400-pool]: for block j and channel c,
@@ -135,21 +151,22 @@ int csa_oracle_compress_bwd(int64_t b, int64_t S, int64_t D, int64_t r, int64_t 
 
 /* ------------------------------------------------------------------ a2 --- */
 /* Indexer scores for a list of query rows [PR6400-mask, PR7152-route]:
- *   I[n, j] = sum_h W[n,h] * max(0, sum_e QI[n,h,e] * KI[b_n, j, e])  for j < n_valid(t_n)
+ *   I[n, j] = sum_h W[n,h] * max(0, sum_e QI[n,h,e] * KI[b_n, j, e])  for valid j
  *   I[n, j] = -inf                                                     otherwise
- * QI [nrows,HI,DI] and W [nrows,HI] hold the listed rows; KI is [b,n_c,DI].
- * I is [nrows, n_c]. */
+ * j is valid for t iff j < n_valid(t) and (with doc [b,S]) token j*r is in
+ * t's document [TT4452-docs].  QI [nrows,HI,DI] and W [nrows,HI] hold the
+ * listed rows; KI is [b,n_c,DI].  I is [nrows, n_c]. */
 int csa_oracle_index_scores(int64_t nc, int64_t r, int64_t HI, int64_t DI,
                             const double* QI, const double* KI, const double* W,
                             int64_t nrows, const int64_t* rows_b, const int64_t* rows_t,
-                            double* I)
+                            int64_t S, const int32_t* doc, double* I)
 {
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t n = 0; n < nrows; ++n) {
         int64_t nv = n_valid_blocks(rows_t[n], r);
         const double* kb = KI + rows_b[n] * nc * DI;
         for (int64_t j = 0; j < nc; ++j) {
-            if (j >= nv) { I[n * nc + j] = -INFINITY; continue; }
+            if (j >= nv || !same_doc(doc, S, rows_b[n], rows_t[n], j * r)) { I[n * nc + j] = -INFINITY; continue; }
             double s = 0.0;
             for (int64_t h = 0; h < HI; ++h) {
                 double dot = 0.0;
@@ -163,10 +180,10 @@ int csa_oracle_index_scores(int64_t nc, int64_t r, int64_t HI, int64_t DI,
 }
 
 /* ------------------------------------------------------------------ a3 --- */
-/* One full top-k per row [PR7152-route]: among valid j sort by
- * (I desc, j asc), keep the first min(K', n_valid) and emit them in ascending
- * j, then -1 padding up to K' = min(K, n_c) [PR6400-mask].  Scores are
- * aligned with the indices; padded slots carry -inf. */
+/* One full top-k per row [PR7152-route]: among valid j (as for the scores)
+ * sort by (I desc, j asc), keep the first min(K', number valid) and emit them
+ * in ascending j, then -1 padding up to K' = min(K, n_c) [PR6400-mask].
+ * Scores are aligned with the indices; padded slots carry -inf. */
 typedef struct { double s; int64_t j; } oracle_cand;
 
 static int cand_cmp(const void* a, const void* b)
@@ -184,8 +201,9 @@ static int int_cmp(const void* a, const void* b)
     return (x > y) - (x < y);
 }
 
-int csa_oracle_topk(int64_t nc, int64_t r, int64_t K, int64_t nrows, const int64_t* rows_t,
-                    const double* I, int32_t* idx, double* score)
+int csa_oracle_topk(int64_t nc, int64_t r, int64_t K, int64_t nrows, const int64_t* rows_b,
+                    const int64_t* rows_t, int64_t S, const int32_t* doc, const double* I,
+                    int32_t* idx, double* score)
 {
     int64_t kp = K < nc ? K : nc;
     int err = ORACLE_OK;
@@ -198,7 +216,12 @@ int csa_oracle_topk(int64_t nc, int64_t r, int64_t K, int64_t nrows, const int64
             if (!buf) continue;
             int64_t nv = n_valid_blocks(rows_t[n], r);
             if (nv > nc) nv = nc;
-            for (int64_t j = 0; j < nv; ++j) { buf[j].s = I[n * nc + j]; buf[j].j = j; }
+            int64_t nval = 0;
+            for (int64_t j = 0; j < nv; ++j) {
+                if (!same_doc(doc, S, rows_b[n], rows_t[n], j * r)) continue;
+                buf[nval].s = I[n * nc + j]; buf[nval].j = j; ++nval;
+            }
+            nv = nval;
             qsort(buf, (size_t)nv, sizeof(oracle_cand), cand_cmp);
             int64_t m = kp < nv ? kp : nv;
             qsort(buf, (size_t)m, sizeof(oracle_cand), int_cmp);
@@ -216,15 +239,19 @@ int csa_oracle_topk(int64_t nc, int64_t r, int64_t K, int64_t nrows, const int64
 /* Candidate rows of query (b, t) [PR6400-gather, PR6400-window, TT4452-op]:
  * the window rows KV[b, u], u in [max(0, t-W+1), t], then one compressed row
  * C[b, j] per slot whose j satisfies 0 <= j < n_valid(t) (idx == NULL: every
- * j < n_valid(t), the dense-over-compressed mode of [PR6400-core]).
+ * j < n_valid(t), the dense-over-compressed mode of [PR6400-core]).  With
+ * doc, window rows of other documents drop out, and so do dense-mode blocks
+ * whose first token is in another document [TT4452-docs].
  * Returns the number of candidates and fills ptrs with row addresses. */
 static int64_t gather_rows(int64_t bi, int64_t t, int64_t S, int64_t D, int64_t W, int64_t r,
                            int64_t nc, int64_t kp, const double* KV, const double* C,
-                           const int32_t* idx_row, const double** ptrs, int64_t* is_c, int64_t* where)
+                           const int32_t* idx_row, const int32_t* doc, const double** ptrs,
+                           int64_t* is_c, int64_t* where)
 {
     int64_t n = 0;
     int64_t u0 = t - W + 1 < 0 ? 0 : t - W + 1;
     for (int64_t u = u0; u <= t; ++u) {
+        if (!same_doc(doc, S, bi, t, u)) continue;
         ptrs[n] = KV + (bi * S + u) * D; is_c[n] = 0; where[n] = u; ++n;
     }
     int64_t nv = n_valid_blocks(t, r);
@@ -237,6 +264,7 @@ static int64_t gather_rows(int64_t bi, int64_t t, int64_t S, int64_t D, int64_t 
         }
     } else {
         for (int64_t j = 0; j < nv; ++j) {
+            if (!same_doc(doc, S, bi, t, j * r)) continue;
             ptrs[n] = C + (bi * nc + j) * D; is_c[n] = 1; where[n] = j; ++n;
         }
     }
@@ -253,7 +281,7 @@ int csa_oracle_attn_fwd(int64_t S, int64_t H, int64_t D, int64_t W, int64_t r, i
                         int64_t kp, const double* Q, const double* KV, const double* C,
                         const int32_t* idx, const double* sink, double scale,
                         int64_t nrows, const int64_t* rows_b, const int64_t* rows_t,
-                        double* O, double* LSE)
+                        const int32_t* doc, double* O, double* LSE)
 {
     int64_t maxc = W + (idx ? kp : nc);
     int err = ORACLE_OK;
@@ -268,7 +296,7 @@ int csa_oracle_attn_fwd(int64_t S, int64_t H, int64_t D, int64_t W, int64_t r, i
         for (int64_t n = 0; n < nrows; ++n) {
             if (!ptrs || !is_c || !where || !l) continue;
             int64_t nc_n = gather_rows(rows_b[n], rows_t[n], S, D, W, r, nc, kp, KV, C,
-                                       idx ? idx + n * kp : NULL, ptrs, is_c, where);
+                                       idx ? idx + n * kp : NULL, doc, ptrs, is_c, where);
             for (int64_t h = 0; h < H; ++h) {
                 const double* q = Q + (n * H + h) * D;
                 double m = sink ? sink[h] : -INFINITY;
@@ -312,7 +340,8 @@ int csa_oracle_attn_bwd(int64_t S, int64_t H, int64_t D, int64_t W, int64_t r, i
                         int64_t kp, const double* Q, const double* KV, const double* C,
                         const int32_t* idx, const double* sink, double scale,
                         int64_t nrows, const int64_t* rows_b, const int64_t* rows_t,
-                        const double* dO, double* dQ, double* dKV, double* dC, double* dsink)
+                        const int32_t* doc, const double* dO, double* dQ, double* dKV, double* dC,
+                        double* dsink)
 {
     int64_t maxc = W + (idx ? kp : nc);
     const double** ptrs = (const double**)malloc(sizeof(double*) * maxc);
@@ -327,7 +356,7 @@ int csa_oracle_attn_bwd(int64_t S, int64_t H, int64_t D, int64_t W, int64_t r, i
     for (int64_t n = 0; n < nrows; ++n) {
         int64_t bi = rows_b[n];
         int64_t nc_n = gather_rows(bi, rows_t[n], S, D, W, r, nc, kp, KV, C,
-                                   idx ? idx + n * kp : NULL, ptrs, is_c, where);
+                                   idx ? idx + n * kp : NULL, doc, ptrs, is_c, where);
         for (int64_t h = 0; h < H; ++h) {
             const double* q = Q + (n * H + h) * D;
             const double* go = dO + (n * H + h) * D;

@@ -466,3 +466,104 @@ def test_attn_rows_subset_matches_full():
                                0.4, 5, 4, rows)
     np.testing.assert_array_equal(os_, o[rows[:, 0], rows[:, 1]])
     np.testing.assert_array_equal(ls_, lse[rows[:, 0], rows[:, 1]])
+
+
+# ------------------------------------------------------------ packed documents
+def _docs(b, S, r, bounds_per_batch):
+    """doc ids [b, S] from segment start positions (multiples of the ratio)."""
+    doc = np.zeros((b, S), dtype=np.int32)
+    for bi, starts in enumerate(bounds_per_batch):
+        for k, s0 in enumerate(starts):
+            doc[bi, s0:] = k + 10 * bi
+    return doc
+
+
+def _doc_attn(q, kv, c, idx, sink, scale, W, r, doc, do=None):
+    b, S = q.shape[:2]
+    rows = oracle.all_rows(b, S)
+    qr = q.reshape(b * S, *q.shape[2:])
+    ir = None if idx is None else idx.reshape(b * S, -1)
+    o, lse = oracle.attn_fwd(qr, kv, c, ir, sink, scale, W, r, rows, doc=doc)
+    if do is None:
+        return o.reshape(q.shape), lse.reshape(b, S, -1)
+    g = oracle.attn_bwd(qr, kv, c, ir, sink, scale, W, r, rows, do.reshape(b * S, *do.shape[2:]), doc=doc)
+    return o.reshape(q.shape), lse.reshape(b, S, -1), g
+
+
+@pytest.mark.parametrize("dense", [False, True])
+def test_docs_attention_matches_dense_formulation(dense):
+    b, S, r, W = 2, 40, 4, 7
+    q, kv, c, idx, sink = _attn_case(b=b, S=S, r=r, W=W, kp=5, seed_idx=not dense)
+    doc = _docs(b, S, r, [[0, 13, 28], [0, 21]])       # starts need not be block-aligned
+    do = rnd(*q.shape)
+    o, lse, (dq, dkv, dc, ds) = _doc_attn(q, kv, c, idx, sink, 0.3, W, r, doc, do)
+    ob, lseb, _, _ = brute.attn_fwd(q, kv, c, idx, sink, 0.3, W, r, doc)
+    dqb, dkvb, dcb, dsb = brute.attn_bwd(q, kv, c, idx, sink, 0.3, W, r, do, doc)
+    for a, e in [(o, ob), (lse, lseb), (dq.reshape(q.shape), dqb), (dkv, dkvb), (dc, dcb), (ds, dsb)]:
+        np.testing.assert_allclose(a, e, rtol=1e-11, atol=1e-11)
+
+
+def test_docs_indexer_matches_dense_formulation_and_never_crosses():
+    b, S, r, HI, DI, K = 2, 48, 4, 3, 5, 6
+    q_i, k_i, w = rnd(b, S, HI, DI), rnd(b, S // r, DI), rnd(b, S, HI)
+    doc = _docs(b, S, r, [[0, 17, 36], [0, 9]])
+    idx, sc, dense = oracle.index_topk(q_i, k_i, w, r, K, doc=doc)
+    Ib = brute.index_scores(q_i, k_i, w, r, doc)
+    np.testing.assert_allclose(dense.reshape(b, S, -1), Ib, rtol=1e-12, atol=1e-12)
+    idxb, _ = brute.topk(Ib, r, K, doc)
+    np.testing.assert_array_equal(idx.reshape(b, S, -1), idxb)
+    ii = idx.reshape(b, S, -1)
+    for bi in range(b):
+        for t in range(S):
+            for j in ii[bi, t]:
+                if j >= 0:
+                    assert doc[bi, j * r] == doc[bi, t] and j < (t + 1) // r
+
+
+def test_docs_segment_equals_standalone_sequence():
+    # A document packed after another gives exactly what the method gives on
+    # that document alone (positions re-based): the document rule reduces the
+    # packed case to the already pinned single-sequence case.
+    S, r, W, H, D, s0 = 48, 4, 9, 2, 5, 20
+    q, kv, c, _, sink = _attn_case(b=1, S=S, r=r, W=W, H=H, D=D, seed_idx=False)
+    doc = _docs(1, S, r, [[0, s0]])
+    o, lse = _doc_attn(q, kv, c, None, sink, 0.5, W, r, doc)
+    o2, lse2 = _doc_attn(q[:, s0:], kv[:, s0:], c[:, s0 // r:], None, sink, 0.5, W, r, None)
+    np.testing.assert_allclose(o[:, s0:], o2, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse[:, s0:], lse2, rtol=1e-13, atol=1e-13)
+    HI, DI, K = 3, 4, 5
+    q_i, k_i, w = rnd(1, S, HI, DI), rnd(1, S // r, DI), rnd(1, S, HI)
+    idx, sc, _ = oracle.index_topk(q_i, k_i, w, r, K, doc=doc)
+    idx2, sc2, _ = oracle.index_topk(q_i[:, s0:], k_i[:, s0 // r:], w[:, s0:], r, K)
+    ii = idx.reshape(1, S, -1)[0, s0:]
+    shifted = np.where(ii >= 0, ii - s0 // r, -1)
+    np.testing.assert_array_equal(shifted, idx2.reshape(S - s0, -1))
+    np.testing.assert_allclose(sc.reshape(1, S, -1)[0, s0:], sc2.reshape(S - s0, -1), rtol=1e-13, atol=1e-13)
+
+
+def test_docs_isolation_perturbing_one_document():
+    b, S, r, W = 1, 40, 4, 6
+    q, kv, c, idx, sink = _attn_case(b=b, S=S, r=r, W=W, seed_idx=False)
+    doc = _docs(b, S, r, [[0, 16]])
+    do = rnd(*q.shape)
+    o, lse, (dq, dkv, dc, _) = _doc_attn(q, kv, c, None, sink, 0.3, W, r, doc, do)
+    kv2, c2, q2 = kv.copy(), c.copy(), q.copy()
+    kv2[:, :16] += rnd(1, 16, kv.shape[2])
+    c2[:, :4] += rnd(1, 4, c.shape[2])
+    q2[:, :16] += rnd(1, 16, *q.shape[2:])
+    o2, lse2, (dq2, dkv2, dc2, _) = _doc_attn(q2, kv2, c2, None, sink, 0.3, W, r, doc, do)
+    np.testing.assert_array_equal(o[:, 16:], o2[:, 16:])
+    np.testing.assert_array_equal(lse[:, 16:], lse2[:, 16:])
+    np.testing.assert_array_equal(dq.reshape(q.shape)[:, 16:], dq2.reshape(q.shape)[:, 16:])
+    np.testing.assert_array_equal(dkv[:, 16:], dkv2[:, 16:])
+    np.testing.assert_array_equal(dc[:, 4:], dc2[:, 4:])
+
+
+def test_docs_single_document_is_the_plain_method():
+    q, kv, c, idx, sink = _attn_case()
+    b, S = q.shape[:2]
+    doc = np.full((b, S), 7, dtype=np.int32)
+    o, lse = _doc_attn(q, kv, c, idx, sink, 0.4, 5, 4, doc)
+    o2, lse2 = _fwd(q, kv, c, idx, sink, 0.4, 5, 4)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)

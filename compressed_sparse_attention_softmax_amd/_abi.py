@@ -62,11 +62,11 @@ def load(path: Optional[str] = None):
     lib.csa_compress_bwd.argtypes = [D, i, vp, vp, i, vp, vp, vp, vp]
     lib.csa_index_topk_workspace.argtypes = [D]
     lib.csa_index_topk_workspace.restype = sz
-    lib.csa_index_topk.argtypes = [D, i, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.csa_sparse_attn_fwd.argtypes = [D, i, vp, vp, vp, vp, vp, f, vp, vp, vp]
+    lib.csa_index_topk.argtypes = [D, i, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.csa_sparse_attn_fwd.argtypes = [D, i, vp, vp, vp, vp, vp, vp, f, vp, vp, vp]
     lib.csa_sparse_attn_bwd_workspace.argtypes = [D]
     lib.csa_sparse_attn_bwd_workspace.restype = sz
-    lib.csa_sparse_attn_bwd.argtypes = [D, i, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.csa_sparse_attn_bwd.argtypes = [D, i, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.csa_last_error.argtypes = []
     lib.csa_last_error.restype = ctypes.c_char_p
     lib.csa_version.argtypes = []
@@ -163,7 +163,11 @@ def csa_index_topk_workspace(dims: csa_dims) -> int:
     return int(load().csa_index_topk_workspace(ctypes.byref(dims)))
 
 
-def csa_index_topk(dims: csa_dims, q_i, k_i, w, idx, score=None, ws=None, stream=None) -> None:
+def _doc_ptr(dims, doc_ids):
+    return _ptr(doc_ids, shape=(dims.b, dims.sq), dtype=torch.int32, name="doc_ids")
+
+
+def csa_index_topk(dims: csa_dims, q_i, k_i, w, idx, score=None, ws=None, stream=None, doc_ids=None) -> None:
     dt = q_i.dtype
     b, S = dims.b, dims.sq
     nc, kp = n_compressed(dims), kprime(dims)
@@ -171,13 +175,13 @@ def csa_index_topk(dims: csa_dims, q_i, k_i, w, idx, score=None, ws=None, stream
     _call("csa_index_topk", ctypes.byref(dims), _dtype_code(q_i),
           _ptr(q_i, shape=(b, S, dims.idx_heads, dims.idx_dim), dtype=dt, name="q_i"),
           _ptr(k_i, shape=(b, nc, dims.idx_dim), dtype=dt, name="k_i"),
-          _ptr(w, shape=(b, S, dims.idx_heads), dtype=f32, name="w"),
+          _ptr(w, shape=(b, S, dims.idx_heads), dtype=f32, name="w"), _doc_ptr(dims, doc_ids),
           _ptr(idx, shape=(b, S, kp), dtype=torch.int32, name="idx"),
           _ptr(score, shape=(b, S, kp), dtype=f32, name="score"),
           _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
 
 
-def _attn_ptrs(dims, q, kv, c, idx, sink):
+def _attn_ptrs(dims, q, kv, c, idx, sink, doc_ids):
     dt = q.dtype
     b, S, H, D = dims.b, dims.sq, dims.h, dims.d
     nc = n_compressed(dims) if c is not None else 0
@@ -185,13 +189,15 @@ def _attn_ptrs(dims, q, kv, c, idx, sink):
         raise CSAError("csa_sparse_attn", -2, f"sink has {sink.numel()} entries, h = {H}")
     return (_ptr(q, shape=(b, S, H, D), dtype=dt, name="q"), _ptr(kv, shape=(b, S, D), dtype=dt, name="kv"),
             _ptr(c, shape=(b, nc, D), dtype=dt, name="c"),
-            _ptr(idx, shape=(b, S, kprime(dims)), dtype=torch.int32, name="idx"),
+            _ptr(idx, shape=(b, S, kprime(dims)), dtype=torch.int32, name="idx"), _doc_ptr(dims, doc_ids),
             _ptr(sink, shape=(H,), dtype=torch.float32, name="sink"))
 
 
-def csa_sparse_attn_fwd(dims: csa_dims, q, kv, c, idx, sink, scale: float, out, lse, stream=None) -> None:
+def csa_sparse_attn_fwd(dims: csa_dims, q, kv, c, idx, sink, scale: float, out, lse, stream=None,
+                        doc_ids=None) -> None:
     b, S, H, D = dims.b, dims.sq, dims.h, dims.d
-    _call("csa_sparse_attn_fwd", ctypes.byref(dims), _dtype_code(q), *_attn_ptrs(dims, q, kv, c, idx, sink),
+    _call("csa_sparse_attn_fwd", ctypes.byref(dims), _dtype_code(q),
+          *_attn_ptrs(dims, q, kv, c, idx, sink, doc_ids),
           ctypes.c_float(scale), _ptr(out, shape=(b, S, H, D), dtype=q.dtype, name="out"),
           _ptr(lse, shape=(b, S, H), dtype=torch.float32, name="lse"), _stream(stream))
 
@@ -201,11 +207,12 @@ def csa_sparse_attn_bwd_workspace(dims: csa_dims) -> int:
 
 
 def csa_sparse_attn_bwd(dims: csa_dims, q, kv, c, idx, sink, scale: float, out, lse, dout, dq, dkv, dc,
-                        dsink=None, ws=None, stream=None) -> None:
+                        dsink=None, ws=None, stream=None, doc_ids=None) -> None:
     b, S, H, D = dims.b, dims.sq, dims.h, dims.d
     f32 = torch.float32
     nc = n_compressed(dims) if c is not None else 0
-    _call("csa_sparse_attn_bwd", ctypes.byref(dims), _dtype_code(q), *_attn_ptrs(dims, q, kv, c, idx, sink),
+    _call("csa_sparse_attn_bwd", ctypes.byref(dims), _dtype_code(q),
+          *_attn_ptrs(dims, q, kv, c, idx, sink, doc_ids),
           ctypes.c_float(scale), _ptr(out, shape=(b, S, H, D), dtype=q.dtype, name="out"),
           _ptr(lse, shape=(b, S, H), dtype=f32, name="lse"),
           _ptr(dout, shape=(b, S, H, D), dtype=q.dtype, name="dout"),

@@ -94,10 +94,11 @@ int check_attn(const csa_dims* dm, int dtype, const void* q, const void* kv, con
 }
 
 csa::AttnArgs attn_args(const csa_dims* dm, const void* q, const void* kv, const void* c,
-                        const int32_t* idx, const float* sink, float scale)
+                        const int32_t* idx, const int32_t* doc_ids, const float* sink, float scale)
 {
     csa::AttnArgs a{};
     a.q = q; a.kv = kv; a.c = c; a.idx = c ? idx : nullptr; a.sink = sink; a.scale = scale;
+    a.doc = doc_ids;
     a.b = dm->b; a.S = dm->sq; a.H = dm->h; a.D = dm->d; a.W = dm->window;
     a.r = c ? dm->ratio : 1;
     a.nc = c ? dm->sq / dm->ratio : 0;
@@ -146,7 +147,8 @@ size_t csa_index_topk_workspace(const csa_dims* dm)
 }
 
 int csa_index_topk(const csa_dims* dm, int dtype, const void* q_i, const void* k_i, const float* w,
-                   int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream)
+                   const int32_t* doc_ids, int32_t* idx, float* score, void* ws, size_t ws_bytes,
+                   void* stream)
 {
     (void)ws; (void)ws_bytes;
     int rc = check_common(dm, dtype, "csa_index_topk");
@@ -161,7 +163,7 @@ int csa_index_topk(const csa_dims* dm, int dtype, const void* q_i, const void* k
     const int kp = kprime(dm);
     if (kp > 2048) return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: K'=%d > 2048", kp);
     csa::IndexArgs a{};
-    a.qi = q_i; a.ki = k_i; a.w = w; a.idx = idx; a.score = score;
+    a.qi = q_i; a.ki = k_i; a.w = w; a.doc = doc_ids; a.idx = idx; a.score = score;
     a.b = dm->b; a.S = dm->sq; a.HI = dm->idx_heads; a.DI = dm->idx_dim; a.r = dm->ratio;
     a.nc = dm->sq / dm->ratio; a.kp = kp;
     if (kp > 0 && csa::index_topk_cap(a, dtype == CSA_BF16) == 0)
@@ -170,14 +172,14 @@ int csa_index_topk(const csa_dims* dm, int dtype, const void* q_i, const void* k
 }
 
 int csa_sparse_attn_fwd(const csa_dims* dm, int dtype, const void* q, const void* kv, const void* c,
-                        const int32_t* idx, const float* sink, float scale, void* out, float* lse,
-                        void* stream)
+                        const int32_t* idx, const int32_t* doc_ids, const float* sink, float scale,
+                        void* out, float* lse, void* stream)
 {
     int rc = check_common(dm, dtype, "csa_sparse_attn_fwd");
     if (rc) return rc;
     if ((rc = check_attn(dm, dtype, q, kv, c, idx, scale, "csa_sparse_attn_fwd"))) return rc;
     if (!out || !lse) return fail(CSA_ERR_ARG, "csa_sparse_attn_fwd: out and lse must be non-NULL");
-    csa::AttnArgs a = attn_args(dm, q, kv, c, idx, sink, scale);
+    csa::AttnArgs a = attn_args(dm, q, kv, c, idx, doc_ids, sink, scale);
     a.out = out; a.lse = lse;
     return hip_status(csa::attn_fwd(a, dtype == CSA_BF16, (hipStream_t)stream), "csa_sparse_attn_fwd");
 }
@@ -199,7 +201,7 @@ size_t csa_sparse_attn_bwd_workspace(const csa_dims* dm)
 }
 
 int csa_sparse_attn_bwd(const csa_dims* dm, int dtype, const void* q, const void* kv, const void* c,
-                        const int32_t* idx, const float* sink, float scale, const void* out,
+                        const int32_t* idx, const int32_t* doc_ids, const float* sink, float scale, const void* out,
                         const float* lse, const void* dout, void* dq, float* dkv, float* dc,
                         float* dsink, void* ws, size_t ws_bytes, void* stream)
 {
@@ -218,7 +220,7 @@ int csa_sparse_attn_bwd(const csa_dims* dm, int dtype, const void* q, const void
     }
     if (dsink && !sink) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: dsink given without sink");
     if (!any && !dsink) return ok();
-    csa::AttnArgs a = attn_args(dm, q, kv, c, idx, sink, scale);
+    csa::AttnArgs a = attn_args(dm, q, kv, c, idx, doc_ids, sink, scale);
     a.out = const_cast<void*>(out); a.lse = const_cast<float*>(lse); a.dout = dout;
     a.dq = dq; a.dkv = dkv; a.dc = dc; a.dsink = dsink;
     const size_t need = csa::attn_bwd_workspace_bytes(a);

@@ -45,6 +45,7 @@ template <typename T> constexpr int row_pad() { return 16 / (int)sizeof(T); }
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
 // (i % 4) of the 8-byte words addressed by lanes 4k + i/4, k = 0..3.
@@ -106,6 +107,7 @@ struct Cand {
     const T* kv;          // batch base of kv
     const T* c;           // batch base of c (nullptr: window only)
     const int32_t* irow;  // index row of the query (nullptr: dense mode)
+    const uint32_t* okb;  // packed documents: LDS bit per window / dense slot, 1 = same document
     int t, D, u0, nwin, nv, nslots;
 
     __device__ __forceinline__ void init(const AttnArgs& p, int bi, int tq)
@@ -115,6 +117,7 @@ struct Cand {
         kv = (const T*)p.kv + (int64_t)bi * p.S * p.D;
         c = p.c ? (const T*)p.c + (int64_t)bi * p.nc * p.D : nullptr;
         irow = (p.c && p.idx) ? p.idx + ((int64_t)bi * p.S + tq) * p.kp : nullptr;
+        okb = nullptr;
         nwin = min(p.W, tq + 1);
         u0 = tq - nwin + 1;
         nv = p.c ? min((tq + 1) / p.r, p.nc) : 0;
@@ -122,15 +125,22 @@ struct Cand {
         nslots = nwin + ncs;
     }
     // Row code of a slot: u (window row), j | 0x40000000 (compressed row),
-    // or -1 (invalid: padding, out of range or not yet valid).  With
-    // `use_ids` the index row is read from its copy `ids` in LDS.
+    // or -1 (invalid: padding, out of range, not yet valid, or another
+    // document).  With `use_ids` the index row is read from its copy `ids` in
+    // LDS.  Entries of a given index row get no document test (the indexer
+    // already applied it); window slots and dense-mode slots do.
+    __device__ __forceinline__ bool ok_bit(int slot) const
+    {
+        return !okb || ((((const lds_u32*)okb)[slot >> 5] >> (slot & 31)) & 1u);
+    }
     __device__ __forceinline__ int code(int slot, bool use_ids, const int32_t* ids) const
     {
-        if (slot < nwin) return u0 + slot;
+        if (slot < nwin) return ok_bit(slot) ? u0 + slot : -1;
         if (slot >= nslots) return -1;
         const int s2 = slot - nwin;
         const int j = use_ids ? ((const lds_i32*)ids)[s2] : (irow ? irow[s2] : s2);
-        return (j < 0 || j >= nv) ? -1 : (j | 0x40000000);
+        const bool ok = j >= 0 && j < nv && (irow || ok_bit(slot));
+        return ok ? (j | 0x40000000) : -1;
     }
     __device__ __forceinline__ const T* row_ptr(int code) const
     {
@@ -158,7 +168,7 @@ template <typename T, int D> constexpr int chunk_bytes() { return CHUNK * D * (i
 
 template <typename T, int D, int HT, int G, bool DQ>
 __global__ __launch_bounds__(256, (D <= 128 && HT <= 2) ? 2 : 1)
-void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict__ csink, int idx_lds)
+void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict__ csink, int idx_lds, int okw)
 {
     constexpr int KS = D / 32, DT = D / 16, QPW = 4 / G;
     constexpr int CHB = chunk_bytes<T, D>();
@@ -201,6 +211,29 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
             const int s0 = qlane + k * WAVE * G;
             iv[k] = s0 < p.kp ? cand.irow[s0] : -1;
         }
+    }
+
+    // Packed documents: one LDS bit per window slot and (dense mode) per
+    // compressed slot, set when the row's document is the query's (okw words
+    // per query slot of the workgroup, after the index rows).
+    if (okw > 0) {
+        uint32_t* okq = reinterpret_cast<uint32_t*>(smem + (size_t)QPW * 2 * CHB +
+                                                    (idx_lds ? (size_t)QPW * p.kp * sizeof(int32_t) : 0)) +
+                        (size_t)qs * okw;
+        const int32_t* dcol = p.doc + (int64_t)bi * p.S;
+        const int dt = dcol[cand.t];
+        const int nbits = cand.nwin + (cand.irow || !p.c ? 0 : cand.nv);
+        for (int s0 = sub * WAVE; s0 < nbits; s0 += WAVE * G) {
+            const int sl = s0 + lane;
+            bool ok = false;
+            if (sl < nbits) ok = dcol[sl < cand.nwin ? cand.u0 + sl : (sl - cand.nwin) * p.r] == dt;
+            const uint64_t m = __ballot(ok);
+            if (lane == 0) {
+                okq[s0 >> 5] = (uint32_t)m;
+                okq[(s0 >> 5) + 1] = (uint32_t)(m >> 32);
+            }
+        }
+        cand.okb = okq;
     }
 
     Frag<T> qb[HT][KS];
@@ -576,12 +609,14 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
     T* rtile = reinterpret_cast<T*>(reinterpret_cast<char*>(cnt_lds) + 3 * TR * 4) + (size_t)wave * RW * RROW;
     Frag<T> rb[ROWS_LDS ? 1 : RT][KS];
     int rkey[RT];
+    [[maybe_unused]] int rdoc[RT];               // packed documents: document of each window row
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int i = i0 + RW * wave + 16 * rt + n16;
         const int key = base_row + i;
         const bool ok = i < nrows_valid && key >= 0 && key < rmax;
         rkey[rt] = ok ? key : -1;
+        rdoc[rt] = (p.doc && win && ok) ? p.doc[(int64_t)bi * p.S + key] : 0;
         const T* src = rows + (int64_t)(ok ? key : 0) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -645,7 +680,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
             } else {
                 unsigned* cnt = cnt_lds + cb * TR;
                 const int nv = min((t + 1) / p.r, p.nc);
-                for (int j = tile_lo + threadIdx.x; j < min(tile_hi, nv); j += NT) cnt[j - tile_lo] = 1u;
+                // dense mode: every valid block once (with documents: blocks of t's document)
+                const int32_t* dcol = p.doc ? p.doc + (int64_t)bi * p.S : nullptr;
+                const int dt = dcol ? dcol[t] : 0;
+                for (int j = tile_lo + threadIdx.x; j < min(tile_hi, nv); j += NT)
+                    if (!dcol || dcol[j * p.r] == dt) cnt[j - tile_lo] = 1u;
             }
         }
     };
@@ -701,6 +740,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
         const float* ls_b = lse_lds + buf * HP;
         const float* dl_b = dlt_lds + buf * HP;
         if constexpr (COMPUTE) {
+        [[maybe_unused]] const int dtq = (p.doc && win) ? p.doc[(int64_t)bi * p.S + t] : 0;
         // every (head, row) pair is computed; rows that are not candidates of t
         // get multiplicity 0 (no branch, so the accumulators stay put).  The
         // multiplicity enters the exponent: m P = 2^(scale log2e S' + log2 m).
@@ -710,7 +750,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
             const int key = rkey[rt];
             float m = 0.f;
             if (key >= 0) {
-                if (win) m = (key <= t && key > t - p.W) ? 1.f : 0.f;
+                if (win) m = (key <= t && key > t - p.W && (!p.doc || rdoc[rt] == dtq)) ? 1.f : 0.f;
                 else m = (float)cnt_lds[cb * TR + key - tile_lo];
             }
             lm[rt] = m > 0.f ? __log2f(m) : -INFINITY;
@@ -911,12 +951,20 @@ hipError_t launch_query(const AttnArgs& p, bool dq, float* delta, float* csink, 
     const size_t with_ids = lds + (size_t)qpw * p.kp * sizeof(int32_t);
     const int idx_lds = (p.idx && p.kp > 0 && with_ids <= (size_t)ATTN_LDS_LIMIT) ? 1 : 0;
     if (idx_lds) lds = with_ids;
+    // document bits: window slots, plus every block in dense mode
+    int okw = 0;
+    if (p.doc) {
+        const int nbits = min(p.W, p.S) + (p.c && !p.idx ? p.nc : 0);
+        okw = (nbits + 63) / 64 * 2;
+        lds += (size_t)qpw * okw * sizeof(uint32_t);
+        if (lds > (size_t)ATTN_LDS_LIMIT) return hipErrorInvalidValue;
+    }
     auto go = [&](auto kern, int qpw_) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         dim3 grid((p.S + qpw_ - 1) / qpw_, p.b);
         TimedLaunch tl(dq ? K_ATTN_DQ : K_ATTN_FWD, st);
-        hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p, delta, csink, idx_lds);
+        hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p, delta, csink, idx_lds, okw);
         return hipGetLastError();
     };
     if (dq) {

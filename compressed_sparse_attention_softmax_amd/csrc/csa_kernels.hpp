@@ -25,6 +25,7 @@ struct IndexArgs {
     const void* qi;
     const void* ki;
     const float* w;
+    const int32_t* doc;   // [b, S] document ids, or nullptr (one document)
     int32_t* idx;
     float* score;
     int b, S, HI, DI, r, nc, kp;
@@ -36,6 +37,7 @@ struct AttnArgs {
     const void* c;        // nullptr: window only
     const int32_t* idx;   // nullptr: every valid compressed row
     const float* sink;    // nullptr: no sink
+    const int32_t* doc;   // [b, S] document ids, or nullptr (one document)
     float scale;
     void* out;
     float* lse;

@@ -199,6 +199,7 @@ template <typename T, int DI, int HT>
 __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict__ qi,
                                                             const T* __restrict__ ki,
                                                             const float* __restrict__ w,
+                                                            const int32_t* __restrict__ doc,
                                                             int32_t* __restrict__ idx,
                                                             float* __restrict__ score, int S,
                                                             int HI, int r, int nc, int kp, int cap)
@@ -255,7 +256,12 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
     static_assert(CPT * 256 == CHUNKS, "a key tile splits evenly over the workgroup");
     // the next key tile is loaded into registers while the current one computes
     uint4 pre[CPT];
+    // packed documents: block j belongs to the document of token j*r
+    const int32_t* dcol = doc ? doc + (int64_t)bi * S : nullptr;
+    const int dt = (dcol && active) ? dcol[t] : 0;
+    int dpre = 0, dcur = 0;
     auto load_tile = [&](int j0) {
+        if (dcol) dpre = j0 + lane < nc ? dcol[(j0 + lane) * r] : 0;
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             const int c = (int)threadIdx.x + 256 * k;
@@ -273,6 +279,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
             const int rr = c / (DI / CH), cc = (c % (DI / CH)) * CH;
             *reinterpret_cast<uint4*>(ktile + rr * ROW + cc) = pre[k];
         }
+        dcur = dpre;
         if (j0 + KT < nv_max) load_tile(j0 + KT);
         __syncthreads();
         if (j0 >= nv) continue;
@@ -299,7 +306,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
         }
         my = my + 0.0f;                        // -0 -> +0: one value per tie class
         const int j = j0 + lane;
-        const bool valid = j < nv;
+        const bool valid = j < nv && (!dcol || dcur == dt);
         const int ntile = min(KT, nv - j0);
         if (cnt + ntile > cap) {
             tau = select_keep(bufs, cnt, kp);
@@ -344,7 +351,7 @@ hipError_t launch_index(const IndexArgs& p, hipStream_t st)
     if (e != hipSuccess) return e;
     dim3 grid((p.S + 3) / 4, p.b);
     TimedLaunch tl(K_INDEX_TOPK, st);
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const T*)p.qi, (const T*)p.ki, p.w, p.idx,
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const T*)p.qi, (const T*)p.ki, p.w, p.doc, p.idx,
                        p.score, p.S, p.HI, p.r, p.nc, kp, cap);
     return hipGetLastError();
 }

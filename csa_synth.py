@@ -176,3 +176,23 @@ def random_topk_indices(wl: Workload, seed: int, device="cpu", repeat_frac: floa
             sel = torch.topk(keys[bi, t, :nv], m).indices.sort().values
             idx[bi, t, :m] = sel.to(torch.int32)
     return idx.to(device)
+
+
+def packed_doc_ids(b: int, sq: int, mean_len: float, seed: int, device="cpu") -> torch.Tensor:
+    """Document ids ``[b,sq]`` int32 for sequences packed from several documents.
+
+    Document lengths are drawn from an exponential length mix with the given
+    mean (at least one token each), so segment starts fall anywhere, not only
+    on compression-block boundaries.  Ids increase along a row and differ
+    between batch rows.  Only random draws happen here.
+    """
+    g = _gen(seed, 60, "cpu")
+    doc = torch.empty(b, sq, dtype=torch.int32)
+    for bi in range(b):
+        pos, k = 0, 0
+        while pos < sq:
+            n = max(1, int(torch.empty(1).exponential_(1.0 / mean_len, generator=g).item()))
+            doc[bi, pos:pos + n] = 1000 * bi + k
+            pos += n
+            k += 1
+    return doc.to(device)

@@ -46,6 +46,13 @@
  *    j < n_valid(t) = (t+1) / ratio.  Block j covers tokens [j*ratio,
  *    (j+1)*ratio); its pooling span is [(j+1)*ratio - span, (j+1)*ratio)
  *    clipped at 0.
+ *  - Packed documents (torchtitan PR #4452, its description of packed
+ *    documents).  doc_ids [b, sq] int32 (nullable: one document per batch
+ *    row) gives each token's document.  Window row u is a candidate of t only
+ *    if doc_ids[u] == doc_ids[t]; block j (tokens [j*ratio, (j+1)*ratio))
+ *    belongs to the document of token j*ratio and is selectable by the
+ *    indexer, and attended in dense mode, only if that is t's document.
+ *    Entries of a given index row are attended as they are.
  *  - Errors.  Every entry point validates its arguments before enqueuing any
  *    work and returns CSA_OK or a negative code; csa_last_error() then returns
  *    a message for the calling thread.  Nothing throws or aborts across the ABI.
@@ -64,7 +71,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 };
 
@@ -115,6 +122,7 @@ size_t csa_index_topk_workspace(const csa_dims* dims);
 /* Learned indexer + streaming top-k (Megatron-LM PR #6400, causal-mask thread;
  * Megatron-LM PR #7152, routing commit messages).
  *   I[t, j] = sum_h w[t, h] * relu(q_i[t, h] . k_i[j])   for j < n_valid(t)
+ *   (and, with doc_ids, j in t's document: see CONVENTIONS)
  * Scores are computed tile by tile on the chip and reduced into a running
  * top-k; the [sq, n_c] score matrix is never written anywhere.  Row (b, t) of
  * idx receives the K' = min(topk, n_c) largest valid scores ordered by
@@ -124,8 +132,8 @@ size_t csa_index_topk_workspace(const csa_dims* dims);
  * holds any softmax scale of the indexer.  ws may be NULL when
  * csa_index_topk_workspace() returns 0. */
 int csa_index_topk(const csa_dims* dims, int dtype, const void* q_i, const void* k_i,
-                   const float* w, int32_t* idx, float* score, void* ws, size_t ws_bytes,
-                   void* stream);
+                   const float* w, const int32_t* doc_ids, int32_t* idx, float* score, void* ws,
+                   size_t ws_bytes, void* stream);
 
 /* Sparse attention forward (Megatron-LM PR #6400 gather and sink threads;
  * torchtitan PR #4452 fused operator).  For query (b, t) and head h the
@@ -138,7 +146,8 @@ int csa_index_topk(const csa_dims* dims, int dtype, const void* q_i, const void*
  *   out[t, h] = sum exp(l - lse) * row     (the row is both key and value)
  * out has dtype, lse is fp32. */
 int csa_sparse_attn_fwd(const csa_dims* dims, int dtype, const void* q, const void* kv,
-                        const void* c, const int32_t* idx, const float* sink, float scale,
+                        const void* c, const int32_t* idx, const int32_t* doc_ids,
+                        const float* sink, float scale,
                         void* out, float* lse, void* stream);
 
 /* Workspace bytes csa_sparse_attn_bwd needs (device memory, 16-byte aligned,
@@ -162,7 +171,8 @@ size_t csa_sparse_attn_bwd_workspace(const csa_dims* dims);
  * ws / ws_bytes: the workspace (CSA_ERR_WORKSPACE if NULL or smaller than
  * csa_sparse_attn_bwd_workspace(dims)). */
 int csa_sparse_attn_bwd(const csa_dims* dims, int dtype, const void* q, const void* kv,
-                        const void* c, const int32_t* idx, const float* sink, float scale,
+                        const void* c, const int32_t* idx, const int32_t* doc_ids,
+                        const float* sink, float scale,
                         const void* out, const float* lse, const void* dout, void* dq,
                         float* dkv, float* dc, float* dsink, void* ws, size_t ws_bytes,
                         void* stream);

@@ -52,8 +52,12 @@ def n_valid(t, ratio, nc):
     return np.minimum((np.asarray(t) + 1) // ratio, nc)
 
 
-def check_topk_rows(gpu_idx, gpu_score, ora_idx, ora_dense, rows_t, ratio, nc, kp, score_tol):
-    """gpu_idx/gpu_score/ora_idx: [n, K']; ora_dense: [n, n_c] oracle scores."""
+def check_topk_rows(gpu_idx, gpu_score, ora_idx, ora_dense, rows_t, ratio, nc, kp, score_tol, docs=False):
+    """gpu_idx/gpu_score/ora_idx: [n, K']; ora_dense: [n, n_c] oracle scores.
+
+    Without documents the selectable blocks of row t are 0..n_valid(t)-1; with
+    ``docs`` they are the blocks the oracle scored (finite entries of its row),
+    which is how the oracle marks the blocks of the query's own document."""
     gpu_idx = np.asarray(gpu_idx)
     ora_idx = np.asarray(ora_idx)
     exact_rows = 0
@@ -61,23 +65,26 @@ def check_topk_rows(gpu_idx, gpu_score, ora_idx, ora_dense, rows_t, ratio, nc, k
     smax = np.abs(ora_dense[np.isfinite(ora_dense)]).max() if np.isfinite(ora_dense).any() else 1.0
     for n, t in enumerate(rows_t):
         nv = int(n_valid(t, ratio, nc))
-        m = min(kp, nv)
+        valid = np.nonzero(np.isfinite(ora_dense[n]))[0] if docs else np.arange(nv)
+        if not docs:
+            assert np.array_equal(valid, np.nonzero(np.isfinite(ora_dense[n]))[0])
+        m = min(kp, len(valid))
         g, o = gpu_idx[n], ora_idx[n]
         assert np.all(g[m:] == -1), f"row t={t}: expected {kp - m} trailing -1, got {g}"
         gs = g[:m]
-        assert np.all(gs >= 0) and np.all(gs < nv), f"row t={t}: index out of [0,{nv})"
+        assert np.all(np.isin(gs, valid)), f"row t={t}: index outside the selectable blocks"
         assert np.all(np.diff(gs) > 0), f"row t={t}: not strictly ascending"
         if gpu_score is not None:
             sc = np.asarray(gpu_score[n])
             assert np.all(np.isneginf(sc[m:]))
             err = np.abs(sc[:m] - ora_dense[n, gs]).max() if m else 0.0
             assert err <= score_tol * smax, f"row t={t}: score error {err} > {score_tol * smax}"
-        if nv <= kp:
-            np.testing.assert_array_equal(gs, np.arange(nv))
+        if len(valid) <= kp:
+            np.testing.assert_array_equal(gs, valid)
             exact_rows += 1
             continue
         sstar = np.min(ora_dense[n, o[:m]])          # the oracle's K'-th score
-        band = set(np.nonzero(np.abs(ora_dense[n, :nv] - sstar) < BAND)[0].tolist())
+        band = set(valid[np.abs(ora_dense[n, valid] - sstar) < BAND].tolist())
         gset = set(gs.tolist()) - band
         oset = set(o[:m].tolist()) - band
         if gset != oset:

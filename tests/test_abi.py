@@ -33,7 +33,7 @@ def test_library_exports_every_header_symbol():
     lib = _lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.csa_version() == 1
+    assert lib.csa_version() == 2
 
 
 def test_dims_struct_matches_header():
@@ -62,17 +62,17 @@ N = None
     ("csa_compress", lambda: (ctypes.byref(_d()), 0, P, P, 5, P, N, N), -2),
     ("csa_compress", lambda: (ctypes.byref(_d()), 0, N, P, 64, P, N, N), -1),
     ("csa_compress_bwd", lambda: (ctypes.byref(_d(sq=0)), 0, P, P, 64, P, P, P, N), -1),
-    ("csa_index_topk", lambda: (ctypes.byref(_d(topk=0)), 0, P, P, P, P, N, N, 0, N), -1),
-    ("csa_index_topk", lambda: (ctypes.byref(_d(idx_dim=48)), 0, P, P, P, P, N, N, 0, N), -4),
-    ("csa_index_topk", lambda: (ctypes.byref(_d(idx_heads=65)), 0, P, P, P, P, N, N, 0, N), -4),
-    ("csa_index_topk", lambda: (ctypes.byref(_d(sq=65536, topk=4096)), 1, P, P, P, P, N, N, 0, N), -4),
-    ("csa_index_topk", lambda: (ctypes.byref(_d()), 0, P, P, N, P, N, N, 0, N), -1),
-    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d(h=65)), 0, P, P, P, P, N, ctypes.c_float(1.0), P, P, N), -4),
-    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d(window=0)), 0, P, P, P, P, N, ctypes.c_float(1.0), P, P, N), -1),
-    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d()), 0, P, P, N, P, N, ctypes.c_float(1.0), P, P, N), -1),
-    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d()), 0, P, P, P, P, N, ctypes.c_float(float("nan")), P, P, N), -1),
-    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d(d=512)), 0, P, P, P, P, N, ctypes.c_float(1.0), P, P, N), -4),
-    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d()), 0, P, P, P, P, N, ctypes.c_float(1.0), N, P, N), -1),
+    ("csa_index_topk", lambda: (ctypes.byref(_d(topk=0)), 0, P, P, P, N, P, N, N, 0, N), -1),
+    ("csa_index_topk", lambda: (ctypes.byref(_d(idx_dim=48)), 0, P, P, P, N, P, N, N, 0, N), -4),
+    ("csa_index_topk", lambda: (ctypes.byref(_d(idx_heads=65)), 0, P, P, P, N, P, N, N, 0, N), -4),
+    ("csa_index_topk", lambda: (ctypes.byref(_d(sq=65536, topk=4096)), 1, P, P, P, N, P, N, N, 0, N), -4),
+    ("csa_index_topk", lambda: (ctypes.byref(_d()), 0, P, P, N, N, P, N, N, 0, N), -1),
+    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d(h=65)), 0, P, P, P, P, N, N, ctypes.c_float(1.0), P, P, N), -4),
+    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d(window=0)), 0, P, P, P, P, N, N, ctypes.c_float(1.0), P, P, N), -1),
+    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d()), 0, P, P, N, P, N, N, ctypes.c_float(1.0), P, P, N), -1),
+    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d()), 0, P, P, P, P, N, N, ctypes.c_float(float("nan")), P, P, N), -1),
+    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d(d=512)), 0, P, P, P, P, N, N, ctypes.c_float(1.0), P, P, N), -4),
+    ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d()), 0, P, P, P, P, N, N, ctypes.c_float(1.0), N, P, N), -1),
 ])
 def test_validation_errors(fn, args, code):
     lib = _lib()
@@ -83,7 +83,7 @@ def test_validation_errors(fn, args, code):
 
 def _bwd(dq, dkv, dc, dsink, sink=P, c=P):
     lib = _lib()
-    return lib.csa_sparse_attn_bwd(ctypes.byref(_d()), 0, P, P, c, P, sink, ctypes.c_float(1.0), P, P, P,
+    return lib.csa_sparse_attn_bwd(ctypes.byref(_d()), 0, P, P, c, P, N, sink, ctypes.c_float(1.0), P, P, P,
                                    dq, dkv, dc, dsink, N, 0, N)
 
 
@@ -122,10 +122,10 @@ def test_workspace_too_small_is_rejected():
     lib = _lib()
     d = _d()
     need = lib.csa_sparse_attn_bwd_workspace(ctypes.byref(d))
-    rc = lib.csa_sparse_attn_bwd(ctypes.byref(d), 0, P, P, P, P, P, ctypes.c_float(1.0), P, P, P,
+    rc = lib.csa_sparse_attn_bwd(ctypes.byref(d), 0, P, P, P, P, N, P, ctypes.c_float(1.0), P, P, P,
                                  P, P, P, N, P, need - 4, N)
     assert rc == -5, lib.csa_last_error()
-    rc = lib.csa_sparse_attn_bwd(ctypes.byref(d), 0, P, P, P, P, P, ctypes.c_float(1.0), P, P, P,
+    rc = lib.csa_sparse_attn_bwd(ctypes.byref(d), 0, P, P, P, P, N, P, ctypes.c_float(1.0), P, P, P,
                                  P, P, P, N, N, 0, N)
     assert rc == -5
 

@@ -74,7 +74,7 @@ def test_compress_fwd_bwd(gpu, name, wl):
 
 
 # ------------------------------------------------------------ indexer / top-k
-def _index_case(wl, seed, rows=None, **over):
+def _index_case(wl, seed, rows=None, doc=None, **over):
     import compressed_sparse_attention_softmax_amd as csa
     inp = csa_synth.make_inputs(wl, seed, device="cuda", parts=("index",))
     inp.update({k: v for k, v in over.items()})
@@ -83,11 +83,13 @@ def _index_case(wl, seed, rows=None, **over):
     idx = torch.full((wl.b, wl.sq, kp), -7, dtype=torch.int32, device="cuda")
     sc = torch.empty(wl.b, wl.sq, kp, dtype=torch.float32, device="cuda")
     assert csa.csa_index_topk_workspace(dm) == 0
-    csa.csa_index_topk(dm, inp["q_i"], inp["k_i"], inp["w"], idx, sc)
+    csa.csa_index_topk(dm, inp["q_i"], inp["k_i"], inp["w"], idx, sc,
+                       doc_ids=None if doc is None else doc.cuda())
     torch.cuda.synchronize()
     rows = oracle.all_rows(wl.b, wl.sq) if rows is None else rows
     qi, ki, w = f64(inp["q_i"]), f64(inp["k_i"]), f64(inp["w"])
-    oidx, osc, dense = oracle.index_topk(qi, ki, w, wl.ratio, wl.topk, rows=rows)
+    oidx, osc, dense = oracle.index_topk(qi, ki, w, wl.ratio, wl.topk, rows=rows,
+                                         doc=None if doc is None else doc.numpy())
     gi = idx.cpu().numpy()[rows[:, 0], rows[:, 1]]
     gs = sc.cpu().numpy()[rows[:, 0], rows[:, 1]]
     return gi, gs, oidx, dense, rows
@@ -128,6 +130,24 @@ def test_index_topk_exact_integer_scores_and_ties(gpu, monkeypatch):
     np.testing.assert_array_equal(gs[gi >= 0], dense[np.nonzero(gi >= 0)[0], gi[gi >= 0]])
 
 
+DOC_INDEX_CASES = [
+    ("tiny_f32", TINY.replace(b=2, sq=301), 40),
+    ("csa4_bf16_b2", CSA4_SMALL.replace(b=2, sq=1500, topk=60), 300),
+    ("csa4_bf16_short_docs", CSA4_SMALL.replace(sq=1200, topk=40), 30),
+]
+
+
+@pytest.mark.parametrize("name,wl,mean", DOC_INDEX_CASES, ids=[c[0] for c in DOC_INDEX_CASES])
+def test_index_topk_packed_documents(gpu, name, wl, mean, monkeypatch):
+    say(f"[index_topk docs] {name} b={wl.b} sq={wl.sq} K={wl.topk} mean doc length {mean}")
+    monkeypatch.setenv("CSA_TOPK_BUFFER", "256")
+    doc = csa_synth.packed_doc_ids(wl.b, wl.sq, mean, 7)
+    gi, gs, oidx, dense, rows = _index_case(wl, 23, doc=doc)
+    exact = check_topk_rows(gi, gs, oidx, dense, rows[:, 1], wl.ratio, wl.n_c, wl.kprime,
+                            score_tol=tol_of(wl.torch_dtype), docs=True)
+    say(f"  rows identical to the oracle: {exact}/{len(rows)}")
+
+
 def test_index_topk_all_zero_keys(gpu):
     wl = CSA4_SMALL.replace(sq=600, topk=30)
     ki = torch.zeros(1, wl.n_c, 128, dtype=torch.bfloat16, device="cuda")
@@ -137,11 +157,15 @@ def test_index_topk_all_zero_keys(gpu):
 
 
 # ------------------------------------------------------------------ attention
-def _attn_case(wl, seed, idx_mode="random", with_sink=True, window_only=False, junk=False, dsink_only=False):
+def _attn_case(wl, seed, idx_mode="random", with_sink=True, window_only=False, junk=False, dsink_only=False,
+               doc_len=None):
     import compressed_sparse_attention_softmax_amd as csa
     inp = csa_synth.make_inputs(wl, seed, device="cuda", parts=("attn", "compress", "bwd"),
                                 with_sink=with_sink)
     b, S, H, D, nc = wl.b, wl.sq, wl.h, wl.d, wl.n_c
+    doc = None if doc_len is None else csa_synth.packed_doc_ids(b, S, doc_len, seed + 2)
+    docn = None if doc is None else doc.numpy()
+    docg = None if doc is None else doc.cuda()
     # compressed rows: the oracle's pooling, cast once to the working dtype
     c = None
     if not window_only:
@@ -151,6 +175,11 @@ def _attn_case(wl, seed, idx_mode="random", with_sink=True, window_only=False, j
     if not window_only and idx_mode != "dense":
         if idx_mode == "random":
             idx = csa_synth.random_topk_indices(wl, seed + 1)
+        elif idx_mode == "indexer":      # the oracle indexer's selection (document-aware)
+            ii = csa_synth.make_inputs(wl, seed + 3, parts=("index",))
+            oi, _, _ = oracle.index_topk(f64(ii["q_i"]), f64(ii["k_i"]), f64(ii["w"]), wl.ratio, wl.topk,
+                                         doc=docn)
+            idx = torch.tensor(oi).reshape(b, S, wl.kprime)
         elif idx_mode == "block0":
             idx = torch.full((b, S, wl.kprime), -1, dtype=torch.int32)
             idx[:, wl.ratio - 1:, 0] = 0
@@ -171,7 +200,7 @@ def _attn_case(wl, seed, idx_mode="random", with_sink=True, window_only=False, j
     dtype = wl.torch_dtype
     out = torch.empty(b, S, H, D, dtype=dtype, device="cuda")
     lse = torch.empty(b, S, H, dtype=torch.float32, device="cuda")
-    csa.csa_sparse_attn_fwd(dm, inp["q"], inp["kv"], c, idx, inp["sink"], wl.scale, out, lse)
+    csa.csa_sparse_attn_fwd(dm, inp["q"], inp["kv"], c, idx, inp["sink"], wl.scale, out, lse, doc_ids=docg)
     dq = torch.empty_like(out)
     dkv = torch.full((b, S, D), 3.0, device="cuda")
     dc = torch.full((b, nc, D), 3.0, device="cuda") if c is not None else None
@@ -180,7 +209,7 @@ def _attn_case(wl, seed, idx_mode="random", with_sink=True, window_only=False, j
     if dsink_only:       # gradient gate closed: only dsink is produced
         dq = dkv = dc = None
     csa.csa_sparse_attn_bwd(dm, inp["q"], inp["kv"], c, idx, inp["sink"], wl.scale, out, lse, inp["do"],
-                            dq, dkv, dc, dsink, ws=ws)
+                            dq, dkv, dc, dsink, ws=ws, doc_ids=docg)
     torch.cuda.synchronize()
     rows = oracle.all_rows(b, S)
     q = f64(inp["q"]).reshape(b * S, H, D)
@@ -190,9 +219,9 @@ def _attn_case(wl, seed, idx_mode="random", with_sink=True, window_only=False, j
     sink = None if inp["sink"] is None else f64(inp["sink"])
     window = wl.window
     ratio = wl.ratio
-    ro, rl = oracle.attn_fwd(q, kv, cc, ii, sink, wl.scale, window, ratio, rows)
+    ro, rl = oracle.attn_fwd(q, kv, cc, ii, sink, wl.scale, window, ratio, rows, doc=docn)
     rdq, rdkv, rdc, rds = oracle.attn_bwd(q, kv, cc, ii, sink, wl.scale, window, ratio, rows,
-                                          f64(inp["do"]).reshape(b * S, H, D))
+                                          f64(inp["do"]).reshape(b * S, H, D), doc=docn)
     tol = tol_of(dtype)
     check_close("out", out.reshape(b * S, H, D), ro, tol)
     check_close("lse", lse.reshape(b * S, H), rl, tol)
@@ -217,6 +246,14 @@ ATTN_CASES = [
     ("csa4_bf16_dense", CSA4_SMALL.replace(sq=500), dict(idx_mode="dense")),
     ("csa4_bf16_window_only", CSA4_SMALL.replace(sq=300), dict(window_only=True)),
     ("csa4_bf16_dsink_only", CSA4_SMALL.replace(sq=300), dict(dsink_only=True)),
+    ("tiny_f32_docs_dense", TINY.replace(b=2, sq=257), dict(idx_mode="dense", doc_len=30)),
+    ("tiny_f32_docs_indexer", TINY.replace(b=2, sq=257), dict(idx_mode="indexer", doc_len=30)),
+    ("csa4_bf16_docs_indexer", CSA4_SMALL.replace(b=2, sq=700, topk=40), dict(idx_mode="indexer", doc_len=150)),
+    ("csa4_bf16_docs_random_idx", CSA4_SMALL.replace(sq=500, topk=40), dict(doc_len=100)),
+    ("csa4_bf16_docs_dense", CSA4_SMALL.replace(sq=600), dict(idx_mode="dense", doc_len=90)),
+    ("csa4_bf16_docs_window_only", CSA4_SMALL.replace(sq=400), dict(window_only=True, doc_len=60)),
+    ("csa4_bf16_docs_h48", CSA4_SMALL.replace(b=2, sq=333, h=48, topk=40), dict(idx_mode="indexer", doc_len=70)),
+    ("d512_bf16_docs", D512_SMALL, dict(idx_mode="indexer", doc_len=80)),
     ("d512_bf16", D512_SMALL, {}),
     ("hca128_bf16_dense", HCA_SMALL, dict(idx_mode="dense")),
 ]

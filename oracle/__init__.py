@@ -12,6 +12,9 @@ Two independent formulations live here:
 * ``brute.py``: a NumPy dense formulation over the unified key axis (raw rows
   followed by compressed rows) plus a sink column, used on tiny inputs to
   cross-check the C oracle.
+* ``indexer_loss.py``: the indexer's training path (teacher target from the
+  attention LSE, the student's selected scores, the KL loss and its
+  gradients), plain NumPy one query row at a time.
 
 All arrays handed to the C oracle are float64 (int32 for index lists).
 """

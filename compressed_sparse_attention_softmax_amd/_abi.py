@@ -24,11 +24,12 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_ARG", -2: "CSA_ERR_SHAPE", -3: "CSA_ERR_DTYP
 # every symbol include/csa.h declares
 EXPORTS = ["csa_compress", "csa_compress_bwd", "csa_index_topk_workspace", "csa_index_topk",
            "csa_sparse_attn_fwd", "csa_sparse_attn_bwd_workspace", "csa_sparse_attn_bwd",
-           "csa_last_error", "csa_version", "csa_timing_enable", "csa_timing_read", "csa_kernel_name"]
+           "csa_indexer_loss_workspace", "csa_indexer_loss", "csa_last_error", "csa_version", "csa_timing_enable", "csa_timing_read", "csa_kernel_name"]
 
 # kernel ids of the timing hook (enum csa_kernel_id)
 CSA_K_COMPRESS_FWD, CSA_K_COMPRESS_BWD, CSA_K_INDEX_TOPK, CSA_K_ATTN_FWD = 0, 1, 2, 3
 CSA_K_ATTN_DQ, CSA_K_ATTN_ROWS, CSA_K_ATTN_REDUCE = 4, 5, 6
+CSA_K_LOSS_QUERY, CSA_K_LOSS_KEYS, CSA_K_LOSS_REDUCE = 7, 8, 9
 
 
 class CSAError(RuntimeError):
@@ -67,6 +68,9 @@ def load(path: Optional[str] = None):
     lib.csa_sparse_attn_bwd_workspace.argtypes = [D]
     lib.csa_sparse_attn_bwd_workspace.restype = sz
     lib.csa_sparse_attn_bwd.argtypes = [D, i, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.csa_indexer_loss_workspace.argtypes = [D]
+    lib.csa_indexer_loss_workspace.restype = sz
+    lib.csa_indexer_loss.argtypes = [D, i, vp, vp, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.csa_last_error.argtypes = []
     lib.csa_last_error.restype = ctypes.c_char_p
     lib.csa_version.argtypes = []
@@ -75,7 +79,7 @@ def load(path: Optional[str] = None):
     lib.csa_kernel_name.argtypes = [i]
     lib.csa_kernel_name.restype = ctypes.c_char_p
     for fn in ("csa_compress", "csa_compress_bwd", "csa_index_topk", "csa_sparse_attn_fwd",
-               "csa_sparse_attn_bwd", "csa_version", "csa_timing_enable", "csa_timing_read"):
+               "csa_sparse_attn_bwd", "csa_indexer_loss", "csa_version", "csa_timing_enable", "csa_timing_read"):
         getattr(lib, fn).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -219,6 +223,29 @@ def csa_sparse_attn_bwd(dims: csa_dims, q, kv, c, idx, sink, scale: float, out, 
           _ptr(dq, shape=(b, S, H, D), dtype=q.dtype, name="dq"),
           _ptr(dkv, shape=(b, S, D), dtype=f32, name="dkv"), _ptr(dc, shape=(b, nc, D), dtype=f32, name="dc"),
           _ptr(dsink, shape=(H,), dtype=f32, name="dsink"), _ptr(ws, name="ws"),
+          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def csa_indexer_loss_workspace(dims: csa_dims) -> int:
+    return int(load().csa_indexer_loss_workspace(ctypes.byref(dims)))
+
+
+def csa_indexer_loss(dims: csa_dims, q, c, lse, q_i, k_i, w, idx, score, scale: float, kl=None, dkl=None,
+                     dq_i=None, dw=None, dk_i=None, ws=None, stream=None) -> None:
+    b, S, H, D = dims.b, dims.sq, dims.h, dims.d
+    HI, DI = dims.idx_heads, dims.idx_dim
+    nc, kp = n_compressed(dims), kprime(dims)
+    dt, f32 = q.dtype, torch.float32
+    _call("csa_indexer_loss", ctypes.byref(dims), _dtype_code(q),
+          _ptr(q, shape=(b, S, H, D), dtype=dt, name="q"), _ptr(c, shape=(b, nc, D), dtype=dt, name="c"),
+          _ptr(lse, shape=(b, S, H), dtype=f32, name="lse"),
+          _ptr(q_i, shape=(b, S, HI, DI), dtype=dt, name="q_i"), _ptr(k_i, shape=(b, nc, DI), dtype=dt, name="k_i"),
+          _ptr(w, shape=(b, S, HI), dtype=f32, name="w"),
+          _ptr(idx, shape=(b, S, kp), dtype=torch.int32, name="idx"),
+          _ptr(score, shape=(b, S, kp), dtype=f32, name="score"), ctypes.c_float(scale),
+          _ptr(dkl, shape=(b, S), dtype=f32, name="dkl"), _ptr(kl, shape=(b, S), dtype=f32, name="kl"),
+          _ptr(dq_i, shape=(b, S, HI, DI), dtype=dt, name="dq_i"), _ptr(dw, shape=(b, S, HI), dtype=f32, name="dw"),
+          _ptr(dk_i, shape=(b, nc, DI), dtype=f32, name="dk_i"), _ptr(ws, name="ws"),
           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
 
 

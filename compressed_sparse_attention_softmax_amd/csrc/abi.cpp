@@ -233,3 +233,78 @@ int csa_sparse_attn_bwd(const csa_dims* dm, int dtype, const void* q, const void
 }
 
 }  // extern "C"
+
+namespace {
+
+int check_loss(const csa_dims* dm, int dtype, const char* fn)
+{
+    if (!supported_d(dm->d)) return fail(CSA_ERR_UNSUPPORTED, "%s: d=%d not in {64,128,512}", fn, dm->d);
+    if (dm->d == 512 && dtype == CSA_F32)
+        return fail(CSA_ERR_UNSUPPORTED, "%s: fp32 with d=512 exceeds the on-chip row tile", fn);
+    if (dm->h < 1 || dm->h > 64) return fail(dm->h < 1 ? CSA_ERR_ARG : CSA_ERR_UNSUPPORTED, "%s: h=%d not in [1, 64]", fn, dm->h);
+    if (dm->ratio < 1) return fail(CSA_ERR_ARG, "%s: ratio=%d must be >= 1", fn, dm->ratio);
+    if (dm->topk < 1) return fail(CSA_ERR_ARG, "%s: topk=%d must be >= 1", fn, dm->topk);
+    if (dm->idx_heads < 1 || dm->idx_heads > 64)
+        return fail(dm->idx_heads < 1 ? CSA_ERR_ARG : CSA_ERR_UNSUPPORTED, "%s: idx_heads=%d not in [1, 64]", fn,
+                    dm->idx_heads);
+    if (dm->idx_dim != 32 && dm->idx_dim != 64 && dm->idx_dim != 128)
+        return fail(CSA_ERR_UNSUPPORTED, "%s: idx_dim=%d not in {32,64,128}", fn, dm->idx_dim);
+    if (kprime(dm) > 2048) return fail(CSA_ERR_UNSUPPORTED, "%s: K'=%d > 2048", fn, kprime(dm));
+    return CSA_OK;
+}
+
+csa::LossArgs loss_args(const csa_dims* dm)
+{
+    csa::LossArgs a{};
+    a.b = dm->b; a.S = dm->sq; a.H = dm->h; a.D = dm->d; a.HI = dm->idx_heads; a.DI = dm->idx_dim;
+    a.r = dm->ratio; a.nc = dm->sq / dm->ratio; a.kp = kprime(dm);
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t csa_indexer_loss_workspace(const csa_dims* dm)
+{
+    if (!dm || dm->b < 1 || dm->sq < 1 || dm->ratio < 1 || dm->topk < 1) return 0;
+    if (dm->idx_dim != 32 && dm->idx_dim != 64 && dm->idx_dim != 128) return 0;
+    return csa::indexer_loss_workspace_bytes(loss_args(dm));
+}
+
+int csa_indexer_loss(const csa_dims* dm, int dtype, const void* q, const void* c, const float* lse,
+                     const void* q_i, const void* k_i, const float* w, const int32_t* idx, const float* score,
+                     float scale, const float* dkl, float* kl, void* dq_i, float* dw, float* dk_i, void* ws,
+                     size_t ws_bytes, void* stream)
+{
+    int rc = check_common(dm, dtype, "csa_indexer_loss");
+    if (rc) return rc;
+    if ((rc = check_loss(dm, dtype, "csa_indexer_loss"))) return rc;
+    if (!std::isfinite(scale)) return fail(CSA_ERR_ARG, "csa_indexer_loss: scale is not finite");
+    // tensors with no elements (no compressed block yet: n_c = K' = 0) may be NULL
+    const bool blocks = dm->sq / dm->ratio > 0;
+    if (!q || !lse || (blocks && (!c || !idx || !score)))
+        return fail(CSA_ERR_ARG, "csa_indexer_loss: q, c, lse, idx and score must be non-NULL");
+    const bool any = dkl || dq_i || dw || dk_i;
+    if (any) {
+        if (!dkl || !dq_i || !dw || (blocks && !dk_i))
+            return fail(CSA_ERR_ARG, "csa_indexer_loss: gradient gate: dkl, dq_i, dw and dk_i must all be given "
+                                     "(or all be NULL)");
+        if (!q_i || !w || (blocks && !k_i))
+            return fail(CSA_ERR_ARG, "csa_indexer_loss: q_i, k_i and w must be non-NULL with gradients");
+    }
+    if (!any && !kl) return ok();
+    csa::LossArgs a = loss_args(dm);
+    a.q = q; a.c = c; a.lse = lse; a.qi = q_i; a.ki = k_i; a.w = w; a.idx = idx; a.score = score;
+    a.scale = scale; a.dkl = dkl; a.kl = kl; a.dqi = dq_i; a.dw = dw; a.dki = dk_i;
+    if (any) {
+        const size_t need = csa::indexer_loss_workspace_bytes(a);
+        if (need > 0 && (!ws || ws_bytes < need))
+            return fail(CSA_ERR_WORKSPACE, "csa_indexer_loss: workspace of %zu bytes needed, %zu given", need,
+                        ws ? ws_bytes : (size_t)0);
+        if (((uintptr_t)ws) & 15) return fail(CSA_ERR_ARG, "csa_indexer_loss: workspace must be 16-byte aligned");
+    }
+    return hip_status(csa::indexer_loss(a, dtype == CSA_BF16, (float*)ws, (hipStream_t)stream), "csa_indexer_loss");
+}
+
+}  // extern "C"

@@ -43,64 +43,6 @@ constexpr int CHUNK = 32;
 
 template <typename T> constexpr int row_pad() { return 16 / (int)sizeof(T); }
 
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) int32_t lds_i32;
-typedef __attribute__((address_space(3))) uint32_t lds_u32;
-
-// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
-// (i % 4) of the 8-byte words addressed by lanes 4k + i/4, k = 0..3.
-__device__ __forceinline__ bf16x4 ds_read_tr(const bf16_t* p)
-{
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-}
-
-// Row-dependent permutation of the 8-element units of an LDS row: unit u of
-// row r is stored at u ^ unit_swz(r, units).  Within any 16 consecutive rows
-// (aligned) the XOR values are all different, so 16 lanes reading the same
-// unit of 16 rows hit 16 different bank groups; within any 8 consecutive
-// rows (aligned) they differ in more than the lowest bit, so 32 lanes reading
-// a unit pair {2m, 2m+1} of 8 rows (the transposing read) hit 16 different
-// bank groups.  `units` (a power of two) is the number of units per row.
-__device__ __forceinline__ int unit_swz(int r, int units)
-{
-    return (((r & 7) << 1) | ((r >> 3) & 1)) & (units - 1);
-}
-
-// MFMA operand whose k index runs over rows of a row-major LDS tile:
-// lane (n = lane%16, g = lane/16) gets column col0 + n of rows
-// r0 + 4g + e (e = 0..3) and r0 + 16 + 4g + (e-4) (e = 4..7).
-// This is the row order in which a 16x16 C tile pair (rows 0-15, 16-31 of a
-// 32-row chunk, lane holding rows 4g+i) feeds the k slots of one operand.
-// `stride` is the row stride in elements; with `swz` the tile is stored with
-// 8-element units permuted per row (unit u of row r at u ^ unit_swz(r)).
-template <typename T>
-__device__ __forceinline__ Frag<T> rows_operand(const T* tile, int stride, int r0, int col0, bool swz)
-{
-    const int lane = lane_id(), g = lane / 16, n16 = lane % 16;
-    Frag<T> f;
-    if constexpr (sizeof(T) == 2) {
-        const int r = r0 + 4 * g + (n16 >> 2);
-        const int c = col0 + 4 * (n16 & 3);
-        auto addr = [&](int rr) {
-            const int cc = swz ? ((((c >> 3) ^ unit_swz(rr, stride >> 3)) << 3) | (c & 7)) : c;
-            return tile + rr * stride + cc;
-        };
-        const bf16x4 a = ds_read_tr(addr(r));
-        const bf16x4 b = ds_read_tr(addr(r + 16));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = b[e]; }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int rr = r0 + 16 * (e / 4) + 4 * g + (e % 4);
-            const int c = col0 + n16;
-            const int cc = swz ? ((((c >> 3) ^ unit_swz(rr, stride >> 3)) << 3) | (c & 7)) : c;
-            f.v[e] = tile[rr * stride + cc];
-        }
-    }
-    return f;
-}
-
 // Candidate list of one query: window slots [0, nwin), then compressed slots.
 template <typename T>
 struct Cand {

@@ -49,6 +49,26 @@ struct AttnArgs {
     int b, S, H, D, W, r, nc, kp;
 };
 
+// Indexer distillation loss (teacher from the attention LSE, KL over the
+// selected blocks) and its gradients into q_i, w and k_i.
+struct LossArgs {
+    const void* q;        // [b, S, H, D] attention queries
+    const void* c;        // [b, nc, D] compressed rows
+    const float* lse;     // [b, S, H] attention forward LSE
+    const void* qi;       // [b, S, HI, DI]
+    const void* ki;       // [b, nc, DI]
+    const float* w;       // [b, S, HI]
+    const int32_t* idx;   // [b, S, kp] selected blocks
+    const float* score;   // [b, S, kp] their indexer scores
+    float scale;
+    const float* dkl;     // [b, S] upstream gradient of each row's KL (nullptr: forward only)
+    float* kl;            // [b, S] or nullptr
+    void* dqi;            // [b, S, HI, DI] (dtype) or nullptr (with dw, dki)
+    float* dw;            // [b, S, HI]
+    float* dki;           // [b, nc, DI]
+    int b, S, H, D, HI, DI, r, nc, kp;
+};
+
 hipError_t compress_fwd(const CompressArgs& p, bool bf16, hipStream_t st);
 hipError_t compress_bwd(const CompressArgs& p, bool bf16, hipStream_t st);
 hipError_t index_topk(const IndexArgs& p, bool bf16, hipStream_t st);
@@ -57,6 +77,8 @@ size_t topk_lds_bytes(int DI, int elem, int cap);
 hipError_t attn_fwd(const AttnArgs& p, bool bf16, hipStream_t st);
 hipError_t attn_bwd(const AttnArgs& p, bool bf16, float* ws, hipStream_t st);
 size_t attn_bwd_workspace_bytes(const AttnArgs& p);
+hipError_t indexer_loss(const LossArgs& p, bool bf16, float* ws, hipStream_t st);
+size_t indexer_loss_workspace_bytes(const LossArgs& p);
 hipError_t zero_fill(float* p, size_t n, hipStream_t st);
 
 }  // namespace csa

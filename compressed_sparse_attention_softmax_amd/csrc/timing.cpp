@@ -91,7 +91,8 @@ int csa_timing_read(int* launches, double* total_ms)
 const char* csa_kernel_name(int kernel)
 {
     static const char* names[csa::K_COUNT] = {"compress_fwd", "compress_bwd", "index_topk", "attn_query_fwd",
-                                               "attn_query_dq", "attn_rows", "attn_reduce"};
+                                               "attn_query_dq", "attn_rows", "attn_reduce", "loss_query",
+                                               "loss_keys", "loss_reduce"};
     return (kernel >= 0 && kernel < csa::K_COUNT) ? names[kernel] : "";
 }
 

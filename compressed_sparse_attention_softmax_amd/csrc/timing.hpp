@@ -16,7 +16,10 @@ enum KernelId {
     K_ATTN_DQ = 4,
     K_ATTN_ROWS = 5,
     K_ATTN_REDUCE = 6,
-    K_COUNT = 7,
+    K_LOSS_QUERY = 7,
+    K_LOSS_KEYS = 8,
+    K_LOSS_REDUCE = 9,
+    K_COUNT = 10,
 };
 
 // RAII bracket around one launch: records the start event at construction and

@@ -7,6 +7,11 @@ The compressed rows produced by ``csa_compress`` feed the attention, and the
 compressed-row gradient of the attention backward feeds the compressor
 backward.  With ``topk == 0`` the indexer is skipped and the attention runs in
 dense mode over every valid compressed row (the heavy-compression layer).
+
+``indexer_loss`` is the indexer's training path: after the attention forward
+it consumes the selected blocks, their scores and the attention LSE and
+produces the distillation loss per query row and its gradients into the
+indexer's inputs.
 """
 from __future__ import annotations
 
@@ -77,3 +82,34 @@ def backward(dims, inp, buf: Buffers, scale: float, stream=None) -> None:
 def step(dims, inp, buf: Buffers, scale: float, stream=None) -> None:
     forward(dims, inp, buf, scale, stream)
     backward(dims, inp, buf, scale, stream)
+
+
+@dataclasses.dataclass
+class LossBuffers:
+    kl: torch.Tensor
+    dq_i: torch.Tensor
+    dw: torch.Tensor
+    dk_i: torch.Tensor
+    ws: torch.Tensor        # csa_indexer_loss_workspace bytes
+
+
+def allocate_loss(dims: abi.csa_dims, dtype: torch.dtype, device="cuda") -> LossBuffers:
+    b, S = dims.b, dims.sq
+    nc = abi.n_compressed(dims)
+    f32 = torch.float32
+    e = dict(device=device)
+    return LossBuffers(
+        kl=torch.empty(b, S, dtype=f32, **e),
+        dq_i=torch.empty(b, S, dims.idx_heads, dims.idx_dim, dtype=dtype, **e),
+        dw=torch.empty(b, S, dims.idx_heads, dtype=f32, **e),
+        dk_i=torch.empty(b, nc, dims.idx_dim, dtype=f32, **e),
+        ws=torch.empty(max(abi.csa_indexer_loss_workspace(dims), 16), dtype=torch.uint8, **e),
+    )
+
+
+def indexer_loss(dims, inp, buf: Buffers, lbuf: LossBuffers, scale: float, dkl, c=None, stream=None) -> None:
+    """Distillation loss of the indexer over the blocks ``buf.idx`` selected, with
+    the attention LSE ``buf.lse``; ``dkl`` [b, sq] weights each row's loss."""
+    abi.csa_indexer_loss(dims, inp["q"], buf.c if c is None else c, buf.lse, inp["q_i"], inp["k_i"], inp["w"],
+                         buf.idx, buf.score, scale, kl=lbuf.kl, dkl=dkl, dq_i=lbuf.dq_i, dw=lbuf.dw,
+                         dk_i=lbuf.dk_i, ws=lbuf.ws, stream=stream)

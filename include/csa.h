@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 };
 
@@ -177,6 +177,43 @@ int csa_sparse_attn_bwd(const csa_dims* dims, int dtype, const void* q, const vo
                         float* dkv, float* dc, float* dsink, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* Workspace bytes csa_indexer_loss needs when gradients are requested
+ * (device memory, 16-byte aligned, owned by the caller, contents on entry
+ * irrelevant): dI ([b, sq, K'] fp32) and fp32 partial rows of dk_i per block
+ * of consecutive queries, reduced in a fixed order.  0 for invalid dims. */
+size_t csa_indexer_loss_workspace(const csa_dims* dims);
+
+/* Indexer distillation loss and its gradients (the indexer's training path;
+ * torchtitan PR #4452, lightning indexer and indexer distillation loss;
+ * Megatron-LM PR #6400, teacher normalisation thread; Megatron-LM PR #7152,
+ * reuse of the routing scores and fp32 scatter of selected gradients).
+ * For row (b, t) the support is the slots s of idx[b, t, :] (the output of
+ * csa_index_topk) with 0 <= j_s < n_valid(t); with lse the per-head LSE of
+ * csa_sparse_attn_fwd for the same row:
+ *   mass[s]    = sum_h exp(scale * <q[t, h], c[j_s]> - lse[t, h])
+ *   target     = mass / sum(mass)            (all zero on an empty support)
+ *   predict    = softmax over the support of score[b, t, s] (the fp32 scores
+ *                csa_index_topk wrote beside idx: the student's logits)
+ *   kl[b, t]   = sum_s target (log target - log predict)          (fp32)
+ * The teacher is detached.  With dkl ([b, sq] fp32, the upstream gradient of
+ * each row's kl) and a = <q_i[t, h], k_i[j_s]>:
+ *   dI[s]      = dkl[t] * (predict[s] * sum(target) - target[s])
+ *   dw[t, h]   = sum_s dI[s] * relu(a)                            (fp32)
+ *   dq_i[t, h] = sum_s dI[s] * w[t, h] * [a > 0] * k_i[j_s]        (dtype)
+ *   dk_i[j]    = sum over (t, s) with j_s = j of dI * w * [a > 0] * q_i[t, h]
+ *                summed over h, accumulated in fp32                (fp32)
+ * Layouts as in CONVENTIONS; lse [b, sq, h], score [b, sq, K'] fp32.
+ * kl may be NULL.  Gradient gate: dkl, dq_i, dw and dk_i are all non-NULL
+ * (then q_i, k_i, w and the workspace are required) or all NULL (the call
+ * only writes kl).  Every element of the outputs is overwritten.  ws /
+ * ws_bytes: CSA_ERR_WORKSPACE if gradients are requested and ws is NULL or
+ * smaller than csa_indexer_loss_workspace(dims). */
+int csa_indexer_loss(const csa_dims* dims, int dtype, const void* q, const void* c,
+                     const float* lse, const void* q_i, const void* k_i, const float* w,
+                     const int32_t* idx, const float* score, float scale,
+                     const float* dkl, float* kl, void* dq_i, float* dw, float* dk_i,
+                     void* ws, size_t ws_bytes, void* stream);
+
 /* Message for the last failing call on this thread ("" if none). */
 const char* csa_last_error(void);
 
@@ -192,6 +229,9 @@ int csa_version(void);
  *   csa_sparse_attn_fwd   -> CSA_K_ATTN_FWD
  *   csa_sparse_attn_bwd   -> CSA_K_ATTN_DQ (dq, Delta, dsink), CSA_K_ATTN_ROWS
  *                            (per-query-block dkv / dc partials), CSA_K_ATTN_REDUCE
+ *   csa_indexer_loss      -> CSA_K_LOSS_QUERY (teacher, kl, dI, dq_i, dw),
+ *                            CSA_K_LOSS_KEYS (per-query-block dk_i partials),
+ *                            CSA_K_LOSS_REDUCE
  * csa_timing_enable(k) makes every later launch of kernel k, from any thread,
  * record one hipEvent before and one after it on the launch stream; -1
  * switches timing off.  Returns CSA_ERR_ARG for an unknown id.
@@ -201,7 +241,8 @@ int csa_version(void);
  * the library on first use and reused; they are the only resource it keeps. */
 enum csa_kernel_id {
     CSA_K_COMPRESS_FWD = 0, CSA_K_COMPRESS_BWD = 1, CSA_K_INDEX_TOPK = 2, CSA_K_ATTN_FWD = 3,
-    CSA_K_ATTN_DQ = 4, CSA_K_ATTN_ROWS = 5, CSA_K_ATTN_REDUCE = 6
+    CSA_K_ATTN_DQ = 4, CSA_K_ATTN_ROWS = 5, CSA_K_ATTN_REDUCE = 6, CSA_K_LOSS_QUERY = 7,
+    CSA_K_LOSS_KEYS = 8, CSA_K_LOSS_REDUCE = 9
 };
 int csa_timing_enable(int kernel);
 int csa_timing_read(int* launches, double* total_ms);

@@ -33,7 +33,7 @@ def test_library_exports_every_header_symbol():
     lib = _lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.csa_version() == 2
+    assert lib.csa_version() == 3
 
 
 def test_dims_struct_matches_header():
@@ -130,6 +130,43 @@ def test_workspace_too_small_is_rejected():
     assert rc == -5
 
 
+def _loss(dims=None, dkl=N, kl=P, dq_i=N, dw=N, dk_i=N, ws=N, ws_bytes=0, q_i=P, scale=1.0):
+    lib = _lib()
+    return lib.csa_indexer_loss(ctypes.byref(dims or _d()), 0, P, P, P, q_i, P, P, P, P, ctypes.c_float(scale),
+                                dkl, kl, dq_i, dw, dk_i, ws, ws_bytes, N)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dims=_d(idx_dim=48)), -4),
+    (dict(dims=_d(idx_heads=65)), -4),
+    (dict(dims=_d(h=65)), -4),
+    (dict(dims=_d(d=96)), -4),
+    (dict(dims=_d(topk=0)), -1),
+    (dict(dims=_d(sq=65536, topk=4096)), -4),
+    (dict(scale=float("inf")), -1),
+    (dict(dkl=P), -1),                              # gradient gate: dq_i, dw, dk_i missing
+    (dict(dkl=P, dq_i=P, dw=P), -1),
+    (dict(dq_i=P, dw=P, dk_i=P), -1),               # gradients without dkl
+    (dict(dkl=P, dq_i=P, dw=P, dk_i=P, q_i=N), -1),  # q_i required with gradients
+    (dict(dkl=P, dq_i=P, dw=P, dk_i=P), -5),        # no workspace
+])
+def test_indexer_loss_validation(kw, code):
+    rc = _loss(**kw)
+    assert rc == code, (kw, rc, _lib().csa_last_error())
+    assert _lib().csa_last_error().decode().startswith("csa_indexer_loss")
+
+
+def test_indexer_loss_nothing_requested_is_a_noop_and_workspace():
+    lib = _lib()
+    assert _loss(kl=N) == 0
+    d = _d()
+    need = lib.csa_indexer_loss_workspace(ctypes.byref(d))
+    kp = min(d.topk, d.sq // d.ratio)
+    assert need >= 4 * (d.b * d.sq * kp + d.sq // d.ratio * d.idx_dim)
+    assert _loss(dkl=P, dq_i=P, dw=P, dk_i=P, ws=P, ws_bytes=need - 4) == -5
+    assert lib.csa_indexer_loss_workspace(None) == 0
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="libcsa.so not found"):
         _abi.load(str(tmp_path / "missing.so"))
@@ -138,12 +175,12 @@ def test_binding_fails_loudly_without_library(tmp_path):
 def test_timing_hook_without_launches():
     # host-only paths: enabling, reading with nothing recorded, names, bad ids
     lib = _lib()
-    assert lib.csa_timing_enable(7) == -1
+    assert lib.csa_timing_enable(10) == -1
     assert lib.csa_timing_enable(-2) == -1
     assert lib.csa_timing_enable(csa.CSA_K_ATTN_ROWS) == 0
     assert csa.csa_timing_read() == (0, 0.0)
     assert lib.csa_timing_enable(-1) == 0
-    names = [csa.csa_kernel_name(k) for k in range(7)]
+    names = [csa.csa_kernel_name(k) for k in range(10)]
     assert names == ["compress_fwd", "compress_bwd", "index_topk", "attn_query_fwd", "attn_query_dq",
-                     "attn_rows", "attn_reduce"]
+                     "attn_rows", "attn_reduce", "loss_query", "loss_keys", "loss_reduce"]
     assert csa.csa_kernel_name(99) == ""

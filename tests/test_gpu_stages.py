@@ -263,3 +263,81 @@ ATTN_CASES = [
 def test_sparse_attention_fwd_bwd(gpu, name, wl, kw):
     say(f"[attn] {name} b={wl.b} sq={wl.sq} h={wl.h} d={wl.d} W={wl.window} r={wl.ratio} K={wl.topk} {kw}")
     _attn_case(wl, 31, **kw)
+
+
+# ------------------------------------------------ indexer distillation loss
+def _loss_case(wl, seed, junk=False, grads=True):
+    import compressed_sparse_attention_softmax_amd as csa
+    from oracle import indexer_loss as il
+    inp = csa_synth.make_inputs(wl, seed, device="cpu", parts=("attn", "compress", "index"))
+    b, S, H, D, nc, kp = wl.b, wl.sq, wl.h, wl.d, wl.n_c, wl.kprime
+    dt = wl.torch_dtype
+    c = torch.tensor(oracle.compress(f64(inp["x"]), f64(inp["z"]), wl.ratio, wl.span)).to(dt)
+    qi, ki, w = f64(inp["q_i"]), f64(inp["k_i"]), f64(inp["w"])
+    oidx, osc, _ = oracle.index_topk(qi, ki, w, wl.ratio, wl.topk)
+    idx = np.asarray(oidx, dtype=np.int32).reshape(b * S, kp).copy()
+    score = np.asarray(osc, dtype=np.float32).reshape(b * S, kp).copy()
+    if junk:
+        g = np.random.default_rng(seed)
+        for n in range(0, b * S, 3):
+            t = n % S
+            nv = min((t + 1) // wl.ratio, nc)
+            if kp >= 3 and nv >= 3:
+                idx[n, 1] = -1                                   # hole
+                idx[n, 2] = nv + int(g.integers(0, 4))           # not yet valid
+    rows = oracle.all_rows(b, S)
+    q64 = f64(inp["q"]).reshape(b * S, H, D)
+    _, lse64 = oracle.attn_fwd(q64, f64(inp["kv"]), f64(c), idx, f64(inp["sink"]), wl.scale, wl.window,
+                               wl.ratio, rows)
+    lse = torch.tensor(lse64, dtype=torch.float32)               # the stage input, rounded once
+    gen = torch.Generator().manual_seed(seed + 5)
+    dkl = torch.randn(b, S, generator=gen)
+    dm = csa.dims_of(wl)
+    cu = lambda a: torch.as_tensor(a).cuda()
+    kl = torch.full((b, S), 7.0, device="cuda")
+    out = {}
+    if grads:
+        out = dict(dq_i=torch.full((b, S, wl.idx_heads, wl.idx_dim), 7.0, dtype=dt, device="cuda"),
+                   dw=torch.full((b, S, wl.idx_heads), 7.0, device="cuda"),
+                   dk_i=torch.full((b, nc, wl.idx_dim), 7.0, device="cuda"))
+        ws = torch.empty(csa.csa_indexer_loss_workspace(dm), dtype=torch.uint8, device="cuda")
+    else:
+        ws = None
+    csa.csa_indexer_loss(dm, cu(inp["q"]), cu(c), cu(lse.reshape(b, S, H)), cu(inp["q_i"]), cu(inp["k_i"]),
+                         cu(inp["w"]), cu(idx.reshape(b, S, kp)), cu(score.reshape(b, S, kp)), wl.scale, kl=kl,
+                         dkl=cu(dkl) if grads else None, ws=ws, **out)
+    torch.cuda.synchronize()
+    # oracle, fed the same rounded values
+    nv = np.minimum((rows[:, 1] + 1) // wl.ratio, nc)
+    valid = (idx >= 0) & (idx < nv[:, None])
+    target = il.teacher_target(q64, f64(c), f64(lse), idx, wl.scale, wl.ratio, rows)
+    r_kl, predict = il.kl_loss(target, np.where(valid, score.astype(np.float64), -np.inf))
+    tol = tol_of(dt)
+    check_close("kl", kl.reshape(-1), r_kl, tol)
+    if grads:
+        rdq, rdw, rdk, _ = il.loss_bwd(qi.reshape(b * S, wl.idx_heads, wl.idx_dim), ki,
+                                       w.reshape(b * S, wl.idx_heads), idx, wl.ratio, rows, target, predict,
+                                       dkl.double().numpy().reshape(-1))
+        check_close("dq_i", out["dq_i"].reshape(b * S, wl.idx_heads, wl.idx_dim), rdq, tol)
+        check_close("dw", out["dw"].reshape(b * S, wl.idx_heads), rdw, tol)
+        check_close("dk_i", out["dk_i"], rdk, tol)
+
+
+LOSS_CASES = [
+    ("tiny_f32", TINY, {}),
+    ("tiny_f32_b2_junk_idx", TINY.replace(b=2, sq=203), dict(junk=True)),
+    ("tiny_f32_kl_only", TINY, dict(grads=False)),
+    ("csa4_bf16", CSA4_SMALL, {}),
+    ("csa4_bf16_k512", CSA4_SMALL.replace(sq=2100, topk=512), {}),
+    ("csa4_bf16_b2_h48_junk", CSA4_SMALL.replace(b=2, sq=333, h=48, topk=40), dict(junk=True)),
+    ("idx_dim64_heads40", CSA4_SMALL.replace(idx_heads=40, idx_dim=64, sq=900, topk=70), {}),
+    ("d512_bf16", D512_SMALL, {}),
+    ("shorter_than_ratio", TINY.replace(sq=3), {}),
+]
+
+
+@pytest.mark.parametrize("name,wl,kw", LOSS_CASES, ids=[c[0] for c in LOSS_CASES])
+def test_indexer_loss(gpu, name, wl, kw):
+    say(f"[indexer_loss] {name} b={wl.b} sq={wl.sq} h={wl.h} d={wl.d} HI={wl.idx_heads} DI={wl.idx_dim} "
+        f"K={wl.topk} {kw}")
+    _loss_case(wl, 41, **kw)

@@ -106,3 +106,67 @@ def test_workload_parity(gpu, name):
     check_close("dz", buf.dz, rdz, tol)
     del buf, inp, inp_b, do_m
     torch.cuda.empty_cache()
+
+
+LOSS_WORKLOADS = [n for n in csa_synth.WORKLOAD_ORDER if csa_synth.WORKLOADS[n].topk > 0]
+N_LOSS_ROWS = {"tiny_f32": 128, "csa4_s4096": 32, "csa4_d512_s8192": 16, "csa4_s65536_skew": 12}
+
+
+@pytest.mark.parametrize("name", LOSS_WORKLOADS)
+def test_workload_indexer_loss(gpu, name):
+    """The indexer's training path at full size after a full forward pass.
+
+    The loss is linear in dkl, so a dkl that is zero except on sampled rows
+    makes every gradient (the sampled rows of dq_i and dw, all of dk_i) an
+    oracle computation over those rows.  The sampled rows are fed the
+    oracle's selection, scores and LSE (and every row the oracle's
+    compressed rows), so both sides see the same inputs there."""
+    import compressed_sparse_attention_softmax_amd as csa
+    from compressed_sparse_attention_softmax_amd import pipeline
+    from oracle import indexer_loss as il
+    wl = csa_synth.WORKLOADS[name]
+    seed = csa_synth.WORKLOAD_SEEDS[name]
+    say(f"[workload loss] {name} seed={seed} b={wl.b} sq={wl.sq} h={wl.h} d={wl.d} K={wl.topk} {wl.dtype}")
+    torch.cuda.empty_cache()
+    inp = csa_synth.make_inputs(wl, seed, device="cuda", parts=("attn", "compress", "index"))
+    dm = csa.dims_of(wl)
+    buf = pipeline.allocate(dm, wl.torch_dtype, wl.z_channels)
+    pipeline.forward(dm, inp, buf, wl.scale)
+    b, S, H, D, nc, r, kp = wl.b, wl.sq, wl.h, wl.d, wl.n_c, wl.ratio, wl.kprime
+    c_or = torch.tensor(oracle.compress(f64(inp["x"]), f64(inp["z"]), r, wl.span)).to(wl.torch_dtype)
+    must = [0, 1, r - 1, r, kp * r - 1, kp * r, S - 1]
+    rows = sample_rows(b, S, N_LOSS_ROWS[name], seed + 7, must)
+    rb, rt = rows[:, 0], rows[:, 1]
+    qi_rows, w_rows = f64(inp["q_i"][rb, rt]), f64(inp["w"][rb, rt])
+    dense = oracle.index_scores(qi_rows, f64(inp["k_i"]), w_rows, r, rows)
+    oidx, osc = oracle.topk(dense, r, wl.topk, rows)
+    q_rows = f64(inp["q"][rb, rt])
+    _, lse_rows = oracle.attn_fwd(q_rows, f64(inp["kv"]), f64(c_or), oidx, f64(inp["sink"]), wl.scale,
+                                  wl.window, r, rows)
+    bt = (torch.tensor(rb).cuda(), torch.tensor(rt).cuda())
+    buf.idx[bt] = torch.tensor(oidx, dtype=torch.int32).cuda()
+    score32 = torch.tensor(osc, dtype=torch.float32)
+    buf.score[bt] = score32.cuda()
+    lse32 = torch.tensor(lse_rows, dtype=torch.float32)
+    buf.lse[bt] = lse32.cuda()
+    gen = torch.Generator().manual_seed(seed + 9)
+    dkl = torch.zeros(b, S, device="cuda")
+    dkl_rows = torch.randn(len(rows), generator=gen)
+    dkl[bt] = dkl_rows.cuda()
+    lbuf = pipeline.allocate_loss(dm, wl.torch_dtype)
+    pipeline.indexer_loss(dm, inp, buf, lbuf, wl.scale, dkl, c=c_or.cuda())
+    torch.cuda.synchronize()
+    tol = tol_of(wl.torch_dtype)
+    target = il.teacher_target(q_rows, f64(c_or), f64(lse32), oidx, wl.scale, r, rows)
+    r_kl, predict = il.kl_loss(target, f64(score32))
+    check_close("kl (sampled rows)", lbuf.kl[bt], r_kl, tol)
+    rdq, rdw, rdk, _ = il.loss_bwd(qi_rows, f64(inp["k_i"]), w_rows, oidx, r, rows, target, predict,
+                                   dkl_rows.double().numpy())
+    check_close("dq_i (sampled rows)", lbuf.dq_i[bt], rdq, tol)
+    check_close("dw (sampled rows)", lbuf.dw[bt], rdw, tol)
+    other = torch.ones(b, S, dtype=torch.bool, device="cuda")
+    other[bt] = False
+    assert torch.count_nonzero(lbuf.dq_i[other]) == 0 and torch.count_nonzero(lbuf.dw[other]) == 0
+    check_close("dk_i", lbuf.dk_i, rdk, tol)
+    del buf, lbuf, inp
+    torch.cuda.empty_cache()

@@ -139,6 +139,59 @@ def cpu_baseline(wl, inp, seed, target_rows):
                        f"bwd one thread")}
 
 
+def bench_indexer_loss(wl, dm, inp, buf, stream, K):
+    """The indexer's training path after the step's forward (not part of the
+    step): csa_indexer_loss over the selected blocks, scores and LSE the last
+    step produced, timed over K calls with events on the same stream.
+
+    Algorithmic work per (query, valid selected block): the teacher's logits
+    2*h*d, the student's recomputed <q_i, k_i> 2*HI*DI and the dq_i product
+    2*HI*DI (query kernel); the dk_i product 2*HI*DI (key-stationary kernel).
+    """
+    import torch
+    import compressed_sparse_attention_softmax_amd as csa
+    from compressed_sparse_attention_softmax_amd import pipeline
+    lbuf = pipeline.allocate_loss(dm, wl.torch_dtype)
+    dkl = torch.full((wl.b, wl.sq), 1.0 / (wl.b * wl.sq), device="cuda")
+
+    def call():
+        pipeline.indexer_loss(dm, inp, buf, lbuf, wl.scale, dkl, stream=stream)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    kms = {}
+    for k in (csa.CSA_K_LOSS_QUERY, csa.CSA_K_LOSS_KEYS, csa.CSA_K_LOSS_REDUCE):
+        csa.csa_timing_enable(k)
+        call()
+        call()
+        n, ms = csa.csa_timing_read()
+        if n:
+            kms[csa.csa_kernel_name(k)] = ms / n
+    csa.csa_timing_enable(-1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_call = e0.elapsed_time(e1) / K
+    t = torch.arange(wl.sq, device="cuda")
+    nv = torch.clamp((t + 1) // wl.ratio, max=wl.n_c).view(1, -1, 1)
+    nsel = float(((buf.idx >= 0) & (buf.idx < nv)).sum().item())
+    hd = 2.0 * wl.idx_heads * wl.idx_dim
+    work = {"loss_query": nsel * (2.0 * wl.h * wl.d + 2 * hd), "loss_keys": nsel * hd}
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    kern = {}
+    for k, fl in work.items():
+        if k in kms:
+            tf = fl / (kms[k] * 1e-3) / 1e12
+            kern[k] = {"avg_launch_ms": kms[k], "algorithmic_flop": fl, "tflops": tf, "frac": tf / peak}
+    log(f"bench: indexer loss {ms_call:.3f} ms/call; kernels(ms) {kms}")
+    return {"ms_per_call": ms_call, "selected_blocks": nsel, "kernel_ms": kms, "kernels": kern,
+            "timing": "HIP events on the launch stream; per-kernel times from the library's timing hook"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,6 +335,8 @@ def main():
                    "max_allocated_bytes": int(torch.cuda.max_memory_allocated())},
         "cpu_baseline": None,
     }
+    if wl.topk > 0:
+        result["indexer_loss"] = bench_indexer_loss(wl, dm, inp, buf, stream, K)
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on a CPU sample ...")
         result["cpu_baseline"] = cpu_baseline(wl, inp, seed, args.cpu_rows)

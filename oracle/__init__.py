@@ -12,6 +12,8 @@ Two independent formulations live here:
 * ``brute.py``: a NumPy dense formulation over the unified key axis (raw rows
   followed by compressed rows) plus a sink column, used on tiny inputs to
   cross-check the C oracle.
+* ``epilogue.py``: the compressor's epilogue (post-pool RMS norm and the
+  rotary embedding of the compressed positions) and its backward.
 * ``indexer_loss.py``: the indexer's training path (teacher target from the
   attention LSE, the student's selected scores, the KL loss and its
   gradients), plain NumPy one query row at a time.

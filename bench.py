@@ -139,6 +139,54 @@ def cpu_baseline(wl, inp, seed, target_rows):
                        f"bwd one thread")}
 
 
+def bench_compress_epilogue(wl, dm, inp, buf, stream, K):
+    """The compressor with its epilogue (RMS norm and RoPE on 64 channels,
+    base 40000), forward and backward, timed over K calls each with events
+    on the step's stream (not part of the step).  The epilogue kernel's
+    algorithmic bytes: forward, the cast rows read and written
+    (2 * b * n_c * d * e); backward, x and z over every block's span, dc read
+    and dy written (fp32)."""
+    import torch
+    import compressed_sparse_attention_softmax_amd as csa
+    D = wl.d
+    g = torch.Generator().manual_seed(3)
+    epi = dict(norm_w=(1.0 + 0.1 * torch.randn(D, generator=g)).cuda(), norm_eps=1e-6, rope_dim=min(64, D),
+               rope_base=40000.0)
+    dnw = torch.empty(D, device="cuda")
+    ws = torch.empty(max(csa.csa_compress_bwd_workspace(dm), 16), dtype=torch.uint8, device="cuda")
+    fwd = lambda: csa.csa_compress(dm, inp["x"], inp["z"], buf.c, None, stream=stream, **epi)
+    bwd = lambda: csa.csa_compress_bwd(dm, inp["x"], inp["z"], buf.dc, buf.dx, buf.dz, stream=stream,
+                                       dnorm_w=dnw, ws=ws, **epi)
+    out = {}
+    for name, fn in (("fwd", fwd), ("bwd", bwd)):
+        fn()
+        csa.csa_timing_enable(csa.CSA_K_COMPRESS_EPI)
+        fn()
+        n, ms = csa.csa_timing_read()
+        csa.csa_timing_enable(-1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[f"{name}_ms_per_call"] = e0.elapsed_time(e1) / K
+        out[f"{name}_epilogue_kernel_ms"] = ms / max(n, 1)
+    e = 2 if wl.dtype == "bf16" else 4
+    rows = wl.b * wl.n_c
+    span_rows = rows * min(wl.span, wl.sq)
+    fb = 2 * rows * D * e
+    bb = span_rows * (D + wl.z_channels) * e + rows * D * 8
+    out["fwd_epilogue_gbs"] = fb / (out["fwd_epilogue_kernel_ms"] * 1e-3) / 1e9
+    out["bwd_epilogue_gbs"] = bb / (out["bwd_epilogue_kernel_ms"] * 1e-3) / 1e9
+    out["config"] = {"norm": "rms, learned weight", "rope_dim": epi["rope_dim"], "rope_base": 40000.0}
+    # leave the step's buffers as the plain step made them
+    csa.csa_compress(dm, inp["x"], inp["z"], buf.c, None, stream=stream)
+    torch.cuda.synchronize()
+    log(f"bench: compressor with epilogue: {out}")
+    return out
+
+
 def bench_indexer_loss(wl, dm, inp, buf, stream, K):
     """The indexer's training path after the step's forward (not part of the
     step): csa_indexer_loss over the selected blocks, scores and LSE the last
@@ -337,6 +385,7 @@ def main():
     }
     if wl.topk > 0:
         result["indexer_loss"] = bench_indexer_loss(wl, dm, inp, buf, stream, K)
+    result["compress_epilogue"] = bench_compress_epilogue(wl, dm, inp, buf, stream, K)
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on a CPU sample ...")
         result["cpu_baseline"] = cpu_baseline(wl, inp, seed, args.cpu_rows)

@@ -22,7 +22,7 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_ARG", -2: "CSA_ERR_SHAPE", -3: "CSA_ERR_DTYP
           -4: "CSA_ERR_UNSUPPORTED", -5: "CSA_ERR_WORKSPACE", -6: "CSA_ERR_HIP"}
 
 # every symbol include/csa.h declares
-EXPORTS = ["csa_compress", "csa_compress_bwd", "csa_index_topk_workspace", "csa_index_topk",
+EXPORTS = ["csa_compress", "csa_compress_bwd_workspace", "csa_compress_bwd", "csa_index_topk_workspace", "csa_index_topk",
            "csa_sparse_attn_fwd", "csa_sparse_attn_bwd_workspace", "csa_sparse_attn_bwd",
            "csa_indexer_loss_workspace", "csa_indexer_loss", "csa_last_error", "csa_version", "csa_timing_enable", "csa_timing_read", "csa_kernel_name"]
 
@@ -30,6 +30,7 @@ EXPORTS = ["csa_compress", "csa_compress_bwd", "csa_index_topk_workspace", "csa_
 CSA_K_COMPRESS_FWD, CSA_K_COMPRESS_BWD, CSA_K_INDEX_TOPK, CSA_K_ATTN_FWD = 0, 1, 2, 3
 CSA_K_ATTN_DQ, CSA_K_ATTN_ROWS, CSA_K_ATTN_REDUCE = 4, 5, 6
 CSA_K_LOSS_QUERY, CSA_K_LOSS_KEYS, CSA_K_LOSS_REDUCE = 7, 8, 9
+CSA_K_COMPRESS_EPI = 10
 
 
 class CSAError(RuntimeError):
@@ -59,8 +60,10 @@ def load(path: Optional[str] = None):
     lib = ctypes.CDLL(p)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     D = ctypes.POINTER(csa_dims)
-    lib.csa_compress.argtypes = [D, i, vp, vp, i, vp, vp, vp]
-    lib.csa_compress_bwd.argtypes = [D, i, vp, vp, i, vp, vp, vp, vp]
+    lib.csa_compress.argtypes = [D, i, vp, vp, i, vp, f, i, f, vp, vp, vp]
+    lib.csa_compress_bwd_workspace.argtypes = [D]
+    lib.csa_compress_bwd_workspace.restype = sz
+    lib.csa_compress_bwd.argtypes = [D, i, vp, vp, i, vp, f, i, f, vp, vp, vp, vp, vp, sz, vp]
     lib.csa_index_topk_workspace.argtypes = [D]
     lib.csa_index_topk_workspace.restype = sz
     lib.csa_index_topk.argtypes = [D, i, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -139,18 +142,25 @@ def kprime(dims: csa_dims) -> int:
     return min(dims.topk, n_compressed(dims))
 
 
-def csa_compress(dims: csa_dims, x, z, c, c32=None, stream=None) -> None:
+def csa_compress(dims: csa_dims, x, z, c, c32=None, stream=None, norm_w=None, norm_eps: float = 1e-6,
+                 rope_dim: int = 0, rope_base: float = 40000.0) -> None:
     dt = x.dtype
     b, S, D = dims.b, dims.sq, dims.d
     zc = z.shape[-1]
     nc = n_compressed(dims)
     _call("csa_compress", ctypes.byref(dims), _dtype_code(x),
           _ptr(x, shape=(b, S, D), dtype=dt, name="x"), _ptr(z, shape=(b, S, zc), dtype=dt, name="z"),
-          zc, _ptr(c, shape=(b, nc, D), dtype=dt, name="c"),
+          zc, _ptr(norm_w, shape=(D,), dtype=torch.float32, name="norm_w"), ctypes.c_float(norm_eps),
+          int(rope_dim), ctypes.c_float(rope_base), _ptr(c, shape=(b, nc, D), dtype=dt, name="c"),
           _ptr(c32, shape=(b, nc, D), dtype=torch.float32, name="c32"), _stream(stream))
 
 
-def csa_compress_bwd(dims: csa_dims, x, z, dc, dx, dz, stream=None) -> None:
+def csa_compress_bwd_workspace(dims: csa_dims) -> int:
+    return int(load().csa_compress_bwd_workspace(ctypes.byref(dims)))
+
+
+def csa_compress_bwd(dims: csa_dims, x, z, dc, dx, dz, stream=None, norm_w=None, norm_eps: float = 1e-6,
+                     rope_dim: int = 0, rope_base: float = 40000.0, dnorm_w=None, ws=None) -> None:
     dt = x.dtype
     b, S, D = dims.b, dims.sq, dims.d
     zc = z.shape[-1]
@@ -158,9 +168,11 @@ def csa_compress_bwd(dims: csa_dims, x, z, dc, dx, dz, stream=None) -> None:
     f32 = torch.float32
     _call("csa_compress_bwd", ctypes.byref(dims), _dtype_code(x),
           _ptr(x, shape=(b, S, D), dtype=dt, name="x"), _ptr(z, shape=(b, S, zc), dtype=dt, name="z"),
-          zc, _ptr(dc, shape=(b, nc, D), dtype=f32, name="dc"),
+          zc, _ptr(norm_w, shape=(D,), dtype=f32, name="norm_w"), ctypes.c_float(norm_eps), int(rope_dim),
+          ctypes.c_float(rope_base), _ptr(dc, shape=(b, nc, D), dtype=f32, name="dc"),
           _ptr(dx, shape=(b, S, D), dtype=f32, name="dx"), _ptr(dz, shape=(b, S, zc), dtype=f32, name="dz"),
-          _stream(stream))
+          _ptr(dnorm_w, shape=(D,), dtype=f32, name="dnorm_w"), _ptr(ws, name="ws"),
+          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
 
 
 def csa_index_topk_workspace(dims: csa_dims) -> int:

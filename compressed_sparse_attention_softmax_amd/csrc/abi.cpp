@@ -106,6 +106,22 @@ csa::AttnArgs attn_args(const csa_dims* dm, const void* q, const void* kv, const
     return a;
 }
 
+int check_epilogue(const csa_dims* dm, const float* norm_w, float eps, int rope_dim, float base, const char* fn)
+{
+    if (norm_w && !(std::isfinite(eps) && eps >= 0.f))
+        return fail(CSA_ERR_ARG, "%s: norm_eps=%g must be finite and >= 0", fn, (double)eps);
+    if (rope_dim < 0 || rope_dim > dm->d || (rope_dim & 1))
+        return fail(CSA_ERR_ARG, "%s: rope_dim=%d must be even and in [0, d=%d]", fn, rope_dim, dm->d);
+    if (rope_dim > 0 && !(std::isfinite(base) && base > 0.f))
+        return fail(CSA_ERR_ARG, "%s: rope_base=%g must be finite and > 0", fn, (double)base);
+    return CSA_OK;
+}
+
+void set_epilogue(csa::CompressArgs& a, const float* norm_w, float eps, int rope_dim, float base)
+{
+    a.norm_w = norm_w; a.eps = eps; a.rope_dim = rope_dim; a.rope_base = base;
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,29 +130,52 @@ int csa_version(void) { return CSA_ABI_VERSION; }
 
 const char* csa_last_error(void) { return g_err.c_str(); }
 
-int csa_compress(const csa_dims* dm, int dtype, const void* x, const void* z, int z_channels, void* c,
-                 float* c32, void* stream)
+int csa_compress(const csa_dims* dm, int dtype, const void* x, const void* z, int z_channels, const float* norm_w,
+                 float norm_eps, int rope_dim, float rope_base, void* c, float* c32, void* stream)
 {
     int rc = check_common(dm, dtype, "csa_compress");
     if (rc) return rc;
     if ((rc = check_compress_dims(dm, z_channels, "csa_compress"))) return rc;
+    if ((rc = check_epilogue(dm, norm_w, norm_eps, rope_dim, rope_base, "csa_compress"))) return rc;
     if (!x || !z || (!c && dm->sq / dm->ratio > 0))
         return fail(CSA_ERR_ARG, "csa_compress: x, z and c must be non-NULL");
     csa::CompressArgs a = compress_args(dm, x, z, z_channels);
     a.c = c; a.c32 = c32;
+    set_epilogue(a, norm_w, norm_eps, rope_dim, rope_base);
     return hip_status(csa::compress_fwd(a, dtype == CSA_BF16, (hipStream_t)stream), "csa_compress");
 }
 
+size_t csa_compress_bwd_workspace(const csa_dims* dm)
+{
+    if (!dm || dm->b < 1 || dm->sq < 1 || dm->ratio < 1 || !supported_d(dm->d)) return 0;
+    csa::CompressArgs a = compress_args(dm, nullptr, nullptr, 1);
+    a.rope_dim = 2;                      // the epilogue's layout
+    return csa::compress_bwd_workspace_bytes(a);
+}
+
 int csa_compress_bwd(const csa_dims* dm, int dtype, const void* x, const void* z, int z_channels,
-                     const float* dc, float* dx, float* dz, void* stream)
+                     const float* norm_w, float norm_eps, int rope_dim, float rope_base, const float* dc, float* dx,
+                     float* dz, float* dnorm_w, void* ws, size_t ws_bytes, void* stream)
 {
     int rc = check_common(dm, dtype, "csa_compress_bwd");
     if (rc) return rc;
     if ((rc = check_compress_dims(dm, z_channels, "csa_compress_bwd"))) return rc;
+    if ((rc = check_epilogue(dm, norm_w, norm_eps, rope_dim, rope_base, "csa_compress_bwd"))) return rc;
     if (!x || !z || (!dc && dm->sq / dm->ratio > 0) || !dx || !dz)
         return fail(CSA_ERR_ARG, "csa_compress_bwd: x, z, dc, dx and dz must be non-NULL");
+    if (dnorm_w && !norm_w) return fail(CSA_ERR_ARG, "csa_compress_bwd: dnorm_w given without norm_w");
     csa::CompressArgs a = compress_args(dm, x, z, z_channels);
     a.dc = dc; a.dx = dx; a.dz = dz;
+    set_epilogue(a, norm_w, norm_eps, rope_dim, rope_base);
+    a.dnorm_w = dnorm_w;
+    const size_t need = csa::compress_bwd_workspace_bytes(a);
+    if (need > 0) {
+        if (!ws || ws_bytes < need)
+            return fail(CSA_ERR_WORKSPACE, "csa_compress_bwd: workspace of %zu bytes needed, %zu given", need,
+                        ws ? ws_bytes : (size_t)0);
+        if (((uintptr_t)ws) & 15) return fail(CSA_ERR_ARG, "csa_compress_bwd: workspace must be 16-byte aligned");
+    }
+    a.ws = (float*)ws;
     return hip_status(csa::compress_bwd(a, dtype == CSA_BF16, (hipStream_t)stream), "csa_compress_bwd");
 }
 

@@ -13,6 +13,18 @@
 // and weighted sum per channel, and the NS partial states are merged with
 // lane shuffles.  NS never exceeds the ratio, so every split owns at least one
 // row of every span (spans are clipped at 0 but keep at least `ratio` rows).
+//
+// Epilogue (same PR: the pooled row, cast once, goes through the
+// compressor's norm; layer configuration thread: the compressed rows get a
+// rotary embedding with base 40000): an RMS norm with a per-channel weight,
+// then the last rope_dim channels of block j's row turned in interleaved
+// pairs (2i, 2i+1) by the angle j * base^(-2i / rope_dim).  It runs in place
+// on the cast rows, one group of D/8 consecutive lanes per row (the row sum
+// by lane shuffles); angles are formed in fp64.  Its backward recomputes the
+// pooled row, applies the transposed rotation and the norm's backward, and
+// hands the gradient of the pooled rows to the pooling backward through the
+// workspace; the weight gradient is summed per workgroup and then over
+// workgroups, in a fixed order.
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
 #include "timing.hpp"
@@ -125,6 +137,157 @@ __global__ __launch_bounds__(256) void compress_fwd_kernel(const T* __restrict__
             for (int e = 0; e < 8; ++e) g.v[e] = v[e];
             store_frag(c32 + o, g);
         }
+    }
+}
+
+// --------------------------------------------------------------- epilogue
+// cos / sin of pair i of block j's rotation (fp64 angle: j * base^(-2i/rope_dim))
+__device__ __forceinline__ void rope_cs(int j, int i, int rope_dim, float base, float& cs, float& sn)
+{
+    const double ang = (double)j * pow((double)base, -2.0 * i / rope_dim);
+    double s2, c2;
+    sincos(ang, &s2, &c2);
+    cs = (float)c2;
+    sn = (float)s2;
+}
+
+// rotate (sign = 1) or rotate back (sign = -1) the pairs of channels
+// [8q, 8q+8) that lie in the last rope_dim channels
+template <int D>
+__device__ __forceinline__ void rope8(float* v, int q, int j, int rope_dim, float base, float sign)
+{
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+        const int ch = 8 * q + 2 * pr;
+        if (ch >= D - rope_dim) {
+            float cs, sn;
+            rope_cs(j, (ch - (D - rope_dim)) / 2, rope_dim, base, cs, sn);
+            sn *= sign;
+            const float x0 = v[2 * pr], x1 = v[2 * pr + 1];
+            v[2 * pr] = x0 * cs - x1 * sn;
+            v[2 * pr + 1] = x0 * sn + x1 * cs;
+        }
+    }
+}
+
+// sum over the D/8 lanes of a row group (consecutive lanes of one wave)
+template <int D>
+__device__ __forceinline__ float group_sum(float v)
+{
+#pragma unroll
+    for (int o = 1; o < D / 8; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// in place on the cast pooled rows c [rows, D]
+template <typename T, int D>
+__global__ __launch_bounds__(256) void compress_epi_fwd_kernel(T* __restrict__ c, const float* __restrict__ nw,
+                                                               float eps, int rope_dim, float base, int64_t rows,
+                                                               int nc)
+{
+    constexpr int G = D / 8;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool live = gid < rows * G;             // whole groups share liveness
+    const int64_t gg = live ? gid : 0;
+    const int q = (int)(gg % G);
+    const int64_t bj = gg / G;
+    const int j = (int)(bj % nc);
+    float v[8];
+    load8(c + bj * D + 8 * q, v);
+    if (nw) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+        const float inv = rsqrtf(group_sum<D>(ss) / D + eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = v[e] * inv * nw[8 * q + e];
+    }
+    rope8<D>(v, q, j, rope_dim, base, 1.f);
+    if (live) {
+        Frag<T> f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f.v[e] = from_f32<T>(v[e]);
+        store_frag(c + bj * D + 8 * q, f);
+    }
+}
+
+// dy (gradient of the pooled rows) into the workspace; per-workgroup sums of
+// the weight gradient into `wpart` [gridDim.x, D]
+template <typename T, int D>
+__global__ __launch_bounds__(256) void compress_epi_bwd_kernel(const T* __restrict__ x, const T* __restrict__ z,
+                                                               int zc, const float* __restrict__ nw, float eps,
+                                                               int rope_dim, float base,
+                                                               const float* __restrict__ dc, float* __restrict__ dy,
+                                                               float* __restrict__ wpart, int S, int r, int L,
+                                                               int64_t rows, int nc)
+{
+    constexpr int G = D / 8, RPW = 256 / G;
+    __shared__ float dws[RPW * D];
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool live = gid < rows * G;
+    const int64_t gg = live ? gid : 0;
+    const int q = (int)(gg % G);
+    const int64_t bj = gg / G;
+    const int j = (int)(bj % nc), bi = (int)(bj / nc);
+    const int hi = (j + 1) * r, lo = max(0, hi - L);
+    float m[8], s[8], a[8], y[8], g[8];
+    span_state<T, D, 1>(x, z, zc, (int64_t)bi * S, lo, hi, q, 0, m, s, a);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = to_f32(from_f32<T>(a[e] / s[e]));   // the cast pooled row
+    const Frag<float> df = load_frag(dc + bj * D + 8 * q);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) g[e] = df.v[e];
+    rope8<D>(g, q, j, rope_dim, base, -1.f);          // transpose of the rotation
+    float out[8], dwv[8];
+    if (nw) {
+        float ss = 0.f, sg = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ss += y[e] * y[e];
+            sg += nw[8 * q + e] * g[e] * y[e];
+        }
+        ss = group_sum<D>(ss);
+        sg = group_sum<D>(sg);
+        const float inv = rsqrtf(ss / D + eps);
+        const float k3 = inv * inv * inv * sg / D;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            out[e] = inv * nw[8 * q + e] * g[e] - k3 * y[e];
+            dwv[e] = live ? g[e] * y[e] * inv : 0.f;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { out[e] = g[e]; dwv[e] = 0.f; }
+    }
+    if (live) {
+        Frag<float> f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f.v[e] = out[e];
+        store_frag(dy + bj * D + 8 * q, f);
+    }
+    if (wpart) {                                      // uniform over the workgroup
+        // slot of this lane in the workgroup's rows (lanes past the last row
+        // write their zeros to their own slot too)
+        const int rw = (int)threadIdx.x / G, ql = (int)threadIdx.x % G;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dws[rw * D + 8 * ql + e] = dwv[e];
+        __syncthreads();
+        for (int ch = threadIdx.x; ch < D; ch += 256) {
+            float acc = 0.f;
+            for (int k = 0; k < RPW; ++k) acc += dws[k * D + ch];
+            wpart[(int64_t)blockIdx.x * D + ch] = acc;
+        }
+    }
+}
+
+// weight gradient: sum of the per-workgroup parts in workgroup order
+__global__ __launch_bounds__(256) void compress_epi_wsum_kernel(const float* __restrict__ wpart, int nparts, int D,
+                                                                float* __restrict__ dnw)
+{
+    for (int ch = threadIdx.x; ch < D; ch += 256) {
+        float acc = 0.f;
+        for (int k = 0; k < nparts; ++k) acc += wpart[(int64_t)k * D + ch];
+        dnw[ch] = acc;
     }
 }
 
@@ -295,29 +458,85 @@ hipError_t launch_compress_bwd(const CompressArgs& p, hipStream_t st)
     }
 }
 
+bool has_epilogue(const CompressArgs& p) { return p.norm_w || p.rope_dim > 0; }
+
+int64_t epi_parts(const CompressArgs& p) { return ((int64_t)p.b * p.nc * (p.D / 8) + 255) / 256; }
+
+template <typename T, int D>
+hipError_t launch_epi_fwd(const CompressArgs& p, hipStream_t st)
+{
+    const int64_t rows = (int64_t)p.b * p.nc;
+    TimedLaunch tl(K_COMPRESS_EPI, st);
+    hipLaunchKernelGGL((compress_epi_fwd_kernel<T, D>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0,
+                       st, (T*)p.c, p.norm_w, p.eps, p.rope_dim, p.rope_base, rows, p.nc);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t compress_fwd_d(const CompressArgs& p, hipStream_t st)
+{
+    hipError_t e = launch_compress_fwd<T, D>(p, st);
+    if (e != hipSuccess || !has_epilogue(p)) return e;
+    return launch_epi_fwd<T, D>(p, st);
+}
+
+// epilogue backward: dy into the workspace, then the pooling backward from dy
+template <typename T, int D>
+hipError_t compress_bwd_d(const CompressArgs& p, hipStream_t st)
+{
+    if (!has_epilogue(p)) return launch_compress_bwd<T, D>(p, st);
+    const int64_t rows = (int64_t)p.b * p.nc;
+    const int64_t parts = epi_parts(p);
+    float* dy = p.ws;
+    float* wpart = p.dnorm_w ? p.ws + rows * D : nullptr;
+    {
+        TimedLaunch tl(K_COMPRESS_EPI, st);
+        hipLaunchKernelGGL((compress_epi_bwd_kernel<T, D>), dim3((unsigned)parts), dim3(256), 0, st, (const T*)p.x,
+                           (const T*)p.z, p.zc, p.norm_w, p.eps, p.rope_dim, p.rope_base, p.dc, dy, wpart, p.S, p.r,
+                           p.L, rows, p.nc);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (wpart) {
+            hipLaunchKernelGGL(compress_epi_wsum_kernel, dim3(1), dim3(256), 0, st, wpart, (int)parts, D, p.dnorm_w);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    }
+    CompressArgs q = p;
+    q.dc = dy;
+    return launch_compress_bwd<T, D>(q, st);
+}
+
 }  // namespace
+
+size_t compress_bwd_workspace_bytes(const CompressArgs& p)
+{
+    if (!has_epilogue(p) || p.nc == 0) return 0;
+    return (size_t)((int64_t)p.b * p.nc * p.D + epi_parts(p) * p.D) * sizeof(float);
+}
 
 hipError_t compress_fwd(const CompressArgs& p, bool bf16, hipStream_t st)
 {
     if (p.nc == 0) return hipSuccess;
     switch (p.D) {
-    case 64: return bf16 ? launch_compress_fwd<bf16_t, 64>(p, st) : launch_compress_fwd<float, 64>(p, st);
-    case 128: return bf16 ? launch_compress_fwd<bf16_t, 128>(p, st) : launch_compress_fwd<float, 128>(p, st);
-    case 512: return bf16 ? launch_compress_fwd<bf16_t, 512>(p, st) : launch_compress_fwd<float, 512>(p, st);
+    case 64: return bf16 ? compress_fwd_d<bf16_t, 64>(p, st) : compress_fwd_d<float, 64>(p, st);
+    case 128: return bf16 ? compress_fwd_d<bf16_t, 128>(p, st) : compress_fwd_d<float, 128>(p, st);
+    case 512: return bf16 ? compress_fwd_d<bf16_t, 512>(p, st) : compress_fwd_d<float, 512>(p, st);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t compress_bwd(const CompressArgs& p, bool bf16, hipStream_t st)
 {
-    if (p.nc == 0) {     // no block: every gradient row is zero
+    if (p.nc == 0) {     // no block: every gradient row is zero, and so is the weight gradient
         hipError_t e = zero_fill(p.dx, (size_t)p.b * p.S * p.D, st);
-        return e != hipSuccess ? e : zero_fill(p.dz, (size_t)p.b * p.S * p.zc, st);
+        if (e == hipSuccess) e = zero_fill(p.dz, (size_t)p.b * p.S * p.zc, st);
+        if (e == hipSuccess && p.dnorm_w) e = zero_fill(p.dnorm_w, (size_t)p.D, st);
+        return e;
     }
     switch (p.D) {
-    case 64: return bf16 ? launch_compress_bwd<bf16_t, 64>(p, st) : launch_compress_bwd<float, 64>(p, st);
-    case 128: return bf16 ? launch_compress_bwd<bf16_t, 128>(p, st) : launch_compress_bwd<float, 128>(p, st);
-    case 512: return bf16 ? launch_compress_bwd<bf16_t, 512>(p, st) : launch_compress_bwd<float, 512>(p, st);
+    case 64: return bf16 ? compress_bwd_d<bf16_t, 64>(p, st) : compress_bwd_d<float, 64>(p, st);
+    case 128: return bf16 ? compress_bwd_d<bf16_t, 128>(p, st) : compress_bwd_d<float, 128>(p, st);
+    case 512: return bf16 ? compress_bwd_d<bf16_t, 512>(p, st) : compress_bwd_d<float, 512>(p, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -19,6 +19,13 @@ struct CompressArgs {
     float* dx;
     float* dz;
     int b, S, D, r, L, nc;
+    // epilogue: RMS norm weight [D] (nullptr: no norm), rotated trailing channels (0: none)
+    const float* norm_w;
+    float eps;
+    int rope_dim;
+    float rope_base;
+    float* dnorm_w;       // [D] weight gradient (backward; nullptr: not wanted)
+    float* ws;            // backward workspace when the epilogue is on
 };
 
 struct IndexArgs {
@@ -71,6 +78,7 @@ struct LossArgs {
 
 hipError_t compress_fwd(const CompressArgs& p, bool bf16, hipStream_t st);
 hipError_t compress_bwd(const CompressArgs& p, bool bf16, hipStream_t st);
+size_t compress_bwd_workspace_bytes(const CompressArgs& p);
 hipError_t index_topk(const IndexArgs& p, bool bf16, hipStream_t st);
 int index_topk_cap(const IndexArgs& p, bool bf16);
 size_t topk_lds_bytes(int DI, int elem, int cap);

@@ -92,7 +92,7 @@ const char* csa_kernel_name(int kernel)
 {
     static const char* names[csa::K_COUNT] = {"compress_fwd", "compress_bwd", "index_topk", "attn_query_fwd",
                                                "attn_query_dq", "attn_rows", "attn_reduce", "loss_query",
-                                               "loss_keys", "loss_reduce"};
+                                               "loss_keys", "loss_reduce", "compress_epilogue"};
     return (kernel >= 0 && kernel < csa::K_COUNT) ? names[kernel] : "";
 }
 

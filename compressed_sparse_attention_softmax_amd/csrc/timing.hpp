@@ -19,7 +19,8 @@ enum KernelId {
     K_LOSS_QUERY = 7,
     K_LOSS_KEYS = 8,
     K_LOSS_REDUCE = 9,
-    K_COUNT = 10,
+    K_COMPRESS_EPI = 10,
+    K_COUNT = 11,
 };
 
 // RAII bracket around one launch: records the start event at construction and

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 3
+#define CSA_ABI_VERSION 4
 
 enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 };
 
@@ -103,18 +103,44 @@ typedef struct csa_dims {
  * weights).  For block j < n_c and channel c:
  *   alpha_u = softmax over u in span(j) of z[u, c]   (z[u, 0] if z_channels == 1)
  *   c32[j, c] = sum_u alpha_u * x[u, c]               (fp32 weights and sum)
- *   c[j, c]   = c32[j, c] rounded once to dtype.
- * z_channels is 1 or d.  c32 may be NULL. */
+ *   y[j, c]   = c32[j, c] rounded once to dtype.
+ * Epilogue (same PR: the compressor's norm after the cast; the compressed
+ * rows' rotary embedding with its own base, 40000 in the layer
+ * configuration), applied when norm_w != NULL or rope_dim > 0:
+ *   n[j, c] = y[j, c] / sqrt(mean_c y[j, c]^2 + norm_eps) * norm_w[c]
+ *             (n = y when norm_w is NULL; norm_w is fp32 [d])
+ *   the last rope_dim channels of n turned in interleaved pairs (2i, 2i+1)
+ *   by the angle j * rope_base^(-2i / rope_dim) (block j at position j)
+ *   c[j, :] = the result rounded to dtype      (c = y without the epilogue)
+ * z_channels is 1 or d; rope_dim is even, 0 <= rope_dim <= d.  c32 (the
+ * pooled rows before the cast and the epilogue) may be NULL. */
 int csa_compress(const csa_dims* dims, int dtype, const void* x, const void* z, int z_channels,
+                 const float* norm_w, float norm_eps, int rope_dim, float rope_base,
                  void* c, float* c32, void* stream);
 
-/* Compressor backward: the gradient of the pooling above given dc (fp32,
- * [b, n_c, d]); the rounding cast is treated as the identity.
- *   dx[u, c] = sum_j alpha_{j,u,c} dc[j, c]
- *   dz[u, c] = sum_j alpha_{j,u,c} dc[j, c] (x[u, c] - c32[j, c])  (summed over c if z_channels == 1)
- * Rows u >= n_c * ratio receive zero. */
+/* Workspace bytes csa_compress_bwd needs when the epilogue is on (device
+ * memory, 16-byte aligned, caller-owned, contents on entry irrelevant): the
+ * gradient of the pooled rows and per-workgroup parts of dnorm_w.  Without
+ * the epilogue no workspace is used.  0 for invalid dims. */
+size_t csa_compress_bwd_workspace(const csa_dims* dims);
+
+/* Compressor backward: the gradient of csa_compress given dc (fp32,
+ * [b, n_c, d]), with the same epilogue arguments; the rounding casts are
+ * treated as the identity.  Through the epilogue (rotation transposed, then
+ * the norm's backward on y):
+ *   dy[j, :]  = gradient of sum(dc * c) with respect to y[j, :]
+ *   dnorm_w[c] = sum_j dn[j, c] y[j, c] / sqrt(mean y^2 + eps)   (fp32 [d], may be NULL;
+ *               must be NULL when norm_w is NULL)
+ * then through the pooling, with g = dy (g = dc without the epilogue):
+ *   dx[u, c] = sum_j alpha_{j,u,c} g[j, c]
+ *   dz[u, c] = sum_j alpha_{j,u,c} g[j, c] (x[u, c] - c32[j, c])  (summed over c if z_channels == 1)
+ * Rows u >= n_c * ratio receive zero.  ws / ws_bytes: needed only with the
+ * epilogue (CSA_ERR_WORKSPACE if then NULL or smaller than
+ * csa_compress_bwd_workspace(dims)). */
 int csa_compress_bwd(const csa_dims* dims, int dtype, const void* x, const void* z,
-                     int z_channels, const float* dc, float* dx, float* dz, void* stream);
+                     int z_channels, const float* norm_w, float norm_eps, int rope_dim,
+                     float rope_base, const float* dc, float* dx, float* dz, float* dnorm_w,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes csa_index_topk needs (0: scores never leave the chip). */
 size_t csa_index_topk_workspace(const csa_dims* dims);
@@ -223,8 +249,8 @@ int csa_version(void);
 /* ---------------------------------------------------------------- timing
  * Benchmark hook, not part of the computation.  Kernel ids of the entry
  * points above (one entry point may launch several kernels):
- *   csa_compress          -> CSA_K_COMPRESS_FWD
- *   csa_compress_bwd      -> CSA_K_COMPRESS_BWD
+ *   csa_compress          -> CSA_K_COMPRESS_FWD, CSA_K_COMPRESS_EPI (epilogue)
+ *   csa_compress_bwd      -> CSA_K_COMPRESS_EPI (epilogue), CSA_K_COMPRESS_BWD
  *   csa_index_topk        -> CSA_K_INDEX_TOPK
  *   csa_sparse_attn_fwd   -> CSA_K_ATTN_FWD
  *   csa_sparse_attn_bwd   -> CSA_K_ATTN_DQ (dq, Delta, dsink), CSA_K_ATTN_ROWS
@@ -242,7 +268,7 @@ int csa_version(void);
 enum csa_kernel_id {
     CSA_K_COMPRESS_FWD = 0, CSA_K_COMPRESS_BWD = 1, CSA_K_INDEX_TOPK = 2, CSA_K_ATTN_FWD = 3,
     CSA_K_ATTN_DQ = 4, CSA_K_ATTN_ROWS = 5, CSA_K_ATTN_REDUCE = 6, CSA_K_LOSS_QUERY = 7,
-    CSA_K_LOSS_KEYS = 8, CSA_K_LOSS_REDUCE = 9
+    CSA_K_LOSS_KEYS = 8, CSA_K_LOSS_REDUCE = 9, CSA_K_COMPRESS_EPI = 10
 };
 int csa_timing_enable(int kernel);
 int csa_timing_read(int* launches, double* total_ms);

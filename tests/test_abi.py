@@ -33,7 +33,7 @@ def test_library_exports_every_header_symbol():
     lib = _lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.csa_version() == 3
+    assert lib.csa_version() == 4
 
 
 def test_dims_struct_matches_header():
@@ -55,13 +55,13 @@ N = None
 
 
 @pytest.mark.parametrize("fn,args,code", [
-    ("csa_compress", lambda: (None, 0, P, P, 64, P, N, N), -1),
-    ("csa_compress", lambda: (ctypes.byref(_d()), 7, P, P, 64, P, N, N), -3),
-    ("csa_compress", lambda: (ctypes.byref(_d(ratio=0)), 0, P, P, 64, P, N, N), -1),
-    ("csa_compress", lambda: (ctypes.byref(_d(d=96)), 0, P, P, 96, P, N, N), -4),
-    ("csa_compress", lambda: (ctypes.byref(_d()), 0, P, P, 5, P, N, N), -2),
-    ("csa_compress", lambda: (ctypes.byref(_d()), 0, N, P, 64, P, N, N), -1),
-    ("csa_compress_bwd", lambda: (ctypes.byref(_d(sq=0)), 0, P, P, 64, P, P, P, N), -1),
+    ("csa_compress", lambda: (None, 0, P, P, 64, N, ctypes.c_float(1e-6), 0, ctypes.c_float(40000.0), P, N, N), -1),
+    ("csa_compress", lambda: (ctypes.byref(_d()), 7, P, P, 64, N, ctypes.c_float(1e-6), 0, ctypes.c_float(40000.0), P, N, N), -3),
+    ("csa_compress", lambda: (ctypes.byref(_d(ratio=0)), 0, P, P, 64, N, ctypes.c_float(1e-6), 0, ctypes.c_float(40000.0), P, N, N), -1),
+    ("csa_compress", lambda: (ctypes.byref(_d(d=96)), 0, P, P, 96, N, ctypes.c_float(1e-6), 0, ctypes.c_float(40000.0), P, N, N), -4),
+    ("csa_compress", lambda: (ctypes.byref(_d()), 0, P, P, 5, N, ctypes.c_float(1e-6), 0, ctypes.c_float(40000.0), P, N, N), -2),
+    ("csa_compress", lambda: (ctypes.byref(_d()), 0, N, P, 64, N, ctypes.c_float(1e-6), 0, ctypes.c_float(40000.0), P, N, N), -1),
+    ("csa_compress_bwd", lambda: (ctypes.byref(_d(sq=0)), 0, P, P, 64, N, ctypes.c_float(1e-6), 0, ctypes.c_float(40000.0), P, P, P, N, N, 0, N), -1),
     ("csa_index_topk", lambda: (ctypes.byref(_d(topk=0)), 0, P, P, P, N, P, N, N, 0, N), -1),
     ("csa_index_topk", lambda: (ctypes.byref(_d(idx_dim=48)), 0, P, P, P, N, P, N, N, 0, N), -4),
     ("csa_index_topk", lambda: (ctypes.byref(_d(idx_heads=65)), 0, P, P, P, N, P, N, N, 0, N), -4),
@@ -79,6 +79,30 @@ def test_validation_errors(fn, args, code):
     rc = getattr(lib, fn)(*args())
     assert rc == code, (fn, rc, lib.csa_last_error())
     assert lib.csa_last_error().decode().startswith(fn)
+
+
+@pytest.mark.parametrize("eps,rope_dim,base,code", [(float("nan"), 0, 1.0, -1), (-1.0, 0, 1.0, -1),
+                                                    (1e-6, 3, 1.0, -1), (1e-6, 66, 1.0, -1), (1e-6, 8, 0.0, -1),
+                                                    (1e-6, 8, float("inf"), -1)])
+def test_compress_epilogue_validation(eps, rope_dim, base, code):
+    lib = _lib()
+    rc = lib.csa_compress(ctypes.byref(_d()), 0, P, P, 64, P, ctypes.c_float(eps), rope_dim, ctypes.c_float(base),
+                          P, N, N)
+    assert rc == code, lib.csa_last_error()
+
+
+def test_compress_bwd_epilogue_workspace():
+    lib = _lib()
+    d = _d()
+    need = lib.csa_compress_bwd_workspace(ctypes.byref(d))
+    assert need >= 4 * d.b * (d.sq // d.ratio) * d.d
+    # with the epilogue on, a missing or short workspace is rejected before any launch
+    args = (ctypes.byref(d), 0, P, P, 64, N, ctypes.c_float(1e-6), 8, ctypes.c_float(40000.0), P, P, P, N)
+    assert lib.csa_compress_bwd(*args, N, 0, N) == -5
+    assert lib.csa_compress_bwd(*args, P, need - 4, N) == -5
+    # dnorm_w needs norm_w
+    assert lib.csa_compress_bwd(ctypes.byref(d), 0, P, P, 64, N, ctypes.c_float(1e-6), 0, ctypes.c_float(1.0),
+                                P, P, P, P, N, 0, N) == -1
 
 
 def _bwd(dq, dkv, dc, dsink, sink=P, c=P):
@@ -175,12 +199,12 @@ def test_binding_fails_loudly_without_library(tmp_path):
 def test_timing_hook_without_launches():
     # host-only paths: enabling, reading with nothing recorded, names, bad ids
     lib = _lib()
-    assert lib.csa_timing_enable(10) == -1
+    assert lib.csa_timing_enable(11) == -1
     assert lib.csa_timing_enable(-2) == -1
     assert lib.csa_timing_enable(csa.CSA_K_ATTN_ROWS) == 0
     assert csa.csa_timing_read() == (0, 0.0)
     assert lib.csa_timing_enable(-1) == 0
-    names = [csa.csa_kernel_name(k) for k in range(10)]
+    names = [csa.csa_kernel_name(k) for k in range(11)]
     assert names == ["compress_fwd", "compress_bwd", "index_topk", "attn_query_fwd", "attn_query_dq",
-                     "attn_rows", "attn_reduce", "loss_query", "loss_keys", "loss_reduce"]
+                     "attn_rows", "attn_reduce", "loss_query", "loss_keys", "loss_reduce", "compress_epilogue"]
     assert csa.csa_kernel_name(99) == ""

@@ -73,6 +73,56 @@ def test_compress_fwd_bwd(gpu, name, wl):
     check_close("dz", dz, rdz, tol)
 
 
+EPI_CASES = [
+    ("tiny_f32_norm_rope_all", TINY, dict(norm=True, rope_dim=64)),
+    ("tiny_f32_rope_only", TINY.replace(sq=203, span=12), dict(norm=False, rope_dim=16)),
+    ("csa4_bf16_norm_rope64", CSA4_SMALL, dict(norm=True, rope_dim=64)),
+    ("csa4_bf16_rowscore_norm", CSA4_SMALL.replace(z_channels=1), dict(norm=True, rope_dim=0)),
+    ("csa4_bf16_frozen_norm_weight", CSA4_SMALL.replace(sq=500), dict(norm=True, rope_dim=64, want_dw=False)),
+    ("d512_bf16_norm_rope64", D512_SMALL, dict(norm=True, rope_dim=64)),
+    ("hca128_bf16_norm_rope64", HCA_SMALL, dict(norm=True, rope_dim=64)),
+    ("shorter_than_ratio", TINY.replace(sq=3), dict(norm=True, rope_dim=8)),
+]
+
+
+@pytest.mark.parametrize("name,wl,kw", EPI_CASES, ids=[c[0] for c in EPI_CASES])
+def test_compress_epilogue(gpu, name, wl, kw):
+    from oracle import epilogue as ep
+    csa = gpu
+    say(f"[compress epilogue] {name} sq={wl.sq} d={wl.d} r={wl.ratio} L={wl.span} zc={wl.z_channels} {kw}")
+    inp = csa_synth.make_inputs(wl, 13, device="cuda", parts=("compress",))
+    dm = csa.dims_of(wl)
+    b, S, D, nc = wl.b, wl.sq, wl.d, wl.n_c
+    g = torch.Generator().manual_seed(17)
+    nw = (1.0 + 0.2 * torch.randn(D, generator=g)) if kw["norm"] else None
+    eps, rope, base = 1e-6, kw["rope_dim"], 40000.0
+    epi = dict(norm_w=None if nw is None else nw.cuda(), norm_eps=eps, rope_dim=rope, rope_base=base)
+    c = torch.empty(b, nc, D, dtype=wl.torch_dtype, device="cuda")
+    c32 = torch.empty(b, nc, D, dtype=torch.float32, device="cuda")
+    csa.csa_compress(dm, inp["x"], inp["z"], c, c32, **epi)
+    dc = torch.randn(b, nc, D, generator=g).cuda()
+    dx = torch.full((b, S, D), 7.0, device="cuda")
+    dz = torch.full((b, S, wl.z_channels), 7.0, device="cuda")
+    want_dw = kw.get("want_dw", True) and nw is not None
+    dnw = torch.full((D,), 7.0, device="cuda") if want_dw else None
+    ws = torch.empty(csa.csa_compress_bwd_workspace(dm), dtype=torch.uint8, device="cuda")
+    csa.csa_compress_bwd(dm, inp["x"], inp["z"], dc, dx, dz, dnorm_w=dnw, ws=ws, **epi)
+    torch.cuda.synchronize()
+    x64, z64 = f64(inp["x"]), f64(inp["z"])
+    pooled = oracle.compress(x64, z64, wl.ratio, wl.span)
+    w64 = None if nw is None else nw.double().numpy()
+    ref = ep.epilogue(pooled, w64, eps, rope, base)
+    dy, rdw = ep.epilogue_bwd(pooled, w64, eps, rope, base, f64(dc))
+    rdx, rdz = oracle.compress_bwd(x64, z64, dy, wl.ratio, wl.span)
+    tol = tol_of(wl.torch_dtype)
+    check_close("c32 (pooled, before the epilogue)", c32, pooled, tol)
+    check_close("c", c, ref, tol)
+    check_close("dx", dx, rdx, tol)
+    check_close("dz", dz, rdz, tol)
+    if want_dw:
+        check_close("dnorm_w", dnw, rdw if nc > 0 else np.zeros(D), tol)
+
+
 # ------------------------------------------------------------ indexer / top-k
 def _index_case(wl, seed, rows=None, doc=None, **over):
     import compressed_sparse_attention_softmax_amd as csa

@@ -14,6 +14,8 @@ Two independent formulations live here:
   cross-check the C oracle.
 * ``epilogue.py``: the compressor's epilogue (post-pool RMS norm and the
   rotary embedding of the compressed positions) and its backward.
+* ``dsa_gqa.py``: the simplified DSA over grouped-query attention (attention
+  over the keys a one-head, unit-weight indexer selected at full resolution).
 * ``indexer_loss.py``: the indexer's training path (teacher target from the
   attention LSE, the student's selected scores, the KL loss and its
   gradients), plain NumPy one query row at a time.

@@ -24,7 +24,8 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_ARG", -2: "CSA_ERR_SHAPE", -3: "CSA_ERR_DTYP
 # every symbol include/csa.h declares
 EXPORTS = ["csa_compress", "csa_compress_bwd_workspace", "csa_compress_bwd", "csa_index_topk_workspace", "csa_index_topk",
            "csa_sparse_attn_fwd", "csa_sparse_attn_bwd_workspace", "csa_sparse_attn_bwd",
-           "csa_indexer_loss_workspace", "csa_indexer_loss", "csa_last_error", "csa_version", "csa_timing_enable", "csa_timing_read", "csa_kernel_name"]
+           "csa_indexer_loss_workspace", "csa_indexer_loss", "csa_dsa_gqa_workspace", "csa_dsa_gqa_fwd",
+           "csa_dsa_gqa_bwd", "csa_last_error", "csa_version", "csa_timing_enable", "csa_timing_read", "csa_kernel_name"]
 
 # kernel ids of the timing hook (enum csa_kernel_id)
 CSA_K_COMPRESS_FWD, CSA_K_COMPRESS_BWD, CSA_K_INDEX_TOPK, CSA_K_ATTN_FWD = 0, 1, 2, 3
@@ -42,6 +43,10 @@ class CSAError(RuntimeError):
 class csa_dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("b", "sq", "h", "d", "ratio", "span", "window", "idx_heads", "idx_dim", "topk")]
+
+
+class csa_gqa_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("b", "sq", "h", "h_kv", "d_qk", "d_v", "topk")]
 
 
 _lib = None
@@ -74,6 +79,11 @@ def load(path: Optional[str] = None):
     lib.csa_indexer_loss_workspace.argtypes = [D]
     lib.csa_indexer_loss_workspace.restype = sz
     lib.csa_indexer_loss.argtypes = [D, i, vp, vp, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, sz, vp]
+    GD = ctypes.POINTER(csa_gqa_dims)
+    lib.csa_dsa_gqa_workspace.argtypes = [GD, i, i]
+    lib.csa_dsa_gqa_workspace.restype = sz
+    lib.csa_dsa_gqa_fwd.argtypes = [GD, i, vp, vp, vp, vp, f, vp, vp, vp, sz, vp]
+    lib.csa_dsa_gqa_bwd.argtypes = [GD, i, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.csa_last_error.argtypes = []
     lib.csa_last_error.restype = ctypes.c_char_p
     lib.csa_version.argtypes = []
@@ -82,7 +92,7 @@ def load(path: Optional[str] = None):
     lib.csa_kernel_name.argtypes = [i]
     lib.csa_kernel_name.restype = ctypes.c_char_p
     for fn in ("csa_compress", "csa_compress_bwd", "csa_index_topk", "csa_sparse_attn_fwd",
-               "csa_sparse_attn_bwd", "csa_indexer_loss", "csa_version", "csa_timing_enable", "csa_timing_read"):
+               "csa_sparse_attn_bwd", "csa_indexer_loss", "csa_dsa_gqa_fwd", "csa_dsa_gqa_bwd", "csa_version", "csa_timing_enable", "csa_timing_read"):
         getattr(lib, fn).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -259,6 +269,38 @@ def csa_indexer_loss(dims: csa_dims, q, c, lse, q_i, k_i, w, idx, score, scale: 
           _ptr(dq_i, shape=(b, S, HI, DI), dtype=dt, name="dq_i"), _ptr(dw, shape=(b, S, HI), dtype=f32, name="dw"),
           _ptr(dk_i, shape=(b, nc, DI), dtype=f32, name="dk_i"), _ptr(ws, name="ws"),
           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def csa_dsa_gqa_workspace(g: csa_gqa_dims, dtype: torch.dtype, backward: bool) -> int:
+    code = CSA_BF16 if dtype == torch.bfloat16 else CSA_F32
+    return int(load().csa_dsa_gqa_workspace(ctypes.byref(g), code, int(backward)))
+
+
+def _gqa_shapes(g: csa_gqa_dims):
+    b, S = g.b, g.sq
+    return dict(q=(b, S, g.h, g.d_qk), k=(b, S, g.h_kv, g.d_qk), v=(b, S, g.h_kv, g.d_v), out=(b, S, g.h, g.d_v),
+                lse=(b, S, g.h), idx=(b, S, min(g.topk, g.sq)))
+
+
+def csa_dsa_gqa_fwd(g: csa_gqa_dims, q, k, v, idx, scale: float, out, lse, ws, stream=None) -> None:
+    sh, dt = _gqa_shapes(g), q.dtype
+    _call("csa_dsa_gqa_fwd", ctypes.byref(g), _dtype_code(q), _ptr(q, shape=sh["q"], dtype=dt, name="q"),
+          _ptr(k, shape=sh["k"], dtype=dt, name="k"), _ptr(v, shape=sh["v"], dtype=dt, name="v"),
+          _ptr(idx, shape=sh["idx"], dtype=torch.int32, name="idx"), ctypes.c_float(scale),
+          _ptr(out, shape=sh["out"], dtype=dt, name="out"), _ptr(lse, shape=sh["lse"], dtype=torch.float32, name="lse"),
+          _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def csa_dsa_gqa_bwd(g: csa_gqa_dims, q, k, v, idx, scale: float, out, lse, dout, dq, dk, dv, ws,
+                    stream=None) -> None:
+    sh, dt, f32 = _gqa_shapes(g), q.dtype, torch.float32
+    _call("csa_dsa_gqa_bwd", ctypes.byref(g), _dtype_code(q), _ptr(q, shape=sh["q"], dtype=dt, name="q"),
+          _ptr(k, shape=sh["k"], dtype=dt, name="k"), _ptr(v, shape=sh["v"], dtype=dt, name="v"),
+          _ptr(idx, shape=sh["idx"], dtype=torch.int32, name="idx"), ctypes.c_float(scale),
+          _ptr(out, shape=sh["out"], dtype=dt, name="out"), _ptr(lse, shape=sh["lse"], dtype=f32, name="lse"),
+          _ptr(dout, shape=sh["out"], dtype=dt, name="dout"), _ptr(dq, shape=sh["q"], dtype=dt, name="dq"),
+          _ptr(dk, shape=sh["k"], dtype=f32, name="dk"), _ptr(dv, shape=sh["v"], dtype=f32, name="dv"),
+          _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
 
 
 def csa_last_error() -> str:

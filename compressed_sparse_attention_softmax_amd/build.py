@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
 
-SOURCES = ["compress.hip", "index_topk.hip", "attn.hip", "indexer_loss.hip", "abi.cpp", "timing.cpp"]
+SOURCES = ["compress.hip", "index_topk.hip", "attn.hip", "indexer_loss.hip", "dsa_gqa.hip", "abi.cpp", "timing.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -198,7 +198,7 @@ int csa_index_topk(const csa_dims* dm, int dtype, const void* q_i, const void* k
     if (dm->idx_heads > 64) return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: idx_heads=%d > 64", dm->idx_heads);
     if (dm->idx_dim != 32 && dm->idx_dim != 64 && dm->idx_dim != 128)
         return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: idx_dim=%d not in {32,64,128}", dm->idx_dim);
-    if (!q_i || !k_i || !w || !idx) return fail(CSA_ERR_ARG, "csa_index_topk: q_i, k_i, w and idx must be non-NULL");
+    if (!q_i || !k_i || !idx) return fail(CSA_ERR_ARG, "csa_index_topk: q_i, k_i and idx must be non-NULL");
     const int kp = kprime(dm);
     if (kp > 2048) return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: K'=%d > 2048", kp);
     csa::IndexArgs a{};
@@ -344,6 +344,89 @@ int csa_indexer_loss(const csa_dims* dm, int dtype, const void* q, const void* c
         if (((uintptr_t)ws) & 15) return fail(CSA_ERR_ARG, "csa_indexer_loss: workspace must be 16-byte aligned");
     }
     return hip_status(csa::indexer_loss(a, dtype == CSA_BF16, (float*)ws, (hipStream_t)stream), "csa_indexer_loss");
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_gqa(const csa_gqa_dims* g, int dtype, const char* fn)
+{
+    if (!g) return fail(CSA_ERR_ARG, "%s: dims is NULL", fn);
+    if (dtype != CSA_F32 && dtype != CSA_BF16) return fail(CSA_ERR_DTYPE, "%s: unknown dtype %d", fn, dtype);
+    if (g->b < 1 || g->sq < 1 || g->h < 1 || g->h_kv < 1 || g->d_qk < 1 || g->d_v < 1 || g->topk < 1)
+        return fail(CSA_ERR_ARG, "%s: b, sq, h, h_kv, d_qk, d_v and topk must be >= 1", fn);
+    if (g->h % g->h_kv) return fail(CSA_ERR_SHAPE, "%s: h=%d is not a multiple of h_kv=%d", fn, g->h, g->h_kv);
+    if (g->h / g->h_kv > 64) return fail(CSA_ERR_UNSUPPORTED, "%s: %d query heads per group > 64", fn, g->h / g->h_kv);
+    if (g->d_qk % 8 || g->d_v % 8) return fail(CSA_ERR_UNSUPPORTED, "%s: d_qk and d_v must be multiples of 8", fn);
+    const int dp = g->d_qk + g->d_v;
+    const bool ok = dtype == CSA_BF16 ? (dp == 64 || dp == 128 || dp == 256 || dp == 512) : (dp == 64 || dp == 128);
+    if (!ok)
+        return fail(CSA_ERR_UNSUPPORTED, "%s: d_qk + d_v = %d not in {64,128,256,512} (bf16) / {64,128} (fp32)", fn,
+                    dp);
+    if ((g->topk < g->sq ? g->topk : g->sq) > 2048) return fail(CSA_ERR_UNSUPPORTED, "%s: K' > 2048", fn);
+    return CSA_OK;
+}
+
+csa::GqaArgs gqa_args(const csa_gqa_dims* g)
+{
+    csa::GqaArgs a{};
+    a.b = g->b; a.S = g->sq; a.H = g->h; a.HKV = g->h_kv; a.DK = g->d_qk; a.DV = g->d_v;
+    a.kp = g->topk < g->sq ? g->topk : g->sq;
+    return a;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need, const char* fn)
+{
+    if (!ws || ws_bytes < need)
+        return fail(CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : (size_t)0);
+    if (((uintptr_t)ws) & 255) return fail(CSA_ERR_ARG, "%s: workspace must be 256-byte aligned", fn);
+    return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t csa_dsa_gqa_workspace(const csa_gqa_dims* g, int dtype, int backward)
+{
+    if (!g || g->b < 1 || g->sq < 1 || g->h < 1 || g->h_kv < 1 || g->h % g->h_kv || g->topk < 1) return 0;
+    const csa::GqaArgs a = gqa_args(g);
+    return csa::dsa_gqa_workspace_bytes(a, dtype == CSA_BF16, backward != 0);
+}
+
+int csa_dsa_gqa_fwd(const csa_gqa_dims* g, int dtype, const void* q, const void* k, const void* v,
+                    const int32_t* idx, float scale, void* out, float* lse, void* ws, size_t ws_bytes, void* stream)
+{
+    int rc = check_gqa(g, dtype, "csa_dsa_gqa_fwd");
+    if (rc) return rc;
+    if (!q || !k || !v || !idx || !out || !lse)
+        return fail(CSA_ERR_ARG, "csa_dsa_gqa_fwd: q, k, v, idx, out and lse must be non-NULL");
+    if (!std::isfinite(scale)) return fail(CSA_ERR_ARG, "csa_dsa_gqa_fwd: scale is not finite");
+    csa::GqaArgs a = gqa_args(g);
+    a.q = q; a.k = k; a.v = v; a.idx = idx; a.scale = scale; a.out = out; a.lse = lse;
+    if ((rc = check_ws(ws, ws_bytes, csa::dsa_gqa_workspace_bytes(a, dtype == CSA_BF16, false), "csa_dsa_gqa_fwd")))
+        return rc;
+    return hip_status(csa::dsa_gqa_fwd(a, dtype == CSA_BF16, ws, (hipStream_t)stream), "csa_dsa_gqa_fwd");
+}
+
+int csa_dsa_gqa_bwd(const csa_gqa_dims* g, int dtype, const void* q, const void* k, const void* v,
+                    const int32_t* idx, float scale, const void* out, const float* lse, const void* dout, void* dq,
+                    float* dk, float* dv, void* ws, size_t ws_bytes, void* stream)
+{
+    int rc = check_gqa(g, dtype, "csa_dsa_gqa_bwd");
+    if (rc) return rc;
+    if (!q || !k || !v || !idx || !out || !lse || !dout)
+        return fail(CSA_ERR_ARG, "csa_dsa_gqa_bwd: q, k, v, idx, out, lse and dout must be non-NULL");
+    if (!dq || !dk || !dv)
+        return fail(CSA_ERR_ARG, "csa_dsa_gqa_bwd: gradient gate: dq, dk and dv must all be given");
+    if (!std::isfinite(scale)) return fail(CSA_ERR_ARG, "csa_dsa_gqa_bwd: scale is not finite");
+    csa::GqaArgs a = gqa_args(g);
+    a.q = q; a.k = k; a.v = v; a.idx = idx; a.scale = scale; a.out = const_cast<void*>(out);
+    a.lse = const_cast<float*>(lse); a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
+    if ((rc = check_ws(ws, ws_bytes, csa::dsa_gqa_workspace_bytes(a, dtype == CSA_BF16, true), "csa_dsa_gqa_bwd")))
+        return rc;
+    return hip_status(csa::dsa_gqa_bwd(a, dtype == CSA_BF16, ws, (hipStream_t)stream), "csa_dsa_gqa_bwd");
 }
 
 }  // extern "C"

@@ -422,14 +422,15 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
         const int h = h0 + 16 * ht + n16;
         if (h >= p.H) continue;
         if constexpr (!DQ) {
+            // no candidate and no sink (possible without a window): O = 0, LSE = -inf
             const float lt = lsum[ht][0];
-            const float inv = 1.f / lt;
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
             T* orow = (T*)p.out + (qrow * p.H + h) * D;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) orow[16 * dt + 4 * g + i] = from_f32<T>(o[dt][ht][i] * inv);
-            if (g == 0) p.lse[qrow * p.H + h] = (m2[ht] + log2f(lt)) * LN2;
+            if (g == 0) p.lse[qrow * p.H + h] = lt > 0.f ? (m2[ht] + log2f(lt)) * LN2 : -INFINITY;
         } else {
             T* drow = (T*)p.dq + (qrow * p.H + h) * D;
 #pragma unroll
@@ -607,7 +608,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
             const int h = threadIdx.x;
             // initial values of the S and dP accumulators of head h: the logit
             // offset -lse/scale (so that scale*log2e*S' = log2 P) and -Delta
-            lse_lds[buf * HP + h] = h < p.H ? -p.lse[qrow * p.H + h] / p.scale : -INFINITY;
+            // (a query with no candidate has LSE = -inf and multiplicity 0 everywhere:
+            // any finite offset keeps its P at 0)
+            const float l = h < p.H ? p.lse[qrow * p.H + h] : 0.f;
+            lse_lds[buf * HP + h] = h < p.H ? (l > -INFINITY ? -l / p.scale : 0.f) : -INFINITY;
             dlt_lds[buf * HP + h] = h < p.H ? -delta[qrow * p.H + h] : 0.f;
         }
         if (!win) {
@@ -819,7 +823,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs p, RowsGeom g
         const int64_t row = tid / V;
         const int bi = (int)(row / p.S), u = (int)(row % p.S);
         const int q_lo = u / geo.Qb;
-        const int q_hi = min(geo.nqb - 1, (u + p.W - 1) / geo.Qb);
+        const int q_hi = p.W > 0 ? min(geo.nqb - 1, (u + p.W - 1) / geo.Qb) : q_lo - 1;   // no window: zero
         float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
         for (int q = q_lo; q <= q_hi; ++q) {
@@ -865,13 +869,13 @@ RowsGeom rows_geometry(const AttnArgs& p)
     const int64_t D = p.D;
     auto part_floats = [&](int qb) {
         const int nqb = (p.S + qb - 1) / qb;
-        return (int64_t)p.b * nqb * ((int64_t)(p.W - 1 + qb) + p.nc) * D;
+        return (int64_t)p.b * nqb * ((int64_t)(p.W > 0 ? p.W - 1 + qb : 0) + p.nc) * D;
     };
     int qb = 32;
     while (qb < 1024 && part_floats(qb) * 4 > ((int64_t)1 << 30)) qb *= 2;
     g.Qb = qb;
     g.nqb = (p.S + qb - 1) / qb;
-    g.WB = p.W - 1 + qb;
+    g.WB = p.W > 0 ? p.W - 1 + qb : 0;           // no window: no band rows
     g.n_wt = (g.WB + g.TR - 1) / g.TR;
     g.n_ct = p.nc > 0 ? (p.nc + g.TR - 1) / g.TR : 0;
     const int64_t delta_floats = ((int64_t)p.b * p.S * p.H + 63) / 64 * 64;
@@ -885,7 +889,10 @@ template <typename T, int D, int HT>
 hipError_t launch_query(const AttnArgs& p, bool dq, float* delta, float* csink, hipStream_t st)
 {
     const int gper = (p.H + 16 * HT - 1) / (16 * HT);
-    const int G = gper <= 1 ? 1 : (gper <= 2 ? 2 : 4);
+    int G = gper <= 1 ? 1 : (gper <= 2 ? 2 : 4);
+    // wide rows with few heads: fewer queries per workgroup so the tiles fit
+    // (the extra waves hold no head and only help gather rows)
+    while (G < 4 && (size_t)(4 / G) * 2 * chunk_bytes<T, D>() > (size_t)ATTN_LDS_LIMIT) G *= 2;
     const int qpw = 4 / G;
     // two chunk tiles per query of the workgroup, then (when they fit) the index rows
     size_t lds = (size_t)qpw * 2 * chunk_bytes<T, D>();
@@ -910,13 +917,13 @@ hipError_t launch_query(const AttnArgs& p, bool dq, float* delta, float* csink, 
         return hipGetLastError();
     };
     if (dq) {
-        switch (gper) {
+        switch (G) {
         case 1: return go(attn_query_kernel<T, D, HT, 1, true>, 4);
         case 2: return go(attn_query_kernel<T, D, HT, 2, true>, 2);
         default: return go(attn_query_kernel<T, D, HT, 4, true>, 1);
         }
     }
-    switch (gper) {
+    switch (G) {
     case 1: return go(attn_query_kernel<T, D, HT, 1, false>, 4);
     case 2: return go(attn_query_kernel<T, D, HT, 2, false>, 2);
     default: return go(attn_query_kernel<T, D, HT, 4, false>, 1);
@@ -932,7 +939,12 @@ hipError_t query_dispatch(const AttnArgs& p, bool dq, float* delta, float* csink
     case 128:
         return p.H <= 16 ? launch_query<T, 128, 1>(p, dq, delta, csink, st)
                          : launch_query<T, 128, 2>(p, dq, delta, csink, st);
-    case 512: return launch_query<T, 512, 1>(p, dq, delta, csink, st);
+    case 256:
+        if constexpr (sizeof(T) == 2) return launch_query<T, 256, 1>(p, dq, delta, csink, st);
+        return hipErrorInvalidValue;
+    case 512:   // fp32 rows of 512 exceed the on-chip tile (rejected at the boundary)
+        if constexpr (sizeof(T) == 2) return launch_query<T, 512, 1>(p, dq, delta, csink, st);
+        return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }
@@ -977,7 +989,12 @@ hipError_t rows_dispatch(const AttnArgs& p, const RowsGeom& geo, float* ws, hipS
     switch (p.D) {
     case 64: return launch_rows<T, 64>(p, geo, ws, st);
     case 128: return launch_rows<T, 128>(p, geo, ws, st);
-    case 512: return launch_rows<T, 512>(p, geo, ws, st);
+    case 256:
+        if constexpr (sizeof(T) == 2) return launch_rows<T, 256>(p, geo, ws, st);
+        return hipErrorInvalidValue;
+    case 512:
+        if constexpr (sizeof(T) == 2) return launch_rows<T, 512>(p, geo, ws, st);
+        return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }
@@ -1011,6 +1028,7 @@ hipError_t attn_bwd(const AttnArgs& p, bool bf16, float* ws, hipStream_t st)
         switch (p.D) {
         case 64: return launch_reduce<64>(p, geo, ws, st);
         case 128: return launch_reduce<128>(p, geo, ws, st);
+        case 256: return launch_reduce<256>(p, geo, ws, st);
         default: return launch_reduce<512>(p, geo, ws, st);
         }
     }

@@ -76,6 +76,23 @@ struct LossArgs {
     int b, S, H, D, HI, DI, r, nc, kp;
 };
 
+// Simplified DSA over grouped-query attention: attention over the selected
+// keys only, query head h reading key/value head h / (H / HKV).
+struct GqaArgs {
+    const void* q;        // [b, S, H, DK]
+    const void* k;        // [b, S, HKV, DK]
+    const void* v;        // [b, S, HKV, DV]
+    const int32_t* idx;   // [b, S, kp] selected keys (valid: 0 <= j <= t)
+    float scale;
+    void* out;            // [b, S, H, DV]
+    float* lse;           // [b, S, H]
+    const void* dout;     // backward: [b, S, H, DV]
+    void* dq;             // [b, S, H, DK] (dtype)
+    float* dk;            // [b, S, HKV, DK]
+    float* dv;            // [b, S, HKV, DV]
+    int b, S, H, HKV, DK, DV, kp;
+};
+
 hipError_t compress_fwd(const CompressArgs& p, bool bf16, hipStream_t st);
 hipError_t compress_bwd(const CompressArgs& p, bool bf16, hipStream_t st);
 size_t compress_bwd_workspace_bytes(const CompressArgs& p);
@@ -87,6 +104,9 @@ hipError_t attn_bwd(const AttnArgs& p, bool bf16, float* ws, hipStream_t st);
 size_t attn_bwd_workspace_bytes(const AttnArgs& p);
 hipError_t indexer_loss(const LossArgs& p, bool bf16, float* ws, hipStream_t st);
 size_t indexer_loss_workspace_bytes(const LossArgs& p);
+size_t dsa_gqa_workspace_bytes(const GqaArgs& p, bool bf16, bool bwd);
+hipError_t dsa_gqa_fwd(const GqaArgs& p, bool bf16, void* ws, hipStream_t st);
+hipError_t dsa_gqa_bwd(const GqaArgs& p, bool bf16, void* ws, hipStream_t st);
 hipError_t zero_fill(float* p, size_t n, hipStream_t st);
 
 }  // namespace csa

@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int hh = 16 * ht + 4 * g + i;
-            wv[ht][i] = (active && hh < HI) ? w[row * HI + hh] : 0.f;
+            wv[ht][i] = (active && hh < HI) ? (w ? w[row * HI + hh] : 1.f) : 0.f;   // no w: unit weights
         }
     }
 

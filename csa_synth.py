@@ -196,3 +196,57 @@ def packed_doc_ids(b: int, sq: int, mean_len: float, seed: int, device="cpu") ->
             pos += n
             k += 1
     return doc.to(device)
+
+
+@dataclasses.dataclass(frozen=True)
+class GqaWorkload:
+    """Shapes of the simplified DSA over grouped-query attention: a one-head
+    indexer at full resolution selects ``topk`` keys per query; attention
+    over those keys with ``h`` query heads sharing ``h_kv`` key/value heads."""
+    name: str
+    b: int
+    sq: int
+    h: int
+    h_kv: int
+    d_qk: int
+    d_v: int
+    topk: int
+    idx_dim: int
+    dtype: str
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def kprime(self) -> int:
+        return min(self.topk, self.sq)
+
+    @property
+    def scale(self) -> float:
+        return self.d_qk ** -0.5
+
+    def replace(self, **kw) -> "GqaWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+GQA_WORKLOADS = {
+    "dsa_gqa_tiny_f32": GqaWorkload("dsa_gqa_tiny_f32", 2, 200, 8, 2, 32, 32, 24, 32, "f32"),
+    "dsa_gqa_s4096": GqaWorkload("dsa_gqa_s4096", 1, 4096, 32, 8, 128, 128, 512, 128, "bf16"),
+}
+
+
+def make_gqa_inputs(wl: GqaWorkload, seed: int, device="cpu") -> Dict[str, torch.Tensor]:
+    """q [b,sq,h,d_qk], k [b,sq,h_kv,d_qk], v [b,sq,h_kv,d_v], dO [b,sq,h,d_v],
+    and the one-head indexer's q_i [b,sq,1,idx_dim], k_i [b,sq,idx_dim]:
+    standard normals (q_i, k_i scaled by 0.5), rounded once to the dtype."""
+    dt = wl.torch_dtype
+    b, S = wl.b, wl.sq
+    return {
+        "q": _normal((b, S, wl.h, wl.d_qk), 1.0, seed, 70, device, dt),
+        "k": _normal((b, S, wl.h_kv, wl.d_qk), 1.0, seed, 71, device, dt),
+        "v": _normal((b, S, wl.h_kv, wl.d_v), 1.0, seed, 72, device, dt),
+        "do": _normal((b, S, wl.h, wl.d_v), 1.0, seed, 73, device, dt),
+        "q_i": _normal((b, S, 1, wl.idx_dim), 0.5, seed, 74, device, dt),
+        "k_i": _normal((b, S, wl.idx_dim), 0.5, seed, 75, device, dt),
+    }

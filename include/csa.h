@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 4
+#define CSA_ABI_VERSION 5
 
 enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 };
 
@@ -155,7 +155,8 @@ size_t csa_index_topk_workspace(const csa_dims* dims);
  * (score desc, index asc), emitted in ascending index, then -1 for the
  * K' - min(K', n_valid(t)) remaining slots.  score (nullable) receives the
  * fp32 scores aligned with idx (-inf on -1 slots).  w is fp32 and already
- * holds any softmax scale of the indexer.  ws may be NULL when
+ * holds any softmax scale of the indexer; w == NULL means unit weights (the
+ * simplified one-head indexer).  ws may be NULL when
  * csa_index_topk_workspace() returns 0. */
 int csa_index_topk(const csa_dims* dims, int dtype, const void* q_i, const void* k_i,
                    const float* w, const int32_t* doc_ids, int32_t* idx, float* score, void* ws,
@@ -239,6 +240,47 @@ int csa_indexer_loss(const csa_dims* dims, int dtype, const void* q, const void*
                      const int32_t* idx, const float* score, float scale,
                      const float* dkl, float* kl, void* dq_i, float* dw, float* dk_i,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------ simplified DSA over GQA
+ * Megatron-LM PR #7152 (description and commit messages): a one-head indexer
+ * without per-head weights selects K' = min(topk, sq) keys per query at full
+ * resolution -- csa_index_topk with ratio 1, idx_heads 1 and w == NULL (unit
+ * weights), so n_valid(t) = t + 1 -- and attention runs over the selected
+ * keys only, with separate keys and values per key/value head:
+ *   query head h reads key/value head g = h / (h / h_kv)
+ *   l   = scale * <q[t, h], k[j, g]>  over the slots j of idx[b, t, :] with
+ *         0 <= j <= t (other slots skipped; a repeated j counts once per slot)
+ *   lse = log sum exp(l), out[t, h] = sum exp(l - lse) v[j, g]
+ *   (no valid slot: out = 0, lse = -inf, no gradient)
+ * No window rows and no sink.  Layouts (row-major, last dim contiguous):
+ * q / out / dout / dq [b, sq, h, d_qk or d_v], k / dk [b, sq, h_kv, d_qk],
+ * v / dv [b, sq, h_kv, d_v], lse [b, sq, h] fp32, idx [b, sq, K'] int32;
+ * dk and dv are fp32 and accumulate every selecting query (fixed order).
+ * h / h_kv <= 64; d_qk + d_v in {64, 128, 256, 512} for bf16, {64, 128} for
+ * fp32; K' <= 2048. */
+typedef struct csa_gqa_dims {
+    int32_t b, sq, h, h_kv, d_qk, d_v, topk;
+} csa_gqa_dims;
+
+/* Workspace bytes of csa_dsa_gqa_fwd (backward == 0) or csa_dsa_gqa_bwd
+ * (backward != 0): device memory, 256-byte aligned, caller-owned, contents on
+ * entry irrelevant.  0 for invalid dims. */
+size_t csa_dsa_gqa_workspace(const csa_gqa_dims* dims, int dtype, int backward);
+
+/* Forward of the attention above. */
+int csa_dsa_gqa_fwd(const csa_gqa_dims* dims, int dtype, const void* q, const void* k,
+                    const void* v, const int32_t* idx, float scale, void* out, float* lse,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Backward, given dout and the forward's out and lse (same inputs):
+ *   dP = <dout, v>, Delta = <dout, out>, dl = P (dP - Delta)
+ *   dq[t, h] = scale sum dl k[j, g]                         (dtype)
+ *   dk[j, g] += scale dl q[t, h],  dv[j, g] += P dout[t, h]  (fp32)
+ * dq, dk and dv are all required. */
+int csa_dsa_gqa_bwd(const csa_gqa_dims* dims, int dtype, const void* q, const void* k,
+                    const void* v, const int32_t* idx, float scale, const void* out,
+                    const float* lse, const void* dout, void* dq, float* dk, float* dv,
+                    void* ws, size_t ws_bytes, void* stream);
 
 /* Message for the last failing call on this thread ("" if none). */
 const char* csa_last_error(void);

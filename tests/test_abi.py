@@ -33,7 +33,7 @@ def test_library_exports_every_header_symbol():
     lib = _lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.csa_version() == 4
+    assert lib.csa_version() == 5
 
 
 def test_dims_struct_matches_header():
@@ -66,7 +66,7 @@ N = None
     ("csa_index_topk", lambda: (ctypes.byref(_d(idx_dim=48)), 0, P, P, P, N, P, N, N, 0, N), -4),
     ("csa_index_topk", lambda: (ctypes.byref(_d(idx_heads=65)), 0, P, P, P, N, P, N, N, 0, N), -4),
     ("csa_index_topk", lambda: (ctypes.byref(_d(sq=65536, topk=4096)), 1, P, P, P, N, P, N, N, 0, N), -4),
-    ("csa_index_topk", lambda: (ctypes.byref(_d()), 0, P, P, N, N, P, N, N, 0, N), -1),
+    ("csa_index_topk", lambda: (ctypes.byref(_d()), 0, P, N, P, N, P, N, N, 0, N), -1),
     ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d(h=65)), 0, P, P, P, P, N, N, ctypes.c_float(1.0), P, P, N), -4),
     ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d(window=0)), 0, P, P, P, P, N, N, ctypes.c_float(1.0), P, P, N), -1),
     ("csa_sparse_attn_fwd", lambda: (ctypes.byref(_d()), 0, P, P, N, P, N, N, ctypes.c_float(1.0), P, P, N), -1),
@@ -189,6 +189,35 @@ def test_indexer_loss_nothing_requested_is_a_noop_and_workspace():
     assert need >= 4 * (d.b * d.sq * kp + d.sq // d.ratio * d.idx_dim)
     assert _loss(dkl=P, dq_i=P, dw=P, dk_i=P, ws=P, ws_bytes=need - 4) == -5
     assert lib.csa_indexer_loss_workspace(None) == 0
+
+
+def _g(**kw):
+    base = dict(b=1, sq=64, h=8, h_kv=2, d_qk=64, d_v=64, topk=16)
+    base.update(kw)
+    return _abi.csa_gqa_dims(*[base[f[0]] for f in _abi.csa_gqa_dims._fields_])
+
+
+@pytest.mark.parametrize("g,dtype,code", [
+    (dict(h=7), 1, -2), (dict(h=256, h_kv=2), 1, -4), (dict(d_qk=128, d_v=64), 1, -4),
+    (dict(d_qk=128, d_v=128), 0, -4), (dict(topk=0), 1, -1), (dict(sq=4096, topk=4096), 1, -4),
+    (dict(d_qk=60, d_v=68), 1, -4), (dict(), 5, -3),
+])
+def test_dsa_gqa_validation(g, dtype, code):
+    lib = _lib()
+    rc = lib.csa_dsa_gqa_fwd(ctypes.byref(_g(**g)), dtype, P, P, P, P, ctypes.c_float(1.0), P, P, P, 1 << 30, N)
+    assert rc == code, lib.csa_last_error()
+
+
+def test_dsa_gqa_workspace_and_gate():
+    lib = _lib()
+    g = _g()
+    need_f = lib.csa_dsa_gqa_workspace(ctypes.byref(g), 1, 0)
+    need_b = lib.csa_dsa_gqa_workspace(ctypes.byref(g), 1, 1)
+    assert 0 < need_f < need_b
+    assert lib.csa_dsa_gqa_fwd(ctypes.byref(g), 1, P, P, P, P, ctypes.c_float(1.0), P, P, P, need_f - 1, N) == -5
+    assert lib.csa_dsa_gqa_bwd(ctypes.byref(g), 1, P, P, P, P, ctypes.c_float(1.0), P, P, P, P, N, P, P,
+                               need_b, N) == -1
+    assert lib.csa_dsa_gqa_workspace(None, 1, 0) == 0
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

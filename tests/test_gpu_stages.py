@@ -391,3 +391,82 @@ def test_indexer_loss(gpu, name, wl, kw):
     say(f"[indexer_loss] {name} b={wl.b} sq={wl.sq} h={wl.h} d={wl.d} HI={wl.idx_heads} DI={wl.idx_dim} "
         f"K={wl.topk} {kw}")
     _loss_case(wl, 41, **kw)
+
+
+# ------------------------------------------ simplified DSA over GQA
+GQA = csa_synth.GQA_WORKLOADS
+
+
+def _gqa_indices(wl, inp, junk=False):
+    """The oracle's one-head, unit-weight, ratio-1 selection [b, sq, K']."""
+    b, S = wl.b, wl.sq
+    idx, _, _ = oracle.index_topk(f64(inp["q_i"]), f64(inp["k_i"]), np.ones((b, S, 1)), 1, wl.topk)
+    idx = np.asarray(idx, dtype=np.int32).reshape(b, S, wl.kprime).copy()
+    if junk:
+        idx[:, 3::5, 1] = idx[:, 3::5, 0]                        # repeated entry
+        idx[:, 7, :] = -1                                        # a query with no valid slot
+        idx[:, 11::7, -1] = np.minimum(np.arange(11, S, 7) + 3, S - 1)[None, :]   # not yet valid
+    return idx
+
+
+def test_index_topk_simplified_one_head(gpu):
+    import compressed_sparse_attention_softmax_amd as csa
+    wl = GQA["dsa_gqa_tiny_f32"].replace(sq=700, topk=60, dtype="bf16", idx_dim=128)
+    say(f"[index_topk simplified] sq={wl.sq} K={wl.topk} DI={wl.idx_dim}")
+    inp = csa_synth.make_gqa_inputs(wl, 3, device="cuda")
+    dm = csa.make_dims(wl.b, wl.sq, ratio=1, idx_heads=1, idx_dim=wl.idx_dim, topk=wl.topk)
+    idx = torch.full((wl.b, wl.sq, wl.kprime), -7, dtype=torch.int32, device="cuda")
+    sc = torch.empty(wl.b, wl.sq, wl.kprime, device="cuda")
+    csa.csa_index_topk(dm, inp["q_i"], inp["k_i"], None, idx, sc)
+    torch.cuda.synchronize()
+    rows = oracle.all_rows(wl.b, wl.sq)
+    oidx, _, dense = oracle.index_topk(f64(inp["q_i"]), f64(inp["k_i"]), np.ones((wl.b, wl.sq, 1)), 1, wl.topk,
+                                       rows=rows)
+    exact = check_topk_rows(idx.cpu().numpy().reshape(-1, wl.kprime), sc.cpu().numpy().reshape(-1, wl.kprime),
+                            oidx, dense, rows[:, 1], 1, wl.sq, wl.kprime, score_tol=tol_of(torch.bfloat16))
+    say(f"  rows identical to the oracle: {exact}/{len(rows)}")
+
+
+GQA_CASES = [
+    ("tiny_f32_dp64", GQA["dsa_gqa_tiny_f32"], {}),
+    ("tiny_f32_junk_idx", GQA["dsa_gqa_tiny_f32"].replace(b=1, sq=150), dict(junk=True)),
+    ("bf16_dp128_g4", GQA["dsa_gqa_s4096"].replace(sq=700, h=16, h_kv=4, d_qk=64, d_v=64, topk=64), {}),
+    ("bf16_dp256_g4", GQA["dsa_gqa_s4096"].replace(sq=600, topk=128), {}),
+    ("bf16_dp256_g16_junk", GQA["dsa_gqa_s4096"].replace(sq=333, h=32, h_kv=2, topk=40), dict(junk=True)),
+    ("bf16_dp512_mqa", GQA["dsa_gqa_s4096"].replace(sq=300, h=8, h_kv=1, d_qk=192, d_v=320, topk=50), {}),
+]
+
+
+@pytest.mark.parametrize("name,wl,kw", GQA_CASES, ids=[c[0] for c in GQA_CASES])
+def test_dsa_gqa_fwd_bwd(gpu, name, wl, kw):
+    import compressed_sparse_attention_softmax_amd as csa
+    from oracle import dsa_gqa
+    say(f"[dsa gqa] {name} b={wl.b} sq={wl.sq} h={wl.h} h_kv={wl.h_kv} d_qk={wl.d_qk} d_v={wl.d_v} "
+        f"K={wl.topk} {wl.dtype} {kw}")
+    inp = csa_synth.make_gqa_inputs(wl, 29, device="cuda")
+    idx = _gqa_indices(wl, inp, **kw)
+    g = csa.csa_gqa_dims(wl.b, wl.sq, wl.h, wl.h_kv, wl.d_qk, wl.d_v, wl.topk)
+    dt = wl.torch_dtype
+    b, S = wl.b, wl.sq
+    out = torch.full((b, S, wl.h, wl.d_v), 7.0, dtype=dt, device="cuda")
+    lse = torch.full((b, S, wl.h), 7.0, device="cuda")
+    ws = torch.empty(csa.csa_dsa_gqa_workspace(g, dt, True), dtype=torch.uint8, device="cuda")
+    idx_d = torch.tensor(idx).cuda()
+    csa.csa_dsa_gqa_fwd(g, inp["q"], inp["k"], inp["v"], idx_d, wl.scale, out, lse, ws)
+    dq = torch.full_like(inp["q"], 7.0)
+    dk = torch.full((b, S, wl.h_kv, wl.d_qk), 7.0, device="cuda")
+    dv = torch.full((b, S, wl.h_kv, wl.d_v), 7.0, device="cuda")
+    csa.csa_dsa_gqa_bwd(g, inp["q"], inp["k"], inp["v"], idx_d, wl.scale, out, lse, inp["do"], dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    q, k, v, do = (f64(inp[n]) for n in ("q", "k", "v", "do"))
+    ro, rl = dsa_gqa.fwd(q, k, v, idx, wl.scale)
+    tol = tol_of(dt)
+    check_close("out", out, ro, tol)
+    empty = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(lse.cpu().numpy()), empty)
+    check_close("lse", lse.cpu().numpy()[~empty], rl[~empty], tol)
+    # the backward is fed the forward's own (rounded) output, as a caller would
+    rdq, rdk, rdv = dsa_gqa.bwd(q, k, v, idx, wl.scale, f64(out), np.where(empty, -np.inf, f64(lse)), do)
+    check_close("dq", dq, rdq, tol)
+    check_close("dk", dk, rdk, tol)
+    check_close("dv", dv, rdv, tol)

@@ -187,6 +187,60 @@ def bench_compress_epilogue(wl, dm, inp, buf, stream, K):
     return out
 
 
+def bench_dsa_gqa(stream, K):
+    """The simplified DSA over GQA (its own synthetic workload, b1 sq4096 h32
+    h_kv8 d128/128, K'=512, one-head indexer with d_i 128): indexer, attention
+    forward and backward, each timed over K calls with events on the stream.
+    Algorithmic work: indexer 2 * d_i per (query, key <= t); attention
+    forward 2 * (d_qk + d_v) per (query, head, valid selected key), backward
+    twice that (the packed zero halves are not counted)."""
+    import torch
+    import csa_synth
+    import compressed_sparse_attention_softmax_amd as csa
+    wl = csa_synth.GQA_WORKLOADS["dsa_gqa_s4096"]
+    inp = csa_synth.make_gqa_inputs(wl, 8, device="cuda")
+    b, S, kp = wl.b, wl.sq, wl.kprime
+    dm = csa.make_dims(b, S, ratio=1, idx_heads=1, idx_dim=wl.idx_dim, topk=wl.topk)
+    g = csa.csa_gqa_dims(b, S, wl.h, wl.h_kv, wl.d_qk, wl.d_v, wl.topk)
+    idx = torch.empty(b, S, kp, dtype=torch.int32, device="cuda")
+    out = torch.empty(b, S, wl.h, wl.d_v, dtype=wl.torch_dtype, device="cuda")
+    lse = torch.empty(b, S, wl.h, device="cuda")
+    dq = torch.empty_like(inp["q"])
+    dk = torch.empty(b, S, wl.h_kv, wl.d_qk, device="cuda")
+    dv = torch.empty(b, S, wl.h_kv, wl.d_v, device="cuda")
+    ws = torch.empty(csa.csa_dsa_gqa_workspace(g, wl.torch_dtype, True), dtype=torch.uint8, device="cuda")
+    calls = {
+        "indexer": lambda: csa.csa_index_topk(dm, inp["q_i"], inp["k_i"], None, idx, None, stream=stream),
+        "attn_fwd": lambda: csa.csa_dsa_gqa_fwd(g, inp["q"], inp["k"], inp["v"], idx, wl.scale, out, lse, ws,
+                                                stream=stream),
+        "attn_bwd": lambda: csa.csa_dsa_gqa_bwd(g, inp["q"], inp["k"], inp["v"], idx, wl.scale, out, lse, inp["do"],
+                                                dq, dk, dv, ws, stream=stream),
+    }
+    for fn in calls.values():
+        fn()
+    torch.cuda.synchronize()
+    ms = {}
+    for name, fn in calls.items():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms[name] = e0.elapsed_time(e1) / K
+    t = torch.arange(S, device="cuda").view(1, -1, 1)
+    nsel = float(((idx >= 0) & (idx <= t)).sum().item())
+    fwd = nsel * wl.h * 2.0 * (wl.d_qk + wl.d_v)
+    ind = float(b * S * (S + 1) / 2) * 2.0 * wl.idx_dim
+    tf = {"indexer": ind, "attn_fwd": fwd, "attn_bwd": 2 * fwd}
+    res = {"workload": {k: getattr(wl, k) for k in ("b", "sq", "h", "h_kv", "d_qk", "d_v", "topk", "idx_dim",
+                                                   "dtype")},
+           "ms": ms, "tokens_per_s": b * S / (sum(ms.values()) * 1e-3),
+           "tflops": {k: tf[k] / (ms[k] * 1e-3) / 1e12 for k in ms}, "selected_keys": nsel}
+    log(f"bench: dsa over gqa: {res}")
+    return res
+
+
 def bench_indexer_loss(wl, dm, inp, buf, stream, K):
     """The indexer's training path after the step's forward (not part of the
     step): csa_indexer_loss over the selected blocks, scores and LSE the last
@@ -386,6 +440,7 @@ def main():
     if wl.topk > 0:
         result["indexer_loss"] = bench_indexer_loss(wl, dm, inp, buf, stream, K)
     result["compress_epilogue"] = bench_compress_epilogue(wl, dm, inp, buf, stream, K)
+    result["dsa_gqa"] = bench_dsa_gqa(stream, K)
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on a CPU sample ...")
         result["cpu_baseline"] = cpu_baseline(wl, inp, seed, args.cpu_rows)

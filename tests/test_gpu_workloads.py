@@ -170,3 +170,56 @@ def test_workload_indexer_loss(gpu, name):
     check_close("dk_i", lbuf.dk_i, rdk, tol)
     del buf, lbuf, inp
     torch.cuda.empty_cache()
+
+
+def test_workload_dsa_gqa(gpu):
+    """The simplified DSA over GQA at its bench size (b1 sq4096 h32 h_kv8
+    d128/128, K'=512): the GPU's one-head selection on sampled rows against
+    the oracle's (near-tie band rule), then attention fed the oracle's
+    selection for every row, checked on sampled rows, with dO zero except on
+    those rows so that dk and dv are oracle computations over them."""
+    import compressed_sparse_attention_softmax_amd as csa
+    from oracle import dsa_gqa
+    wl = csa_synth.GQA_WORKLOADS["dsa_gqa_s4096"]
+    say(f"[workload dsa gqa] {wl}")
+    inp = csa_synth.make_gqa_inputs(wl, 8, device="cuda")
+    b, S, kp = wl.b, wl.sq, wl.kprime
+    dm = csa.make_dims(b, S, ratio=1, idx_heads=1, idx_dim=wl.idx_dim, topk=wl.topk)
+    gidx = torch.empty(b, S, kp, dtype=torch.int32, device="cuda")
+    gsc = torch.empty(b, S, kp, device="cuda")
+    csa.csa_index_topk(dm, inp["q_i"], inp["k_i"], None, gidx, gsc)
+    oidx, _, _ = oracle.index_topk(f64(inp["q_i"]), f64(inp["k_i"]), np.ones((b, S, 1)), 1, wl.topk)
+    oidx = np.asarray(oidx, dtype=np.int32).reshape(b, S, kp)
+    rows = sample_rows(b, S, 24, 8, [0, 1, kp - 1, kp, S - 1])
+    rb, rt = rows[:, 0], rows[:, 1]
+    dense = oracle.index_scores(f64(inp["q_i"][rb, rt]), f64(inp["k_i"]), np.ones((len(rows), 1)), 1, rows)
+    exact = check_topk_rows(gidx[rb, rt].cpu().numpy(), gsc[rb, rt].cpu().numpy(), oidx[rb, rt], dense, rt, 1, S, kp,
+                            score_tol=tol_of(wl.torch_dtype))
+    say(f"  top-k rows identical: {exact}/{len(rows)}")
+    g = csa.csa_gqa_dims(b, S, wl.h, wl.h_kv, wl.d_qk, wl.d_v, wl.topk)
+    dt = wl.torch_dtype
+    out = torch.empty(b, S, wl.h, wl.d_v, dtype=dt, device="cuda")
+    lse = torch.empty(b, S, wl.h, device="cuda")
+    ws = torch.empty(csa.csa_dsa_gqa_workspace(g, dt, True), dtype=torch.uint8, device="cuda")
+    idx_d = torch.tensor(oidx).cuda()
+    csa.csa_dsa_gqa_fwd(g, inp["q"], inp["k"], inp["v"], idx_d, wl.scale, out, lse, ws)
+    bt = (torch.tensor(rb).cuda(), torch.tensor(rt).cuda())
+    do = torch.zeros_like(inp["do"])
+    do[bt] = inp["do"][bt]
+    dq = torch.empty_like(inp["q"])
+    dk = torch.empty(b, S, wl.h_kv, wl.d_qk, device="cuda")
+    dv = torch.empty(b, S, wl.h_kv, wl.d_v, device="cuda")
+    csa.csa_dsa_gqa_bwd(g, inp["q"], inp["k"], inp["v"], idx_d, wl.scale, out, lse, do, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    q, k, v = (f64(inp[n]) for n in ("q", "k", "v"))
+    ro, rl = dsa_gqa.fwd(q, k, v, oidx, wl.scale, rows=rows)
+    tol = tol_of(dt)
+    check_close("out (sampled rows)", out[bt], ro[rb, rt], tol)
+    check_close("lse (sampled rows)", lse[bt], rl[rb, rt], tol)
+    rdq, rdk, rdv = dsa_gqa.bwd(q, k, v, oidx, wl.scale, f64(out), f64(lse), f64(do), rows=rows)
+    check_close("dq (sampled rows)", dq[bt], rdq[rb, rt], tol)
+    other = torch.ones(b, S, dtype=torch.bool, device="cuda")
+    other[bt] = False
+    assert torch.count_nonzero(dq[other]) == 0
+    check_close("dk", dk, rdk, tol)
+    check_close("dv", dv, rdv, tol)

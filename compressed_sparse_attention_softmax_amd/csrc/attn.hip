@@ -703,6 +703,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
         }
 #pragma unroll
         for (int kk = 0; kk < HP / 32; ++kk) {
+            // a head pair with no head (h <= 32); not in the bf16 d = 128
+            // instantiation, where the branch costs more than it saves at h = 64
+            if constexpr (!(sizeof(T) == 2 && D == 128)) {
+                if (32 * kk >= p.H) break;
+            }
             Frag<T> pa[RT], sa[RT];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {

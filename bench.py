@@ -301,6 +301,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="csa4_s4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the step only (skip the indexer loss, compressor epilogue and DSA-over-GQA lines)")
     ap.add_argument("--cpu-rows", type=int, default=96)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (HBM counter calibration)")
@@ -437,10 +439,11 @@ def main():
                    "max_allocated_bytes": int(torch.cuda.max_memory_allocated())},
         "cpu_baseline": None,
     }
-    if wl.topk > 0:
-        result["indexer_loss"] = bench_indexer_loss(wl, dm, inp, buf, stream, K)
-    result["compress_epilogue"] = bench_compress_epilogue(wl, dm, inp, buf, stream, K)
-    result["dsa_gqa"] = bench_dsa_gqa(stream, K)
+    if not args.no_extras:
+        if wl.topk > 0:
+            result["indexer_loss"] = bench_indexer_loss(wl, dm, inp, buf, stream, K)
+        result["compress_epilogue"] = bench_compress_epilogue(wl, dm, inp, buf, stream, K)
+        result["dsa_gqa"] = bench_dsa_gqa(stream, K)
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on a CPU sample ...")
         result["cpu_baseline"] = cpu_baseline(wl, inp, seed, args.cpu_rows)

@@ -28,10 +28,26 @@ N_BWD_ROWS = {"tiny_f32": 256, "csa4_s4096": 48, "csa4_d512_s8192": 24, "hca128_
 
 @pytest.mark.parametrize("name", csa_synth.WORKLOAD_ORDER)
 def test_workload_parity(gpu, name):
+    _whole_pass(csa_synth.WORKLOADS[name], csa_synth.WORKLOAD_SEEDS[name], N_ROWS[name], N_BWD_ROWS[name])
+
+
+# the largest index rows the kernels take (K' = 2048) with the widest rows
+# (d = 512): the largest LDS footprint of the query kernels (two 32-row
+# tiles of 1 KiB rows plus the index row) and of the indexer's candidate buffer
+MAX_CASES = [
+    ("d512_topk2048", csa_synth.WORKLOADS["csa4_d512_s8192"].replace(sq=8300, topk=2048), 16, 8),
+]
+
+
+@pytest.mark.parametrize("name,wl,nf,nb", MAX_CASES, ids=[c[0] for c in MAX_CASES])
+def test_maximum_sizes(gpu, name, wl, nf, nb):
+    _whole_pass(wl, 17, nf, nb)
+
+
+def _whole_pass(wl, seed, n_rows, n_bwd_rows):
     import compressed_sparse_attention_softmax_amd as csa
     from compressed_sparse_attention_softmax_amd import pipeline
-    wl = csa_synth.WORKLOADS[name]
-    seed = csa_synth.WORKLOAD_SEEDS[name]
+    name = wl.name
     say(f"[workload] {name} seed={seed} b={wl.b} sq={wl.sq} h={wl.h} d={wl.d} r={wl.ratio} "
         f"L={wl.span} W={wl.window} K={wl.topk} {wl.dtype}")
     torch.cuda.empty_cache()
@@ -53,7 +69,7 @@ def test_workload_parity(gpu, name):
     must = [0, 1, r - 1, r, wl.window - 1, wl.window, S - 1, S - 2]
     if wl.kprime:
         must += [wl.kprime * r - 2, wl.kprime * r - 1, wl.kprime * r]
-    rows = sample_rows(b, S, N_ROWS[name], seed, must)
+    rows = sample_rows(b, S, n_rows, seed, must)
     rb, rt = rows[:, 0], rows[:, 1]
 
     if wl.topk > 0:
@@ -79,7 +95,7 @@ def test_workload_parity(gpu, name):
     check_close("lse", buf.lse[ra_b, ra_t], lse_ref, tol)
 
     # backward with dO restricted to a subset of those rows
-    nb = min(N_BWD_ROWS[name], len(rows_a))
+    nb = min(n_bwd_rows, len(rows_a))
     sel = np.random.default_rng(seed).choice(len(rows_a), nb, replace=False)
     sel.sort()
     rows_b = rows_a[sel]

@@ -465,10 +465,10 @@ template <typename T, int D> constexpr int rows_stage_buffers()
 template <typename T, int D> constexpr int rows_waves_t() { return (sizeof(T) == 2 && D <= 128) ? 8 : 4; }
 template <typename T, int D> constexpr int rows_per_wave_t() { return D <= 128 ? 256 / rows_waves_t<T, D>() : 16; }
 // LDS bytes of the key-stationary kernel without / with its key-row tile
-template <typename T, int D> constexpr size_t rows_lds_base()
+template <typename T, int D, int QS = 1> constexpr size_t rows_lds_base()
 {
     return 2 * (size_t)rows_stage_buffers<T, D>() * 64 * D * sizeof(T) + 4 * 64 * 4 +
-           (size_t)3 * rows_waves_t<T, D>() * rows_per_wave_t<T, D>() * 4;
+           (size_t)3 * QS * rows_waves_t<T, D>() * rows_per_wave_t<T, D>() * 4;
 }
 template <typename T, int D> constexpr size_t rows_lds_tile()
 {
@@ -487,13 +487,19 @@ struct RowsGeom {
     int64_t win_off, comp_off;         // float offsets of the two partial regions in the workspace
 };
 
-template <typename T, int D, int RW, int NW>
+template <typename T, int D, int RW, int NW, int QS>
 __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsGeom geo,
                                                            const float* __restrict__ delta,
                                                            float* __restrict__ ws)
 {
     constexpr int KS = D / 32, DT = D / 16, RT = RW / 16, TR = NW * RW, NT = 64 * NW;
     constexpr int HP = 64;                       // heads, padded to 4 head tiles
+    // QS > 1 (key/value groups of few heads, no window): the 64 head slots
+    // hold HS heads of each of QS consecutive queries, which share the tile's
+    // rows; slot h belongs to query t + h / HS, head h % HS
+    constexpr int HS = HP / QS;
+    constexpr int CTR = QS * NW * RW;            // multiplicities per count buffer
+    static_assert(QS == 1 || HS >= 4, "a lane's four head slots belong to one query");
     constexpr int QELEMS = HP * D;               // one staged q (or dO) block
     constexpr int NBUF = rows_stage_buffers<T, D>();
     constexpr int L16 = QELEMS * (int)sizeof(T) / 16;   // 16-byte pieces per block
@@ -549,7 +555,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
     // LDS budget allows) in a wave-private LDS tile to leave registers for S / dP
     constexpr bool ROWS_LDS = rows_tile_in_lds<T, D>();
     constexpr int RROW = D + row_pad<T>();
-    T* rtile = reinterpret_cast<T*>(reinterpret_cast<char*>(cnt_lds) + 3 * TR * 4) + (size_t)wave * RW * RROW;
+    T* rtile = reinterpret_cast<T*>(reinterpret_cast<char*>(cnt_lds) + 3 * CTR * 4) + (size_t)wave * RW * RROW;
     Frag<T> rb[ROWS_LDS ? 1 : RT][KS];
     int rkey[RT];
     [[maybe_unused]] int rdoc[RT];               // packed documents: document of each window row
@@ -597,11 +603,23 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
             const int pos = pr * E;                       // element position in LDS row
             const int unit = (pos >> 3) ^ unit_swz(h, D / 8);   // source unit
             const int srcel = (unit << 3) | (pos & 7);
-            const int hh = h < p.H ? h : 0;               // padded heads read row 0 (masked later)
             const size_t wbase = (size_t)(k * NW + wave) * WAVE * 16;  // wave's 1 KiB in bytes
-            __builtin_amdgcn_global_load_lds((const void*)(qsrc + hh * D + srcel),
+            const T* qp = qsrc;
+            const T* dp_ = dsrc;
+            if constexpr (QS == 1) {
+                const int hh = h < p.H ? h : 0;           // padded heads read row 0 (masked later)
+                qp += hh * D + srcel;
+                dp_ += hh * D + srcel;
+            } else {
+                // stacked slots: query t + h / HS, head h % HS (slots past the block read row 0 of t)
+                const int tq = t + h / HS, hq = h % HS;
+                const int64_t soff = (hq < p.H && tq < tb) ? ((int64_t)(tq - t) * p.H + hq) * D : 0;
+                qp += soff + srcel;
+                dp_ += soff + srcel;
+            }
+            __builtin_amdgcn_global_load_lds((const void*)qp,
                                              (__attribute__((address_space(3))) void*)((char*)qdst + wbase), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(dsrc + hh * D + srcel),
+            __builtin_amdgcn_global_load_lds((const void*)dp_,
                                              (__attribute__((address_space(3))) void*)((char*)ddst + wbase), 16, 0, 0);
         }
         if (threadIdx.x < HP) {
@@ -610,11 +628,20 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
             // offset -lse/scale (so that scale*log2e*S' = log2 P) and -Delta
             // (a query with no candidate has LSE = -inf and multiplicity 0 everywhere:
             // any finite offset keeps its P at 0)
-            const float l = h < p.H ? p.lse[qrow * p.H + h] : 0.f;
-            lse_lds[buf * HP + h] = h < p.H ? (l > -INFINITY ? -l / p.scale : 0.f) : -INFINITY;
-            dlt_lds[buf * HP + h] = h < p.H ? -delta[qrow * p.H + h] : 0.f;
+            if constexpr (QS == 1) {
+                const float l = h < p.H ? p.lse[qrow * p.H + h] : 0.f;
+                lse_lds[buf * HP + h] = h < p.H ? (l > -INFINITY ? -l / p.scale : 0.f) : -INFINITY;
+                dlt_lds[buf * HP + h] = h < p.H ? -delta[qrow * p.H + h] : 0.f;
+            } else {
+                const int tq = t + h / HS, hq = h % HS;
+                const bool hv = hq < p.H && tq < tb;
+                const int64_t hrow = (qrow + (tq - t)) * p.H + hq;
+                const float l = hv ? p.lse[hrow] : 0.f;
+                lse_lds[buf * HP + h] = hv ? (l > -INFINITY ? -l / p.scale : 0.f) : -INFINITY;
+                dlt_lds[buf * HP + h] = hv ? -delta[hrow] : 0.f;
+            }
         }
-        if (!win) {
+        if (!win && QS == 1) {
             if (p.idx) {
                 // index entries are only loaded here; count() consumes them later
                 const int32_t* irow = p.idx + qrow * p.kp;
@@ -624,7 +651,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
                     jreg[k] = s < p.kp ? irow[s] : -1;
                 }
             } else {
-                unsigned* cnt = cnt_lds + cb * TR;
+                unsigned* cnt = cnt_lds + cb * CTR;
                 const int nv = min((t + 1) / p.r, p.nc);
                 // dense mode: every valid block once (with documents: blocks of t's document)
                 const int32_t* dcol = p.doc ? p.doc + (int64_t)bi * p.S : nullptr;
@@ -637,7 +664,20 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
     // multiplicities of the tile's rows for query t from the staged index entries
     auto count = [&](int t, int cb) {
         if (win || !p.idx) return;
-        unsigned* cnt = cnt_lds + cb * TR;
+        unsigned* cnt = cnt_lds + cb * CTR;
+        if constexpr (QS > 1) {
+            // the stack's index rows, read here (no register prefetch)
+            for (int qs = 0; qs < QS && t + qs < tb; ++qs) {
+                const int tq = t + qs;
+                const int nvq = min((tq + 1) / p.r, p.nc);
+                const int32_t* irow = p.idx + ((int64_t)bi * p.S + tq) * p.kp;
+                for (int s = threadIdx.x; s < p.kp; s += NT) {
+                    const int j = irow[s];
+                    if (j >= 0 && j < nvq && j >= tile_lo && j < tile_hi) atomicAdd(&cnt[qs * (NW * RW) + j - tile_lo], 1u);
+                }
+            }
+            return;
+        }
         const int nv = min((t + 1) / p.r, p.nc);
 #pragma unroll
         for (int k = 0; k < IDX_REGS; ++k) {
@@ -647,7 +687,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
     };
 
     if (!win) {
-        for (int i = threadIdx.x; i < 3 * TR; i += NT) cnt_lds[i] = 0u;
+        for (int i = threadIdx.x; i < 3 * CTR; i += NT) cnt_lds[i] = 0u;
         __syncthreads();
     }
     const float sl2 = p.scale * LOG2E;
@@ -664,12 +704,12 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
     live = __any(live);
     auto query_loop = [&](auto compute_tag) {
     constexpr bool COMPUTE = decltype(compute_tag)::value;
-    for (int t = ta; t < tb; ++t) {
-        const int it = t - ta, buf = NBUF == 2 ? (it & 1) : 0, cb = it % 3;
+    for (int t = ta; t < tb; t += QS) {
+        const int it = (t - ta) / QS, buf = NBUF == 2 ? (it & 1) : 0, cb = it % 3;
         if constexpr (NBUF == 2) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();                               // stage(t) visible; compute(t-1) done
-            if (t + 1 < tb) stage(t + 1, buf ^ 1, (it + 1) % 3);
+            if (t + QS < tb) stage(t + QS, buf ^ 1, (it + 1) % 3);
         } else {
             __syncthreads();                               // compute(t-1) done with the buffer
             stage(t, 0, cb);
@@ -678,8 +718,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
             __syncthreads();                               // stage(t) visible
         }
         if (!win) {                                        // buffer of t+2: last read by compute(t-1)
-            unsigned* nxt = cnt_lds + ((it + 2) % 3) * TR;
-            for (int i = threadIdx.x; i < TR; i += NT) nxt[i] = 0u;
+            unsigned* nxt = cnt_lds + ((it + 2) % 3) * CTR;
+            for (int i = threadIdx.x; i < CTR; i += NT) nxt[i] = 0u;
         }
         const T* q_lds = stage_base + (size_t)(2 * buf) * QELEMS;
         const T* do_lds = q_lds + QELEMS;
@@ -691,21 +731,30 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
         // get multiplicity 0 (no branch, so the accumulators stay put).  The
         // multiplicity enters the exponent: m P = 2^(scale log2e S' + log2 m).
         float lm[RT];                                      // log2 of the multiplicity, -inf for 0
+        [[maybe_unused]] float lmq[QS > 1 ? 4 : 1][RT];   // stacked queries: per head tile
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int key = rkey[rt];
             float m = 0.f;
             if (key >= 0) {
                 if (win) m = (key <= t && key > t - p.W && (!p.doc || rdoc[rt] == dtq)) ? 1.f : 0.f;
-                else m = (float)cnt_lds[cb * TR + key - tile_lo];
+                else m = (float)cnt_lds[cb * CTR + key - tile_lo];
             }
             lm[rt] = m > 0.f ? __log2f(m) : -INFINITY;
+            if constexpr (QS > 1) {
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht) {
+                    const int qs = (16 * ht + 4 * g) / HS;     // this lane's query in the stack
+                    const float mq = key >= 0 ? (float)cnt_lds[cb * CTR + qs * (NW * RW) + key - tile_lo] : 0.f;
+                    lmq[ht][rt] = mq > 0.f ? __log2f(mq) : -INFINITY;
+                }
+            }
         }
 #pragma unroll
         for (int kk = 0; kk < HP / 32; ++kk) {
             // a head pair with no head (h <= 32); not in the bf16 d = 128
             // instantiation, where the branch costs more than it saves at h = 64
-            if constexpr (!(sizeof(T) == 2 && D == 128)) {
+            if constexpr (!(sizeof(T) == 2 && D == 128) && QS == 1) {
                 if (32 * kk >= p.H) break;
             }
             Frag<T> pa[RT], sa[RT];
@@ -741,7 +790,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
                     // scaled dS = scale (m P) (dP - Delta)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float e = fast_exp2(fmaf(sv[i], sl2, lm[rt]));
+                        float lmv = lm[rt];
+                        if constexpr (QS > 1) lmv = lmq[ht][rt];
+                        const float e = fast_exp2(fmaf(sv[i], sl2, lmv));
                         pa[rt].v[4 * hh + i] = from_f32<T>(e);
                         sa[rt].v[4 * hh + i] = from_f32<T>((dp[i] * p.scale) * e);
                     }
@@ -769,7 +820,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
         }
         }
         if constexpr (NBUF == 2) {
-            if (t + 1 < tb) count(t + 1, (it + 1) % 3);     // its index loads had compute(t) to land
+            if (t + QS < tb) count(t + QS, (it + 1) % 3);   // its index loads had compute(t) to land
         }
     }
     };
@@ -968,13 +1019,13 @@ hipError_t launch_reduce(const AttnArgs& p, const RowsGeom& geo, float* ws, hipS
     return hipGetLastError();
 }
 
-template <typename T, int D>
-hipError_t launch_rows(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStream_t st)
+template <typename T, int D, int QS>
+hipError_t launch_rows_qs(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStream_t st)
 {
     constexpr int RW = rows_per_wave_t<T, D>(), NW = rows_waves_t<T, D>();
-    const size_t lds = rows_lds_base<T, D>() + (rows_tile_in_lds<T, D>() ? rows_lds_tile<T, D>() : 0);
+    const size_t lds = rows_lds_base<T, D, QS>() + (rows_tile_in_lds<T, D>() ? rows_lds_tile<T, D>() : 0);
     if (lds > (size_t)ATTN_LDS_LIMIT) return hipErrorInvalidValue;
-    auto kern = attn_rows_kernel<T, D, RW, NW>;
+    auto kern = attn_rows_kernel<T, D, RW, NW, QS>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int ntiles = geo.n_wt + (p.c ? geo.n_ct : 0);
@@ -986,6 +1037,23 @@ hipError_t launch_rows(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStr
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return launch_reduce<D>(p, geo, ws, st);
+}
+
+// Queries stacked in the 64 head slots: for the window-free path with an
+// index list and at most 16 heads per query (d = 256 only, where the
+// grouped-query path runs), 64 / (heads rounded up to a power of two >= 4)
+// consecutive queries share one pass over the tile's rows.
+template <typename T, int D>
+hipError_t launch_rows(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStream_t st)
+{
+    if constexpr (sizeof(T) == 2 && D == 256) {
+        if (p.W == 0 && p.idx && p.H <= 16 && geo.Qb % 16 == 0) {
+            if (p.H <= 4) return launch_rows_qs<T, D, 16>(p, geo, ws, st);
+            if (p.H <= 8) return launch_rows_qs<T, D, 8>(p, geo, ws, st);
+            return launch_rows_qs<T, D, 4>(p, geo, ws, st);
+        }
+    }
+    return launch_rows_qs<T, D, 1>(p, geo, ws, st);
 }
 
 template <typename T>

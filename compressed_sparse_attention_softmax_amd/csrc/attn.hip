@@ -927,7 +927,9 @@ RowsGeom rows_geometry(const AttnArgs& p)
         const int nqb = (p.S + qb - 1) / qb;
         return (int64_t)p.b * nqb * ((int64_t)(p.W > 0 ? p.W - 1 + qb : 0) + p.nc) * D;
     };
-    int qb = 32;
+    // window-free rows of every position (the grouped-query path) reach a
+    // whole causal prefix: longer query blocks keep the partial rows small
+    int qb = (p.W == 0 && p.r == 1) ? 128 : 32;
     while (qb < 1024 && part_floats(qb) * 4 > ((int64_t)1 << 30)) qb *= 2;
     g.Qb = qb;
     g.nqb = (p.S + qb - 1) / qb;

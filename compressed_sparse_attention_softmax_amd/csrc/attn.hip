@@ -108,7 +108,7 @@ struct Cand {
 //   dQ^T[d, h] += R^T dS'^T           same operand shapes
 template <typename T, int D> constexpr int chunk_bytes() { return CHUNK * D * (int)sizeof(T); }
 
-template <typename T, int D, int HT, int G, bool DQ>
+template <typename T, int D, int HT, int G, bool DQ, int KSP>
 __global__ __launch_bounds__(256, (D <= 128 && HT <= 2) ? 2 : 1)
 void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict__ csink, int idx_lds, int okw)
 {
@@ -260,20 +260,28 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
         [[maybe_unused]] f32x4 dp[HT][2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
+            // KSP > 0: rows packed as [k | v] (the first KSP k-steps are the key
+            // half) with q = [q | 0] and dO = [0 | dO]: the logits read the key
+            // half, dP the value half (the zero halves are skipped)
             Frag<T> ra[KS];
             const int r = 16 * rt + n16;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) ra[ks] = load_frag(tile + r * D + (((4 * ks + g) ^ unit_swz(r, D / 8)) << 3));
+            for (int ks = 0; ks < KS; ++ks) {
+                if (KSP > 0 && !DQ && ks >= KSP) ra[ks] = zero_frag<T>();
+                else ra[ks] = load_frag(tile + r * D + (((4 * ks + g) ^ unit_swz(r, D / 8)) << 3));
+            }
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
                 f32x4 acc = f4zero();
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) acc = mfma16(ra[ks], qb[ht][ks], acc);
+                for (int ks = 0; ks < KS; ++ks)
+                    if (KSP == 0 || ks < KSP) acc = mfma16(ra[ks], qb[ht][ks], acc);
                 s[ht][rt] = acc;
                 if constexpr (DQ) {
                     f32x4 a2 = f32x4{-dlt[ht], -dlt[ht], -dlt[ht], -dlt[ht]};
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) a2 = mfma16(ra[ks], db[ht][ks], a2);
+                    for (int ks = 0; ks < KS; ++ks)
+                        if (KSP == 0 || ks >= KSP) a2 = mfma16(ra[ks], db[ht][ks], a2);
                     dp[ht][rt] = a2;
                 }
             }
@@ -345,9 +353,11 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
                     }
             }
         }
-        // O^T += R^T P^T   (or dQ^T += R^T dS'^T)
+        // O^T += R^T P^T   (or dQ^T += R^T dS'^T); packed rows: O needs the
+        // value half only, dQ the key half only
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
+            if (KSP > 0 && (DQ ? dt >= 2 * KSP : dt < 2 * KSP)) continue;
             const Frag<T> a = rows_operand<T>(tile, D, 0, 16 * dt, true);
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) o[dt][ht] = mfma16(a, pb[ht], o[dt][ht]);
@@ -487,7 +497,7 @@ struct RowsGeom {
     int64_t win_off, comp_off;         // float offsets of the two partial regions in the workspace
 };
 
-template <typename T, int D, int RW, int NW, int QS>
+template <typename T, int D, int RW, int NW, int QS, int KSP>
 __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsGeom geo,
                                                            const float* __restrict__ delta,
                                                            float* __restrict__ ws)
@@ -772,8 +782,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int off = hrow * D + (((4 * ks + g) ^ unit_swz(hrow, D / 8)) << 3);   // d = 32 ks + 8 g
-                    qa[ks] = load_frag(q_lds + off);
-                    da[ks] = load_frag(do_lds + off);
+                    // packed [k | v] rows (KSP > 0): q lives in the key half, dO in the value half
+                    qa[ks] = (KSP > 0 && ks >= KSP) ? zero_frag<T>() : load_frag(q_lds + off);
+                    da[ks] = (KSP > 0 && ks < KSP) ? zero_frag<T>() : load_frag(do_lds + off);
                 }
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
@@ -783,8 +794,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
                         Frag<T> bk;
                         if constexpr (ROWS_LDS) bk = load_frag(rtile + (16 * rt + n16) * RROW + 32 * ks + 8 * g);
                         else bk = rb[rt][ks];
-                        sv = mfma16(qa[ks], bk, sv);
-                        dp = mfma16(da[ks], bk, dp);
+                        if (KSP == 0 || ks < KSP) sv = mfma16(qa[ks], bk, sv);
+                        if (KSP == 0 || ks >= KSP) dp = mfma16(da[ks], bk, dp);
                     }
                     // sv = S - lse/scale, dp = dP - Delta:  m P = 2^(sv sl2 + lm),
                     // scaled dS = scale (m P) (dP - Delta)
@@ -802,8 +813,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
             }
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const Frag<T> dob = rows_operand<T>(do_lds, D, 32 * kk, 16 * dt, true);
-                const Frag<T> qbf = rows_operand<T>(q_lds, D, 32 * kk, 16 * dt, true);
+                // packed rows: the key half of dR is dS'^T q, the value half P^T dO
+                const bool khalf = KSP > 0 && dt < 2 * KSP, vhalf = KSP > 0 && dt >= 2 * KSP;
+                const Frag<T> dob = khalf ? zero_frag<T>() : rows_operand<T>(do_lds, D, 32 * kk, 16 * dt, true);
+                const Frag<T> qbf = vhalf ? zero_frag<T>() : rows_operand<T>(q_lds, D, 32 * kk, 16 * dt, true);
                 if constexpr (sizeof(T) == 2 && RT == 4) {
                     mfma16x8_acc(acc[0][dt], acc[1][dt], acc[2][dt], acc[3][dt], pa, sa, dob, qbf);
                 } else if constexpr (sizeof(T) == 2 && RT == 2) {
@@ -811,8 +824,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
                 } else {
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) {
-                        mfma16_acc(acc[rt][dt], pa[rt], dob);
-                        mfma16_acc(acc[rt][dt], sa[rt], qbf);
+                        if (!khalf) mfma16_acc(acc[rt][dt], pa[rt], dob);
+                        if (!vhalf) mfma16_acc(acc[rt][dt], sa[rt], qbf);
                     }
                 }
             }
@@ -943,8 +956,8 @@ RowsGeom rows_geometry(const AttnArgs& p)
     return g;
 }
 
-template <typename T, int D, int HT>
-hipError_t launch_query(const AttnArgs& p, bool dq, float* delta, float* csink, hipStream_t st)
+template <typename T, int D, int HT, int KSP>
+hipError_t launch_query_k(const AttnArgs& p, bool dq, float* delta, float* csink, hipStream_t st)
 {
     const int gper = (p.H + 16 * HT - 1) / (16 * HT);
     int G = gper <= 1 ? 1 : (gper <= 2 ? 2 : 4);
@@ -976,16 +989,27 @@ hipError_t launch_query(const AttnArgs& p, bool dq, float* delta, float* csink, 
     };
     if (dq) {
         switch (G) {
-        case 1: return go(attn_query_kernel<T, D, HT, 1, true>, 4);
-        case 2: return go(attn_query_kernel<T, D, HT, 2, true>, 2);
-        default: return go(attn_query_kernel<T, D, HT, 4, true>, 1);
+        case 1: return go(attn_query_kernel<T, D, HT, 1, true, KSP>, 4);
+        case 2: return go(attn_query_kernel<T, D, HT, 2, true, KSP>, 2);
+        default: return go(attn_query_kernel<T, D, HT, 4, true, KSP>, 1);
         }
     }
     switch (G) {
-    case 1: return go(attn_query_kernel<T, D, HT, 1, false>, 4);
-    case 2: return go(attn_query_kernel<T, D, HT, 2, false>, 2);
-    default: return go(attn_query_kernel<T, D, HT, 4, false>, 1);
+    case 1: return go(attn_query_kernel<T, D, HT, 1, false, KSP>, 4);
+    case 2: return go(attn_query_kernel<T, D, HT, 2, false, KSP>, 2);
+    default: return go(attn_query_kernel<T, D, HT, 4, false, KSP>, 1);
     }
+}
+
+// packed [k | v] rows of 128 + 128 channels (the grouped-query path) skip
+// their zero halves
+template <typename T, int D, int HT>
+hipError_t launch_query(const AttnArgs& p, bool dq, float* delta, float* csink, hipStream_t st)
+{
+    if constexpr (sizeof(T) == 2 && D == 256) {
+        if (p.dsplit == 128) return launch_query_k<T, D, HT, 4>(p, dq, delta, csink, st);
+    }
+    return launch_query_k<T, D, HT, 0>(p, dq, delta, csink, st);
 }
 
 template <typename T>
@@ -1021,13 +1045,13 @@ hipError_t launch_reduce(const AttnArgs& p, const RowsGeom& geo, float* ws, hipS
     return hipGetLastError();
 }
 
-template <typename T, int D, int QS>
-hipError_t launch_rows_qs(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStream_t st)
+template <typename T, int D, int QS, int KSP>
+hipError_t launch_rows_qk(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStream_t st)
 {
     constexpr int RW = rows_per_wave_t<T, D>(), NW = rows_waves_t<T, D>();
     const size_t lds = rows_lds_base<T, D, QS>() + (rows_tile_in_lds<T, D>() ? rows_lds_tile<T, D>() : 0);
     if (lds > (size_t)ATTN_LDS_LIMIT) return hipErrorInvalidValue;
-    auto kern = attn_rows_kernel<T, D, RW, NW, QS>;
+    auto kern = attn_rows_kernel<T, D, RW, NW, QS, KSP>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int ntiles = geo.n_wt + (p.c ? geo.n_ct : 0);
@@ -1045,6 +1069,15 @@ hipError_t launch_rows_qs(const AttnArgs& p, const RowsGeom& geo, float* ws, hip
 // index list and at most 16 heads per query (d = 256 only, where the
 // grouped-query path runs), 64 / (heads rounded up to a power of two >= 4)
 // consecutive queries share one pass over the tile's rows.
+template <typename T, int D, int QS>
+hipError_t launch_rows_qs(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStream_t st)
+{
+    if constexpr (sizeof(T) == 2 && D == 256) {
+        if (p.dsplit == 128) return launch_rows_qk<T, D, QS, 4>(p, geo, ws, st);
+    }
+    return launch_rows_qk<T, D, QS, 0>(p, geo, ws, st);
+}
+
 template <typename T, int D>
 hipError_t launch_rows(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStream_t st)
 {

@@ -54,6 +54,10 @@ struct AttnArgs {
     float* dc;
     float* dsink;
     int b, S, H, D, W, r, nc, kp;
+    // rows packed as [k | v] with q = [q | 0] and dO = [0 | dO] (the
+    // grouped-query path): the first dsplit channels are the key half; the
+    // kernels skip the products with a zero half (0: no packing)
+    int dsplit;
 };
 
 // Indexer distillation loss (teacher from the attention LSE, KL over the

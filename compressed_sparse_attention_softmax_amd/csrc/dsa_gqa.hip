@@ -11,16 +11,16 @@
 // row [k | v] of width d_qk + d_v, queries into [q | 0] and, in the
 // backward, dO into [0 | dO] and O into [0 | O]; with no window (W = 0), no
 // sink and ratio 1 the packed rows act as the "compressed" rows selected by
-// the index list, and
+// the index list (the kernels, told where the key half ends, skip the
+// products with a zero half at d_qk + d_v = 256), and
 //   logits  = <[q | 0], [k | v]>            = <q, k>
 //   O'      = sum P [k | v],                  O = its v half
 //   Delta   = <[0 | dO], [0 | O]>           = <dO, O>
 //   dq'     = scale sum dS [k | v],           dq = its k half
 //   drow    = sum P [0 | dO] + scale dS [q | 0] = [dk | dv].
 // The groups run one after another on the caller's stream; the packing and
-// unpacking kernels are plain element-wise copies.  The zero halves cost
-// matrix-core work (about half of each product), the price of reusing the
-// tuned kernels unchanged.
+// unpacking kernels are plain element-wise copies.  At other widths the zero
+// halves cost matrix-core work (about half of each product).
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
 
@@ -42,6 +42,8 @@ AttnArgs group_args(const GqaArgs& p)
     a.scale = p.scale;
     a.idx = p.idx;
     a.b = p.b; a.S = p.S; a.H = p.H / p.HKV; a.D = p.DK + p.DV; a.W = 0; a.r = 1; a.nc = p.S; a.kp = p.kp;
+    // the kernels skip the zero halves when the key half is whole k-steps
+    a.dsplit = (p.DK % 32 == 0) ? p.DK : 0;
     return a;
 }
 

@@ -434,20 +434,31 @@ __global__ __launch_bounds__(NT) void loss_keys_kernel(LossArgs p, KeysGeom geo,
 }
 
 // dk_i[b, j, :] = sum over query blocks that reach block j of their partial
-// rows, in query-block order.
+// rows.  A workgroup takes 64 consecutive float4 columns of the output and
+// splits the query blocks of each over 4 lanes (block q to lane q % 4); the
+// four partial sums are then added in lane order, so the order is fixed.
 __global__ __launch_bounds__(NT) void loss_reduce_kernel(LossArgs p, KeysGeom geo, const float* __restrict__ part)
 {
-    const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;   // one float4 of one row
+    __shared__ f32x4 red[4][64];
+    const int col = threadIdx.x % 64, split = threadIdx.x / 64;
     const int v4 = p.DI / 4;
-    if (i >= (int64_t)p.b * p.nc * v4) return;
-    const int v = (int)(i % v4);
-    const int64_t bj = i / v4;
-    const int j = (int)(bj % p.nc), bi = (int)(bj / p.nc);
-    const int qlo = ((j + 1) * p.r - 1) / geo.Qb;
+    const int64_t i = (int64_t)blockIdx.x * 64 + col;   // one float4 of one row
+    const bool live = i < (int64_t)p.b * p.nc * v4;
     f32x4 s = f4zero();
-    for (int q = qlo; q < geo.nqb; ++q)
-        s += *reinterpret_cast<const f32x4*>(part + ((((int64_t)bi * geo.nqb + q) * p.nc) + j) * p.DI + 4 * v);
-    *reinterpret_cast<f32x4*>(p.dki + bj * p.DI + 4 * v) = s;
+    int64_t bj = 0;
+    int v = 0;
+    if (live) {
+        v = (int)(i % v4);
+        bj = i / v4;
+        const int j = (int)(bj % p.nc), bi = (int)(bj / p.nc);
+        const int qlo = ((j + 1) * p.r - 1) / geo.Qb;
+        for (int q = qlo + split; q < geo.nqb; q += 4)
+            s += *reinterpret_cast<const f32x4*>(part + ((((int64_t)bi * geo.nqb + q) * p.nc) + j) * p.DI + 4 * v);
+    }
+    red[split][col] = s;
+    __syncthreads();
+    if (split == 0 && live)
+        *reinterpret_cast<f32x4*>(p.dki + bj * p.DI + 4 * v) = ((red[0][col] + red[1][col]) + red[2][col]) + red[3][col];
 }
 
 KeysGeom keys_geometry(const LossArgs& p)
@@ -492,11 +503,10 @@ hipError_t launch_loss(const LossArgs& p, float* ws, hipStream_t st)
         hipLaunchKernelGGL(kk, dim3((unsigned)(groups * 8 * geo.ntiles)), dim3(NT), klds, st, p, geo, ws, part);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int64_t threads = (int64_t)p.b * p.nc * (p.DI / 4);
+    const int64_t cols = (int64_t)p.b * p.nc * (p.DI / 4);
     {
         TimedLaunch tl(K_LOSS_REDUCE, st);
-        hipLaunchKernelGGL(loss_reduce_kernel, dim3((unsigned)((threads + NT - 1) / NT)), dim3(NT), 0, st, p, geo,
-                           part);
+        hipLaunchKernelGGL(loss_reduce_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(NT), 0, st, p, geo, part);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

@@ -434,6 +434,10 @@ GQA_CASES = [
     ("bf16_dp256_g4", GQA["dsa_gqa_s4096"].replace(sq=600, topk=128), {}),
     ("bf16_dp256_g16_junk", GQA["dsa_gqa_s4096"].replace(sq=333, h=32, h_kv=2, topk=40), dict(junk=True)),
     ("bf16_dp512_mqa", GQA["dsa_gqa_s4096"].replace(sq=300, h=8, h_kv=1, d_qk=192, d_v=320, topk=50), {}),
+    ("bf16_dp64", GQA["dsa_gqa_s4096"].replace(sq=257, h=8, h_kv=2, d_qk=32, d_v=32, topk=30), {}),
+    ("f32_dp128", GQA["dsa_gqa_tiny_f32"].replace(sq=190, d_qk=64, d_v=64), {}),
+    ("bf16_dp256_one_head_per_group", GQA["dsa_gqa_s4096"].replace(sq=260, h=8, h_kv=8, topk=33), {}),
+    ("bf16_dp256_unequal_halves", GQA["dsa_gqa_s4096"].replace(sq=211, h=16, h_kv=4, d_qk=96, d_v=160, topk=40), {}),
 ]
 
 

@@ -303,7 +303,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="time the step only (skip the indexer loss, compressor epilogue and DSA-over-GQA lines)")
-    ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--cpu-rows", type=int, default=1536,
+                    help="query rows of the oracle's CPU sample (about 10-30 s of CPU work)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (HBM counter calibration)")
     args = ap.parse_args()

@@ -14,11 +14,21 @@
 // One KV head serves all h query heads, so the rows a query gathers are
 // shared by its heads and the natural matrix-core tile is (heads x rows x d).
 //
-// Forward and dQ (query-major, sparse): a wave owns one query and a group of
-// 16*HT heads and walks its candidate list in chunks of 32 rows (window rows
-// first, then compressed slots).  Rows are loaded from global memory straight
-// into MFMA operand registers; a wave-private LDS tile holds the same rows
-// for the contraction over rows, read with ds_read_b64_tr_b16.
+// Forward and dQ (query-major, sparse): the G waves of a query each own 16*HT
+// of its heads and walk its candidate list in chunks of 32 rows (window rows
+// first, then compressed slots).  The lanes gather a chunk's rows into
+// registers while the previous chunk computes and store them into a
+// double-buffered, swizzled LDS tile that the query's waves share; the
+// logits read the tile as MFMA operands, and the contraction over rows reads
+// it transposed with ds_read_b64_tr_b16.
+//
+// Variants of the same kernels: packed documents (an LDS bit per window or
+// dense slot of the query's document); no window (W = 0: only selected rows;
+// a query without a candidate gets O = 0 and LSE = -inf); rows packed as
+// [k | v] with q = [q | 0] and dO = [0 | dO] (KSP > 0: the zero halves'
+// products are skipped), which is how the grouped-query path runs through
+// here; and in the key-stationary kernel, QS > 1 consecutive queries of few
+// heads each stacked in the 64 head slots.
 //
 // dKV / dC (key-stationary, masked): fp32 atomics cannot absorb one add per
 // (query, row, d) -- a row is selected by hundreds of queries -- so the row

@@ -474,3 +474,49 @@ def test_dsa_gqa_fwd_bwd(gpu, name, wl, kw):
     check_close("dq", dq, rdq, tol)
     check_close("dk", dk, rdk, tol)
     check_close("dv", dv, rdv, tol)
+
+
+def test_indexer_loss_dense_warmup_by_composition(gpu):
+    """The dense warm-up form of the distillation loss (teacher and student
+    over every valid block, not only the selected ones) composed from the
+    entry points: the indexer with K' = n_c returns every valid block and its
+    score, the attention's dense mode returns the dense LSE, and the loss
+    takes both."""
+    import compressed_sparse_attention_softmax_amd as csa
+    from oracle import indexer_loss as il
+    wl = CSA4_SMALL.replace(sq=700)
+    wl = wl.replace(topk=wl.n_c)
+    say(f"[indexer_loss dense warm-up] sq={wl.sq} n_c={wl.n_c}")
+    inp = csa_synth.make_inputs(wl, 43, device="cuda", parts=("attn", "compress", "index"))
+    b, S, H, D, nc = wl.b, wl.sq, wl.h, wl.d, wl.n_c
+    dm = csa.dims_of(wl)
+    c = torch.tensor(oracle.compress(f64(inp["x"]), f64(inp["z"]), wl.ratio, wl.span)).to(wl.torch_dtype).cuda()
+    idx = torch.empty(b, S, nc, dtype=torch.int32, device="cuda")
+    sc = torch.empty(b, S, nc, device="cuda")
+    csa.csa_index_topk(dm, inp["q_i"], inp["k_i"], inp["w"], idx, sc)
+    out = torch.empty(b, S, H, D, dtype=wl.torch_dtype, device="cuda")
+    lse = torch.empty(b, S, H, device="cuda")
+    csa.csa_sparse_attn_fwd(dm, inp["q"], inp["kv"], c, None, inp["sink"], wl.scale, out, lse)
+    kl = torch.empty(b, S, device="cuda")
+    dkl = torch.ones(b, S, device="cuda")
+    dq_i = torch.empty_like(inp["q_i"])
+    dw = torch.empty(b, S, wl.idx_heads, device="cuda")
+    dk_i = torch.empty(b, nc, wl.idx_dim, device="cuda")
+    ws = torch.empty(csa.csa_indexer_loss_workspace(dm), dtype=torch.uint8, device="cuda")
+    csa.csa_indexer_loss(dm, inp["q"], c, lse, inp["q_i"], inp["k_i"], inp["w"], idx, sc, wl.scale, kl=kl, dkl=dkl,
+                         dq_i=dq_i, dw=dw, dk_i=dk_i, ws=ws)
+    torch.cuda.synchronize()
+    rows = oracle.all_rows(b, S)
+    # every valid block, in order: exactly what the indexer must return at K' = n_c
+    nv = np.minimum((rows[:, 1] + 1) // wl.ratio, nc)
+    full = np.where(np.arange(nc)[None, :] < nv[:, None], np.arange(nc)[None, :], -1).astype(np.int32)
+    np.testing.assert_array_equal(idx.cpu().numpy().reshape(-1, nc), full)
+    q64 = f64(inp["q"]).reshape(b * S, H, D)
+    _, rl = oracle.attn_fwd(q64, f64(inp["kv"]), f64(c), None, f64(inp["sink"]), wl.scale, wl.window, wl.ratio, rows)
+    qi, w = f64(inp["q_i"]).reshape(b * S, wl.idx_heads, wl.idx_dim), f64(inp["w"]).reshape(b * S, wl.idx_heads)
+    got = il.indexer_loss(q64, f64(c), rl, qi, f64(inp["k_i"]), w, full, wl.scale, wl.ratio, rows, dkl=np.ones(b * S))
+    tol = tol_of(wl.torch_dtype)
+    check_close("kl", kl.reshape(-1), got["kl"], tol)
+    check_close("dq_i", dq_i.reshape(b * S, wl.idx_heads, wl.idx_dim), got["dq_i"], tol)
+    check_close("dw", dw.reshape(b * S, wl.idx_heads), got["dw"], tol)
+    check_close("dk_i", dk_i, got["dk_i"], tol)

@@ -607,6 +607,13 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
     // multiplicities of the tile's rows for query t in cnt buffer `cb`.
     constexpr int IDX_REGS = 2048 / NT;           // K' <= 2048
     int jreg[IDX_REGS];
+    // stacked queries with a selection bitmap: stage() loads the bitmap words
+    // of the stack's (query, tile row) entries and the queries' repeat flags,
+    // and the following count() turns them into multiplicities
+    static_assert(QS == 1 || CTR % NT == 0, "whole bitmap entries per thread");
+    constexpr int SEL_REGS = QS > 1 ? CTR / NT : 1;
+    [[maybe_unused]] uint32_t sword[SEL_REGS];
+    [[maybe_unused]] uint32_t srep = 0u;
     auto stage = [&](int t, int buf, int cb) {
         const int64_t qrow = (int64_t)bi * p.S + t;
         const T* qsrc = (const T*)p.q + qrow * p.H * D;
@@ -680,13 +687,34 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
                     if (!dcol || dcol[j * p.r] == dt) cnt[j - tile_lo] = 1u;
             }
         }
+        if constexpr (QS > 1) {
+            if (!win && p.idx && p.selmap) {
+                const uint32_t* mrow = p.selmap + (int64_t)bi * p.S * p.selw;
+#pragma unroll
+                for (int k = 0; k < SEL_REGS; ++k) {
+                    const int e = threadIdx.x + NT * k, tq = t + e / TR, key = tile_lo + e % TR;
+                    sword[k] = (tq < tb && key < tile_hi) ? mrow[(int64_t)tq * p.selw + (key >> 5)] : 0u;
+                }
+                srep = (lane < QS && t + lane < tb) ? mrow[(int64_t)(t + lane) * p.selw + p.selw - 1] : 0u;
+            }
+        }
     };
     // multiplicities of the tile's rows for query t from the staged index entries
     auto count = [&](int t, int cb) {
         if (win || !p.idx) return;
         unsigned* cnt = cnt_lds + cb * CTR;
         if constexpr (QS > 1) {
-            // the stack's index rows, read here (no register prefetch)
+            // bitmap path: every wave loaded the same repeat flags, so all
+            // threads take the same branch; a bit is a multiplicity of 0 or 1
+            if (p.selmap && !__any(srep != 0u)) {
+#pragma unroll
+                for (int k = 0; k < SEL_REGS; ++k) {
+                    const int e = threadIdx.x + NT * k, key = tile_lo + e % TR;
+                    cnt[e] = (sword[k] >> (key & 31)) & 1u;
+                }
+                return;
+            }
+            // a stack with a repeated entry (or no bitmap): its index rows, read here
             for (int qs = 0; qs < QS && t + qs < tb; ++qs) {
                 const int tq = t + qs;
                 const int nvq = min((tq + 1) / p.r, p.nc);
@@ -1092,6 +1120,7 @@ template <typename T, int D>
 hipError_t launch_rows(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStream_t st)
 {
     if constexpr (sizeof(T) == 2 && D == 256) {
+        // the same test as attn_bwd_stacks_queries
         if (p.W == 0 && p.idx && p.H <= 16 && geo.Qb % 16 == 0) {
             if (p.H <= 4) return launch_rows_qs<T, D, 16>(p, geo, ws, st);
             if (p.H <= 8) return launch_rows_qs<T, D, 8>(p, geo, ws, st);
@@ -1117,7 +1146,57 @@ hipError_t rows_dispatch(const AttnArgs& p, const RowsGeom& geo, float* ws, hipS
     }
 }
 
+// Selection bitmap of the index rows: one workgroup per (query, batch) sets
+// the bits of the query's valid entries in LDS (an entry whose bit is already
+// set is a repeat), then writes the row of words and the repeat flag.
+__global__ __launch_bounds__(256) void selmap_kernel(const int32_t* __restrict__ idx, uint32_t* __restrict__ map,
+                                                     int S, int kp, int r, int nc, int selw)
+{
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    uint32_t* bits = reinterpret_cast<uint32_t*>(smem);
+    __shared__ uint32_t rep;
+    const int t = blockIdx.x, nw = selw - 1;
+    const int64_t row = (int64_t)blockIdx.y * S + t;
+    for (int i = threadIdx.x; i < nw; i += 256) bits[i] = 0u;
+    if (threadIdx.x == 0) rep = 0u;
+    __syncthreads();
+    const int nv = min((t + 1) / r, nc);
+    const int32_t* irow = idx + row * kp;
+    for (int s = threadIdx.x; s < kp; s += 256) {
+        const int j = irow[s];
+        if (j >= 0 && j < nv) {
+            const uint32_t bit = 1u << (j & 31);
+            if (atomicOr(&bits[j >> 5], bit) & bit) atomicOr(&rep, 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t* out = map + row * selw;
+    for (int i = threadIdx.x; i < nw; i += 256) out[i] = bits[i];
+    if (threadIdx.x == 0) out[nw] = rep;
+}
+
 }  // namespace
+
+int selmap_words(const AttnArgs& p)
+{
+    const int64_t w = ((int64_t)p.nc + 31) / 32 + 1;
+    return (w - 1) * 4 <= 64 * 1024 ? (int)w : 0;
+}
+
+hipError_t build_selmap(const AttnArgs& p, uint32_t* map, hipStream_t st)
+{
+    const int w = selmap_words(p);
+    if (!p.idx || w == 0 || p.b > 65535) return hipErrorInvalidValue;
+    if (p.S == 0) return hipSuccess;
+    hipLaunchKernelGGL(selmap_kernel, dim3((unsigned)p.S, (unsigned)p.b), dim3(256), (size_t)(w - 1) * 4, st, p.idx, map,
+                       p.S, p.kp, p.r, p.nc, w);
+    return hipGetLastError();
+}
+
+bool attn_bwd_stacks_queries(const AttnArgs& p, bool bf16)
+{
+    return bf16 && p.D == 256 && p.W == 0 && p.idx && p.H <= 16 && rows_geometry(p).Qb % 16 == 0;
+}
 
 size_t attn_bwd_workspace_bytes(const AttnArgs& p)
 {

@@ -58,6 +58,12 @@ struct AttnArgs {
     // grouped-query path): the first dsplit channels are the key half; the
     // kernels skip the products with a zero half (0: no packing)
     int dsplit;
+    // optional selection bitmap of the index rows (built by build_selmap):
+    // row (b, t) holds selw words, bit j of the first selw - 1 words set when
+    // a valid entry of idx[b, t] names row j, and a last word that is nonzero
+    // when such an entry repeats.  nullptr: the kernels scan the index rows.
+    const uint32_t* selmap;
+    int selw;
 };
 
 // Indexer distillation loss (teacher from the attention LSE, KL over the
@@ -106,6 +112,13 @@ size_t topk_lds_bytes(int DI, int elem, int cap);
 hipError_t attn_fwd(const AttnArgs& p, bool bf16, hipStream_t st);
 hipError_t attn_bwd(const AttnArgs& p, bool bf16, float* ws, hipStream_t st);
 size_t attn_bwd_workspace_bytes(const AttnArgs& p);
+// words per selection-bitmap row for p (0: too wide to build on chip)
+int selmap_words(const AttnArgs& p);
+// map: p.b * p.S * selmap_words(p) words; fills it from p.idx
+hipError_t build_selmap(const AttnArgs& p, uint32_t* map, hipStream_t st);
+// true when the backward's key-stationary kernel stacks queries (and then
+// reads p.selmap when it is set)
+bool attn_bwd_stacks_queries(const AttnArgs& p, bool bf16);
 hipError_t indexer_loss(const LossArgs& p, bool bf16, float* ws, hipStream_t st);
 size_t indexer_loss_workspace_bytes(const LossArgs& p);
 size_t dsa_gqa_workspace_bytes(const GqaArgs& p, bool bf16, bool bwd);

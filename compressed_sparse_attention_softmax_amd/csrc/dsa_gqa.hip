@@ -33,7 +33,8 @@ constexpr int NT = 256;
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 struct Layout {
-    size_t rows, q, out, lse, dout, dq, dc, dkv, attn, total;
+    size_t rows, q, out, lse, dout, dq, dc, dkv, attn, sel, total;
+    int selw;   // words per selection-bitmap row (0: no bitmap)
 };
 
 AttnArgs group_args(const GqaArgs& p)
@@ -64,6 +65,10 @@ Layout layout(const GqaArgs& p, size_t e, bool bwd)
         l.dc = off;   off += align256(bs * Dp * 4);
         l.dkv = off;  off += align256(bs * Dp * 4);
         l.attn = off; off += align256(attn_bwd_workspace_bytes(a));
+        // the selection bitmap, built once and read by every group's backward
+        a.idx = reinterpret_cast<const int32_t*>(16);
+        l.selw = attn_bwd_stacks_queries(a, e == 2) ? selmap_words(a) : 0;
+        l.sel = off;  off += align256((size_t)p.b * p.S * l.selw * 4);
     }
     l.total = off;
     return l;
@@ -198,9 +203,11 @@ hipError_t run_bwd(const GqaArgs& p, char* ws, hipStream_t st)
     float* dcg = reinterpret_cast<float*>(ws + l.dc);
     float* dkvg = reinterpret_cast<float*>(ws + l.dkv);
     float* aws = reinterpret_cast<float*>(ws + l.attn);
+    uint32_t* sel = l.selw ? reinterpret_cast<uint32_t*>(ws + l.sel) : nullptr;
     hipLaunchKernelGGL(pack_rows_kernel<T>, grid_for((int64_t)p.HKV * bs * dp), dim3(NT), 0, st, (const T*)p.k,
                        (const T*)p.v, rows, bs, p.HKV, p.DK, p.DV);
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess && sel) e = build_selmap(group_args(p), sel, st);
     for (int g = 0; g < p.HKV && e == hipSuccess; ++g) {
         hipLaunchKernelGGL(pack_heads_kernel<T>, grid_for(bs * hg * dp), dim3(NT), 0, st, (const T*)p.q, qg, bs,
                            p.H, hg, g, p.DK, dp, 0);
@@ -219,6 +226,8 @@ hipError_t run_bwd(const GqaArgs& p, char* ws, hipStream_t st)
         a.dq = dqg;
         a.dkv = dkvg;
         a.dc = dcg;
+        a.selmap = sel;
+        a.selw = l.selw;
         if ((e = attn_bwd(a, sizeof(T) == 2, aws, st)) != hipSuccess) break;
         hipLaunchKernelGGL((unpack_heads_kernel<T, T>), grid_for(bs * hg * p.DK), dim3(NT), 0, st, dqg, (T*)p.dq, bs,
                            p.H, hg, g, p.DK, dp, 0);

@@ -402,7 +402,9 @@ def _gqa_indices(wl, inp, junk=False):
     b, S = wl.b, wl.sq
     idx, _, _ = oracle.index_topk(f64(inp["q_i"]), f64(inp["k_i"]), np.ones((b, S, 1)), 1, wl.topk)
     idx = np.asarray(idx, dtype=np.int32).reshape(b, S, wl.kprime).copy()
-    if junk:
+    if junk == "one":
+        idx[:, 40, 1] = idx[:, 40, 0]                            # one repeat: its stack scans the index rows
+    elif junk:
         idx[:, 3::5, 1] = idx[:, 3::5, 0]                        # repeated entry
         idx[:, 7, :] = -1                                        # a query with no valid slot
         idx[:, 11::7, -1] = np.minimum(np.arange(11, S, 7) + 3, S - 1)[None, :]   # not yet valid
@@ -438,6 +440,7 @@ GQA_CASES = [
     ("f32_dp128", GQA["dsa_gqa_tiny_f32"].replace(sq=190, d_qk=64, d_v=64), {}),
     ("bf16_dp256_one_head_per_group", GQA["dsa_gqa_s4096"].replace(sq=260, h=8, h_kv=8, topk=33), {}),
     ("bf16_dp256_unequal_halves", GQA["dsa_gqa_s4096"].replace(sq=211, h=16, h_kv=4, d_qk=96, d_v=160, topk=40), {}),
+    ("bf16_dp256_g4_one_repeat", GQA["dsa_gqa_s4096"].replace(sq=400, h=8, h_kv=2, topk=64), dict(junk="one")),
 ]
 
 

@@ -21,6 +21,8 @@
 // The groups run one after another on the caller's stream; the packing and
 // unpacking kernels are plain element-wise copies.  At other widths the zero
 // halves cost matrix-core work (about half of each product).
+#include <initializer_list>
+
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
 
@@ -74,10 +76,14 @@ Layout layout(const GqaArgs& p, size_t e, bool bwd)
     return l;
 }
 
+// The copies below move whole 16-byte units (U = uint4) when every width is
+// a multiple of one and every tensor is 16-byte aligned, else single
+// elements (U = the element type); widths and offsets are in units of U.
+
 // rows[g, b, s, :] = [k[b, s, g, :] | v[b, s, g, :]]
-template <typename T>
-__global__ __launch_bounds__(NT) void pack_rows_kernel(const T* __restrict__ k, const T* __restrict__ v,
-                                                       T* __restrict__ rows, int64_t bs, int hkv, int dk, int dv)
+template <typename U>
+__global__ __launch_bounds__(NT) void pack_rows_kernel(const U* __restrict__ k, const U* __restrict__ v,
+                                                       U* __restrict__ rows, int64_t bs, int hkv, int dk, int dv)
 {
     const int dp = dk + dv;
     const int64_t n = (int64_t)hkv * bs * dp;
@@ -90,56 +96,61 @@ __global__ __launch_bounds__(NT) void pack_rows_kernel(const T* __restrict__ k, 
     }
 }
 
-// dst[b, s, hl, :] = [zeros(lo) | src[b, s, g * hg + hl, :] | zeros(hi)] with
-// the source row placed at column `at` (0: the k half, dk: the v half)
-template <typename T>
-__global__ __launch_bounds__(NT) void pack_heads_kernel(const T* __restrict__ src, T* __restrict__ dst, int64_t bs,
-                                                        int H, int hg, int g, int w, int dp, int at)
+// Heads g*hg + hl of q (and, in the backward, of O and dO) into the group's
+// packed buffers [q | 0], [0 | O], [0 | dO].  The zero halves are written
+// only when `zeros` (the buffers are reused group after group and the halves
+// stay zero); the backward also gathers the group's LSE columns.
+template <typename U>
+__global__ __launch_bounds__(NT) void pack_group_kernel(const U* __restrict__ q, const U* __restrict__ out,
+                                                        const U* __restrict__ dout, U* __restrict__ qg,
+                                                        U* __restrict__ og, U* __restrict__ dog,
+                                                        const float* __restrict__ lse, float* __restrict__ lg,
+                                                        int64_t bs, int H, int hg, int g, int dk, int dv, int zeros)
 {
+    const int dp = dk + dv;
     const int64_t n = bs * hg * dp;
     for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
         const int c = (int)(i % dp);
-        const int64_t sh = i / dp;
-        const int hl = (int)(sh % hg);
-        const int64_t s = sh / hg;
-        const int cc = c - at;
-        dst[i] = (cc >= 0 && cc < w) ? src[(s * H + g * hg + hl) * w + cc] : (T)0.0f;
+        const int64_t sh = i / dp;                                  // s * hg + hl
+        const int64_t srow = (sh / hg) * H + g * hg + sh % hg;      // row of the full-head tensors
+        if (c < dk) {
+            qg[i] = q[srow * dk + c];
+            if (zeros && og) {
+                og[i] = U{};
+                dog[i] = U{};
+            }
+        } else {
+            if (og) {
+                og[i] = out[srow * dv + (c - dk)];
+                dog[i] = dout[srow * dv + (c - dk)];
+            }
+            if (zeros) qg[i] = U{};
+        }
+        if (lg && c == 0) lg[sh] = lse[srow];
     }
 }
 
-// dst[b, s, g * hg + hl, :] = src[b, s, hl, at : at + w]  (dst of type U)
-template <typename T, typename U>
-__global__ __launch_bounds__(NT) void unpack_heads_kernel(const T* __restrict__ src, U* __restrict__ dst, int64_t bs,
-                                                          int H, int hg, int g, int w, int dp, int at)
+// dst[b, s, g * hg + hl, :] = src[b, s, hl, at : at + w], and (forward) the
+// group's LSE columns back into the full-head LSE
+template <typename U>
+__global__ __launch_bounds__(NT) void unpack_group_kernel(const U* __restrict__ src, U* __restrict__ dst,
+                                                          const float* __restrict__ lg, float* __restrict__ lse,
+                                                          int64_t bs, int H, int hg, int g, int w, int dp, int at)
 {
     const int64_t n = bs * hg * w;
     for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
         const int c = (int)(i % w);
         const int64_t sh = i / w;
-        const int hl = (int)(sh % hg);
-        const int64_t s = sh / hg;
-        dst[(s * H + g * hg + hl) * w + c] = (U)to_f32(src[(s * hg + hl) * dp + at + c]);
+        const int64_t srow = (sh / hg) * H + g * hg + sh % hg;
+        dst[srow * w + c] = src[sh * dp + at + c];
+        if (lse && c == 0) lse[srow] = lg[sh];
     }
 }
 
-// lse[b, s, g * hg + hl] = src[b, s, hl], or the reverse (to_group)
-__global__ __launch_bounds__(NT) void move_lse_kernel(const float* __restrict__ src, float* __restrict__ dst,
-                                                      int64_t bs, int H, int hg, int g, int to_group)
-{
-    const int64_t n = bs * hg;
-    for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
-        const int64_t s = i / hg;
-        const int hl = (int)(i % hg);
-        const int64_t full = s * H + g * hg + hl;
-        if (to_group) dst[i] = src[full];
-        else dst[full] = src[i];
-    }
-}
-
-// dk[b, s, g, :] = dc[b, s, 0:dk], dv[b, s, g, :] = dc[b, s, dk:]
-__global__ __launch_bounds__(NT) void unpack_kv_kernel(const float* __restrict__ dc, float* __restrict__ dkk,
-                                                       float* __restrict__ dvv, int64_t bs, int hkv, int g, int dk,
-                                                       int dv)
+// dk[b, s, g, :] = dc[b, s, 0:dk], dv[b, s, g, :] = dc[b, s, dk:]   (fp32)
+template <typename U>
+__global__ __launch_bounds__(NT) void unpack_kv_kernel(const U* __restrict__ dc, U* __restrict__ dkk,
+                                                       U* __restrict__ dvv, int64_t bs, int hkv, int g, int dk, int dv)
 {
     const int dp = dk + dv;
     const int64_t n = bs * dp;
@@ -157,8 +168,53 @@ dim3 grid_for(int64_t n)
     return dim3((unsigned)(blocks < 8192 ? (blocks > 0 ? blocks : 1) : 8192));
 }
 
-template <typename T>
-hipError_t run_fwd(const GqaArgs& p, char* ws, hipStream_t st)
+bool units16(std::initializer_list<const void*> ptrs, std::initializer_list<int64_t> bytes)
+{
+    for (const void* q : ptrs)
+        if (((uintptr_t)q) & 15) return false;
+    for (int64_t b : bytes)
+        if (b % 16) return false;
+    return true;
+}
+
+// element copies in units of U: V elements of T per unit
+template <typename T, typename U>
+struct Packer {
+    static constexpr int V = (int)(sizeof(U) / sizeof(T));
+    const GqaArgs& p;
+    int64_t bs;
+    int hg, dp;
+    hipStream_t st;
+
+    void rows(T* dst) const
+    {
+        const int64_t n = (int64_t)p.HKV * bs * dp / V;
+        hipLaunchKernelGGL(pack_rows_kernel<U>, grid_for(n), dim3(NT), 0, st, (const U*)p.k, (const U*)p.v, (U*)dst, bs,
+                           p.HKV, p.DK / V, p.DV / V);
+    }
+    void group_in(int g, T* qg, T* og, T* dog, float* lg, bool zeros) const
+    {
+        hipLaunchKernelGGL(pack_group_kernel<U>, grid_for(bs * hg * dp / V), dim3(NT), 0, st, (const U*)p.q,
+                           (const U*)p.out, (const U*)p.dout, (U*)qg, (U*)og, (U*)dog, p.lse, lg, bs, p.H, hg, g,
+                           p.DK / V, p.DV / V, zeros ? 1 : 0);
+    }
+    void group_out(int g, const T* src, T* dst, const float* lg, float* lse, int w, int at) const
+    {
+        hipLaunchKernelGGL(unpack_group_kernel<U>, grid_for(bs * hg * w / V), dim3(NT), 0, st, (const U*)src, (U*)dst,
+                           lg, lse, bs, p.H, hg, g, w / V, dp / V, at / V);
+    }
+};
+
+template <typename U>
+void unpack_kv(const GqaArgs& p, const float* dc, int64_t bs, int g, hipStream_t st)
+{
+    constexpr int V = (int)(sizeof(U) / sizeof(float));
+    hipLaunchKernelGGL(unpack_kv_kernel<U>, grid_for(bs * (p.DK + p.DV) / V), dim3(NT), 0, st, (const U*)dc, (U*)p.dk,
+                       (U*)p.dv, bs, p.HKV, g, p.DK / V, p.DV / V);
+}
+
+template <typename T, typename U>
+hipError_t run_fwd_u(const GqaArgs& p, char* ws, hipStream_t st)
 {
     const Layout l = layout(p, sizeof(T), false);
     const int hg = p.H / p.HKV, dp = p.DK + p.DV;
@@ -167,12 +223,11 @@ hipError_t run_fwd(const GqaArgs& p, char* ws, hipStream_t st)
     T* qg = reinterpret_cast<T*>(ws + l.q);
     T* og = reinterpret_cast<T*>(ws + l.out);
     float* lg = reinterpret_cast<float*>(ws + l.lse);
-    hipLaunchKernelGGL(pack_rows_kernel<T>, grid_for((int64_t)p.HKV * bs * dp), dim3(NT), 0, st, (const T*)p.k,
-                       (const T*)p.v, rows, bs, p.HKV, p.DK, p.DV);
+    const Packer<T, U> pk{p, bs, hg, dp, st};
+    pk.rows(rows);
     hipError_t e = hipGetLastError();
     for (int g = 0; g < p.HKV && e == hipSuccess; ++g) {
-        hipLaunchKernelGGL(pack_heads_kernel<T>, grid_for(bs * hg * dp), dim3(NT), 0, st, (const T*)p.q, qg, bs,
-                           p.H, hg, g, p.DK, dp, 0);
+        pk.group_in(g, qg, nullptr, nullptr, nullptr, g == 0);
         if ((e = hipGetLastError()) != hipSuccess) break;
         AttnArgs a = group_args(p);
         a.q = qg;
@@ -180,16 +235,14 @@ hipError_t run_fwd(const GqaArgs& p, char* ws, hipStream_t st)
         a.out = og;
         a.lse = lg;
         if ((e = attn_fwd(a, sizeof(T) == 2, st)) != hipSuccess) break;
-        hipLaunchKernelGGL((unpack_heads_kernel<T, T>), grid_for(bs * hg * p.DV), dim3(NT), 0, st, og, (T*)p.out, bs,
-                           p.H, hg, g, p.DV, dp, p.DK);
-        hipLaunchKernelGGL(move_lse_kernel, grid_for(bs * hg), dim3(NT), 0, st, lg, p.lse, bs, p.H, hg, g, 0);
+        pk.group_out(g, og, (T*)p.out, lg, p.lse, p.DV, p.DK);
         e = hipGetLastError();
     }
     return e;
 }
 
-template <typename T>
-hipError_t run_bwd(const GqaArgs& p, char* ws, hipStream_t st)
+template <typename T, typename U, typename UF>
+hipError_t run_bwd_u(const GqaArgs& p, char* ws, hipStream_t st)
 {
     const Layout l = layout(p, sizeof(T), true);
     const int hg = p.H / p.HKV, dp = p.DK + p.DV;
@@ -204,18 +257,12 @@ hipError_t run_bwd(const GqaArgs& p, char* ws, hipStream_t st)
     float* dkvg = reinterpret_cast<float*>(ws + l.dkv);
     float* aws = reinterpret_cast<float*>(ws + l.attn);
     uint32_t* sel = l.selw ? reinterpret_cast<uint32_t*>(ws + l.sel) : nullptr;
-    hipLaunchKernelGGL(pack_rows_kernel<T>, grid_for((int64_t)p.HKV * bs * dp), dim3(NT), 0, st, (const T*)p.k,
-                       (const T*)p.v, rows, bs, p.HKV, p.DK, p.DV);
+    const Packer<T, U> pk{p, bs, hg, dp, st};
+    pk.rows(rows);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && sel) e = build_selmap(group_args(p), sel, st);
     for (int g = 0; g < p.HKV && e == hipSuccess; ++g) {
-        hipLaunchKernelGGL(pack_heads_kernel<T>, grid_for(bs * hg * dp), dim3(NT), 0, st, (const T*)p.q, qg, bs,
-                           p.H, hg, g, p.DK, dp, 0);
-        hipLaunchKernelGGL(pack_heads_kernel<T>, grid_for(bs * hg * dp), dim3(NT), 0, st, (const T*)p.out, og, bs,
-                           p.H, hg, g, p.DV, dp, p.DK);
-        hipLaunchKernelGGL(pack_heads_kernel<T>, grid_for(bs * hg * dp), dim3(NT), 0, st, (const T*)p.dout, dog, bs,
-                           p.H, hg, g, p.DV, dp, p.DK);
-        hipLaunchKernelGGL(move_lse_kernel, grid_for(bs * hg), dim3(NT), 0, st, p.lse, lg, bs, p.H, hg, g, 1);
+        pk.group_in(g, qg, og, dog, lg, g == 0);
         if ((e = hipGetLastError()) != hipSuccess) break;
         AttnArgs a = group_args(p);
         a.q = qg;
@@ -229,13 +276,29 @@ hipError_t run_bwd(const GqaArgs& p, char* ws, hipStream_t st)
         a.selmap = sel;
         a.selw = l.selw;
         if ((e = attn_bwd(a, sizeof(T) == 2, aws, st)) != hipSuccess) break;
-        hipLaunchKernelGGL((unpack_heads_kernel<T, T>), grid_for(bs * hg * p.DK), dim3(NT), 0, st, dqg, (T*)p.dq, bs,
-                           p.H, hg, g, p.DK, dp, 0);
-        hipLaunchKernelGGL(unpack_kv_kernel, grid_for(bs * dp), dim3(NT), 0, st, dcg, p.dk, p.dv, bs, p.HKV, g, p.DK,
-                           p.DV);
+        pk.group_out(g, dqg, (T*)p.dq, nullptr, nullptr, p.DK, 0);
+        unpack_kv<UF>(p, dcg, bs, g, st);
         e = hipGetLastError();
     }
     return e;
+}
+
+template <typename T>
+hipError_t run_fwd(const GqaArgs& p, char* ws, hipStream_t st)
+{
+    const int64_t e = sizeof(T);
+    if (units16({p.q, p.k, p.v, p.out}, {p.DK * e, p.DV * e})) return run_fwd_u<T, uint4>(p, ws, st);
+    return run_fwd_u<T, T>(p, ws, st);
+}
+
+template <typename T>
+hipError_t run_bwd(const GqaArgs& p, char* ws, hipStream_t st)
+{
+    const int64_t e = sizeof(T);
+    const bool vt = units16({p.q, p.k, p.v, p.out, p.dout, p.dq}, {p.DK * e, p.DV * e});
+    const bool vf = units16({p.dk, p.dv}, {p.DK * 4, p.DV * 4});
+    if (vt) return vf ? run_bwd_u<T, uint4, uint4>(p, ws, st) : run_bwd_u<T, uint4, float>(p, ws, st);
+    return vf ? run_bwd_u<T, T, uint4>(p, ws, st) : run_bwd_u<T, T, float>(p, ws, st);
 }
 
 }  // namespace

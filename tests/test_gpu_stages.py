@@ -441,6 +441,9 @@ GQA_CASES = [
     ("bf16_dp256_one_head_per_group", GQA["dsa_gqa_s4096"].replace(sq=260, h=8, h_kv=8, topk=33), {}),
     ("bf16_dp256_unequal_halves", GQA["dsa_gqa_s4096"].replace(sq=211, h=16, h_kv=4, d_qk=96, d_v=160, topk=40), {}),
     ("bf16_dp256_g4_one_repeat", GQA["dsa_gqa_s4096"].replace(sq=400, h=8, h_kv=2, topk=64), dict(junk="one")),
+    # q starts 2 bytes past an alignment boundary: the packing copies single elements
+    ("bf16_dp128_misaligned_q", GQA["dsa_gqa_s4096"].replace(sq=300, h=8, h_kv=2, d_qk=64, d_v=64, topk=40),
+     dict(misalign=True)),
 ]
 
 
@@ -451,7 +454,12 @@ def test_dsa_gqa_fwd_bwd(gpu, name, wl, kw):
     say(f"[dsa gqa] {name} b={wl.b} sq={wl.sq} h={wl.h} h_kv={wl.h_kv} d_qk={wl.d_qk} d_v={wl.d_v} "
         f"K={wl.topk} {wl.dtype} {kw}")
     inp = csa_synth.make_gqa_inputs(wl, 29, device="cuda")
-    idx = _gqa_indices(wl, inp, **kw)
+    idx = _gqa_indices(wl, inp, junk=kw.get("junk", False))
+    if kw.get("misalign"):
+        qm = torch.empty(inp["q"].numel() + 1, dtype=inp["q"].dtype, device="cuda")[1:].view(inp["q"].shape)
+        qm.copy_(inp["q"])
+        assert qm.data_ptr() % 16 != 0
+        inp["q"] = qm
     g = csa.csa_gqa_dims(wl.b, wl.sq, wl.h, wl.h_kv, wl.d_qk, wl.d_v, wl.topk)
     dt = wl.torch_dtype
     b, S = wl.b, wl.sq

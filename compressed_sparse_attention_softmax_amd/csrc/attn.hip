@@ -39,7 +39,15 @@
 // pairs that are not candidates.  Partial sums per query block go to a
 // workspace and one reduction kernel adds them up: no atomics, and the sum
 // order is fixed.
+#include <algorithm>
+#include <array>
+#include <functional>
+#include <map>
+#include <mutex>
+#include <queue>
 #include <type_traits>
+#include <utility>
+#include <vector>
 
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
@@ -501,10 +509,19 @@ template <typename T, int D> constexpr bool rows_tile_in_lds()
     return !(sizeof(T) == 2 && D <= 128) && rows_lds_base<T, D>() + rows_lds_tile<T, D>() <= (size_t)ATTN_LDS_LIMIT;
 }
 
+// Workgroup schedule of the key-stationary kernel: with nmap > 0 the grid
+// has nmap workgroups and workgroup i takes unit map[i] = (batch, query
+// block) index * tiles + tile slot (ROWS_IDLE: none); the host fills the
+// table so that every unit of one query block runs on one XCD and the XCDs
+// get equal work.  nmap = 0: the closed-form round-robin schedule.
+constexpr int ROWS_MAP_MAX = 768;
+constexpr uint16_t ROWS_IDLE = 0xffff;
 struct RowsGeom {
     int Qb, nqb, WB, n_wt, n_ct, TR;   // query block, blocks, band rows, tiles, tile rows
     int64_t sink_off;                  // float offset of the per-query dsink terms [H, b*S]
     int64_t win_off, comp_off;         // float offsets of the two partial regions in the workspace
+    int nmap;
+    uint16_t map[ROWS_MAP_MAX];
 };
 
 template <typename T, int D, int RW, int NW, int QS, int KSP>
@@ -535,13 +552,24 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
     const int g = lane / 16, n16 = lane % 16;
     // Workgroups go to the 8 XCDs round-robin by linear id.  All tiles of one
     // query block are mapped to the same XCD, so its staged q / dO rows are
-    // fetched from HBM once into that XCD's L2; query blocks are dealt to the
-    // XCDs in turn, heaviest (latest queries: longest valid prefix) first.
+    // fetched from HBM once into that XCD's L2.  Without a schedule table,
+    // query blocks are dealt to the XCDs in turn, heaviest (latest queries:
+    // longest valid prefix) first; the table (rows_geometry) balances them.
     const int ntiles = geo.n_wt + (p.c ? geo.n_ct : 0);
-    const int lin = blockIdx.x, xcd = lin & 7, kx = lin >> 3;
-    const int qbi = (kx / ntiles) * 8 + xcd;     // index over (batch, query block)
+    const int lin = blockIdx.x;
+    int qbi, slot;                               // index over (batch, query block); tile slot
+    if (geo.nmap > 0) {
+        const int e = geo.map[lin];
+        if (e == ROWS_IDLE) return;
+        qbi = e / ntiles;
+        slot = e % ntiles;
+    } else {
+        const int xcd = lin & 7, kx = lin >> 3;
+        qbi = (kx / ntiles) * 8 + xcd;
+        slot = kx % ntiles;
+    }
     if (qbi >= p.b * geo.nqb) return;
-    const int bi = qbi / geo.nqb, qb = geo.nqb - 1 - qbi % geo.nqb, slot = kx % ntiles;
+    const int bi = qbi / geo.nqb, qb = geo.nqb - 1 - qbi % geo.nqb;
     const int t0 = qb * geo.Qb, t1 = min(p.S, t0 + geo.Qb);
     const bool win = slot < geo.n_wt;
     const int tile = win ? slot : slot - geo.n_wt;
@@ -969,19 +997,14 @@ __global__ void zero_fill_kernel(float* __restrict__ p, size_t n)
 // ------------------------------------------------------------------ host
 int rows_per_wave(int D) { return D <= 128 ? 64 : 16; }
 
-RowsGeom rows_geometry(const AttnArgs& p)
+namespace {
+
+// Layout of the key-stationary kernel's units and workspace for query blocks
+// of qb queries.
+void rows_layout(RowsGeom& g, const AttnArgs& p, int qb)
 {
-    RowsGeom g{};
-    g.TR = 4 * rows_per_wave(p.D);
     const int64_t D = p.D;
-    auto part_floats = [&](int qb) {
-        const int nqb = (p.S + qb - 1) / qb;
-        return (int64_t)p.b * nqb * ((int64_t)(p.W > 0 ? p.W - 1 + qb : 0) + p.nc) * D;
-    };
-    // window-free rows of every position (the grouped-query path) reach a
-    // whole causal prefix: longer query blocks keep the partial rows small
-    int qb = (p.W == 0 && p.r == 1) ? 128 : 32;
-    while (qb < 1024 && part_floats(qb) * 4 > ((int64_t)1 << 30)) qb *= 2;
+    g.TR = 4 * rows_per_wave(p.D);
     g.Qb = qb;
     g.nqb = (p.S + qb - 1) / qb;
     g.WB = p.W > 0 ? p.W - 1 + qb : 0;           // no window: no band rows
@@ -991,6 +1014,163 @@ RowsGeom rows_geometry(const AttnArgs& p)
     g.sink_off = delta_floats;
     g.win_off = g.sink_off + delta_floats;
     g.comp_off = g.win_off + (int64_t)p.b * g.nqb * g.WB * D;
+    g.nmap = 0;
+}
+
+int64_t rows_partial_floats(const AttnArgs& p, int qb)
+{
+    const int nqb = (p.S + qb - 1) / qb;
+    return (int64_t)p.b * nqb * ((int64_t)(p.W > 0 ? p.W - 1 + qb : 0) + p.nc) * p.D;
+}
+
+// Queries that unit (query block qb, tile slot) walks, as the kernel derives
+// them; -1 when the unit exits at once.
+int rows_unit_queries(const RowsGeom& g, const AttnArgs& p, int qb, int slot)
+{
+    const int t0 = qb * g.Qb, t1 = std::min(p.S, t0 + g.Qb);
+    const bool win = slot < g.n_wt;
+    const int i0 = (win ? slot : slot - g.n_wt) * g.TR;
+    if (win) {
+        if (i0 >= g.WB) return -1;
+        const int lo = t0 - p.W + 1 + i0, hi = t0 - p.W + 1 + std::min(i0 + g.TR, g.WB);
+        return std::max(0, std::min(t1, hi + p.W - 1) - std::max(t0, lo));
+    }
+    const int nvmax = std::min(t1 / p.r, p.nc);
+    if (i0 >= nvmax) return -1;
+    return std::max(0, t1 - std::max(t0, (i0 + 1) * p.r - 1));
+}
+
+// Cost model of a schedule: a unit costs its queries plus a fixed overhead
+// (row loads, pipeline fill, partial writes) in query steps; one workgroup
+// per CU; each XCD (32 CUs on MI355X) hands its units, in order, to the
+// first free CU.  Returns the finishing time of the last CU.
+constexpr int N_XCD = 8, CU_PER_XCD = 32;
+constexpr double UNIT_OVERHEAD = 2.0;
+
+double rows_makespan(const std::vector<double> (&lists)[N_XCD])
+{
+    double worst = 0.0;
+    for (int x = 0; x < N_XCD; ++x) {
+        std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
+        for (int i = 0; i < CU_PER_XCD; ++i) cu.push(0.0);
+        double last = 0.0;
+        for (const double c : lists[x]) {
+            const double t = cu.top() + c;
+            cu.pop();
+            cu.push(t);
+            last = std::max(last, t);
+        }
+        worst = std::max(worst, last);
+    }
+    return worst;
+}
+
+double unit_cost(int queries) { return queries < 0 ? 0.0 : queries + UNIT_OVERHEAD; }
+
+// the closed-form round-robin schedule of the kernel (nmap = 0)
+double rows_roundrobin_makespan(const RowsGeom& g, const AttnArgs& p)
+{
+    const int ntiles = g.n_wt + g.n_ct, nblk = p.b * g.nqb;
+    const int64_t grid = (int64_t)(nblk + 7) / 8 * 8 * ntiles;
+    std::vector<double> lists[N_XCD];
+    for (int64_t lin = 0; lin < grid; ++lin) {
+        const int xcd = (int)(lin & 7), kx = (int)(lin >> 3);
+        const int qbi = (kx / ntiles) * 8 + xcd;
+        if (qbi >= nblk) continue;
+        lists[xcd].push_back(unit_cost(rows_unit_queries(g, p, g.nqb - 1 - qbi % g.nqb, kx % ntiles)));
+    }
+    return rows_makespan(lists);
+}
+
+// A table schedule: query blocks, heaviest first, each to the XCD with the
+// fewest live units so far (then the least work); each XCD runs its units
+// longest first.  Returns false when the table would not fit.
+bool rows_table_plan(RowsGeom& g, const AttnArgs& p, double& makespan)
+{
+    const int ntiles = g.n_wt + g.n_ct, nblk = p.b * g.nqb;
+    if ((int64_t)nblk * ntiles > ROWS_MAP_MAX) return false;
+    struct Unit { int code; double cost; };
+    std::vector<std::vector<Unit>> blk(nblk);
+    std::vector<std::pair<double, int>> order;
+    for (int qbi = 0; qbi < nblk; ++qbi) {
+        double tot = 0.0;
+        for (int slot = 0; slot < ntiles; ++slot) {
+            const int n = rows_unit_queries(g, p, g.nqb - 1 - qbi % g.nqb, slot);
+            blk[qbi].push_back({qbi * ntiles + slot, unit_cost(n)});
+            tot += unit_cost(n);
+        }
+        order.push_back({-tot, qbi});
+    }
+    std::stable_sort(order.begin(), order.end());
+    std::vector<Unit> per[N_XCD];
+    int live[N_XCD] = {};
+    double work[N_XCD] = {};
+    for (const auto& o : order) {
+        int best = 0;
+        for (int x = 1; x < N_XCD; ++x)
+            if (live[x] < live[best] || (live[x] == live[best] && work[x] < work[best])) best = x;
+        for (const Unit& u : blk[o.second]) {
+            per[best].push_back(u);
+            live[best] += u.cost > 0.0;
+            work[best] += u.cost;
+        }
+    }
+    size_t len = 0;
+    std::vector<double> lists[N_XCD];
+    for (int x = 0; x < N_XCD; ++x) {
+        std::stable_sort(per[x].begin(), per[x].end(), [](const Unit& a, const Unit& b) { return a.cost > b.cost; });
+        for (const Unit& u : per[x]) lists[x].push_back(u.cost);
+        len = std::max(len, per[x].size());
+    }
+    if (len * N_XCD > (size_t)ROWS_MAP_MAX) return false;
+    makespan = rows_makespan(lists);
+    g.nmap = (int)(len * N_XCD);
+    for (int i = 0; i < g.nmap; ++i) {
+        const int x = i % N_XCD, k = i / N_XCD;
+        g.map[i] = k < (int)per[x].size() ? (uint16_t)per[x][k].code : ROWS_IDLE;
+    }
+    return true;
+}
+
+}  // namespace
+
+// Query block length and schedule of the key-stationary kernel.  They depend
+// on the dimensions only (never on which optional inputs are given), so the
+// workspace size a caller queries is the one the call uses.  The default is
+// 32 queries (doubled while the partial rows would exceed 1 GiB; 128 for the
+// window-free ratio-1 path) with the round-robin schedule; with a window,
+// block lengths of 16..128 with a balanced table are tried, and the one with
+// the shortest modelled finishing time wins.  Results are cached per shape.
+RowsGeom rows_geometry(const AttnArgs& p)
+{
+    using Key = std::array<int, 7>;
+    static std::mutex mu;
+    static std::map<Key, RowsGeom> cache;
+    const Key key{p.b, p.S, p.H, p.D, p.W, p.r, p.nc};
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        const auto it = cache.find(key);
+        if (it != cache.end()) return it->second;
+    }
+    int qb = (p.W == 0 && p.r == 1) ? 128 : 32;
+    while (qb < 1024 && rows_partial_floats(p, qb) * 4 > ((int64_t)1 << 30)) qb *= 2;
+    RowsGeom g{};
+    rows_layout(g, p, qb);
+    if (p.W > 0) {
+        double best = rows_roundrobin_makespan(g, p);
+        RowsGeom cand{};
+        for (int q = 16; q <= 128; ++q) {
+            if (rows_partial_floats(p, q) * 4 > ((int64_t)1 << 30)) continue;
+            rows_layout(cand, p, q);
+            double m;
+            if (rows_table_plan(cand, p, m) && m < best) {
+                best = m;
+                g = cand;
+            }
+        }
+    }
+    std::lock_guard<std::mutex> lk(mu);
+    cache.emplace(key, g);
     return g;
 }
 
@@ -1094,7 +1274,7 @@ hipError_t launch_rows_qk(const AttnArgs& p, const RowsGeom& geo, float* ws, hip
     if (e != hipSuccess) return e;
     const int ntiles = geo.n_wt + (p.c ? geo.n_ct : 0);
     const int64_t groups = ((int64_t)p.b * geo.nqb + 7) / 8;     // rounds of 8 query blocks
-    dim3 grid((unsigned)(groups * 8 * ntiles));
+    dim3 grid((unsigned)(geo.nmap > 0 ? geo.nmap : groups * 8 * ntiles));
     {
         TimedLaunch tl(K_ATTN_ROWS, st);
         hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, st, p, geo, ws, ws);

@@ -209,9 +209,14 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
         for (int ks = 0; ks < KS; ++ks)
             qb[ht][ks] = hv ? load_frag(qp + h * D + 32 * ks + 8 * g) : zero_frag<T>();
         if constexpr (!DQ) {
+            // the running reference starts finite: a chunk whose rows are all
+            // masked (another document) has logits -inf, and -inf against a
+            // reference of -inf gives NaN; the sink's mass relative to the
+            // reference seeds the sum
             const bool sk = p.sink && hv;
-            m2[ht] = sk ? p.sink[h] * LOG2E : -INFINITY;
-            const float l0 = sk ? 1.f : 0.f;
+            const float sl = sk ? p.sink[h] * LOG2E : -INFINITY;
+            m2[ht] = fmaxf(sl, -1e30f);
+            const float l0 = sk ? fast_exp2(sl - m2[ht]) : 0.f;
             lsum[ht] = f32x4{l0, l0, l0, l0};
         } else {
             // Delta[h] = <dO[t, h], O[t, h]>; dO kept as the B operand of dP^T

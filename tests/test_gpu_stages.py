@@ -304,6 +304,12 @@ ATTN_CASES = [
     ("csa4_bf16_docs_window_only", CSA4_SMALL.replace(sq=400), dict(window_only=True, doc_len=60)),
     ("csa4_bf16_docs_h48", CSA4_SMALL.replace(b=2, sq=333, h=48, topk=40), dict(idx_mode="indexer", doc_len=70)),
     ("d512_bf16_docs", D512_SMALL, dict(idx_mode="indexer", doc_len=80)),
+    # no sink, short documents: the first row chunks of many windows lie
+    # wholly in an earlier document (every logit of the chunk masked)
+    ("csa4_bf16_docs_nosink", CSA4_SMALL.replace(b=2, sq=500, topk=40),
+     dict(idx_mode="indexer", doc_len=40, with_sink=False)),
+    ("csa4_bf16_docs_window_only_nosink", CSA4_SMALL.replace(sq=400),
+     dict(window_only=True, doc_len=40, with_sink=False)),
     ("d512_bf16", D512_SMALL, {}),
     ("hca128_bf16_dense", HCA_SMALL, dict(idx_mode="dense")),
 ]

@@ -198,8 +198,11 @@ int csa_index_topk(const csa_dims* dm, int dtype, const void* q_i, const void* k
     if (dm->idx_heads > 64) return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: idx_heads=%d > 64", dm->idx_heads);
     if (dm->idx_dim != 32 && dm->idx_dim != 64 && dm->idx_dim != 128)
         return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: idx_dim=%d not in {32,64,128}", dm->idx_dim);
-    if (!q_i || !k_i || !idx) return fail(CSA_ERR_ARG, "csa_index_topk: q_i, k_i and idx must be non-NULL");
     const int kp = kprime(dm);
+    if (!q_i) return fail(CSA_ERR_ARG, "csa_index_topk: q_i must be non-NULL");
+    // sq < ratio: no block exists, K' = 0, idx / score / k_i have no elements
+    if (kp == 0) return ok();
+    if (!k_i || !idx) return fail(CSA_ERR_ARG, "csa_index_topk: k_i and idx must be non-NULL");
     if (kp > 2048) return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: K'=%d > 2048", kp);
     csa::IndexArgs a{};
     a.qi = q_i; a.ki = k_i; a.w = w; a.doc = doc_ids; a.idx = idx; a.score = score;

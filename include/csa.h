@@ -157,7 +157,8 @@ size_t csa_index_topk_workspace(const csa_dims* dims);
  * fp32 scores aligned with idx (-inf on -1 slots).  w is fp32 and already
  * holds any softmax scale of the indexer; w == NULL means unit weights (the
  * simplified one-head indexer).  ws may be NULL when
- * csa_index_topk_workspace() returns 0. */
+ * csa_index_topk_workspace() returns 0.  When sq < ratio no block exists
+ * (K' = 0): the call does nothing, and k_i, idx and score may be NULL. */
 int csa_index_topk(const csa_dims* dims, int dtype, const void* q_i, const void* k_i,
                    const float* w, const int32_t* doc_ids, int32_t* idx, float* score, void* ws,
                    size_t ws_bytes, void* stream);

@@ -120,6 +120,14 @@ def test_gradient_gate_is_all_or_nothing(missing):
     assert missing in _lib().csa_last_error().decode()
 
 
+def test_index_topk_without_blocks_is_a_noop():
+    # sq < ratio: K' = min(topk, n_c) = 0, so k_i, idx and score are empty (NULL)
+    lib = _lib()
+    assert lib.csa_index_topk(ctypes.byref(_d(sq=3)), 0, P, N, P, N, N, N, N, 0, N) == 0
+    assert lib.csa_index_topk(ctypes.byref(_d(sq=3)), 0, N, N, P, N, N, N, N, 0, N) == -1
+    assert lib.csa_index_topk(ctypes.byref(_d(sq=4)), 0, P, N, P, N, N, N, N, 0, N) == -1
+
+
 def test_gradient_gate_all_null_is_a_noop():
     assert _bwd(N, N, N, N) == 0
 

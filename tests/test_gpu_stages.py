@@ -151,6 +151,8 @@ INDEX_CASES = [
     ("csa4_bf16_b2_ragged", CSA4_SMALL.replace(b=2, sq=1027, topk=50), None),
     ("streaming_cuts", CSA4_SMALL.replace(sq=4096, topk=100), "256"),
     ("idx_dim64_heads40", CSA4_SMALL.replace(idx_heads=40, idx_dim=64, sq=900, topk=70), None),
+    ("one_block", CSA4_SMALL.replace(sq=5, topk=40), None),
+    ("b3_sq9", CSA4_SMALL.replace(b=3, sq=9, topk=1), None),
 ]
 
 
@@ -312,6 +314,13 @@ ATTN_CASES = [
      dict(window_only=True, doc_len=40, with_sink=False)),
     ("d512_bf16", D512_SMALL, {}),
     ("hca128_bf16_dense", HCA_SMALL, dict(idx_mode="dense")),
+    # degenerate lengths: one token; shorter than the ratio (no compressed
+    # row at all, the zero-size tensors arrive as NULL); one compressed row
+    ("tiny_f32_sq1", TINY.replace(sq=1), {}),
+    ("csa4_bf16_shorter_than_ratio", CSA4_SMALL.replace(sq=3), {}),
+    ("csa4_bf16_sq1_window_only", CSA4_SMALL.replace(sq=1), dict(window_only=True)),
+    ("csa4_bf16_sq5_dense", CSA4_SMALL.replace(sq=5), dict(idx_mode="dense")),
+    ("csa4_bf16_b3_sq9", CSA4_SMALL.replace(b=3, sq=9, topk=2), {}),
 ]
 
 

@@ -44,6 +44,22 @@ def test_maximum_sizes(gpu, name, wl, nf, nb):
     _whole_pass(wl, 17, nf, nb)
 
 
+# the shortest sequences: one token, shorter than the ratio (no compressed
+# row: the indexer has nothing to select and the attention sees the window
+# only), and one compressed row, in the bench's and the fp32 configuration
+MIN_CASES = [
+    ("csa4_sq1", csa_synth.WORKLOADS["csa4_s4096"].replace(sq=1)),
+    ("csa4_sq3", csa_synth.WORKLOADS["csa4_s4096"].replace(sq=3)),
+    ("csa4_sq5", csa_synth.WORKLOADS["csa4_s4096"].replace(sq=5)),
+    ("tiny_f32_sq3_b2", csa_synth.WORKLOADS["tiny_f32"].replace(b=2, sq=3)),
+]
+
+
+@pytest.mark.parametrize("name,wl", MIN_CASES, ids=[c[0] for c in MIN_CASES])
+def test_minimum_sizes(gpu, name, wl):
+    _whole_pass(wl, 19, 16, 16)
+
+
 def _whole_pass(wl, seed, n_rows, n_bwd_rows):
     import compressed_sparse_attention_softmax_amd as csa
     from compressed_sparse_attention_softmax_amd import pipeline
@@ -72,7 +88,7 @@ def _whole_pass(wl, seed, n_rows, n_bwd_rows):
     rows = sample_rows(b, S, n_rows, seed, must)
     rb, rt = rows[:, 0], rows[:, 1]
 
-    if wl.topk > 0:
+    if wl.topk > 0 and wl.kprime > 0:
         qi = f64(inp["q_i"][rb, rt])
         w = f64(inp["w"][rb, rt])
         dense = oracle.index_scores(qi, f64(inp["k_i"]), w, r, rows)

@@ -321,6 +321,12 @@ ATTN_CASES = [
     ("csa4_bf16_sq1_window_only", CSA4_SMALL.replace(sq=1), dict(window_only=True)),
     ("csa4_bf16_sq5_dense", CSA4_SMALL.replace(sq=5), dict(idx_mode="dense")),
     ("csa4_bf16_b3_sq9", CSA4_SMALL.replace(b=3, sq=9, topk=2), {}),
+    # head counts that leave head slots of the 16-wide tiles empty: one
+    # head, one past 32, and 17 heads at d = 64
+    ("csa4_bf16_h1", CSA4_SMALL.replace(sq=300, h=1, topk=40), {}),
+    ("csa4_bf16_h33", CSA4_SMALL.replace(sq=300, h=33, topk=40), {}),
+    ("bf16_d64_h17", CSA4_SMALL.replace(sq=300, h=17, d=64, z_channels=64, topk=40), {}),
+    ("tiny_f32_h5", TINY.replace(h=5), {}),
 ]
 
 

@@ -42,7 +42,7 @@ def count_work(wl, idx):
     bwd = 2 x fwd, indexer = sum_{b,t} n_valid(t) * idx_heads * 2 * idx_dim.  Padding (-1)
     and not-yet-valid slots are never counted."""
     import torch
-    dev = idx.device if idx is not None else "cuda"
+    dev = idx.device if idx is not None else "cpu"
     t = torch.arange(wl.sq, device=dev)
     nwin = torch.clamp(t + 1, max=wl.window)
     nv = torch.clamp((t + 1) // wl.ratio, max=wl.n_c)

@@ -248,11 +248,15 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
     [[maybe_unused]] Frag<T> ones;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones.v[e] = (T)1.0f;
+    // wide rows (d >= 256): the dQ accumulators live in AGPRs (inline-asm
+    // MFMAs, read once after a drain), which frees the VGPRs the d = 512 dq
+    // kernel otherwise spills; at d <= 128 the compiler's own allocation wins
+    constexpr bool OACC = DQ && sizeof(T) == 2 && D >= 256 && (DT * HT == 16 || DT * HT == 32);
     f32x4 o[DT][HT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) o[dt][ht] = f4zero();
+        for (int ht = 0; ht < HT; ++ht) o[dt][ht] = OACC ? agpr_zero() : f4zero();
 
     // Gather chunk c0's rows into registers; returns the chunk's candidate
     // mask.  Lane q = 64 sub + lane of the query's waves owns row q / LPR of the
@@ -383,7 +387,10 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
             if (KSP > 0 && (DQ ? dt >= 2 * KSP : dt < 2 * KSP)) continue;
             const Frag<T> a = rows_operand<T>(tile, D, 0, 16 * dt, true);
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) o[dt][ht] = mfma16(a, pb[ht], o[dt][ht]);
+            for (int ht = 0; ht < HT; ++ht) {
+                if constexpr (OACC) mfma16_acc(o[dt][ht], a, pb[ht]);
+                else o[dt][ht] = mfma16(a, pb[ht], o[dt][ht]);
+            }
         }
     };
 
@@ -448,6 +455,7 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
         // before its later writes to it.
         if constexpr (G > 1) __syncthreads();
     }
+    if constexpr (OACC) agpr_drain<DT * HT>(&o[0][0]);
     if (!active) return;
     // epilogue: lane holds X^T[d = 16 dt + 4g + i][h = h0 + 16 ht + n16]
 #pragma unroll

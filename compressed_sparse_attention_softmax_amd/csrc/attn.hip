@@ -265,8 +265,11 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
     const int my_r = (sub * WAVE + lane) / LPR, my_j = (sub * WAVE + lane) % LPR;
     piece_t rg[NPL];
     auto fetch = [&](int c0) -> uint32_t {
-        const uint32_t mask = (uint32_t)__ballot(cand.code(c0 + (lane & 31), use_ids, ids) >= 0);
-        const T* rp = cand.row_ptr(cand.code(c0 + my_r, use_ids, ids)) + my_j * E16;
+        // lane l (and l + 32) resolves slot c0 + l % 32; the lanes that load
+        // row my_r take its code from lane my_r
+        const int cl = cand.code(c0 + (lane & 31), use_ids, ids);
+        const uint32_t mask = (uint32_t)__ballot(cl >= 0);
+        const T* rp = cand.row_ptr(__shfl(cl, my_r)) + my_j * E16;
 #pragma unroll
         for (int k = 0; k < NPL; ++k) rg[k] = *reinterpret_cast<const piece_t*>(rp + k * LPR * E16);
         return mask;

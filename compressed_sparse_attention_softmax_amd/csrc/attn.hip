@@ -385,14 +385,28 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
         }
         // O^T += R^T P^T   (or dQ^T += R^T dS'^T); packed rows: O needs the
         // value half only, dQ the key half only
+        if constexpr (OACC) {
+            // AGPR accumulators: four d tiles per asm block (HT == 1, so
+            // o[dt .. dt+3][0] are consecutive); 2 * KSP is a multiple of 4
+            static_assert(HT == 1 && DT % 4 == 0 && (KSP == 0 || (2 * KSP) % 4 == 0), "OACC layout");
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            if (KSP > 0 && (DQ ? dt >= 2 * KSP : dt < 2 * KSP)) continue;
-            const Frag<T> a = rows_operand<T>(tile, D, 0, 16 * dt, true);
+            for (int dt = 0; dt < DT; dt += 4) {
+                if (KSP > 0 && (DQ ? dt >= 2 * KSP : dt < 2 * KSP)) continue;
+                Frag<T> a[4], b[4];
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                if constexpr (OACC) mfma16_acc(o[dt][ht], a, pb[ht]);
-                else o[dt][ht] = mfma16(a, pb[ht], o[dt][ht]);
+                for (int j = 0; j < 4; ++j) {
+                    a[j] = rows_operand<T>(tile, D, 0, 16 * (dt + j), true);
+                    b[j] = pb[0];
+                }
+                mfma16_4_acc(&o[dt][0], a, b);
+            }
+        } else {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                if (KSP > 0 && (DQ ? dt >= 2 * KSP : dt < 2 * KSP)) continue;
+                const Frag<T> a = rows_operand<T>(tile, D, 0, 16 * dt, true);
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) o[dt][ht] = mfma16(a, pb[ht], o[dt][ht]);
             }
         }
     };
@@ -893,17 +907,44 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
                 // (no scheduling barrier: the S / dP MFMAs of the next head tile
                 // interleave with this tile's exponentials)
             }
+            // dR += P^T dO + dS'^T q; bf16 accumulates in AGPRs through asm
+            // blocks of 8 (or 4) MFMAs.  Packed rows: the key half of dR is
+            // dS'^T q, the value half P^T dO (2 * KSP is a multiple of 4, so a
+            // group of four d tiles lies in one half).
+            if constexpr (sizeof(T) == 2 && RT == 2) {
+                static_assert(KSP == 0 && DT % 2 == 0, "two-row-tile blocks");
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                // packed rows: the key half of dR is dS'^T q, the value half P^T dO
-                const bool khalf = KSP > 0 && dt < 2 * KSP, vhalf = KSP > 0 && dt >= 2 * KSP;
-                const Frag<T> dob = khalf ? zero_frag<T>() : rows_operand<T>(do_lds, D, 32 * kk, 16 * dt, true);
-                const Frag<T> qbf = vhalf ? zero_frag<T>() : rows_operand<T>(q_lds, D, 32 * kk, 16 * dt, true);
-                if constexpr (sizeof(T) == 2 && RT == 4) {
-                    mfma16x8_acc(acc[0][dt], acc[1][dt], acc[2][dt], acc[3][dt], pa, sa, dob, qbf);
-                } else if constexpr (sizeof(T) == 2 && RT == 2) {
-                    mfma16x4_acc(acc[0][dt], acc[1][dt], pa, sa, dob, qbf);
-                } else {
+                for (int dt = 0; dt < DT; dt += 2) {
+                    Frag<T> dob[2], qbf[2];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        dob[j] = rows_operand<T>(do_lds, D, 32 * kk, 16 * (dt + j), true);
+                        qbf[j] = rows_operand<T>(q_lds, D, 32 * kk, 16 * (dt + j), true);
+                    }
+                    mfma16_2x2_acc(acc[0][dt], acc[0][dt + 1], acc[1][dt], acc[1][dt + 1], pa, sa, dob, qbf);
+                }
+            } else if constexpr (sizeof(T) == 2 && RT == 1) {
+                static_assert(DT % 4 == 0 && (KSP == 0 || (2 * KSP) % 4 == 0), "one-row-tile blocks");
+#pragma unroll
+                for (int dt = 0; dt < DT; dt += 4) {
+                    const bool khalf = KSP > 0 && dt < 2 * KSP, vhalf = KSP > 0 && dt >= 2 * KSP;
+                    Frag<T> dob[4], qbf[4], pp[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        dob[j] = khalf ? zero_frag<T>() : rows_operand<T>(do_lds, D, 32 * kk, 16 * (dt + j), true);
+                        qbf[j] = vhalf ? zero_frag<T>() : rows_operand<T>(q_lds, D, 32 * kk, 16 * (dt + j), true);
+                        pp[j] = khalf ? sa[0] : pa[0];
+                    }
+                    if (khalf) mfma16_4_acc(&acc[0][dt], pp, qbf);
+                    else if (vhalf) mfma16_4_acc(&acc[0][dt], pp, dob);
+                    else mfma16_1x4_acc(&acc[0][dt], pa[0], sa[0], dob, qbf);
+                }
+            } else {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const bool khalf = KSP > 0 && dt < 2 * KSP, vhalf = KSP > 0 && dt >= 2 * KSP;
+                    const Frag<T> dob = khalf ? zero_frag<T>() : rows_operand<T>(do_lds, D, 32 * kk, 16 * dt, true);
+                    const Frag<T> qbf = vhalf ? zero_frag<T>() : rows_operand<T>(q_lds, D, 32 * kk, 16 * dt, true);
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) {
                         if (!khalf) mfma16_acc(acc[rt][dt], pa[rt], dob);

@@ -41,14 +41,20 @@ __device__ __forceinline__ f32x4 mfma16(const Frag<float>& a, const Frag<float>&
 
 // Accumulating MFMA with the accumulator pinned to the AGPR file ("+a"): a
 // loop-carried accumulator then never moves between register files.  The
-// compiler's hazard checks do not look inside inline asm, so the asm carries
-// its own: s_nop 1 provides the two wait states an MFMA needs after a VALU
-// write of any of its source registers, and agpr_drain() must separate the
-// last of these MFMAs from every other read of the accumulators.  Back-to-back
-// accumulation into the same registers needs no wait states.
+// compiler's hazard checks do not look inside inline asm, so every asm block
+// below is self-contained: it opens with s_nop 1 (the 2 wait states an MFMA
+// needs after a VALU or v_accvgpr write of any of its sources) and closes
+// with CSA_MFMA_TAIL, 10 wait states: more than any read or write of a
+// v_mfma_f32_16x16x32_bf16 result needs on gfx950 (a 4-pass XDL op; the
+// compiler itself separates such a result from a VALU read by 8).  Whatever
+// the register allocator places after a block -- a copy of an accumulator, a
+// spill, a phi move at a loop exit -- therefore sees settled registers.
+// Back-to-back accumulation into the same registers inside a block needs no
+// wait states.  Blocks hold up to 8 MFMAs so that the tails cost little.
+#define CSA_MFMA_TAIL "\n\ts_nop 9"
 __device__ __forceinline__ void mfma16_acc(f32x4& acc, const Frag<bf16_t>& a, const Frag<bf16_t>& b)
 {
-    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a.v), "v"(b.v));
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" CSA_MFMA_TAIL : "+a"(acc) : "v"(a.v), "v"(b.v));
 }
 __device__ __forceinline__ void mfma16_acc(f32x4& acc, const Frag<float>& a, const Frag<float>& b)
 {
@@ -68,7 +74,7 @@ __device__ __forceinline__ void mfma16x8_acc(f32x4& c0, f32x4& c1, f32x4& c2, f3
         "v_mfma_f32_16x16x32_bf16 %0, %8, %13, %0\n\t"
         "v_mfma_f32_16x16x32_bf16 %1, %9, %13, %1\n\t"
         "v_mfma_f32_16x16x32_bf16 %2, %10, %13, %2\n\t"
-        "v_mfma_f32_16x16x32_bf16 %3, %11, %13, %3"
+        "v_mfma_f32_16x16x32_bf16 %3, %11, %13, %3" CSA_MFMA_TAIL
         : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3)
         : "v"(pa[0].v), "v"(pa[1].v), "v"(pa[2].v), "v"(pa[3].v), "v"(sa[0].v), "v"(sa[1].v), "v"(sa[2].v),
           "v"(sa[3].v), "v"(b0.v), "v"(b1.v));
@@ -83,9 +89,59 @@ __device__ __forceinline__ void mfma16x4_acc(f32x4& c0, f32x4& c1, const Frag<bf
         "v_mfma_f32_16x16x32_bf16 %0, %2, %6, %0\n\t"
         "v_mfma_f32_16x16x32_bf16 %1, %3, %6, %1\n\t"
         "v_mfma_f32_16x16x32_bf16 %0, %4, %7, %0\n\t"
-        "v_mfma_f32_16x16x32_bf16 %1, %5, %7, %1"
+        "v_mfma_f32_16x16x32_bf16 %1, %5, %7, %1" CSA_MFMA_TAIL
         : "+a"(c0), "+a"(c1)
         : "v"(pa[0].v), "v"(pa[1].v), "v"(sa[0].v), "v"(sa[1].v), "v"(b0.v), "v"(b1.v));
+}
+
+// Eight accumulating MFMAs: c_rj += pa[r] * b0[j], then c_rj += sa[r] * b1[j],
+// r, j = 0..1 (two row tiles x two column tiles of a product pair).
+__device__ __forceinline__ void mfma16_2x2_acc(f32x4& c00, f32x4& c01, f32x4& c10, f32x4& c11, const Frag<bf16_t>* pa,
+                                               const Frag<bf16_t>* sa, const Frag<bf16_t>* b0, const Frag<bf16_t>* b1)
+{
+    asm("s_nop 1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %0, %4, %8, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %2, %5, %8, %2\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %4, %9, %1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %3, %5, %9, %3\n\t"
+        "v_mfma_f32_16x16x32_bf16 %0, %6, %10, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %2, %7, %10, %2\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %6, %11, %1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %3, %7, %11, %3" CSA_MFMA_TAIL
+        : "+a"(c00), "+a"(c01), "+a"(c10), "+a"(c11)
+        : "v"(pa[0].v), "v"(pa[1].v), "v"(sa[0].v), "v"(sa[1].v), "v"(b0[0].v), "v"(b0[1].v), "v"(b1[0].v),
+          "v"(b1[1].v));
+}
+
+// Eight accumulating MFMAs: c_j += pa * b0[j], then c_j += sa * b1[j], j = 0..3
+// (one row tile x four column tiles of a product pair).
+__device__ __forceinline__ void mfma16_1x4_acc(f32x4* c, const Frag<bf16_t>& pa, const Frag<bf16_t>& sa,
+                                               const Frag<bf16_t>* b0, const Frag<bf16_t>* b1)
+{
+    asm("s_nop 1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %0, %4, %6, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %4, %7, %1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %2, %4, %8, %2\n\t"
+        "v_mfma_f32_16x16x32_bf16 %3, %4, %9, %3\n\t"
+        "v_mfma_f32_16x16x32_bf16 %0, %5, %10, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %5, %11, %1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %2, %5, %12, %2\n\t"
+        "v_mfma_f32_16x16x32_bf16 %3, %5, %13, %3" CSA_MFMA_TAIL
+        : "+a"(c[0]), "+a"(c[1]), "+a"(c[2]), "+a"(c[3])
+        : "v"(pa.v), "v"(sa.v), "v"(b0[0].v), "v"(b0[1].v), "v"(b0[2].v), "v"(b0[3].v), "v"(b1[0].v), "v"(b1[1].v),
+          "v"(b1[2].v), "v"(b1[3].v));
+}
+
+// Four independent accumulating MFMAs: c_j += a[j] * b[j], j = 0..3.
+__device__ __forceinline__ void mfma16_4_acc(f32x4* c, const Frag<bf16_t>* a, const Frag<bf16_t>* b)
+{
+    asm("s_nop 1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %0, %4, %8, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %5, %9, %1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %2, %6, %10, %2\n\t"
+        "v_mfma_f32_16x16x32_bf16 %3, %7, %11, %3" CSA_MFMA_TAIL
+        : "+a"(c[0]), "+a"(c[1]), "+a"(c[2]), "+a"(c[3])
+        : "v"(a[0].v), "v"(a[1].v), "v"(a[2].v), "v"(a[3].v), "v"(b[0].v), "v"(b[1].v), "v"(b[2].v), "v"(b[3].v));
 }
 
 // Zero accumulator created in the AGPR file (an MFMA of zero operands), so
@@ -99,9 +155,9 @@ __device__ __forceinline__ f32x4 agpr_zero()
     return acc;
 }
 
-// 32 wait states after the last mfma16_acc on accumulators a[0..N) (more than
-// the latest read-after-MFMA-write requirement), ordered after every one of
-// them because the asm reads and writes all N.
+// Ordering point after the last mfma16_acc on accumulators a[0..N): the asm
+// reads and writes all N, so no later use moves above it (the blocks are
+// already settled by their own MFMA_TAIL; the extra wait states are kept).
 template <int N> __device__ __forceinline__ void agpr_drain(f32x4* a);
 template <> __device__ __forceinline__ void agpr_drain<8>(f32x4* a)
 {

@@ -23,7 +23,8 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_ARG", -2: "CSA_ERR_SHAPE", -3: "CSA_ERR_DTYP
 
 # every symbol include/csa.h declares
 EXPORTS = ["csa_compress", "csa_compress_bwd_workspace", "csa_compress_bwd", "csa_index_topk_workspace", "csa_index_topk",
-           "csa_sparse_attn_fwd", "csa_sparse_attn_bwd_workspace", "csa_sparse_attn_bwd",
+           "csa_sparse_attn_fwd", "csa_sparse_attn_bwd_workspace", "csa_sparse_attn_bwd_query_block",
+           "csa_sparse_attn_bwd",
            "csa_indexer_loss_workspace", "csa_indexer_loss", "csa_dsa_gqa_workspace", "csa_dsa_gqa_fwd",
            "csa_dsa_gqa_bwd", "csa_last_error", "csa_version", "csa_timing_enable", "csa_timing_read", "csa_kernel_name"]
 
@@ -75,6 +76,8 @@ def load(path: Optional[str] = None):
     lib.csa_sparse_attn_fwd.argtypes = [D, i, vp, vp, vp, vp, vp, vp, f, vp, vp, vp]
     lib.csa_sparse_attn_bwd_workspace.argtypes = [D]
     lib.csa_sparse_attn_bwd_workspace.restype = sz
+    lib.csa_sparse_attn_bwd_query_block.argtypes = [D, i]
+    lib.csa_sparse_attn_bwd_query_block.restype = i
     lib.csa_sparse_attn_bwd.argtypes = [D, i, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.csa_indexer_loss_workspace.argtypes = [D]
     lib.csa_indexer_loss_workspace.restype = sz
@@ -230,6 +233,10 @@ def csa_sparse_attn_fwd(dims: csa_dims, q, kv, c, idx, sink, scale: float, out, 
 
 def csa_sparse_attn_bwd_workspace(dims: csa_dims) -> int:
     return int(load().csa_sparse_attn_bwd_workspace(ctypes.byref(dims)))
+
+
+def csa_sparse_attn_bwd_query_block(dims: csa_dims, with_compressed: bool = True) -> int:
+    return int(load().csa_sparse_attn_bwd_query_block(ctypes.byref(dims), int(bool(with_compressed))))
 
 
 def csa_sparse_attn_bwd(dims: csa_dims, q, kv, c, idx, sink, scale: float, out, lse, dout, dq, dkv, dc,

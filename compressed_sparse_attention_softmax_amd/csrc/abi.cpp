@@ -10,7 +10,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
+#include <utility>
 
 #include "csa.h"
 #include "csa_kernels.hpp"
@@ -43,6 +45,18 @@ int hip_status(hipError_t e, const char* where)
 }
 
 bool supported_d(int d) { return d == 64 || d == 128 || d == 512; }
+
+// Every tensor base pointer of the CSA calls must be 16-byte aligned: the
+// kernels move rows in 16-byte pieces (and fp32 rows in float4s).  NULL
+// pointers are not checked here (each call decides which may be NULL).
+typedef std::pair<const char*, const void*> named_ptr;
+int check_aligned(const char* fn, std::initializer_list<named_ptr> ptrs)
+{
+    for (const named_ptr& p : ptrs)
+        if (p.second && (reinterpret_cast<uintptr_t>(p.second) & 15))
+            return fail(CSA_ERR_ARG, "%s: %s is not 16-byte aligned", fn, p.first);
+    return CSA_OK;
+}
 
 int check_common(const csa_dims* dm, int dtype, const char* fn)
 {
@@ -139,6 +153,8 @@ int csa_compress(const csa_dims* dm, int dtype, const void* x, const void* z, in
     if ((rc = check_epilogue(dm, norm_w, norm_eps, rope_dim, rope_base, "csa_compress"))) return rc;
     if (!x || !z || (!c && dm->sq / dm->ratio > 0))
         return fail(CSA_ERR_ARG, "csa_compress: x, z and c must be non-NULL");
+    if ((rc = check_aligned("csa_compress", {{"x", x}, {"z", z}, {"norm_w", norm_w}, {"c", c}, {"c32", c32}})))
+        return rc;
     csa::CompressArgs a = compress_args(dm, x, z, z_channels);
     a.c = c; a.c32 = c32;
     set_epilogue(a, norm_w, norm_eps, rope_dim, rope_base);
@@ -164,6 +180,9 @@ int csa_compress_bwd(const csa_dims* dm, int dtype, const void* x, const void* z
     if (!x || !z || (!dc && dm->sq / dm->ratio > 0) || !dx || !dz)
         return fail(CSA_ERR_ARG, "csa_compress_bwd: x, z, dc, dx and dz must be non-NULL");
     if (dnorm_w && !norm_w) return fail(CSA_ERR_ARG, "csa_compress_bwd: dnorm_w given without norm_w");
+    if ((rc = check_aligned("csa_compress_bwd", {{"x", x}, {"z", z}, {"norm_w", norm_w}, {"dc", dc}, {"dx", dx},
+                                                 {"dz", dz}, {"dnorm_w", dnorm_w}})))
+        return rc;
     csa::CompressArgs a = compress_args(dm, x, z, z_channels);
     a.dc = dc; a.dx = dx; a.dz = dz;
     set_epilogue(a, norm_w, norm_eps, rope_dim, rope_base);
@@ -204,6 +223,9 @@ int csa_index_topk(const csa_dims* dm, int dtype, const void* q_i, const void* k
     if (kp == 0) return ok();
     if (!k_i || !idx) return fail(CSA_ERR_ARG, "csa_index_topk: k_i and idx must be non-NULL");
     if (kp > 2048) return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: K'=%d > 2048", kp);
+    if ((rc = check_aligned("csa_index_topk", {{"q_i", q_i}, {"k_i", k_i}, {"w", w}, {"doc_ids", doc_ids},
+                                               {"idx", idx}, {"score", score}})))
+        return rc;
     csa::IndexArgs a{};
     a.qi = q_i; a.ki = k_i; a.w = w; a.doc = doc_ids; a.idx = idx; a.score = score;
     a.b = dm->b; a.S = dm->sq; a.HI = dm->idx_heads; a.DI = dm->idx_dim; a.r = dm->ratio;
@@ -221,6 +243,10 @@ int csa_sparse_attn_fwd(const csa_dims* dm, int dtype, const void* q, const void
     if (rc) return rc;
     if ((rc = check_attn(dm, dtype, q, kv, c, idx, scale, "csa_sparse_attn_fwd"))) return rc;
     if (!out || !lse) return fail(CSA_ERR_ARG, "csa_sparse_attn_fwd: out and lse must be non-NULL");
+    if ((rc = check_aligned("csa_sparse_attn_fwd", {{"q", q}, {"kv", kv}, {"c", c}, {"idx", idx},
+                                                    {"doc_ids", doc_ids}, {"sink", sink}, {"out", out},
+                                                    {"lse", lse}})))
+        return rc;
     csa::AttnArgs a = attn_args(dm, q, kv, c, idx, doc_ids, sink, scale);
     a.out = out; a.lse = lse;
     return hip_status(csa::attn_fwd(a, dtype == CSA_BF16, (hipStream_t)stream), "csa_sparse_attn_fwd");
@@ -242,6 +268,17 @@ size_t csa_sparse_attn_bwd_workspace(const csa_dims* dm)
     return w0;
 }
 
+int csa_sparse_attn_bwd_query_block(const csa_dims* dm, int with_compressed)
+{
+    if (!dm || dm->b < 1 || dm->sq < 1 || dm->h < 1 || dm->window < 1 || !supported_d(dm->d)) return 0;
+    if (with_compressed && dm->ratio < 1) return 0;
+    csa::AttnArgs a{};
+    a.b = dm->b; a.S = dm->sq; a.H = dm->h; a.D = dm->d; a.W = dm->window;
+    a.r = with_compressed ? dm->ratio : 1;
+    a.nc = with_compressed ? dm->sq / dm->ratio : 0;
+    return csa::attn_bwd_query_block(a);
+}
+
 int csa_sparse_attn_bwd(const csa_dims* dm, int dtype, const void* q, const void* kv, const void* c,
                         const int32_t* idx, const int32_t* doc_ids, const float* sink, float scale, const void* out,
                         const float* lse, const void* dout, void* dq, float* dkv, float* dc,
@@ -261,6 +298,11 @@ int csa_sparse_attn_bwd(const csa_dims* dm, int dtype, const void* q, const void
         if (want_c && !dc) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: gradient gate: dc is NULL while other gradients are requested");
     }
     if (dsink && !sink) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: dsink given without sink");
+    if ((rc = check_aligned("csa_sparse_attn_bwd", {{"q", q}, {"kv", kv}, {"c", c}, {"idx", idx},
+                                                    {"doc_ids", doc_ids}, {"sink", sink}, {"out", out},
+                                                    {"lse", lse}, {"dout", dout}, {"dq", dq}, {"dkv", dkv},
+                                                    {"dc", dc}, {"dsink", dsink}})))
+        return rc;
     if (!any && !dsink) return ok();
     csa::AttnArgs a = attn_args(dm, q, kv, c, idx, doc_ids, sink, scale);
     a.out = const_cast<void*>(out); a.lse = const_cast<float*>(lse); a.dout = dout;
@@ -335,6 +377,10 @@ int csa_indexer_loss(const csa_dims* dm, int dtype, const void* q, const void* c
         if (!q_i || !w || (blocks && !k_i))
             return fail(CSA_ERR_ARG, "csa_indexer_loss: q_i, k_i and w must be non-NULL with gradients");
     }
+    if ((rc = check_aligned("csa_indexer_loss", {{"q", q}, {"c", c}, {"lse", lse}, {"q_i", q_i}, {"k_i", k_i},
+                                                 {"w", w}, {"idx", idx}, {"score", score}, {"dkl", dkl},
+                                                 {"kl", kl}, {"dq_i", dq_i}, {"dw", dw}, {"dk_i", dk_i}})))
+        return rc;
     if (!any && !kl) return ok();
     csa::LossArgs a = loss_args(dm);
     a.q = q; a.c = c; a.lse = lse; a.qi = q_i; a.ki = k_i; a.w = w; a.idx = idx; a.score = score;

@@ -1197,7 +1197,8 @@ bool rows_table_plan(RowsGeom& g, const AttnArgs& p, double& makespan)
 // 32 queries (doubled while the partial rows would exceed 1 GiB; 128 for the
 // window-free ratio-1 path) with the round-robin schedule; with a window,
 // block lengths of 16..128 with a balanced table are tried, and the one with
-// the shortest modelled finishing time wins.  Results are cached per shape.
+// the shortest modelled finishing time wins.  Results are cached per shape (at
+// most 64 shapes; the cache is emptied when it is full).
 RowsGeom rows_geometry(const AttnArgs& p)
 {
     using Key = std::array<int, 7>;
@@ -1227,6 +1228,7 @@ RowsGeom rows_geometry(const AttnArgs& p)
         }
     }
     std::lock_guard<std::mutex> lk(mu);
+    if (cache.size() >= 64) cache.clear();      // bounded: a long-running caller with many shapes
     cache.emplace(key, g);
     return g;
 }
@@ -1434,6 +1436,8 @@ bool attn_bwd_stacks_queries(const AttnArgs& p, bool bf16)
 {
     return bf16 && p.D == 256 && p.W == 0 && p.idx && p.H <= 16 && rows_geometry(p).Qb % 16 == 0;
 }
+
+int attn_bwd_query_block(const AttnArgs& p) { return rows_geometry(p).Qb; }
 
 size_t attn_bwd_workspace_bytes(const AttnArgs& p)
 {

@@ -112,6 +112,8 @@ size_t topk_lds_bytes(int DI, int elem, int cap);
 hipError_t attn_fwd(const AttnArgs& p, bool bf16, hipStream_t st);
 hipError_t attn_bwd(const AttnArgs& p, bool bf16, float* ws, hipStream_t st);
 size_t attn_bwd_workspace_bytes(const AttnArgs& p);
+// consecutive queries per block of the backward's fixed-order row reduction
+int attn_bwd_query_block(const AttnArgs& p);
 // words per selection-bitmap row for p (0: too wide to build on chip)
 int selmap_words(const AttnArgs& p);
 // map: p.b * p.S * selmap_words(p) words; fills it from p.idx

@@ -376,21 +376,14 @@ hipError_t index_topk(const IndexArgs& p, bool bf16, hipStream_t st)
     }
 }
 
-// Candidate-buffer capacity per query (entries).  The whole valid prefix
-// when it fits on chip (no cut ever happens), else twice K' rounded up to a
-// tile, which leaves room for a full tile after every cut.  The environment
-// variable CSA_TOPK_BUFFER lowers the capacity (never below that minimum) so
-// that tests can drive the cut path at small sizes.  0 = does not fit.
+// Candidate-buffer capacity per query (entries): the whole valid prefix when
+// it fits on chip (no cut ever happens), else twice K' rounded up to a tile,
+// which leaves room for a full tile after every cut.  0 = does not fit.
 int index_topk_cap(const IndexArgs& p, bool bf16)
 {
     const int elem = bf16 ? 2 : 4;
     const int nc64 = (p.nc + 63) / 64 * 64, kp64 = (p.kp + 63) / 64 * 64;
     int cap = nc64;
-    const char* env = std::getenv("CSA_TOPK_BUFFER");
-    const int env_cap = env ? std::atoi(env) : 0;
-    if (env_cap > 0 && env_cap < cap) cap = env_cap;
-    if (cap < nc64 && cap < 2 * kp64) cap = 2 * kp64;
-    cap = (cap + 63) / 64 * 64;
     if (topk_lds_bytes(p.DI, elem, cap) > (size_t)INDEX_LDS_LIMIT) cap = 2 * kp64;
     if (topk_lds_bytes(p.DI, elem, cap) > (size_t)INDEX_LDS_LIMIT) return 0;
     return cap;

@@ -37,7 +37,9 @@
  *      q_i     [b, sq, idx_heads, idx_dim];  k_i [b, n_c, idx_dim]
  *      w       [b, sq, idx_heads];   lse [b, sq, h];  sink, dsink [h]
  *      idx, score [b, sq, K'],  K' = min(topk, n_c)
- *    Base pointers must be 16-byte aligned.
+ *    Base pointers must be 16-byte aligned (the CSA calls return CSA_ERR_ARG,
+ *    naming the argument, for any non-NULL tensor that is not; the DSA-over-GQA
+ *    calls accept any element-aligned tensor).
  *  - Dtypes.  `dtype` is CSA_F32 or CSA_BF16 and applies to q, kv, c, x, z,
  *    q_i, k_i, out, dout, dq.  Always fp32: w, sink, lse, score, c32, dkv,
  *    dc, dsink, dx, dz.  All arithmetic is fp32 (scores, softmax, accumulation).
@@ -184,6 +186,13 @@ int csa_sparse_attn_fwd(const csa_dims* dims, int dtype, const void* q, const vo
  * block of consecutive queries, which the call reduces in a fixed order (the
  * results do not depend on scheduling).  0 for invalid dims. */
 size_t csa_sparse_attn_bwd_workspace(const csa_dims* dims);
+
+/* Diagnostic: the number of consecutive queries per block of the backward's
+ * fixed-order reduction of dkv / dc (the backward sums each block's partial
+ * rows, then the blocks in order) for these dims, with (with_compressed != 0)
+ * or without compressed rows.  Tests use it to give every block a query with
+ * a nonzero gradient.  0 for invalid dims. */
+int csa_sparse_attn_bwd_query_block(const csa_dims* dims, int with_compressed);
 
 /* Sparse attention backward: the gradient of csa_sparse_attn_fwd given dout,
  * with out and lse from that forward (same inputs).  With

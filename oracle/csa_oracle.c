@@ -336,6 +336,64 @@ int csa_oracle_attn_fwd(int64_t S, int64_t H, int64_t D, int64_t W, int64_t r, i
  * The forward is recomputed here from the same inputs.  dQ [nrows,H,D] is
  * overwritten; dKV [b,S,D], dC [b,n_c,D] and dsink [H] are accumulated into
  * (the caller zeroes them). */
+/* One query row's backward: dQ of the row is written, its contributions to
+ * the gathered rows and the sink are added into dKV / dC / dsink. */
+static void attn_bwd_row(int64_t n, int64_t S, int64_t H, int64_t D, int64_t W, int64_t r, int64_t nc,
+                         int64_t kp, const double* Q, const double* KV, const double* C,
+                         const int32_t* idx, const double* sink, double scale,
+                         const int64_t* rows_b, const int64_t* rows_t, const int32_t* doc,
+                         const double* dO, double* dQ, double* dKV, double* dC, double* dsink,
+                         const double** ptrs, int64_t* is_c, int64_t* where, double* l, double* o)
+{
+    int64_t bi = rows_b[n];
+    int64_t nc_n = gather_rows(bi, rows_t[n], S, D, W, r, nc, kp, KV, C,
+                               idx ? idx + n * kp : NULL, doc, ptrs, is_c, where);
+    for (int64_t h = 0; h < H; ++h) {
+        const double* q = Q + (n * H + h) * D;
+        const double* go = dO + (n * H + h) * D;
+        double* gq = dQ + (n * H + h) * D;
+        /* forward recompute */
+        double m = sink ? sink[h] : -INFINITY;
+        for (int64_t c = 0; c < nc_n; ++c) {
+            double dot = 0.0;
+            for (int64_t e = 0; e < D; ++e) dot += q[e] * ptrs[c][e];
+            l[c] = scale * dot;
+            if (l[c] > m) m = l[c];
+        }
+        double den = sink ? exp(sink[h] - m) : 0.0;
+        for (int64_t c = 0; c < nc_n; ++c) den += exp(l[c] - m);
+        double lse = m + log(den);
+        for (int64_t e = 0; e < D; ++e) o[e] = 0.0;
+        for (int64_t c = 0; c < nc_n; ++c) {
+            double p = exp(l[c] - lse);
+            for (int64_t e = 0; e < D; ++e) o[e] += p * ptrs[c][e];
+        }
+        /* backward */
+        double delta = 0.0;
+        for (int64_t e = 0; e < D; ++e) delta += go[e] * o[e];
+        for (int64_t e = 0; e < D; ++e) gq[e] = 0.0;
+        for (int64_t c = 0; c < nc_n; ++c) {
+            double p = exp(l[c] - lse);
+            double dp = 0.0;
+            for (int64_t e = 0; e < D; ++e) dp += go[e] * ptrs[c][e];
+            double dl = p * (dp - delta);
+            double* dst = is_c[c] ? dC + (bi * nc + where[c]) * D : dKV + (bi * S + where[c]) * D;
+            for (int64_t e = 0; e < D; ++e) {
+                gq[e] += scale * dl * ptrs[c][e];
+                dst[e] += p * go[e] + scale * dl * q[e];
+            }
+        }
+        if (sink && dsink) dsink[h] -= exp(sink[h] - lse) * delta;
+    }
+}
+
+/* Rows are dealt to BWD_CHUNKS chunks (row n to chunk n % BWD_CHUNKS); each
+ * chunk adds its rows, in row order, into a buffer of its own, and the chunk
+ * buffers are then added into dKV / dC / dsink in chunk order.  The chunks
+ * run on the available threads; the sum is grouped the same way whatever the
+ * thread count, so the result is deterministic. */
+#define BWD_CHUNKS 16
+
 int csa_oracle_attn_bwd(int64_t S, int64_t H, int64_t D, int64_t W, int64_t r, int64_t nc,
                         int64_t kp, const double* Q, const double* KV, const double* C,
                         const int32_t* idx, const double* sink, double scale,
@@ -343,58 +401,47 @@ int csa_oracle_attn_bwd(int64_t S, int64_t H, int64_t D, int64_t W, int64_t r, i
                         const int32_t* doc, const double* dO, double* dQ, double* dKV, double* dC,
                         double* dsink)
 {
+    if (nrows <= 0) return ORACLE_OK;
     int64_t maxc = W + (idx ? kp : nc);
-    const double** ptrs = (const double**)malloc(sizeof(double*) * maxc);
-    int64_t* is_c = (int64_t*)malloc(sizeof(int64_t) * maxc);
-    int64_t* where = (int64_t*)malloc(sizeof(int64_t) * maxc);
-    double* l = (double*)malloc(sizeof(double) * maxc);
-    double* o = (double*)malloc(sizeof(double) * D);
-    if (!ptrs || !is_c || !where || !l || !o) {
-        free(ptrs); free(is_c); free(where); free(l); free(o);
-        return ORACLE_ERR;
-    }
-    for (int64_t n = 0; n < nrows; ++n) {
-        int64_t bi = rows_b[n];
-        int64_t nc_n = gather_rows(bi, rows_t[n], S, D, W, r, nc, kp, KV, C,
-                                   idx ? idx + n * kp : NULL, doc, ptrs, is_c, where);
-        for (int64_t h = 0; h < H; ++h) {
-            const double* q = Q + (n * H + h) * D;
-            const double* go = dO + (n * H + h) * D;
-            double* gq = dQ + (n * H + h) * D;
-            /* forward recompute */
-            double m = sink ? sink[h] : -INFINITY;
-            for (int64_t c = 0; c < nc_n; ++c) {
-                double dot = 0.0;
-                for (int64_t e = 0; e < D; ++e) dot += q[e] * ptrs[c][e];
-                l[c] = scale * dot;
-                if (l[c] > m) m = l[c];
-            }
-            double den = sink ? exp(sink[h] - m) : 0.0;
-            for (int64_t c = 0; c < nc_n; ++c) den += exp(l[c] - m);
-            double lse = m + log(den);
-            for (int64_t e = 0; e < D; ++e) o[e] = 0.0;
-            for (int64_t c = 0; c < nc_n; ++c) {
-                double p = exp(l[c] - lse);
-                for (int64_t e = 0; e < D; ++e) o[e] += p * ptrs[c][e];
-            }
-            /* backward */
-            double delta = 0.0;
-            for (int64_t e = 0; e < D; ++e) delta += go[e] * o[e];
-            for (int64_t e = 0; e < D; ++e) gq[e] = 0.0;
-            for (int64_t c = 0; c < nc_n; ++c) {
-                double p = exp(l[c] - lse);
-                double dp = 0.0;
-                for (int64_t e = 0; e < D; ++e) dp += go[e] * ptrs[c][e];
-                double dl = p * (dp - delta);
-                double* dst = is_c[c] ? dC + (bi * nc + where[c]) * D : dKV + (bi * S + where[c]) * D;
-                for (int64_t e = 0; e < D; ++e) {
-                    gq[e] += scale * dl * ptrs[c][e];
-                    dst[e] += p * go[e] + scale * dl * q[e];
-                }
-            }
-            if (sink && dsink) dsink[h] -= exp(sink[h] - lse) * delta;
+    int64_t nb = 0;
+    for (int64_t n = 0; n < nrows; ++n)
+        if (rows_b[n] + 1 > nb) nb = rows_b[n] + 1;
+    const int64_t nch = nrows < BWD_CHUNKS ? nrows : BWD_CHUNKS;
+    const int64_t n_kv = nb * S * D, n_c = nb * nc * D, per = n_kv + n_c + H;
+    double* part = (double*)calloc((size_t)(nch * per), sizeof(double));
+    if (!part) return ORACLE_ERR;
+    int err = ORACLE_OK;
+#pragma omp parallel
+    {
+        const double** ptrs = (const double**)malloc(sizeof(double*) * maxc);
+        int64_t* is_c = (int64_t*)malloc(sizeof(int64_t) * maxc);
+        int64_t* where = (int64_t*)malloc(sizeof(int64_t) * maxc);
+        double* l = (double*)malloc(sizeof(double) * maxc);
+        double* o = (double*)malloc(sizeof(double) * D);
+        if (!ptrs || !is_c || !where || !l || !o) err = ORACLE_ERR;
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t k = 0; k < nch; ++k) {
+            if (!ptrs || !is_c || !where || !l || !o) continue;
+            double* pk = part + k * per;
+            for (int64_t n = k; n < nrows; n += nch)
+                attn_bwd_row(n, S, H, D, W, r, nc, kp, Q, KV, C, idx, sink, scale, rows_b, rows_t, doc, dO,
+                             dQ, pk, pk + n_kv, pk + n_kv + n_c, ptrs, is_c, where, l, o);
         }
+        free(ptrs); free(is_c); free(where); free(l); free(o);
     }
-    free(ptrs); free(is_c); free(where); free(l); free(o);
-    return ORACLE_OK;
+    if (err == ORACLE_OK) {
+#pragma omp parallel for schedule(static)
+        for (int64_t e = 0; e < n_kv; ++e)
+            for (int64_t k = 0; k < nch; ++k) dKV[e] += part[k * per + e];
+        if (dC) {
+#pragma omp parallel for schedule(static)
+            for (int64_t e = 0; e < n_c; ++e)
+                for (int64_t k = 0; k < nch; ++k) dC[e] += part[k * per + n_kv + e];
+        }
+        if (sink && dsink)
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t k = 0; k < nch; ++k) dsink[h] += part[k * per + n_kv + n_c + h];
+    }
+    free(part);
+    return err;
 }

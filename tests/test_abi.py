@@ -245,3 +245,64 @@ def test_timing_hook_without_launches():
     assert names == ["compress_fwd", "compress_bwd", "index_topk", "attn_query_fwd", "attn_query_dq",
                      "attn_rows", "attn_reduce", "loss_query", "loss_keys", "loss_reduce", "compress_epilogue"]
     assert csa.csa_kernel_name(99) == ""
+
+
+M = ctypes.c_void_p(24)   # non-NULL and not 16-byte aligned (never dereferenced)
+F1, F4 = ctypes.c_float(1.0), ctypes.c_float(40000.0)
+
+
+def _fwd_args(**over):
+    a = dict(q=P, kv=P, c=P, idx=P, doc=N, sink=P, out=P, lse=P)
+    a.update(over)
+    return (ctypes.byref(_d()), 1, a["q"], a["kv"], a["c"], a["idx"], a["doc"], a["sink"], F1, a["out"], a["lse"], N)
+
+
+@pytest.mark.parametrize("name", ["q", "kv", "c", "idx", "sink", "out", "lse", "doc"])
+def test_attn_fwd_rejects_misaligned_tensors(name):
+    lib = _lib()
+    rc = lib.csa_sparse_attn_fwd(*_fwd_args(**{name: M}))
+    msg = lib.csa_last_error().decode()
+    assert rc == -1 and "16-byte aligned" in msg and msg.split(": ")[1].startswith(name if name != "doc" else "doc_ids")
+
+
+@pytest.mark.parametrize("pos,name", [(2, "q"), (3, "kv"), (4, "c"), (11, "dout"), (12, "dq"), (13, "dkv"),
+                                      (14, "dc"), (15, "dsink")])
+def test_attn_bwd_rejects_misaligned_tensors(pos, name):
+    lib = _lib()
+    args = [ctypes.byref(_d()), 1, P, P, P, P, N, P, F1, P, P, P, P, P, P, P, N, 0, N]
+    args[pos] = M
+    rc = lib.csa_sparse_attn_bwd(*args)
+    assert rc == -1 and f"{name} is not 16-byte aligned" in lib.csa_last_error().decode()
+
+
+@pytest.mark.parametrize("pos,name", [(2, "x"), (3, "z"), (9, "c"), (10, "c32")])
+def test_compress_rejects_misaligned_tensors(pos, name):
+    lib = _lib()
+    args = [ctypes.byref(_d()), 1, P, P, 64, N, ctypes.c_float(1e-6), 0, F4, P, P, N]
+    args[pos] = M
+    rc = lib.csa_compress(*args)
+    assert rc == -1 and f"{name} is not 16-byte aligned" in lib.csa_last_error().decode()
+
+
+@pytest.mark.parametrize("pos,name", [(2, "x"), (3, "z"), (9, "dc"), (10, "dx"), (11, "dz")])
+def test_compress_bwd_rejects_misaligned_tensors(pos, name):
+    lib = _lib()
+    args = [ctypes.byref(_d()), 1, P, P, 64, N, ctypes.c_float(1e-6), 0, F4, P, P, P, N, N, 0, N]
+    args[pos] = M
+    rc = lib.csa_compress_bwd(*args)
+    assert rc == -1 and f"{name} is not 16-byte aligned" in lib.csa_last_error().decode()
+
+
+@pytest.mark.parametrize("pos,name", [(2, "q_i"), (3, "k_i"), (4, "w"), (6, "idx"), (7, "score")])
+def test_index_topk_rejects_misaligned_tensors(pos, name):
+    lib = _lib()
+    args = [ctypes.byref(_d()), 1, P, P, P, N, P, P, N, 0, N]
+    args[pos] = M
+    rc = lib.csa_index_topk(*args)
+    assert rc == -1 and f"{name} is not 16-byte aligned" in lib.csa_last_error().decode()
+
+
+def test_indexer_loss_rejects_misaligned_tensors():
+    lib = _lib()
+    rc = lib.csa_indexer_loss(ctypes.byref(_d()), 1, M, P, P, P, P, P, P, P, F1, N, P, N, N, N, N, 0, N)
+    assert rc == -1 and "q is not 16-byte aligned" in lib.csa_last_error().decode()

@@ -15,7 +15,7 @@ import torch
 
 import csa_synth
 import oracle
-from parity import check_close, check_topk_rows, f64, say, tol_of
+from parity import check_close, check_topk_rows, f64, sample_rows, say, tol_of
 
 pytestmark = pytest.mark.gpu
 
@@ -137,64 +137,80 @@ def _index_case(wl, seed, rows=None, doc=None, **over):
                        doc_ids=None if doc is None else doc.cuda())
     torch.cuda.synchronize()
     rows = oracle.all_rows(wl.b, wl.sq) if rows is None else rows
-    qi, ki, w = f64(inp["q_i"]), f64(inp["k_i"]), f64(inp["w"])
-    oidx, osc, dense = oracle.index_topk(qi, ki, w, wl.ratio, wl.topk, rows=rows,
-                                         doc=None if doc is None else doc.numpy())
-    gi = idx.cpu().numpy()[rows[:, 0], rows[:, 1]]
-    gs = sc.cpu().numpy()[rows[:, 0], rows[:, 1]]
+    rb, rt = torch.tensor(rows[:, 0]).cuda(), torch.tensor(rows[:, 1]).cuda()
+    dnp = None if doc is None else doc.numpy()
+    dense = oracle.index_scores(f64(inp["q_i"][rb, rt]), f64(inp["k_i"]), f64(inp["w"][rb, rt]), wl.ratio, rows,
+                                dnp)
+    oidx, _ = oracle.topk(dense, wl.ratio, wl.topk, rows, dnp)
+    gi = idx[rb, rt].cpu().numpy()
+    gs = sc[rb, rt].cpu().numpy()
     return gi, gs, oidx, dense, rows
 
 
+# Cases with "rows": the oracle checks that many sampled query rows (always
+# including the edges).  The sq = 32768 cases have n_c = 8192 blocks, more
+# than the on-chip candidate buffer holds, so the streaming top-k runs its
+# cut path (a buffer of 2 K' entries rounded to a tile, refilled and cut
+# many times per row).
 INDEX_CASES = [
     ("tiny_f32", TINY, None),
     ("csa4_bf16", CSA4_SMALL.replace(sq=1536), None),
     ("csa4_bf16_b2_ragged", CSA4_SMALL.replace(b=2, sq=1027, topk=50), None),
-    ("streaming_cuts", CSA4_SMALL.replace(sq=4096, topk=100), "256"),
+    ("streaming_cuts", CSA4_SMALL.replace(sq=32768, topk=100), 384),
+    ("streaming_cuts_b2_ragged", CSA4_SMALL.replace(b=2, sq=32771, topk=130), 256),
     ("idx_dim64_heads40", CSA4_SMALL.replace(idx_heads=40, idx_dim=64, sq=900, topk=70), None),
     ("one_block", CSA4_SMALL.replace(sq=5, topk=40), None),
     ("b3_sq9", CSA4_SMALL.replace(b=3, sq=9, topk=1), None),
 ]
 
 
-@pytest.mark.parametrize("name,wl,cap", INDEX_CASES, ids=[c[0] for c in INDEX_CASES])
-def test_index_topk(gpu, name, wl, cap, monkeypatch):
-    say(f"[index_topk] {name} b={wl.b} sq={wl.sq} HI={wl.idx_heads} DI={wl.idx_dim} K={wl.topk} cap={cap}")
-    if cap:
-        monkeypatch.setenv("CSA_TOPK_BUFFER", cap)
-    gi, gs, oidx, dense, rows = _index_case(wl, 21)
+def _edge_rows(wl, n, seed):
+    kp, r = wl.kprime, wl.ratio
+    must = [0, 1, r - 1, r, kp * r - 2, kp * r - 1, kp * r, 2 * kp * r, wl.sq // 2, wl.sq - 2, wl.sq - 1]
+    return sample_rows(wl.b, wl.sq, n, seed, must)
+
+
+@pytest.mark.parametrize("name,wl,nrows", INDEX_CASES, ids=[c[0] for c in INDEX_CASES])
+def test_index_topk(gpu, name, wl, nrows):
+    say(f"[index_topk] {name} b={wl.b} sq={wl.sq} HI={wl.idx_heads} DI={wl.idx_dim} K={wl.topk} rows={nrows}")
+    rows = None if nrows is None else _edge_rows(wl, nrows, 21)
+    gi, gs, oidx, dense, rows = _index_case(wl, 21, rows=rows)
     exact = check_topk_rows(gi, gs, oidx, dense, rows[:, 1], wl.ratio, wl.n_c, wl.kprime,
                             score_tol=tol_of(wl.torch_dtype))
     say(f"  rows identical to the oracle: {exact}/{len(rows)}")
 
 
-def test_index_topk_exact_integer_scores_and_ties(gpu, monkeypatch):
+def test_index_topk_exact_integer_scores_and_ties(gpu):
     # small integer inputs make every fp32 score exact, so the GPU must match
-    # the oracle bit for bit, including the lowest-index rule on exact ties
-    monkeypatch.setenv("CSA_TOPK_BUFFER", "128")
-    wl = CSA4_SMALL.replace(sq=2048, topk=40, idx_heads=8)
+    # the oracle bit for bit, including the lowest-index rule on exact ties;
+    # n_c = 8192 blocks drive the streaming cut path
+    wl = CSA4_SMALL.replace(sq=32768, topk=40, idx_heads=8)
     g = torch.Generator().manual_seed(5)
     qi = torch.randint(-2, 3, (1, wl.sq, 8, 128), generator=g).to(torch.bfloat16)
     ki = torch.randint(-1, 2, (1, wl.n_c, 128), generator=g).to(torch.bfloat16)
     ki[0, 100:140] = ki[0, 7]                                   # many identical keys
+    ki[0, 5000:5100] = ki[0, 4000]
     w = (torch.randint(-2, 5, (1, wl.sq, 8), generator=g).float() / 4)
-    gi, gs, oidx, dense, rows = _index_case(wl, 0, q_i=qi.cuda(), k_i=ki.cuda(), w=w.cuda())
+    rows = _edge_rows(wl, 512, 0)
+    gi, gs, oidx, dense, rows = _index_case(wl, 0, rows=rows, q_i=qi.cuda(), k_i=ki.cuda(), w=w.cuda())
     np.testing.assert_array_equal(gi, oidx)
     np.testing.assert_array_equal(gs[gi >= 0], dense[np.nonzero(gi >= 0)[0], gi[gi >= 0]])
 
 
 DOC_INDEX_CASES = [
-    ("tiny_f32", TINY.replace(b=2, sq=301), 40),
-    ("csa4_bf16_b2", CSA4_SMALL.replace(b=2, sq=1500, topk=60), 300),
-    ("csa4_bf16_short_docs", CSA4_SMALL.replace(sq=1200, topk=40), 30),
+    ("tiny_f32", TINY.replace(b=2, sq=301), 40, None),
+    ("csa4_bf16_b2", CSA4_SMALL.replace(b=2, sq=1500, topk=60), 300, None),
+    ("csa4_bf16_short_docs", CSA4_SMALL.replace(sq=1200, topk=40), 30, None),
+    ("csa4_bf16_streaming_cuts", CSA4_SMALL.replace(sq=32768, topk=64), 2000, 256),
 ]
 
 
-@pytest.mark.parametrize("name,wl,mean", DOC_INDEX_CASES, ids=[c[0] for c in DOC_INDEX_CASES])
-def test_index_topk_packed_documents(gpu, name, wl, mean, monkeypatch):
-    say(f"[index_topk docs] {name} b={wl.b} sq={wl.sq} K={wl.topk} mean doc length {mean}")
-    monkeypatch.setenv("CSA_TOPK_BUFFER", "256")
+@pytest.mark.parametrize("name,wl,mean,nrows", DOC_INDEX_CASES, ids=[c[0] for c in DOC_INDEX_CASES])
+def test_index_topk_packed_documents(gpu, name, wl, mean, nrows):
+    say(f"[index_topk docs] {name} b={wl.b} sq={wl.sq} K={wl.topk} mean doc length {mean} rows={nrows}")
     doc = csa_synth.packed_doc_ids(wl.b, wl.sq, mean, 7)
-    gi, gs, oidx, dense, rows = _index_case(wl, 23, doc=doc)
+    rows = None if nrows is None else _edge_rows(wl, nrows, 23)
+    gi, gs, oidx, dense, rows = _index_case(wl, 23, rows=rows, doc=doc)
     exact = check_topk_rows(gi, gs, oidx, dense, rows[:, 1], wl.ratio, wl.n_c, wl.kprime,
                             score_tol=tol_of(wl.torch_dtype), docs=True)
     say(f"  rows identical to the oracle: {exact}/{len(rows)}")

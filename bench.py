@@ -378,6 +378,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="time the step only (skip the indexer loss, compressor epilogue and DSA-over-GQA lines)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step as one HIP graph replay (reported beside the eager headline)")
     ap.add_argument("--cpu-rows", type=int, default=1536,
                     help="query rows of the oracle's CPU sample (about 10-30 s of CPU work)")
     ap.add_argument("--cpu-oracle-report", type=int, default=0, metavar="MAX_ROWS",
@@ -411,16 +413,18 @@ def main():
     scale = wl.scale
     sink = inp["sink"]
 
+    cur = {"s": stream}      # launch stream of the calls (None = the current stream, e.g. a capture stream)
+
     def stage_calls():
-        yield lambda: csa.csa_compress(dm, inp["x"], inp["z"], buf.c, None, stream=stream)
+        yield lambda: csa.csa_compress(dm, inp["x"], inp["z"], buf.c, None, stream=cur["s"])
         yield (lambda: csa.csa_index_topk(dm, inp["q_i"], inp["k_i"], inp["w"], buf.idx, buf.score,
-                                          stream=stream)) if buf.idx is not None else None
+                                          stream=cur["s"])) if buf.idx is not None else None
         yield lambda: csa.csa_sparse_attn_fwd(dm, inp["q"], inp["kv"], buf.c, buf.idx, sink, scale, buf.out,
-                                              buf.lse, stream=stream)
+                                              buf.lse, stream=cur["s"])
         yield lambda: csa.csa_sparse_attn_bwd(dm, inp["q"], inp["kv"], buf.c, buf.idx, sink, scale, buf.out,
                                               buf.lse, inp["do"], buf.dq, buf.dkv, buf.dc, buf.dsink,
-                                              ws=buf.ws, stream=stream)
-        yield lambda: csa.csa_compress_bwd(dm, inp["x"], inp["z"], buf.dc, buf.dx, buf.dz, stream=stream)
+                                              ws=buf.ws, stream=cur["s"])
+        yield lambda: csa.csa_compress_bwd(dm, inp["x"], inp["z"], buf.dc, buf.dx, buf.dz, stream=cur["s"])
 
     calls = list(stage_calls())
 
@@ -459,19 +463,46 @@ def main():
     dom_id = [csa.csa_kernel_name(k) for k in range(7)].index(dom_k)
 
     K = args.steps
-    # the timed region: K steps, one pair of HIP events per step on the
-    # stream, bracketed by device synchronisation; nothing else recorded
-    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(K):
-        step_ev[k][0].record(stream)
-        one_step()
-        step_ev[k][1].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    step_ms = sorted(a.elapsed_time(b) for a, b in step_ev)
-    ms_median = step_ms[K // 2] if K % 2 else 0.5 * (step_ms[K // 2 - 1] + step_ms[K // 2])
+
+    def timed(run):
+        """K steps, one pair of HIP events per step on the stream, bracketed by
+        device synchronisation; returns (sorted step ms, wall seconds)."""
+        step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(K):
+            step_ev[k][0].record(stream)
+            run()
+            step_ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in step_ev), time.perf_counter() - t0
+
+    def median(v):
+        return v[K // 2] if K % 2 else 0.5 * (v[K // 2 - 1] + v[K // 2])
+
+    # the headline: eager launches.  With --graph the step is also captured as
+    # one HIP graph (the entry points enqueue kernels only: no memset nodes, no
+    # host synchronisation) and its replays are reported beside it (on this
+    # stack a replay has measured slower than the eager launches)
+    step_ms, elapsed = timed(one_step)
+    graph_ms = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        cur["s"] = None
+        with torch.cuda.stream(side):
+            one_step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_step()
+        cur["s"] = stream
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        graph_ms = median(timed(graph.replay)[0])
+    ms_median = median(step_ms)
 
     # a second pass of K steps (not the headline): per-stage events, and the
     # dominant kernel timed around every launch by the library's hook
@@ -515,9 +546,10 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
-        "ms_per_step_timing": "median of per-step HIP event pairs on the stream over the K timed steps",
+        "ms_per_step_timing": "median of per-step HIP event pairs on the stream over the K timed steps (eager launches)",
         "ms_per_step_wall_mean": elapsed * 1e3 / K,
         "ms_per_step_min_max": [step_ms[0], step_ms[-1]],
+        "ms_per_step_graph_median": graph_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

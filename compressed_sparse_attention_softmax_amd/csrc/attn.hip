@@ -833,8 +833,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
         const float* dl_b = dlt_lds + buf * HP;
         if constexpr (COMPUTE) {
         [[maybe_unused]] const int dtq = (p.doc && win) ? p.doc[(int64_t)bi * p.S + t] : 0;
-        // every (head, row) pair is computed; rows that are not candidates of t
-        // get multiplicity 0 (no branch, so the accumulators stay put).  The
+        // every (head, row) pair of a wave with a candidate of t is computed;
+        // its rows that are not candidates get multiplicity 0.  The
         // multiplicity enters the exponent: m P = 2^(scale log2e S' + log2 m).
         float lm[RT];                                      // log2 of the multiplicity, -inf for 0
         [[maybe_unused]] float lmq[QS > 1 ? 4 : 1][RT];   // stacked queries: per head tile
@@ -856,6 +856,20 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
                 }
             }
         }
+        // a wave none of whose rows is a candidate of t (outside t's window,
+        // not selected by t) skips t's products; it still stages and meets
+        // the barriers with the others
+        bool anyrow = false;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if constexpr (QS > 1) {
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht) anyrow |= lmq[ht][rt] > -INFINITY;
+            } else {
+                anyrow |= lm[rt] > -INFINITY;
+            }
+        }
+        if (__any(anyrow)) {
 #pragma unroll
         for (int kk = 0; kk < HP / 32; ++kk) {
             // a head pair with no head (h <= 32); not in the bf16 d = 128
@@ -904,8 +918,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
                         sa[rt].v[4 * hh + i] = from_f32<T>((dp[i] * p.scale) * e);
                     }
                 }
-                // (no scheduling barrier: the S / dP MFMAs of the next head tile
-                // interleave with this tile's exponentials)
+                // (no scheduling barrier here or between head-tile pairs: the S /
+                // dP MFMAs of the next head tile interleave with this tile's
+                // exponentials)
             }
             // dR += P^T dO + dS'^T q; bf16 accumulates in AGPRs through asm
             // blocks of 8 (or 4) MFMAs.  Packed rows: the key half of dR is
@@ -952,7 +967,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
                     }
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
+        }
         }
         }
         if constexpr (NBUF == 2) {

@@ -24,7 +24,7 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_ARG", -2: "CSA_ERR_SHAPE", -3: "CSA_ERR_DTYP
 # every symbol include/csa.h declares
 EXPORTS = ["csa_compress", "csa_compress_bwd_workspace", "csa_compress_bwd", "csa_index_topk_workspace", "csa_index_topk",
            "csa_sparse_attn_fwd", "csa_sparse_attn_bwd_workspace", "csa_sparse_attn_bwd_query_block",
-           "csa_sparse_attn_bwd",
+           "csa_sparse_attn_bwd", "csa_sparse_attn_bwd_noalloc",
            "csa_indexer_loss_workspace", "csa_indexer_loss", "csa_dsa_gqa_workspace", "csa_dsa_gqa_fwd",
            "csa_dsa_gqa_bwd", "csa_last_error", "csa_version", "csa_timing_enable", "csa_timing_read", "csa_kernel_name"]
 
@@ -79,6 +79,7 @@ def load(path: Optional[str] = None):
     lib.csa_sparse_attn_bwd_query_block.argtypes = [D, i]
     lib.csa_sparse_attn_bwd_query_block.restype = i
     lib.csa_sparse_attn_bwd.argtypes = [D, i, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.csa_sparse_attn_bwd_noalloc.argtypes = [D, i, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.csa_indexer_loss_workspace.argtypes = [D]
     lib.csa_indexer_loss_workspace.restype = sz
     lib.csa_indexer_loss.argtypes = [D, i, vp, vp, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -95,7 +96,7 @@ def load(path: Optional[str] = None):
     lib.csa_kernel_name.argtypes = [i]
     lib.csa_kernel_name.restype = ctypes.c_char_p
     for fn in ("csa_compress", "csa_compress_bwd", "csa_index_topk", "csa_sparse_attn_fwd",
-               "csa_sparse_attn_bwd", "csa_indexer_loss", "csa_dsa_gqa_fwd", "csa_dsa_gqa_bwd", "csa_version", "csa_timing_enable", "csa_timing_read"):
+               "csa_sparse_attn_bwd", "csa_sparse_attn_bwd_noalloc", "csa_indexer_loss", "csa_dsa_gqa_fwd", "csa_dsa_gqa_bwd", "csa_version", "csa_timing_enable", "csa_timing_read"):
         getattr(lib, fn).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -253,6 +254,23 @@ def csa_sparse_attn_bwd(dims: csa_dims, q, kv, c, idx, sink, scale: float, out, 
           _ptr(dkv, shape=(b, S, D), dtype=f32, name="dkv"), _ptr(dc, shape=(b, nc, D), dtype=f32, name="dc"),
           _ptr(dsink, shape=(H,), dtype=f32, name="dsink"), _ptr(ws, name="ws"),
           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def csa_sparse_attn_bwd_noalloc(dims: csa_dims, q, kv, c, idx, sink, scale: float, out, lse, dout, dq, dkv, dc,
+                                dsink=None, stream=None, doc_ids=None) -> None:
+    """csa_sparse_attn_bwd with the library's fixed device scratch instead of a
+    caller workspace (for callers that cannot allocate)."""
+    b, S, H, D = dims.b, dims.sq, dims.h, dims.d
+    f32 = torch.float32
+    nc = n_compressed(dims) if c is not None else 0
+    _call("csa_sparse_attn_bwd_noalloc", ctypes.byref(dims), _dtype_code(q),
+          *_attn_ptrs(dims, q, kv, c, idx, sink, doc_ids),
+          ctypes.c_float(scale), _ptr(out, shape=(b, S, H, D), dtype=q.dtype, name="out"),
+          _ptr(lse, shape=(b, S, H), dtype=f32, name="lse"),
+          _ptr(dout, shape=(b, S, H, D), dtype=q.dtype, name="dout"),
+          _ptr(dq, shape=(b, S, H, D), dtype=q.dtype, name="dq"),
+          _ptr(dkv, shape=(b, S, D), dtype=f32, name="dkv"), _ptr(dc, shape=(b, nc, D), dtype=f32, name="dc"),
+          _ptr(dsink, shape=(H,), dtype=f32, name="dsink"), _stream(stream))
 
 
 def csa_indexer_loss_workspace(dims: csa_dims) -> int:

@@ -279,34 +279,59 @@ int csa_sparse_attn_bwd_query_block(const csa_dims* dm, int with_compressed)
     return csa::attn_bwd_query_block(a);
 }
 
+}  // extern "C"
+
+namespace {
+
+// validation and arguments of the attention backward (both entry points)
+int attn_bwd_prepare(const csa_dims* dm, int dtype, const void* q, const void* kv, const void* c, const int32_t* idx,
+                     const int32_t* doc_ids, const float* sink, float scale, const void* out, const float* lse,
+                     const void* dout, void* dq, float* dkv, float* dc, float* dsink, const char* fn,
+                     csa::AttnArgs& a, bool& noop)
+{
+    noop = false;
+    int rc = check_common(dm, dtype, fn);
+    if (rc) return rc;
+    if ((rc = check_attn(dm, dtype, q, kv, c, idx, scale, fn))) return rc;
+    if (!out || !lse || !dout) return fail(CSA_ERR_ARG, "%s: out, lse and dout must be non-NULL", fn);
+    // all-or-nothing gradient gate
+    const bool want_c = c != nullptr;
+    const bool any = dq || dkv || dc;
+    if (!want_c && dc) return fail(CSA_ERR_ARG, "%s: dc given without compressed rows c", fn);
+    if (any) {
+        if (!dq) return fail(CSA_ERR_ARG, "%s: gradient gate: dq is NULL while other gradients are requested", fn);
+        if (!dkv) return fail(CSA_ERR_ARG, "%s: gradient gate: dkv is NULL while other gradients are requested", fn);
+        if (want_c && !dc) return fail(CSA_ERR_ARG, "%s: gradient gate: dc is NULL while other gradients are requested", fn);
+    }
+    if (dsink && !sink) return fail(CSA_ERR_ARG, "%s: dsink given without sink", fn);
+    if ((rc = check_aligned(fn, {{"q", q}, {"kv", kv}, {"c", c}, {"idx", idx}, {"doc_ids", doc_ids},
+                                 {"sink", sink}, {"out", out}, {"lse", lse}, {"dout", dout}, {"dq", dq},
+                                 {"dkv", dkv}, {"dc", dc}, {"dsink", dsink}})))
+        return rc;
+    if (!any && !dsink) {
+        noop = true;
+        return ok();
+    }
+    a = attn_args(dm, q, kv, c, idx, doc_ids, sink, scale);
+    a.out = const_cast<void*>(out); a.lse = const_cast<float*>(lse); a.dout = dout;
+    a.dq = dq; a.dkv = dkv; a.dc = dc; a.dsink = dsink;
+    return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int csa_sparse_attn_bwd(const csa_dims* dm, int dtype, const void* q, const void* kv, const void* c,
                         const int32_t* idx, const int32_t* doc_ids, const float* sink, float scale, const void* out,
                         const float* lse, const void* dout, void* dq, float* dkv, float* dc,
                         float* dsink, void* ws, size_t ws_bytes, void* stream)
 {
-    int rc = check_common(dm, dtype, "csa_sparse_attn_bwd");
-    if (rc) return rc;
-    if ((rc = check_attn(dm, dtype, q, kv, c, idx, scale, "csa_sparse_attn_bwd"))) return rc;
-    if (!out || !lse || !dout) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: out, lse and dout must be non-NULL");
-    // all-or-nothing gradient gate
-    const bool want_c = c != nullptr;
-    const bool any = dq || dkv || dc;
-    if (!want_c && dc) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: dc given without compressed rows c");
-    if (any) {
-        if (!dq) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: gradient gate: dq is NULL while other gradients are requested");
-        if (!dkv) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: gradient gate: dkv is NULL while other gradients are requested");
-        if (want_c && !dc) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: gradient gate: dc is NULL while other gradients are requested");
-    }
-    if (dsink && !sink) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: dsink given without sink");
-    if ((rc = check_aligned("csa_sparse_attn_bwd", {{"q", q}, {"kv", kv}, {"c", c}, {"idx", idx},
-                                                    {"doc_ids", doc_ids}, {"sink", sink}, {"out", out},
-                                                    {"lse", lse}, {"dout", dout}, {"dq", dq}, {"dkv", dkv},
-                                                    {"dc", dc}, {"dsink", dsink}})))
-        return rc;
-    if (!any && !dsink) return ok();
-    csa::AttnArgs a = attn_args(dm, q, kv, c, idx, doc_ids, sink, scale);
-    a.out = const_cast<void*>(out); a.lse = const_cast<float*>(lse); a.dout = dout;
-    a.dq = dq; a.dkv = dkv; a.dc = dc; a.dsink = dsink;
+    csa::AttnArgs a{};
+    bool noop = false;
+    int rc = attn_bwd_prepare(dm, dtype, q, kv, c, idx, doc_ids, sink, scale, out, lse, dout, dq, dkv, dc, dsink,
+                              "csa_sparse_attn_bwd", a, noop);
+    if (rc || noop) return rc;
     const size_t need = csa::attn_bwd_workspace_bytes(a);
     if (!ws || ws_bytes < need)
         return fail(CSA_ERR_WORKSPACE, "csa_sparse_attn_bwd: workspace of %zu bytes needed, %zu given",
@@ -314,6 +339,29 @@ int csa_sparse_attn_bwd(const csa_dims* dm, int dtype, const void* q, const void
     if (((uintptr_t)ws) & 15) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: workspace must be 16-byte aligned");
     hipStream_t st = (hipStream_t)stream;
     return hip_status(csa::attn_bwd(a, dtype == CSA_BF16, (float*)ws, st), "csa_sparse_attn_bwd");
+}
+
+int csa_sparse_attn_bwd_noalloc(const csa_dims* dm, int dtype, const void* q, const void* kv, const void* c,
+                                const int32_t* idx, const int32_t* doc_ids, const float* sink, float scale,
+                                const void* out, const float* lse, const void* dout, void* dq, float* dkv,
+                                float* dc, float* dsink, void* stream)
+{
+    csa::AttnArgs a{};
+    bool noop = false;
+    int rc = attn_bwd_prepare(dm, dtype, q, kv, c, idx, doc_ids, sink, scale, out, lse, dout, dq, dkv, dc, dsink,
+                              "csa_sparse_attn_bwd_noalloc", a, noop);
+    if (rc || noop) return rc;
+    const size_t need = csa::attn_bwd_workspace_bytes(a);
+    static_assert(csa::ATTN_BWD_SCRATCH_BYTES == (size_t)CSA_BWD_SCRATCH_BYTES, "header and library agree");
+    if (need > csa::ATTN_BWD_SCRATCH_BYTES)
+        return fail(CSA_ERR_UNSUPPORTED,
+                    "csa_sparse_attn_bwd_noalloc: these dims need %zu bytes of scratch, more than the fixed %zu "
+                    "(use csa_sparse_attn_bwd with a caller workspace)", need, csa::ATTN_BWD_SCRATCH_BYTES);
+    void* scr = nullptr;
+    hipError_t e = csa::attn_bwd_scratch(&scr);
+    if (e != hipSuccess) return hip_status(e, "csa_sparse_attn_bwd_noalloc: scratch address");
+    return hip_status(csa::attn_bwd(a, dtype == CSA_BF16, (float*)scr, (hipStream_t)stream),
+                      "csa_sparse_attn_bwd_noalloc");
 }
 
 }  // extern "C"

@@ -1461,6 +1461,36 @@ size_t attn_bwd_workspace_bytes(const AttnArgs& p)
     return (size_t)floats * 4;
 }
 
+// ----------------------------------------------- the backward's fixed scratch
+// For callers that cannot allocate (graph capture, serving loops): the
+// backward's workspace in a file-scope device array of ATTN_BWD_SCRATCH_BYTES,
+// one copy per GPU, held until the process ends.  Host code never uses the
+// array's name as an address: the device address of each GPU's copy comes
+// from hipGetSymbolAddress, once per device with that device current.
+namespace {
+__device__ __align__(256) char scratch[ATTN_BWD_SCRATCH_BYTES];
+constexpr int SCRATCH_MAX_DEVICES = 64;
+}  // namespace
+
+hipError_t attn_bwd_scratch(void** ptr)
+{
+    static std::mutex mu;
+    static void* addr[SCRATCH_MAX_DEVICES] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void* a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = a;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
 hipError_t attn_fwd(const AttnArgs& p, bool bf16, hipStream_t st)
 {
     if (p.S == 0) return hipSuccess;

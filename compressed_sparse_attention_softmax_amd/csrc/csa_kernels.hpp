@@ -114,6 +114,10 @@ hipError_t attn_bwd(const AttnArgs& p, bool bf16, float* ws, hipStream_t st);
 size_t attn_bwd_workspace_bytes(const AttnArgs& p);
 // consecutive queries per block of the backward's fixed-order row reduction
 int attn_bwd_query_block(const AttnArgs& p);
+// the backward's fixed scratch (a device array, one copy per GPU): its bytes,
+// and the address of the current device's copy (looked up once per device)
+constexpr size_t ATTN_BWD_SCRATCH_BYTES = (size_t)64 << 20;
+hipError_t attn_bwd_scratch(void** ptr);
 // words per selection-bitmap row for p (0: too wide to build on chip)
 int selmap_words(const AttnArgs& p);
 // map: p.b * p.S * selmap_words(p) words; fills it from p.idx

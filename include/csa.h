@@ -214,6 +214,25 @@ int csa_sparse_attn_bwd(const csa_dims* dims, int dtype, const void* q, const vo
                         float* dkv, float* dc, float* dsink, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * backward as csa_sparse_attn_bwd, same arguments minus the workspace, which
+ * here is a fixed array of CSA_BWD_SCRATCH_BYTES in the library's device
+ * memory (one copy per GPU the library runs on, held until the process
+ * ends; its address is looked up on the first call on each device).  The
+ * call allocates nothing.  Returns CSA_ERR_UNSUPPORTED when the dims need more
+ * scratch than that (csa_sparse_attn_bwd_workspace(dims) bytes; the bench
+ * workload b 1, sq 4096, h 64, d 128, n_c 1024 needs 44.5 MiB).  Nothing in
+ * the scratch needs to start at zero: every element is written before it is
+ * read.  Calls that overlap on one GPU (different streams, or threads) share
+ * the one array and race: serialise them. */
+#define CSA_BWD_SCRATCH_BYTES ((size_t)64 << 20)
+int csa_sparse_attn_bwd_noalloc(const csa_dims* dims, int dtype, const void* q, const void* kv,
+                                const void* c, const int32_t* idx, const int32_t* doc_ids,
+                                const float* sink, float scale, const void* out, const float* lse,
+                                const void* dout, void* dq, float* dkv, float* dc, float* dsink,
+                                void* stream);
+
 /* Workspace bytes csa_indexer_loss needs when gradients are requested
  * (device memory, 16-byte aligned, owned by the caller, contents on entry
  * irrelevant): dI ([b, sq, K'] fp32) and fp32 partial rows of dk_i per block

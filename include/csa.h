@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 5
+#define CSA_ABI_VERSION 6
 
 enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 };
 

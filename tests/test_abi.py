@@ -33,7 +33,7 @@ def test_library_exports_every_header_symbol():
     lib = _lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.csa_version() == 5
+    assert lib.csa_version() == 6
 
 
 def test_dims_struct_matches_header():

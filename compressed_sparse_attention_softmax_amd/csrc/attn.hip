@@ -130,7 +130,7 @@ template <typename T, int D, int HT, int G, bool DQ, int KSP>
 __global__ __launch_bounds__(256, (D <= 128 && HT <= 2) ? 2 : 1)
 void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict__ csink, int idx_lds, int okw)
 {
-    constexpr int KS = D / 32, DT = D / 16, QPW = 4 / G;
+    constexpr int KS = D / 32, DT = D / 16, QPW = (G == 2 && D <= 128) ? 1 : 4 / G;
     constexpr int CHB = chunk_bytes<T, D>();
     constexpr int PPR = D * (int)sizeof(T) / 16;  // 16-byte pieces per row
     constexpr int E16 = 16 / (int)sizeof(T);      // elements per piece
@@ -1256,7 +1256,10 @@ hipError_t launch_query_k(const AttnArgs& p, bool dq, float* delta, float* csink
     // wide rows with few heads: fewer queries per workgroup so the tiles fit
     // (the extra waves hold no head and only help gather rows)
     while (G < 4 && (size_t)(4 / G) * 2 * chunk_bytes<T, D>() > (size_t)ATTN_LDS_LIMIT) G *= 2;
-    const int qpw = 4 / G;
+    // a query whose heads need two waves runs alone in its workgroup (d <=
+    // 128): each chunk barrier then couples only the waves that share the
+    // tile, and no workgroup runs extra rounds for a longer neighbour
+    const int qpw = (G == 2 && D <= 128) ? 1 : 4 / G;
     // two chunk tiles per query of the workgroup, then (when they fit) the index rows
     size_t lds = (size_t)qpw * 2 * chunk_bytes<T, D>();
     if (lds > (size_t)ATTN_LDS_LIMIT) return hipErrorInvalidValue;
@@ -1276,19 +1279,19 @@ hipError_t launch_query_k(const AttnArgs& p, bool dq, float* delta, float* csink
         if (e != hipSuccess) return e;
         dim3 grid((p.S + qpw_ - 1) / qpw_, p.b);
         TimedLaunch tl(dq ? K_ATTN_DQ : K_ATTN_FWD, st);
-        hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p, delta, csink, idx_lds, okw);
+        hipLaunchKernelGGL(kern, grid, dim3(64 * G * qpw_), lds, st, p, delta, csink, idx_lds, okw);
         return hipGetLastError();
     };
     if (dq) {
         switch (G) {
         case 1: return go(attn_query_kernel<T, D, HT, 1, true, KSP>, 4);
-        case 2: return go(attn_query_kernel<T, D, HT, 2, true, KSP>, 2);
+        case 2: return go(attn_query_kernel<T, D, HT, 2, true, KSP>, qpw);
         default: return go(attn_query_kernel<T, D, HT, 4, true, KSP>, 1);
         }
     }
     switch (G) {
     case 1: return go(attn_query_kernel<T, D, HT, 1, false, KSP>, 4);
-    case 2: return go(attn_query_kernel<T, D, HT, 2, false, KSP>, 2);
+    case 2: return go(attn_query_kernel<T, D, HT, 2, false, KSP>, qpw);
     default: return go(attn_query_kernel<T, D, HT, 4, false, KSP>, 1);
     }
 }

@@ -24,8 +24,8 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_ARG", -2: "CSA_ERR_SHAPE", -3: "CSA_ERR_DTYP
 # every symbol include/csa.h declares
 EXPORTS = ["csa_compress", "csa_compress_bwd_workspace", "csa_compress_bwd", "csa_index_topk_workspace", "csa_index_topk",
            "csa_sparse_attn_fwd", "csa_sparse_attn_bwd_workspace", "csa_sparse_attn_bwd_query_block",
-           "csa_sparse_attn_bwd", "csa_sparse_attn_bwd_noalloc",
-           "csa_indexer_loss_workspace", "csa_indexer_loss", "csa_dsa_gqa_workspace", "csa_dsa_gqa_fwd",
+           "csa_sparse_attn_bwd", "csa_sparse_attn_bwd_noalloc", "csa_sparse_attn_fwd_strided",
+           "csa_sparse_attn_bwd_strided", "csa_indexer_loss_workspace", "csa_indexer_loss", "csa_dsa_gqa_workspace", "csa_dsa_gqa_fwd",
            "csa_dsa_gqa_bwd", "csa_last_error", "csa_version", "csa_timing_enable", "csa_timing_read", "csa_kernel_name"]
 
 # kernel ids of the timing hook (enum csa_kernel_id)
@@ -44,6 +44,10 @@ class CSAError(RuntimeError):
 class csa_dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("b", "sq", "h", "d", "ratio", "span", "window", "idx_heads", "idx_dim", "topk")]
+
+
+class csa_attn_strides(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("q_b", "q_s", "q_h", "kv_b", "kv_s", "lse_b", "lse_s")]
 
 
 class csa_gqa_dims(ctypes.Structure):
@@ -80,6 +84,10 @@ def load(path: Optional[str] = None):
     lib.csa_sparse_attn_bwd_query_block.restype = i
     lib.csa_sparse_attn_bwd.argtypes = [D, i, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.csa_sparse_attn_bwd_noalloc.argtypes = [D, i, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp]
+    ST = ctypes.POINTER(csa_attn_strides)
+    lib.csa_sparse_attn_fwd_strided.argtypes = [D, ST, i, vp, vp, vp, vp, vp, vp, f, vp, vp, vp]
+    lib.csa_sparse_attn_bwd_strided.argtypes = [D, ST, i, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                sz, vp]
     lib.csa_indexer_loss_workspace.argtypes = [D]
     lib.csa_indexer_loss_workspace.restype = sz
     lib.csa_indexer_loss.argtypes = [D, i, vp, vp, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -96,7 +104,8 @@ def load(path: Optional[str] = None):
     lib.csa_kernel_name.argtypes = [i]
     lib.csa_kernel_name.restype = ctypes.c_char_p
     for fn in ("csa_compress", "csa_compress_bwd", "csa_index_topk", "csa_sparse_attn_fwd",
-               "csa_sparse_attn_bwd", "csa_sparse_attn_bwd_noalloc", "csa_indexer_loss", "csa_dsa_gqa_fwd", "csa_dsa_gqa_bwd", "csa_version", "csa_timing_enable", "csa_timing_read"):
+               "csa_sparse_attn_bwd", "csa_sparse_attn_bwd_noalloc", "csa_sparse_attn_fwd_strided",
+               "csa_sparse_attn_bwd_strided", "csa_indexer_loss", "csa_dsa_gqa_fwd", "csa_dsa_gqa_bwd", "csa_version", "csa_timing_enable", "csa_timing_read"):
         getattr(lib, fn).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -271,6 +280,77 @@ def csa_sparse_attn_bwd_noalloc(dims: csa_dims, q, kv, c, idx, sink, scale: floa
           _ptr(dq, shape=(b, S, H, D), dtype=q.dtype, name="dq"),
           _ptr(dkv, shape=(b, S, D), dtype=f32, name="dkv"), _ptr(dc, shape=(b, nc, D), dtype=f32, name="dc"),
           _ptr(dsink, shape=(H,), dtype=f32, name="dsink"), _stream(stream))
+
+
+def _strided_ptr(t, shape, dtype, name, like=None):
+    """Pointer of a view of logical shape `shape` whose last axis is contiguous;
+    with `like` (a tensor of the same family) its strides must match on every
+    axis of extent > 1."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must be contiguous along its last axis")
+    if like is not None:
+        for ax, n in enumerate(shape[:-1]):
+            if n > 1 and t.stride(ax) != like.stride(ax):
+                raise ValueError(f"{name} strides {t.stride()} differ from {like.stride()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def attn_strides_of(q, kv, lse) -> csa_attn_strides:
+    """csa_attn_strides of views q [b, sq, h, d], kv [b, sq, d] and lse [b, sq, h]."""
+    return csa_attn_strides(q.stride(0), q.stride(1), q.stride(2), kv.stride(0), kv.stride(1), lse.stride(0),
+                            lse.stride(1))
+
+
+def _strided_attn_ptrs(dims, q, kv, c, idx, sink, doc_ids):
+    dt = q.dtype
+    b, S, H, D = dims.b, dims.sq, dims.h, dims.d
+    nc = n_compressed(dims) if c is not None else 0
+    if sink is not None and sink.numel() != H:
+        raise CSAError("csa_sparse_attn", -2, f"sink has {sink.numel()} entries, h = {H}")
+    return (_strided_ptr(q, (b, S, H, D), dt, "q"), _strided_ptr(kv, (b, S, D), dt, "kv"),
+            _ptr(c, shape=(b, nc, D), dtype=dt, name="c"),
+            _ptr(idx, shape=(b, S, kprime(dims)), dtype=torch.int32, name="idx"), _doc_ptr(dims, doc_ids),
+            _ptr(sink, shape=(H,), dtype=torch.float32, name="sink"))
+
+
+def csa_sparse_attn_fwd_strided(dims: csa_dims, q, kv, c, idx, sink, scale: float, out, lse, stream=None,
+                                doc_ids=None) -> None:
+    """csa_sparse_attn_fwd over strided views (e.g. sequence-major tensors
+    viewed as [b, sq, ...]); out shares q's strides.  c, idx, doc_ids and sink
+    stay contiguous."""
+    b, S, H, D = dims.b, dims.sq, dims.h, dims.d
+    st = attn_strides_of(q, kv, lse)
+    _call("csa_sparse_attn_fwd_strided", ctypes.byref(dims), ctypes.byref(st), _dtype_code(q),
+          *_strided_attn_ptrs(dims, q, kv, c, idx, sink, doc_ids), ctypes.c_float(scale),
+          _strided_ptr(out, (b, S, H, D), q.dtype, "out", like=q),
+          _strided_ptr(lse, (b, S, H), torch.float32, "lse"), _stream(stream))
+
+
+def csa_sparse_attn_bwd_strided(dims: csa_dims, q, kv, c, idx, sink, scale: float, out, lse, dout, dq, dkv, dc,
+                                dsink=None, ws=None, stream=None, doc_ids=None) -> None:
+    """csa_sparse_attn_bwd over strided views: out, dout and dq share q's
+    strides, dkv (fp32) shares kv's element strides."""
+    b, S, H, D = dims.b, dims.sq, dims.h, dims.d
+    f32 = torch.float32
+    nc = n_compressed(dims) if c is not None else 0
+    st = attn_strides_of(q, kv, lse)
+    _call("csa_sparse_attn_bwd_strided", ctypes.byref(dims), ctypes.byref(st), _dtype_code(q),
+          *_strided_attn_ptrs(dims, q, kv, c, idx, sink, doc_ids), ctypes.c_float(scale),
+          _strided_ptr(out, (b, S, H, D), q.dtype, "out", like=q),
+          _strided_ptr(lse, (b, S, H), f32, "lse"),
+          _strided_ptr(dout, (b, S, H, D), q.dtype, "dout", like=q),
+          _strided_ptr(dq, (b, S, H, D), q.dtype, "dq", like=q),
+          _strided_ptr(dkv, (b, S, D), f32, "dkv", like=kv), _ptr(dc, shape=(b, nc, D), dtype=f32, name="dc"),
+          _ptr(dsink, shape=(H,), dtype=f32, name="dsink"), _ptr(ws, name="ws"),
+          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
 
 
 def csa_indexer_loss_workspace(dims: csa_dims) -> int:

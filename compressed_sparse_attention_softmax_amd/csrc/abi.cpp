@@ -7,12 +7,14 @@
 // caller may capture the calls into a graph).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <initializer_list>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "csa.h"
 #include "csa_kernels.hpp"
@@ -117,7 +119,59 @@ csa::AttnArgs attn_args(const csa_dims* dm, const void* q, const void* kv, const
     a.r = c ? dm->ratio : 1;
     a.nc = c ? dm->sq / dm->ratio : 0;
     a.kp = (c && idx) ? kprime(dm) : 0;
+    a.set_contiguous();
     return a;
+}
+
+// Element strides of the strided attention calls.  For each tensor family the
+// axes of extent > 1 (plus the contiguous last axis of the row) must be laid
+// out without overlap: sorted by stride, every stride is at least the previous
+// stride times the previous extent, so no two elements share an address.
+// q-like and kv-like strides are multiples of 16 bytes (rows stay aligned for
+// the 16-byte loads); axes of extent 1 are not checked (never multiplied by
+// anything but 0).
+struct Axis { int64_t stride, extent; };
+
+bool no_overlap(std::vector<Axis> ax)
+{
+    std::vector<Axis> live;
+    for (const Axis& a : ax)
+        if (a.extent > 1) live.push_back(a);
+    std::sort(live.begin(), live.end(), [](const Axis& x, const Axis& y) { return x.stride < y.stride; });
+    for (size_t i = 1; i < live.size(); ++i)
+        if (live[i - 1].stride < 1 || live[i].stride < live[i - 1].stride * live[i - 1].extent) return false;
+    return live.empty() || live[0].stride >= 1;
+}
+
+int check_strides(const csa_dims* dm, int dtype, const csa_attn_strides* st, const char* fn)
+{
+    if (!st) return CSA_OK;
+    const int64_t e = dtype == CSA_BF16 ? 8 : 4;       // elements per 16 bytes
+    const int64_t b = dm->b, s = dm->sq, h = dm->h, d = dm->d;
+    const struct { int64_t v, n; const char* name; } al[] = {
+        {st->q_b, b, "q_b"}, {st->q_s, s, "q_s"}, {st->q_h, h, "q_h"}, {st->kv_b, b, "kv_b"}, {st->kv_s, s, "kv_s"}};
+    for (const auto& x : al)
+        if (x.n > 1 && (x.v < 1 || x.v % e))
+            return fail(CSA_ERR_ARG, "%s: stride %s = %lld must be a positive multiple of %lld elements", fn, x.name,
+                        (long long)x.v, (long long)e);
+    if (!no_overlap({{1, d}, {st->q_b, b}, {st->q_s, s}, {st->q_h, h}}))
+        return fail(CSA_ERR_ARG, "%s: q strides (%lld, %lld, %lld) make rows overlap", fn, (long long)st->q_b,
+                    (long long)st->q_s, (long long)st->q_h);
+    if (!no_overlap({{1, d}, {st->kv_b, b}, {st->kv_s, s}}))
+        return fail(CSA_ERR_ARG, "%s: kv strides (%lld, %lld) make rows overlap", fn, (long long)st->kv_b,
+                    (long long)st->kv_s);
+    if (!no_overlap({{1, h}, {st->lse_b, b}, {st->lse_s, s}}))
+        return fail(CSA_ERR_ARG, "%s: lse strides (%lld, %lld) make rows overlap", fn, (long long)st->lse_b,
+                    (long long)st->lse_s);
+    return CSA_OK;
+}
+
+void apply_strides(csa::AttnArgs& a, const csa_attn_strides* st)
+{
+    if (!st) return;
+    a.qsb = st->q_b; a.qst = st->q_s; a.qsh = st->q_h;
+    a.kvsb = st->kv_b; a.kvst = st->kv_s;
+    a.lsb = st->lse_b; a.lst = st->lse_s;
 }
 
 int check_epilogue(const csa_dims* dm, const float* norm_w, float eps, int rope_dim, float base, const char* fn)
@@ -235,21 +289,46 @@ int csa_index_topk(const csa_dims* dm, int dtype, const void* q_i, const void* k
     return hip_status(csa::index_topk(a, dtype == CSA_BF16, (hipStream_t)stream), "csa_index_topk");
 }
 
+}  // extern "C"
+
+namespace {
+
+int attn_fwd_call(const csa_dims* dm, const csa_attn_strides* st, int dtype, const void* q, const void* kv,
+                  const void* c, const int32_t* idx, const int32_t* doc_ids, const float* sink, float scale,
+                  void* out, float* lse, void* stream, const char* fn)
+{
+    int rc = check_common(dm, dtype, fn);
+    if (rc) return rc;
+    if ((rc = check_attn(dm, dtype, q, kv, c, idx, scale, fn))) return rc;
+    if ((rc = check_strides(dm, dtype, st, fn))) return rc;
+    if (!out || !lse) return fail(CSA_ERR_ARG, "%s: out and lse must be non-NULL", fn);
+    if ((rc = check_aligned(fn, {{"q", q}, {"kv", kv}, {"c", c}, {"idx", idx}, {"doc_ids", doc_ids},
+                                 {"sink", sink}, {"out", out}, {"lse", lse}})))
+        return rc;
+    csa::AttnArgs a = attn_args(dm, q, kv, c, idx, doc_ids, sink, scale);
+    apply_strides(a, st);
+    a.out = out; a.lse = lse;
+    return hip_status(csa::attn_fwd(a, dtype == CSA_BF16, (hipStream_t)stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
 int csa_sparse_attn_fwd(const csa_dims* dm, int dtype, const void* q, const void* kv, const void* c,
                         const int32_t* idx, const int32_t* doc_ids, const float* sink, float scale,
                         void* out, float* lse, void* stream)
 {
-    int rc = check_common(dm, dtype, "csa_sparse_attn_fwd");
-    if (rc) return rc;
-    if ((rc = check_attn(dm, dtype, q, kv, c, idx, scale, "csa_sparse_attn_fwd"))) return rc;
-    if (!out || !lse) return fail(CSA_ERR_ARG, "csa_sparse_attn_fwd: out and lse must be non-NULL");
-    if ((rc = check_aligned("csa_sparse_attn_fwd", {{"q", q}, {"kv", kv}, {"c", c}, {"idx", idx},
-                                                    {"doc_ids", doc_ids}, {"sink", sink}, {"out", out},
-                                                    {"lse", lse}})))
-        return rc;
-    csa::AttnArgs a = attn_args(dm, q, kv, c, idx, doc_ids, sink, scale);
-    a.out = out; a.lse = lse;
-    return hip_status(csa::attn_fwd(a, dtype == CSA_BF16, (hipStream_t)stream), "csa_sparse_attn_fwd");
+    return attn_fwd_call(dm, nullptr, dtype, q, kv, c, idx, doc_ids, sink, scale, out, lse, stream,
+                         "csa_sparse_attn_fwd");
+}
+
+int csa_sparse_attn_fwd_strided(const csa_dims* dm, const csa_attn_strides* strides, int dtype, const void* q,
+                                const void* kv, const void* c, const int32_t* idx, const int32_t* doc_ids,
+                                const float* sink, float scale, void* out, float* lse, void* stream)
+{
+    return attn_fwd_call(dm, strides, dtype, q, kv, c, idx, doc_ids, sink, scale, out, lse, stream,
+                         "csa_sparse_attn_fwd_strided");
 }
 
 size_t csa_sparse_attn_bwd_workspace(const csa_dims* dm)
@@ -287,12 +366,13 @@ namespace {
 int attn_bwd_prepare(const csa_dims* dm, int dtype, const void* q, const void* kv, const void* c, const int32_t* idx,
                      const int32_t* doc_ids, const float* sink, float scale, const void* out, const float* lse,
                      const void* dout, void* dq, float* dkv, float* dc, float* dsink, const char* fn,
-                     csa::AttnArgs& a, bool& noop)
+                     csa::AttnArgs& a, bool& noop, const csa_attn_strides* st = nullptr)
 {
     noop = false;
     int rc = check_common(dm, dtype, fn);
     if (rc) return rc;
     if ((rc = check_attn(dm, dtype, q, kv, c, idx, scale, fn))) return rc;
+    if ((rc = check_strides(dm, dtype, st, fn))) return rc;
     if (!out || !lse || !dout) return fail(CSA_ERR_ARG, "%s: out, lse and dout must be non-NULL", fn);
     // all-or-nothing gradient gate
     const bool want_c = c != nullptr;
@@ -313,9 +393,36 @@ int attn_bwd_prepare(const csa_dims* dm, int dtype, const void* q, const void* k
         return ok();
     }
     a = attn_args(dm, q, kv, c, idx, doc_ids, sink, scale);
+    apply_strides(a, st);
     a.out = const_cast<void*>(out); a.lse = const_cast<float*>(lse); a.dout = dout;
     a.dq = dq; a.dkv = dkv; a.dc = dc; a.dsink = dsink;
     return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+}  // extern "C"
+
+namespace {
+
+int attn_bwd_call(const csa_dims* dm, const csa_attn_strides* strides, int dtype, const void* q, const void* kv,
+                  const void* c, const int32_t* idx, const int32_t* doc_ids, const float* sink, float scale,
+                  const void* out, const float* lse, const void* dout, void* dq, float* dkv, float* dc,
+                  float* dsink, void* ws, size_t ws_bytes, void* stream, const char* fn)
+{
+    csa::AttnArgs a{};
+    bool noop = false;
+    int rc = attn_bwd_prepare(dm, dtype, q, kv, c, idx, doc_ids, sink, scale, out, lse, dout, dq, dkv, dc, dsink,
+                              fn, a, noop, strides);
+    if (rc || noop) return rc;
+    const size_t need = csa::attn_bwd_workspace_bytes(a);
+    if (!ws || ws_bytes < need)
+        return fail(CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    ws ? ws_bytes : (size_t)0);
+    if (((uintptr_t)ws) & 15) return fail(CSA_ERR_ARG, "%s: workspace must be 16-byte aligned", fn);
+    return hip_status(csa::attn_bwd(a, dtype == CSA_BF16, (float*)ws, (hipStream_t)stream), fn);
 }
 
 }  // namespace
@@ -327,18 +434,18 @@ int csa_sparse_attn_bwd(const csa_dims* dm, int dtype, const void* q, const void
                         const float* lse, const void* dout, void* dq, float* dkv, float* dc,
                         float* dsink, void* ws, size_t ws_bytes, void* stream)
 {
-    csa::AttnArgs a{};
-    bool noop = false;
-    int rc = attn_bwd_prepare(dm, dtype, q, kv, c, idx, doc_ids, sink, scale, out, lse, dout, dq, dkv, dc, dsink,
-                              "csa_sparse_attn_bwd", a, noop);
-    if (rc || noop) return rc;
-    const size_t need = csa::attn_bwd_workspace_bytes(a);
-    if (!ws || ws_bytes < need)
-        return fail(CSA_ERR_WORKSPACE, "csa_sparse_attn_bwd: workspace of %zu bytes needed, %zu given",
-                    need, ws ? ws_bytes : (size_t)0);
-    if (((uintptr_t)ws) & 15) return fail(CSA_ERR_ARG, "csa_sparse_attn_bwd: workspace must be 16-byte aligned");
-    hipStream_t st = (hipStream_t)stream;
-    return hip_status(csa::attn_bwd(a, dtype == CSA_BF16, (float*)ws, st), "csa_sparse_attn_bwd");
+    return attn_bwd_call(dm, nullptr, dtype, q, kv, c, idx, doc_ids, sink, scale, out, lse, dout, dq, dkv, dc, dsink,
+                         ws, ws_bytes, stream, "csa_sparse_attn_bwd");
+}
+
+int csa_sparse_attn_bwd_strided(const csa_dims* dm, const csa_attn_strides* strides, int dtype, const void* q,
+                                const void* kv, const void* c, const int32_t* idx, const int32_t* doc_ids,
+                                const float* sink, float scale, const void* out, const float* lse,
+                                const void* dout, void* dq, float* dkv, float* dc, float* dsink, void* ws,
+                                size_t ws_bytes, void* stream)
+{
+    return attn_bwd_call(dm, strides, dtype, q, kv, c, idx, doc_ids, sink, scale, out, lse, dout, dq, dkv, dc, dsink,
+                         ws, ws_bytes, stream, "csa_sparse_attn_bwd_strided");
 }
 
 int csa_sparse_attn_bwd_noalloc(const csa_dims* dm, int dtype, const void* q, const void* kv, const void* c,

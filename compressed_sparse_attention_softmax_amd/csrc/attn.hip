@@ -68,13 +68,15 @@ struct Cand {
     const T* c;           // batch base of c (nullptr: window only)
     const int32_t* irow;  // index row of the query (nullptr: dense mode)
     const uint32_t* okb;  // packed documents: LDS bit per window / dense slot, 1 = same document
+    int64_t kst;          // element stride between consecutive kv rows
     int t, D, u0, nwin, nv, nslots;
 
     __device__ __forceinline__ void init(const AttnArgs& p, int bi, int tq)
     {
         t = tq;
         D = p.D;
-        kv = (const T*)p.kv + (int64_t)bi * p.S * p.D;
+        kv = (const T*)p.kv + (int64_t)bi * p.kvsb;
+        kst = p.kvst;
         c = p.c ? (const T*)p.c + (int64_t)bi * p.nc * p.D : nullptr;
         irow = (p.c && p.idx) ? p.idx + ((int64_t)bi * p.S + tq) * p.kp : nullptr;
         okb = nullptr;
@@ -104,9 +106,9 @@ struct Cand {
     }
     __device__ __forceinline__ const T* row_ptr(int code) const
     {
-        const T* base = (code >= 0 && (code & 0x40000000)) ? c : kv;
+        const bool isc = code >= 0 && (code & 0x40000000);
         const int row = code < 0 ? t : (code & 0x3fffffff);
-        return base + (int64_t)row * D;
+        return isc ? c + (int64_t)row * D : kv + (int64_t)row * kst;
     }
 };
 
@@ -153,10 +155,12 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
     Cand<T> cand;
     cand.init(p, bi, active ? t : p.S - 1);
     const int64_t qrow = (int64_t)bi * p.S + (active ? t : p.S - 1);
+    const int64_t qoff = (int64_t)bi * p.qsb + (int64_t)(active ? t : p.S - 1) * p.qst;   // q-like tensors
+    const int64_t loff = (int64_t)bi * p.lsb + (int64_t)(active ? t : p.S - 1) * p.lst;   // lse
     const float sl2 = p.scale * LOG2E;
     [[maybe_unused]] const float isl2 = 1.f / sl2;
     [[maybe_unused]] const float lsc = __log2f(p.scale);
-    const T* qp = (const T*)p.q + qrow * p.H * D;
+    const T* qp = (const T*)p.q + qoff;
     // The query's index row goes to LDS once (per-chunk slot lookups then do
     // not wait on memory).  Its loads are issued first, into registers, so
     // that they overlap the loads of Q (dO, O) below.
@@ -207,7 +211,7 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
         const bool hv = h < p.H;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qb[ht][ks] = hv ? load_frag(qp + h * D + 32 * ks + 8 * g) : zero_frag<T>();
+            qb[ht][ks] = hv ? load_frag(qp + h * p.qsh + 32 * ks + 8 * g) : zero_frag<T>();
         if constexpr (!DQ) {
             // the running reference starts finite: a chunk whose rows are all
             // masked (another document) has logits -inf, and -inf against a
@@ -220,8 +224,8 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
             lsum[ht] = f32x4{l0, l0, l0, l0};
         } else {
             // Delta[h] = <dO[t, h], O[t, h]>; dO kept as the B operand of dP^T
-            const T* dop = (const T*)p.dout + (qrow * p.H + h) * D;
-            const T* op = (const T*)p.out + (qrow * p.H + h) * D;
+            const T* dop = (const T*)p.dout + qoff + h * p.qsh;
+            const T* op = (const T*)p.out + qoff + h * p.qsh;
             float part = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -234,7 +238,7 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
             }
             part = rows_sum(part);
             dlt[ht] = part;
-            lse2[ht] = hv ? p.lse[qrow * p.H + h] * LOG2E : INFINITY;
+            lse2[ht] = hv ? p.lse[loff + h] * LOG2E : INFINITY;
             if (active && hv && g == 0) {
                 delta[qrow * p.H + h] = part;
                 // this query's term of dsink[h], head-major; summed in a fixed order later
@@ -483,14 +487,14 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
             // no candidate and no sink (possible without a window): O = 0, LSE = -inf
             const float lt = lsum[ht][0];
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
-            T* orow = (T*)p.out + (qrow * p.H + h) * D;
+            T* orow = (T*)p.out + qoff + h * p.qsh;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) orow[16 * dt + 4 * g + i] = from_f32<T>(o[dt][ht][i] * inv);
-            if (g == 0) p.lse[qrow * p.H + h] = lt > 0.f ? (m2[ht] + log2f(lt)) * LN2 : -INFINITY;
+            if (g == 0) p.lse[loff + h] = lt > 0.f ? (m2[ht] + log2f(lt)) * LN2 : -INFINITY;
         } else {
-            T* drow = (T*)p.dq + (qrow * p.H + h) * D;
+            T* drow = (T*)p.dq + qoff + h * p.qsh;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -615,7 +619,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
         base_row = 0;
         nrows_valid = nvmax;
     }
-    const T* rows = win ? (const T*)p.kv + (int64_t)bi * p.S * D : (const T*)p.c + (int64_t)bi * p.nc * D;
+    const T* rows = win ? (const T*)p.kv + (int64_t)bi * p.kvsb : (const T*)p.c + (int64_t)bi * p.nc * D;
+    const int64_t rstride = win ? p.kvst : (int64_t)D;
     const int rmax = win ? p.S : p.nc;
     const int tile_lo = base_row + i0;           // key range of the tile
     const int tile_hi = base_row + min(i0 + TR, nrows_valid);
@@ -644,7 +649,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
         const bool ok = i < nrows_valid && key >= 0 && key < rmax;
         rkey[rt] = ok ? key : -1;
         rdoc[rt] = (p.doc && win && ok) ? p.doc[(int64_t)bi * p.S + key] : 0;
-        const T* src = rows + (int64_t)(ok ? key : 0) * D;
+        const T* src = rows + (int64_t)(ok ? key : 0) * rstride;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const Frag<T> f = load_frag(src + 32 * ks + 8 * g);
@@ -674,8 +679,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
     [[maybe_unused]] uint32_t srep = 0u;
     auto stage = [&](int t, int buf, int cb) {
         const int64_t qrow = (int64_t)bi * p.S + t;
-        const T* qsrc = (const T*)p.q + qrow * p.H * D;
-        const T* dsrc = (const T*)p.dout + qrow * p.H * D;
+        const int64_t qoff = (int64_t)bi * p.qsb + (int64_t)t * p.qst;
+        const T* qsrc = (const T*)p.q + qoff;
+        const T* dsrc = (const T*)p.dout + qoff;
         T* qdst = stage_base + (size_t)(2 * buf) * QELEMS;
         T* ddst = qdst + QELEMS;
         constexpr int PER_ROW = D * (int)sizeof(T) / 16;   // 16-byte pieces per row
@@ -693,12 +699,12 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
             const T* dp_ = dsrc;
             if constexpr (QS == 1) {
                 const int hh = h < p.H ? h : 0;           // padded heads read row 0 (masked later)
-                qp += hh * D + srcel;
-                dp_ += hh * D + srcel;
+                qp += hh * p.qsh + srcel;
+                dp_ += hh * p.qsh + srcel;
             } else {
                 // stacked slots: query t + h / HS, head h % HS (slots past the block read row 0 of t)
                 const int tq = t + h / HS, hq = h % HS;
-                const int64_t soff = (hq < p.H && tq < tb) ? ((int64_t)(tq - t) * p.H + hq) * D : 0;
+                const int64_t soff = (hq < p.H && tq < tb) ? (int64_t)(tq - t) * p.qst + (int64_t)hq * p.qsh : 0;
                 qp += soff + srcel;
                 dp_ += soff + srcel;
             }
@@ -714,14 +720,14 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
             // (a query with no candidate has LSE = -inf and multiplicity 0 everywhere:
             // any finite offset keeps its P at 0)
             if constexpr (QS == 1) {
-                const float l = h < p.H ? p.lse[qrow * p.H + h] : 0.f;
+                const float l = h < p.H ? p.lse[(int64_t)bi * p.lsb + (int64_t)t * p.lst + h] : 0.f;
                 lse_lds[buf * HP + h] = h < p.H ? (l > -INFINITY ? -l / p.scale : 0.f) : -INFINITY;
                 dlt_lds[buf * HP + h] = h < p.H ? -delta[qrow * p.H + h] : 0.f;
             } else {
                 const int tq = t + h / HS, hq = h % HS;
                 const bool hv = hq < p.H && tq < tb;
                 const int64_t hrow = (qrow + (tq - t)) * p.H + hq;
-                const float l = hv ? p.lse[hrow] : 0.f;
+                const float l = hv ? p.lse[(int64_t)bi * p.lsb + (int64_t)tq * p.lst + hq] : 0.f;
                 lse_lds[buf * HP + h] = hv ? (l > -INFINITY ? -l / p.scale : 0.f) : -INFINITY;
                 dlt_lds[buf * HP + h] = hv ? -delta[hrow] : 0.f;
             }
@@ -1039,7 +1045,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs p, RowsGeom g
                 ws + geo.win_off + (((int64_t)bi * geo.nqb + q) * geo.WB + i) * D + 4 * v);
             s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
         }
-        *reinterpret_cast<float4*>(p.dkv + row * D + 4 * v) = s;
+        *reinterpret_cast<float4*>(p.dkv + (int64_t)bi * p.kvsb + (int64_t)u * p.kvst + 4 * v) = s;
     } else if (tid < nkv + nct) {
         const int64_t k = tid - nkv;
         const int v = k % V;

@@ -64,6 +64,17 @@ struct AttnArgs {
     // when such an entry repeats.  nullptr: the kernels scan the index rows.
     const uint32_t* selmap;
     int selw;
+    // element strides: q-like tensors (q, out, dout, dq) along b, sequence,
+    // head; kv-like (kv, dkv) along b and sequence; lse along b and sequence
+    // (the last dimension is always contiguous).  set_contiguous() gives the
+    // batch-major layout.
+    int64_t qsb, qst, qsh, kvsb, kvst, lsb, lst;
+    void set_contiguous()
+    {
+        qsh = D; qst = (int64_t)H * D; qsb = (int64_t)S * H * D;
+        kvst = D; kvsb = (int64_t)S * D;
+        lst = H; lsb = (int64_t)S * H;
+    }
 };
 
 // Indexer distillation loss (teacher from the attention LSE, KL over the

@@ -47,6 +47,7 @@ AttnArgs group_args(const GqaArgs& p)
     a.b = p.b; a.S = p.S; a.H = p.H / p.HKV; a.D = p.DK + p.DV; a.W = 0; a.r = 1; a.nc = p.S; a.kp = p.kp;
     // the kernels skip the zero halves when the key half is whole k-steps
     a.dsplit = (p.DK % 32 == 0) ? p.DK : 0;
+    a.set_contiguous();                       // the packed buffers are batch-major
     return a;
 }
 

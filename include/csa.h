@@ -37,6 +37,9 @@
  *      q_i     [b, sq, idx_heads, idx_dim];  k_i [b, n_c, idx_dim]
  *      w       [b, sq, idx_heads];   lse [b, sq, h];  sink, dsink [h]
  *      idx, score [b, sq, K'],  K' = min(topk, n_c)
+ *    The *_strided attention calls take the q-like, kv-like and lse layouts
+ *    as element strides instead (csa_attn_strides); every other tensor keeps
+ *    the layout above.
  *    Base pointers must be 16-byte aligned (the CSA calls return CSA_ERR_ARG,
  *    naming the argument, for any non-NULL tensor that is not; the DSA-over-GQA
  *    calls accept any element-aligned tensor).
@@ -73,7 +76,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 6
+#define CSA_ABI_VERSION 7
 
 enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 };
 
@@ -231,6 +234,43 @@ int csa_sparse_attn_bwd_noalloc(const csa_dims* dims, int dtype, const void* q, 
                                 const void* c, const int32_t* idx, const int32_t* doc_ids,
                                 const float* sink, float scale, const void* out, const float* lse,
                                 const void* dout, void* dq, float* dkv, float* dc, float* dsink,
+                                void* stream);
+
+/* Element strides (in elements, not bytes) of the attention tensors for the
+ * *_strided calls, so that a caller holding sequence-major tensors (the
+ * SBHD layout of Megatron-LM PR #6400: [sq, b, h, d]) passes views instead
+ * of transposed copies.  The last axis (d for q-like and kv-like, h for lse)
+ * stays contiguous.
+ *   q_b, q_s, q_h   q, out, dout and dq (one layout for all four)
+ *   kv_b, kv_s      kv and dkv (dkv uses the same element strides in fp32)
+ *   lse_b, lse_s    lse
+ * Axes of extent > 1 must not overlap (sorted by stride, each stride at least
+ * the previous one times its extent, the contiguous axis first); q-like and
+ * kv-like strides of such axes are multiples of 16 bytes (8 bf16 or 4 fp32
+ * elements).  Otherwise CSA_ERR_ARG naming the stride.  Axes of extent 1 are
+ * ignored.  c, dc, idx, doc_ids, sink and dsink keep the contiguous layout. */
+typedef struct csa_attn_strides {
+    int64_t q_b, q_s, q_h;
+    int64_t kv_b, kv_s;
+    int64_t lse_b, lse_s;
+} csa_attn_strides;
+
+/* csa_sparse_attn_fwd over strided q, kv, out and lse (strides == NULL: the
+ * contiguous layout, identical to csa_sparse_attn_fwd). */
+int csa_sparse_attn_fwd_strided(const csa_dims* dims, const csa_attn_strides* strides, int dtype,
+                                const void* q, const void* kv, const void* c, const int32_t* idx,
+                                const int32_t* doc_ids, const float* sink, float scale, void* out,
+                                float* lse, void* stream);
+
+/* csa_sparse_attn_bwd over strided q, kv, out, lse, dout, dq and dkv
+ * (strides == NULL: identical to csa_sparse_attn_bwd).  The workspace is
+ * the same size (csa_sparse_attn_bwd_workspace(dims)) and the results are
+ * bit-identical to the contiguous call on the same values. */
+int csa_sparse_attn_bwd_strided(const csa_dims* dims, const csa_attn_strides* strides, int dtype,
+                                const void* q, const void* kv, const void* c, const int32_t* idx,
+                                const int32_t* doc_ids, const float* sink, float scale,
+                                const void* out, const float* lse, const void* dout, void* dq,
+                                float* dkv, float* dc, float* dsink, void* ws, size_t ws_bytes,
                                 void* stream);
 
 /* Workspace bytes csa_indexer_loss needs when gradients are requested

@@ -33,7 +33,7 @@ def test_library_exports_every_header_symbol():
     lib = _lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.csa_version() == 6
+    assert lib.csa_version() == 7
 
 
 def test_dims_struct_matches_header():
@@ -306,3 +306,81 @@ def test_indexer_loss_rejects_misaligned_tensors():
     lib = _lib()
     rc = lib.csa_indexer_loss(ctypes.byref(_d()), 1, M, P, P, P, P, P, P, P, F1, N, P, N, N, N, N, 0, N)
     assert rc == -1 and "q is not 16-byte aligned" in lib.csa_last_error().decode()
+
+
+def _sbhd(b=2, sq=64, h=4, d=64):
+    """Element strides of sequence-major q [sq, b, h, d], kv [sq, b, d], lse [sq, b, h]."""
+    return _abi.csa_attn_strides(h * d, b * h * d, d, d, b * d, h, b * h)
+
+
+def _strided_fwd(st, dims=None, **over):
+    a = dict(q=P, kv=P, c=P, idx=P, doc=N, sink=P, out=P, lse=P)
+    a.update(over)
+    return (ctypes.byref(dims or _d(b=2)), None if st is None else ctypes.byref(st), 1, a["q"], a["kv"], a["c"],
+            a["idx"], a["doc"], a["sink"], F1, a["out"], a["lse"], N)
+
+
+def test_strides_struct_matches_header():
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct csa_attn_strides \{(.*?)\} csa_attn_strides;", src, re.S).group(1)
+    names = re.findall(r"([a-z_]+)[,;]", body.replace("int64_t", ""))
+    assert names == [f[0] for f in _abi.csa_attn_strides._fields_]
+    assert ctypes.sizeof(_abi.csa_attn_strides) == 56
+
+
+@pytest.mark.parametrize("st", [None, "sbhd", "contiguous"])
+def test_strided_fwd_accepts_valid_strides(st):
+    # valid strides pass validation; the misaligned q is then what is reported
+    lib = _lib()
+    s = {"sbhd": _sbhd(), "contiguous": _abi.csa_attn_strides(64 * 4 * 64, 4 * 64, 64, 64 * 64, 64, 64 * 4, 4),
+         None: None}[st]
+    rc = lib.csa_sparse_attn_fwd_strided(*_strided_fwd(s, q=M))
+    assert rc == -1 and "q is not 16-byte aligned" in lib.csa_last_error().decode()
+
+
+@pytest.mark.parametrize("field,value,text", [
+    ("q_s", 516, "stride q_s"),          # not a multiple of 8 bf16 elements
+    ("kv_b", 0, "stride kv_b"),
+    ("q_h", 32, "q strides"),            # heads overlap rows of 64
+    ("kv_s", 32, "kv strides"),
+    ("q_b", 512, "q strides"),           # batch and sequence alias
+    ("lse_s", 1, "lse strides"),         # sequence steps inside the 4 heads
+])
+def test_strided_fwd_rejects_bad_strides(field, value, text):
+    lib = _lib()
+    st = _sbhd()
+    setattr(st, field, value)
+    rc = lib.csa_sparse_attn_fwd_strided(*_strided_fwd(st))
+    assert rc == -1 and text in lib.csa_last_error().decode()
+
+
+def test_strided_axes_of_extent_one_are_ignored():
+    lib = _lib()
+    st = _sbhd(b=1)
+    st.q_b = st.kv_b = st.lse_b = 0          # b == 1: never multiplied by anything but 0
+    rc = lib.csa_sparse_attn_fwd_strided(*_strided_fwd(st, dims=_d(b=1), q=M))
+    assert rc == -1 and "q is not 16-byte aligned" in lib.csa_last_error().decode()
+
+
+def test_strided_bwd_validates_strides_then_workspace():
+    lib = _lib()
+    args = [ctypes.byref(_d(b=2)), ctypes.byref(_sbhd()), 1, P, P, P, P, N, P, F1, P, P, P, P, P, P, P, N, 0, N]
+    assert lib.csa_sparse_attn_bwd_strided(*args) == -5
+    bad = _sbhd()
+    bad.kv_s = 36
+    args[1] = ctypes.byref(bad)
+    assert lib.csa_sparse_attn_bwd_strided(*args) == -1
+    assert "stride kv_s" in lib.csa_last_error().decode()
+
+
+def test_strided_binding_checks_stride_agreement():
+    # CPU tensors are refused before any stride logic runs; the stride helper
+    # itself is checked on CPU views
+    import torch
+    q = torch.zeros(64, 2, 4, 64, dtype=torch.bfloat16).transpose(0, 1)
+    kv = torch.zeros(64, 2, 64, dtype=torch.bfloat16).transpose(0, 1)
+    lse = torch.zeros(64, 2, 4).transpose(0, 1)
+    st = _abi.attn_strides_of(q, kv, lse)
+    assert (st.q_b, st.q_s, st.q_h, st.kv_b, st.kv_s, st.lse_b, st.lse_s) == (256, 512, 64, 64, 128, 4, 8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _abi._strided_ptr(q, (2, 64, 4, 64), torch.bfloat16, "q")

@@ -256,6 +256,13 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
     // MFMAs, read once after a drain), which frees the VGPRs the d = 512 dq
     // kernel otherwise spills; at d <= 128 the compiler's own allocation wins
     constexpr bool OACC = DQ && sizeof(T) == 2 && D >= 256 && (DT * HT == 16 || DT * HT == 32);
+    // bf16 reads a chunk's transposed rows all at once (fp32, and the one-wave
+    // 32-head dQ kernel, have no registers to spare for that)
+    constexpr bool EARLY = sizeof(T) == 2 && !(DQ && G == 1 && HT == 2);
+    // chunks gathered ahead into registers: two (the gather latency then
+    // spans two rounds) in the bf16 forward at d <= 128 with heads split over
+    // waves, where the registers allow; one elsewhere
+    constexpr int GDEPTH = (!DQ && sizeof(T) == 2 && D <= 128 && !(G == 1 && HT == 2)) ? 2 : 1;
     f32x4 o[DT][HT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -267,24 +274,24 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
     // chunk and its pieces (q % LPR) + LPR k, k < NPL: it resolves that row's
     // address itself, and its loads differ by immediate offsets only.
     const int my_r = (sub * WAVE + lane) / LPR, my_j = (sub * WAVE + lane) % LPR;
-    piece_t rg[NPL];
-    auto fetch = [&](int c0) -> uint32_t {
+    piece_t rg[GDEPTH][NPL];
+    auto fetch = [&](int c0, piece_t (&r)[NPL]) -> uint32_t {
         // lane l (and l + 32) resolves slot c0 + l % 32; the lanes that load
         // row my_r take its code from lane my_r
         const int cl = cand.code(c0 + (lane & 31), use_ids, ids);
         const uint32_t mask = (uint32_t)__ballot(cl >= 0);
         const T* rp = cand.row_ptr(__shfl(cl, my_r)) + my_j * E16;
 #pragma unroll
-        for (int k = 0; k < NPL; ++k) rg[k] = *reinterpret_cast<const piece_t*>(rp + k * LPR * E16);
+        for (int k = 0; k < NPL; ++k) r[k] = *reinterpret_cast<const piece_t*>(rp + k * LPR * E16);
         return mask;
     };
     // write the gathered rows to buffer buf, units permuted per row
-    auto stash = [&](int buf) {
+    auto stash = [&](int buf, const piece_t (&r)[NPL]) {
         T* dst = reinterpret_cast<T*>(tiles + (size_t)buf * CHB) + my_r * D;
 #pragma unroll
         for (int k = 0; k < NPL; ++k) {
             const int pos = (my_j + LPR * k) * E16;
-            *reinterpret_cast<piece_t*>(dst + ((((pos >> 3) ^ unit_swz(my_r, D / 8))) << 3) + (pos & 7)) = rg[k];
+            *reinterpret_cast<piece_t*>(dst + ((((pos >> 3) ^ unit_swz(my_r, D / 8))) << 3) + (pos & 7)) = r[k];
         }
     };
 
@@ -404,6 +411,20 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
                 }
                 mfma16_4_acc(&o[dt][0], a, b);
             }
+        } else if constexpr (EARLY) {
+            // every transposing read is issued before the first MFMA (one LDS
+            // round trip per chunk rather than one per d tile)
+            Frag<T> rt[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                if (!(KSP > 0 && (DQ ? dt >= 2 * KSP : dt < 2 * KSP))) rt[dt] = rows_operand<T>(tile, D, 0, 16 * dt, true);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                if (KSP > 0 && (DQ ? dt >= 2 * KSP : dt < 2 * KSP)) continue;
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) o[dt][ht] = mfma16(rt[dt], pb[ht], o[dt][ht]);
+            }
         } else {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
@@ -462,19 +483,35 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
     // every load so far (Q, dO, O, the index row) has landed: the loop below
     // then waits only on its own row gathers
     __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)
-    uint32_t mcur = 0u, mnext = 0u;
-    if (nch > 0) { mcur = fetch(0); stash(0); }
-    if (nch > 1) mnext = fetch(CHUNK);
+    // Round k computes chunk k from one LDS tile, writes chunk k+1 into the
+    // other and gathers chunk k + 1 + GDEPTH into registers.  G > 1: chunk
+    // k+1 fully written, chunk k read by every wave, before the next round
+    // reads k+1 and refills k's tile.  G == 1: a wave's LDS accesses run in
+    // order, so its own reads of a tile finish before its later writes to it.
+    uint32_t mk[3] = {0u, 0u, 0u};                // masks of chunks k, k+1, k+2
+    if (nch > 0) { mk[0] = fetch(0, rg[0]); stash(0, rg[0]); }
+#pragma unroll
+    for (int j = 1; j <= GDEPTH; ++j)
+        if (nch > j) mk[j] = fetch(CHUNK * j, rg[j % GDEPTH]);
     if constexpr (G > 1) __syncthreads();
-    for (int k = 0; k < nloop; ++k) {
-        if (G == 1 || k < nch) process(reinterpret_cast<const T*>(tiles + (size_t)(k & 1) * CHB), mcur);
-        if (k + 1 < nch) { stash((k + 1) & 1); mcur = mnext; }
-        if (k + 2 < nch) mnext = fetch(CHUNK * (k + 2));
-        // G > 1: chunk k+1 fully written, chunk k read by every wave, before
-        // the next round reads k+1 and refills k's buffer.  G == 1: a wave's
-        // LDS accesses run in order, so its own reads of a buffer finish
-        // before its later writes to it.
+    // r: the registers holding chunk k+1, which then receive chunk k + 1 + GDEPTH
+    auto round = [&](int k, piece_t (&r)[NPL]) {
+        if (G == 1 || k < nch) process(reinterpret_cast<const T*>(tiles + (size_t)(k & 1) * CHB), mk[0]);
+        if (k + 1 < nch) {
+            stash((k + 1) & 1, r);
+            mk[0] = mk[1];
+            mk[1] = mk[2];
+        }
+        if (k + 1 + GDEPTH < nch) mk[GDEPTH] = fetch(CHUNK * (k + 1 + GDEPTH), r);
         if constexpr (G > 1) __syncthreads();
+    };
+    if constexpr (GDEPTH == 1) {
+        for (int k = 0; k < nloop; ++k) round(k, rg[0]);
+    } else {
+        for (int k = 0; k < nloop; k += 2) {      // the register sets alternate
+            round(k, rg[1]);
+            if (k + 1 < nloop) round(k + 1, rg[0]);
+        }
     }
     if constexpr (OACC) agpr_drain<DT * HT>(&o[0][0]);
     if (!active) return;

@@ -31,6 +31,14 @@ whose block j satisfies 0 <= j < min((t+1)//ratio, n_c) are its support):
   counts once per slot).  a = <q_i[t,h], k_i[j_s]>; the ReLU's derivative at
   0 is taken as 0.
 
+Dense warm-up form (Megatron-LM PR #7152, the commit adding the dense
+warm-up tile plan: the dense teacher scores every attention head against
+the same keys, the indexer against all of them): the support of row t is
+every valid block j < min((t+1)//ratio, n_c) instead of the selected slots;
+teacher, student, KL and gradients are the ones above over that support
+(``dense_warmup_loss``).  Written over dense per-row matrices, not through
+the slot functions above.
+
 Plain NumPy, one query row at a time; library matmuls and exp/log only.
 """
 from __future__ import annotations
@@ -158,5 +166,59 @@ def indexer_loss(q_rows, c, lse_rows, q_i_rows, k_i, w_rows, idx_rows, scale, ra
     out = dict(target=target, scores=scores, predict=predict, kl=kl)
     if dkl is not None:
         dq, dw, dk, dI = loss_bwd(q_i_rows, k_i, w_rows, idx_rows, ratio, rows, target, predict, dkl)
+        out.update(dq_i=dq, dw=dw, dk_i=dk, dI=dI)
+    return out
+
+
+def dense_warmup_loss(q_rows, c, lse_rows, q_i_rows, k_i, w_rows, scale, ratio, rows, dkl=None):
+    """Dense warm-up loss over every valid block of each listed row.
+
+    q_rows [n,H,D], c [b,n_c,D], lse_rows [n,H], q_i_rows [n,HI,DI],
+    k_i [b,n_c,DI], w_rows [n,HI], rows [n,2] (batch, t), dkl [n] or None.
+    Returns a dict with target [n,n_c], scores [n,n_c] (-inf past n_valid),
+    predict [n,n_c], kl [n] and, with ``dkl``, dq_i, dw, dk_i and dI [n,n_c]."""
+    q = np.asarray(q_rows, np.float64)
+    c = np.asarray(c, np.float64)
+    lse = np.asarray(lse_rows, np.float64)
+    qi = np.asarray(q_i_rows, np.float64)
+    k = np.asarray(k_i, np.float64)
+    w = np.asarray(w_rows, np.float64)
+    n = q.shape[0]
+    nc = c.shape[1]
+    target = np.zeros((n, nc))
+    scores = np.full((n, nc), -np.inf)
+    predict = np.zeros((n, nc))
+    kl = np.zeros(n)
+    grads = dkl is not None
+    if grads:
+        dkl = np.asarray(dkl, np.float64)
+        dq, dw, dk, dI = np.zeros_like(qi), np.zeros_like(w), np.zeros_like(k), np.zeros((n, nc))
+    for r in range(n):
+        b, t = int(rows[r, 0]), int(rows[r, 1])
+        nv = min((t + 1) // ratio, nc)
+        if nv == 0:
+            continue
+        # teacher: log of the head-summed probability mass of each block
+        logits = scale * (q[r] @ c[b, :nv].T)                     # [H, nv]
+        log_mass = _logsumexp(logits - lse[r][:, None], axis=0)   # [nv]
+        tg = np.exp(log_mass - _logsumexp(log_mass, axis=0))
+        target[r, :nv] = tg
+        # student: weighted ReLU scores of the indexer and their softmax
+        a = qi[r] @ k[b, :nv].T                                   # [HI, nv]
+        I = w[r] @ np.maximum(a, 0.0)
+        scores[r, :nv] = I
+        logp = I - _logsumexp(I, axis=0)
+        predict[r, :nv] = np.exp(logp)
+        pos = tg > 0
+        kl[r] = np.sum(tg[pos] * (np.log(tg[pos]) - logp[pos]))
+        if grads:
+            g = dkl[r] * (predict[r, :nv] * tg.sum() - tg)
+            dI[r, :nv] = g
+            dw[r] = np.maximum(a, 0.0) @ g
+            coef = w[r][:, None] * (a > 0) * g[None, :]           # [HI, nv]
+            dq[r] = coef @ k[b, :nv]
+            dk[b, :nv] += coef.T @ qi[r]
+    out = dict(target=target, scores=scores, predict=predict, kl=kl)
+    if grads:
         out.update(dq_i=dq, dw=dw, dk_i=dk, dI=dI)
     return out

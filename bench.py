@@ -316,6 +316,69 @@ def bench_dsa_gqa(stream, K):
     return res
 
 
+DENSE_LOSS_BUDGET = 64 << 20
+
+
+def bench_indexer_loss_dense(wl, dm, inp, buf, stream, K):
+    """The dense warm-up form of the indexer loss (every valid block is the
+    support) on the step's inputs, its workspace planned for a 64 MiB budget,
+    timed over K calls with events on the same stream (the step's LSE stands
+    in for the warm-up's dense one: the timing does not depend on its values).
+
+    Algorithmic work per (query, valid block): the teacher's logits 2*h*d, the
+    student's <q_i, k_i> 2*HI*DI, the dq_i product 2*HI*DI (query kernel) and
+    the dk_i product 2*HI*DI (key-stationary kernel); recomputed products are
+    not counted.
+    """
+    import torch
+    import compressed_sparse_attention_softmax_amd as csa
+    ws_bytes = csa.csa_indexer_loss_dense_workspace(dm, DENSE_LOSS_BUDGET)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    b, S, nc = wl.b, wl.sq, wl.n_c
+    kl = torch.empty(b, S, device="cuda")
+    dkl = torch.full((b, S), 1.0 / (b * S), device="cuda")
+    dq_i = torch.empty(b, S, wl.idx_heads, wl.idx_dim, dtype=wl.torch_dtype, device="cuda")
+    dw = torch.empty(b, S, wl.idx_heads, device="cuda")
+    dk_i = torch.empty(b, nc, wl.idx_dim, device="cuda")
+
+    def call():
+        csa.csa_indexer_loss_dense(dm, inp["q"], buf.c, buf.lse, inp["q_i"], inp["k_i"], inp["w"], wl.scale, kl=kl,
+                                   dkl=dkl, dq_i=dq_i, dw=dw, dk_i=dk_i, ws=ws, stream=stream)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    kms = {}
+    for k in (csa.CSA_K_LOSS_QUERY, csa.CSA_K_LOSS_KEYS, csa.CSA_K_LOSS_REDUCE):
+        csa.csa_timing_enable(k)
+        call()
+        n, ms = csa.csa_timing_read()
+        if n:
+            kms[csa.csa_kernel_name(k)] = ms          # summed over the call's query chunks
+    csa.csa_timing_enable(-1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_call = e0.elapsed_time(e1) / K
+    pairs = float(b * sum(min((t + 1) // wl.ratio, nc) for t in range(S)))
+    hd = 2.0 * wl.idx_heads * wl.idx_dim
+    work = {"loss_query": pairs * (2.0 * wl.h * wl.d + 2 * hd), "loss_keys": pairs * hd}
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    kern = {}
+    for k, fl in work.items():
+        if k in kms:
+            tf = fl / (kms[k] * 1e-3) / 1e12
+            kern[k] = {"ms_per_call": kms[k], "algorithmic_flop": fl, "tflops": tf, "frac": tf / peak}
+    log(f"bench: dense warm-up indexer loss {ms_call:.3f} ms/call, workspace {ws_bytes} B "
+        f"(budget {DENSE_LOSS_BUDGET}); kernels(ms) {kms}")
+    return {"ms_per_call": ms_call, "valid_blocks": pairs, "workspace_bytes": ws_bytes,
+            "budget_bytes": DENSE_LOSS_BUDGET, "kernel_ms": kms, "kernels": kern,
+            "timing": "HIP events on the launch stream; per-kernel times from the library's timing hook"}
+
+
 def bench_indexer_loss(wl, dm, inp, buf, stream, K):
     """The indexer's training path after the step's forward (not part of the
     step): csa_indexer_loss over the selected blocks, scores and LSE the last
@@ -573,6 +636,8 @@ def main():
     if not args.no_extras:
         if wl.topk > 0:
             result["indexer_loss"] = bench_indexer_loss(wl, dm, inp, buf, stream, K)
+        if wl.n_c > 0:
+            result["indexer_loss_dense"] = bench_indexer_loss_dense(wl, dm, inp, buf, stream, K)
         result["compress_epilogue"] = bench_compress_epilogue(wl, dm, inp, buf, stream, K)
         result["dsa_gqa"] = bench_dsa_gqa(stream, K)
     if not args.no_cpu_baseline:

@@ -25,7 +25,8 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_ARG", -2: "CSA_ERR_SHAPE", -3: "CSA_ERR_DTYP
 EXPORTS = ["csa_compress", "csa_compress_bwd_workspace", "csa_compress_bwd", "csa_index_topk_workspace", "csa_index_topk",
            "csa_sparse_attn_fwd", "csa_sparse_attn_bwd_workspace", "csa_sparse_attn_bwd_query_block",
            "csa_sparse_attn_bwd", "csa_sparse_attn_bwd_noalloc", "csa_sparse_attn_fwd_strided",
-           "csa_sparse_attn_bwd_strided", "csa_indexer_loss_workspace", "csa_indexer_loss", "csa_dsa_gqa_workspace", "csa_dsa_gqa_fwd",
+           "csa_sparse_attn_bwd_strided", "csa_indexer_loss_workspace", "csa_indexer_loss", "csa_indexer_loss_dense_workspace",
+           "csa_indexer_loss_dense", "csa_dsa_gqa_workspace", "csa_dsa_gqa_fwd",
            "csa_dsa_gqa_bwd", "csa_last_error", "csa_version", "csa_timing_enable", "csa_timing_read", "csa_kernel_name"]
 
 # kernel ids of the timing hook (enum csa_kernel_id)
@@ -91,6 +92,9 @@ def load(path: Optional[str] = None):
     lib.csa_indexer_loss_workspace.argtypes = [D]
     lib.csa_indexer_loss_workspace.restype = sz
     lib.csa_indexer_loss.argtypes = [D, i, vp, vp, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.csa_indexer_loss_dense_workspace.argtypes = [D, sz]
+    lib.csa_indexer_loss_dense_workspace.restype = sz
+    lib.csa_indexer_loss_dense.argtypes = [D, i, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, sz, vp]
     GD = ctypes.POINTER(csa_gqa_dims)
     lib.csa_dsa_gqa_workspace.argtypes = [GD, i, i]
     lib.csa_dsa_gqa_workspace.restype = sz
@@ -105,7 +109,7 @@ def load(path: Optional[str] = None):
     lib.csa_kernel_name.restype = ctypes.c_char_p
     for fn in ("csa_compress", "csa_compress_bwd", "csa_index_topk", "csa_sparse_attn_fwd",
                "csa_sparse_attn_bwd", "csa_sparse_attn_bwd_noalloc", "csa_sparse_attn_fwd_strided",
-               "csa_sparse_attn_bwd_strided", "csa_indexer_loss", "csa_dsa_gqa_fwd", "csa_dsa_gqa_bwd", "csa_version", "csa_timing_enable", "csa_timing_read"):
+               "csa_sparse_attn_bwd_strided", "csa_indexer_loss", "csa_indexer_loss_dense", "csa_dsa_gqa_fwd", "csa_dsa_gqa_bwd", "csa_version", "csa_timing_enable", "csa_timing_read"):
         getattr(lib, fn).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -370,6 +374,29 @@ def csa_indexer_loss(dims: csa_dims, q, c, lse, q_i, k_i, w, idx, score, scale: 
           _ptr(w, shape=(b, S, HI), dtype=f32, name="w"),
           _ptr(idx, shape=(b, S, kp), dtype=torch.int32, name="idx"),
           _ptr(score, shape=(b, S, kp), dtype=f32, name="score"), ctypes.c_float(scale),
+          _ptr(dkl, shape=(b, S), dtype=f32, name="dkl"), _ptr(kl, shape=(b, S), dtype=f32, name="kl"),
+          _ptr(dq_i, shape=(b, S, HI, DI), dtype=dt, name="dq_i"), _ptr(dw, shape=(b, S, HI), dtype=f32, name="dw"),
+          _ptr(dk_i, shape=(b, nc, DI), dtype=f32, name="dk_i"), _ptr(ws, name="ws"),
+          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def csa_indexer_loss_dense_workspace(dims: csa_dims, budget: int = 0) -> int:
+    """Bytes the dense warm-up loss's plan uses within ``budget`` (at least its minimum)."""
+    return int(load().csa_indexer_loss_dense_workspace(ctypes.byref(dims), int(budget)))
+
+
+def csa_indexer_loss_dense(dims: csa_dims, q, c, lse, q_i, k_i, w, scale: float, kl=None, dkl=None, dq_i=None,
+                           dw=None, dk_i=None, ws=None, stream=None) -> None:
+    """Dense warm-up form of the indexer loss: every valid block is the support."""
+    b, S, H, D = dims.b, dims.sq, dims.h, dims.d
+    HI, DI = dims.idx_heads, dims.idx_dim
+    nc = n_compressed(dims)
+    dt, f32 = q.dtype, torch.float32
+    _call("csa_indexer_loss_dense", ctypes.byref(dims), _dtype_code(q),
+          _ptr(q, shape=(b, S, H, D), dtype=dt, name="q"), _ptr(c, shape=(b, nc, D), dtype=dt, name="c"),
+          _ptr(lse, shape=(b, S, H), dtype=f32, name="lse"),
+          _ptr(q_i, shape=(b, S, HI, DI), dtype=dt, name="q_i"), _ptr(k_i, shape=(b, nc, DI), dtype=dt, name="k_i"),
+          _ptr(w, shape=(b, S, HI), dtype=f32, name="w"), ctypes.c_float(scale),
           _ptr(dkl, shape=(b, S), dtype=f32, name="dkl"), _ptr(kl, shape=(b, S), dtype=f32, name="kl"),
           _ptr(dq_i, shape=(b, S, HI, DI), dtype=dt, name="dq_i"), _ptr(dw, shape=(b, S, HI), dtype=f32, name="dw"),
           _ptr(dk_i, shape=(b, nc, DI), dtype=f32, name="dk_i"), _ptr(ws, name="ws"),

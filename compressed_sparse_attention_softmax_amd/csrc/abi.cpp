@@ -475,20 +475,20 @@ int csa_sparse_attn_bwd_noalloc(const csa_dims* dm, int dtype, const void* q, co
 
 namespace {
 
-int check_loss(const csa_dims* dm, int dtype, const char* fn)
+int check_loss(const csa_dims* dm, int dtype, const char* fn, bool dense = false)
 {
     if (!supported_d(dm->d)) return fail(CSA_ERR_UNSUPPORTED, "%s: d=%d not in {64,128,512}", fn, dm->d);
     if (dm->d == 512 && dtype == CSA_F32)
         return fail(CSA_ERR_UNSUPPORTED, "%s: fp32 with d=512 exceeds the on-chip row tile", fn);
     if (dm->h < 1 || dm->h > 64) return fail(dm->h < 1 ? CSA_ERR_ARG : CSA_ERR_UNSUPPORTED, "%s: h=%d not in [1, 64]", fn, dm->h);
     if (dm->ratio < 1) return fail(CSA_ERR_ARG, "%s: ratio=%d must be >= 1", fn, dm->ratio);
-    if (dm->topk < 1) return fail(CSA_ERR_ARG, "%s: topk=%d must be >= 1", fn, dm->topk);
+    if (!dense && dm->topk < 1) return fail(CSA_ERR_ARG, "%s: topk=%d must be >= 1", fn, dm->topk);
     if (dm->idx_heads < 1 || dm->idx_heads > 64)
         return fail(dm->idx_heads < 1 ? CSA_ERR_ARG : CSA_ERR_UNSUPPORTED, "%s: idx_heads=%d not in [1, 64]", fn,
                     dm->idx_heads);
     if (dm->idx_dim != 32 && dm->idx_dim != 64 && dm->idx_dim != 128)
         return fail(CSA_ERR_UNSUPPORTED, "%s: idx_dim=%d not in {32,64,128}", fn, dm->idx_dim);
-    if (kprime(dm) > 2048) return fail(CSA_ERR_UNSUPPORTED, "%s: K'=%d > 2048", fn, kprime(dm));
+    if (!dense && kprime(dm) > 2048) return fail(CSA_ERR_UNSUPPORTED, "%s: K'=%d > 2048", fn, kprime(dm));
     return CSA_OK;
 }
 
@@ -497,6 +497,7 @@ csa::LossArgs loss_args(const csa_dims* dm)
     csa::LossArgs a{};
     a.b = dm->b; a.S = dm->sq; a.H = dm->h; a.D = dm->d; a.HI = dm->idx_heads; a.DI = dm->idx_dim;
     a.r = dm->ratio; a.nc = dm->sq / dm->ratio; a.kp = kprime(dm);
+    a.t_begin = 0; a.t_count = dm->sq;
     return a;
 }
 
@@ -548,6 +549,43 @@ int csa_indexer_loss(const csa_dims* dm, int dtype, const void* q, const void* c
         if (((uintptr_t)ws) & 15) return fail(CSA_ERR_ARG, "csa_indexer_loss: workspace must be 16-byte aligned");
     }
     return hip_status(csa::indexer_loss(a, dtype == CSA_BF16, (float*)ws, (hipStream_t)stream), "csa_indexer_loss");
+}
+
+size_t csa_indexer_loss_dense_workspace(const csa_dims* dm, size_t budget)
+{
+    if (!dm || dm->b < 1 || dm->sq < 1 || dm->ratio < 1) return 0;
+    if (dm->idx_dim != 32 && dm->idx_dim != 64 && dm->idx_dim != 128) return 0;
+    return csa::indexer_loss_dense_workspace_bytes(loss_args(dm), budget);
+}
+
+int csa_indexer_loss_dense(const csa_dims* dm, int dtype, const void* q, const void* c, const float* lse,
+                           const void* q_i, const void* k_i, const float* w, float scale, const float* dkl,
+                           float* kl, void* dq_i, float* dw, float* dk_i, void* ws, size_t ws_bytes, void* stream)
+{
+    const char* fn = "csa_indexer_loss_dense";
+    int rc = check_common(dm, dtype, fn);
+    if (rc) return rc;
+    if ((rc = check_loss(dm, dtype, fn, true))) return rc;
+    if (!std::isfinite(scale)) return fail(CSA_ERR_ARG, "%s: scale is not finite", fn);
+    const bool blocks = dm->sq / dm->ratio > 0;
+    if (!q || !lse || !q_i || !w || (blocks && (!c || !k_i)))
+        return fail(CSA_ERR_ARG, "%s: q, c, lse, q_i, k_i and w must be non-NULL", fn);
+    const bool any = dkl || dq_i || dw || dk_i;
+    if (any && (!dkl || !dq_i || !dw || (blocks && !dk_i)))
+        return fail(CSA_ERR_ARG, "%s: gradient gate: dkl, dq_i, dw and dk_i must all be given (or all be NULL)", fn);
+    if ((rc = check_aligned(fn, {{"q", q}, {"c", c}, {"lse", lse}, {"q_i", q_i}, {"k_i", k_i}, {"w", w},
+                                 {"dkl", dkl}, {"kl", kl}, {"dq_i", dq_i}, {"dw", dw}, {"dk_i", dk_i}})))
+        return rc;
+    if (!any && !kl) return ok();
+    csa::LossArgs a = loss_args(dm);
+    a.q = q; a.c = c; a.lse = lse; a.qi = q_i; a.ki = k_i; a.w = w;
+    a.scale = scale; a.dkl = dkl; a.kl = kl; a.dqi = dq_i; a.dw = dw; a.dki = dk_i;
+    const size_t need = csa::indexer_loss_dense_workspace_bytes(a, 0);
+    if (!ws || ws_bytes < need)
+        return fail(CSA_ERR_WORKSPACE, "%s: workspace of at least %zu bytes needed, %zu given", fn, need,
+                    ws ? ws_bytes : (size_t)0);
+    if (((uintptr_t)ws) & 15) return fail(CSA_ERR_ARG, "%s: workspace must be 16-byte aligned", fn);
+    return hip_status(csa::indexer_loss_dense(a, dtype == CSA_BF16, (float*)ws, ws_bytes, (hipStream_t)stream), fn);
 }
 
 }  // extern "C"

@@ -95,6 +95,13 @@ struct LossArgs {
     float* dw;            // [b, S, HI]
     float* dki;           // [b, nc, DI]
     int b, S, H, D, HI, DI, r, nc, kp;
+    // queries [t_begin, t_begin + t_count) of this launch (the dense form
+    // runs the queries chunk by chunk; the selected form in one launch)
+    int t_begin, t_count;
+    // dense warm-up form (every valid block is the support): floats per
+    // workspace row of a query; 0: the selected form
+    int dense_ld;
+    int dk_accumulate;    // the reduction adds into dk_i instead of overwriting it
 };
 
 // Simplified DSA over grouped-query attention: attention over the selected
@@ -138,6 +145,10 @@ hipError_t build_selmap(const AttnArgs& p, uint32_t* map, hipStream_t st);
 bool attn_bwd_stacks_queries(const AttnArgs& p, bool bf16);
 hipError_t indexer_loss(const LossArgs& p, bool bf16, float* ws, hipStream_t st);
 size_t indexer_loss_workspace_bytes(const LossArgs& p);
+// dense warm-up form: the bytes its plan uses within `budget` (at least the
+// smallest plan), and the call on a workspace of ws_bytes (the plan fitting it)
+size_t indexer_loss_dense_workspace_bytes(const LossArgs& p, size_t budget);
+hipError_t indexer_loss_dense(const LossArgs& p, bool bf16, float* ws, size_t ws_bytes, hipStream_t st);
 size_t dsa_gqa_workspace_bytes(const GqaArgs& p, bool bf16, bool bwd);
 hipError_t dsa_gqa_fwd(const GqaArgs& p, bool bf16, void* ws, hipStream_t st);
 hipError_t dsa_gqa_bwd(const GqaArgs& p, bool bf16, void* ws, hipStream_t st);

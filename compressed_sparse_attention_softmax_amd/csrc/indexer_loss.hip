@@ -281,12 +281,235 @@ __global__ __launch_bounds__(NT) void loss_query_kernel(LossArgs p, float* __res
     }
 }
 
+// ------------------------------------------------ dense warm-up, per query
+// Contiguous rows j0 .. j0 + LCH - 1 of a [rows, W] matrix (rows past the
+// last, jmax, read row jmax: their results are masked).
+template <typename T, int W>
+__device__ __forceinline__ void rows_fetch(piece_t* r, const T* base, int j0, int jmax)
+{
+    constexpr int PPR = chunk_ppr<T, W>(), NP = chunk_np<T, W>(), E16 = 16 / (int)sizeof(T);
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+        const int pc = (int)threadIdx.x + NT * k;
+        const int rr = min(pc / PPR, LCH - 1), pp = pc % PPR;
+        r[k] = *reinterpret_cast<const piece_t*>(base + (int64_t)min(j0 + rr, jmax) * W + pp * E16);
+    }
+}
+
+// Dense warm-up form: the support of query t is every valid block j <
+// n_valid(t).  One workgroup per query of the launch's chunk, teacher heads
+// and indexer heads split 16 per wave.  Pass 1 walks the blocks in chunks of
+// 32 (c rows and k_i rows in double-buffered LDS tiles), forms each wave's
+// per-block log2 teacher mass and its part of the student score
+// I = sum_h w_h relu(a_h); the waves' parts are combined by the thread that
+// owns the block (thread j mod 256) and written to the query's two workspace
+// rows (A: log2 mass, I: score; dense_ld floats each).  The owners then form
+// the target / student statistics, the KL and dI (over A), reading back only
+// what they wrote themselves.  Pass 2 (gradients) walks the k_i rows again
+// as the selected form's pass 2 does, with dI handed over through LDS.
+template <typename T, int D, int DI>
+__global__ __launch_bounds__(NT) void loss_dense_query_kernel(LossArgs p, float* __restrict__ rows)
+{
+    constexpr int KS = D / 32, KSI = DI / 32, DTI = DI / 16;
+    constexpr int CB = LCH * D * (int)sizeof(T), KB = LCH * DI * (int)sizeof(T);
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    T* ct = reinterpret_cast<T*>(smem);                          // [2][LCH][D] c rows
+    T* kt = reinterpret_cast<T*>(smem + 2 * CB);                 // [2][LCH][DI] k_i rows
+    float* tpart = reinterpret_cast<float*>(smem + 2 * CB + 2 * KB);   // [2][4][LCH] per-wave log2 masses
+    float* spart = tpart + 2 * 4 * LCH;                          // [2][4][LCH] per-wave student parts
+    float* dib = spart + 2 * 4 * LCH;                            // [2][LCH] dI of a chunk (pass 2)
+    float* red = dib + 2 * LCH;                                  // [4]
+    const int wave = threadIdx.x / WAVE, lane = lane_id(), g = lane / 16, n16 = lane % 16;
+    const int bi = blockIdx.y;
+    const int tl = p.t_count - 1 - (int)blockIdx.x;              // latest queries (most blocks) first
+    const int t = p.t_begin + tl;
+    const int64_t row = (int64_t)bi * p.S + t;
+    float* arow = rows + ((int64_t)bi * p.t_count + tl) * 2 * p.dense_ld;
+    float* irow = arow + p.dense_ld;
+    const int nv = min((t + 1) / p.r, p.nc);
+    const int nch = (nv + LCH - 1) / LCH;
+    const bool grads = p.dqi != nullptr;
+    const int owner = (int)threadIdx.x / LCH, oi = (int)threadIdx.x % LCH;   // blocks j = 256 m + threadIdx.x
+
+    // ------------------------------------------ pass 1: teacher and student
+    const T* qrow = (const T*)p.q + row * p.H * D;
+    const T* qirow = (const T*)p.qi + row * p.HI * DI;
+    const int hh = 16 * wave + n16;                              // A-row head of this lane
+    Frag<T> qf[KS], qif[KSI];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = hh < p.H ? load_frag(qrow + hh * D + 32 * ks + 8 * g) : zero_frag<T>();
+#pragma unroll
+    for (int ks = 0; ks < KSI; ++ks) qif[ks] = hh < p.HI ? load_frag(qirow + hh * DI + 32 * ks + 8 * g) : zero_frag<T>();
+    float lse2[4], w4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = 16 * wave + 4 * g + i;                     // result-row head of element i
+        lse2[i] = h < p.H ? p.lse[row * p.H + h] * LOG2E : INFINITY;   // +inf: padded heads add nothing
+        w4[i] = h < p.HI ? p.w[row * p.HI + h] : 0.f;
+    }
+    const float sl2 = p.scale * LOG2E;
+    const T* cb = (const T*)p.c + (int64_t)bi * p.nc * D;
+    const T* kb = (const T*)p.ki + (int64_t)bi * p.nc * DI;
+    const int jmax = max(p.nc - 1, 0);
+    piece_t cr[chunk_np<T, D>()], kr[chunk_np<T, DI>()];
+    if (nch > 0) {
+        rows_fetch<T, D>(cr, cb, 0, jmax); chunk_stash<T, D>(cr, ct);
+        rows_fetch<T, DI>(kr, kb, 0, jmax); chunk_stash<T, DI>(kr, kt);
+    }
+    if (nch > 1) { rows_fetch<T, D>(cr, cb, LCH, jmax); rows_fetch<T, DI>(kr, kb, LCH, jmax); }
+    __syncthreads();
+    for (int k = 0; k < nch; ++k) {
+        const T* ctile = ct + (size_t)(k & 1) * LCH * D;
+        const T* ktile = kt + (size_t)(k & 1) * LCH * DI;
+        float* tp = tpart + (k & 1) * 4 * LCH;
+        float* sp = spart + (k & 1) * 4 * LCH;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            // S[h, r] for the wave's 16 heads (m) and 16 rows (n); log2 mass over the heads
+            f32x4 acc = f4zero();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) acc = mfma16(qf[ks], tile_frag<T, D>(ctile, 16 * rt + n16, ks, g), acc);
+            float x[4];
+            float m = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = fmaf(acc[i], sl2, -lse2[i]);
+                m = fmaxf(m, x[i]);
+            }
+            m = rows_max(m);
+            float sum = 0.f;
+            if (m > -INFINITY) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sum += fast_exp2(x[i] - m);
+            }
+            sum = rows_sum(sum);
+            // a[h, r] of the wave's 16 indexer heads; the weighted ReLU sum over them
+            f32x4 a = f4zero();
+#pragma unroll
+            for (int ks = 0; ks < KSI; ++ks) a = mfma16(qif[ks], tile_frag<T, DI>(ktile, 16 * rt + n16, ks, g), a);
+            float sv = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv += w4[i] * fmaxf(a[i], 0.f);
+            sv = rows_sum(sv);
+            if (g == 0) {
+                tp[wave * LCH + 16 * rt + n16] = m > -INFINITY ? m + __log2f(sum) : -INFINITY;
+                sp[wave * LCH + 16 * rt + n16] = sv;
+            }
+        }
+        if (k + 1 < nch) {
+            chunk_stash<T, D>(cr, ct + (size_t)((k + 1) & 1) * LCH * D);
+            chunk_stash<T, DI>(kr, kt + (size_t)((k + 1) & 1) * LCH * DI);
+        }
+        if (k + 2 < nch) {
+            rows_fetch<T, D>(cr, cb, LCH * (k + 2), jmax);
+            rows_fetch<T, DI>(kr, kb, LCH * (k + 2), jmax);
+        }
+        __syncthreads();
+        // the owners of chunk k combine its four wave parts (the next write of
+        // these parts comes after the next barrier)
+        if (owner == (k & 7)) {
+            const int j = k * LCH + oi;
+            if (j < nv) {
+                const float l0 = tp[oi], l1 = tp[LCH + oi], l2 = tp[2 * LCH + oi], l3 = tp[3 * LCH + oi];
+                const float M = fmaxf(fmaxf(l0, l1), fmaxf(l2, l3));
+                arow[j] = M > -INFINITY ? M + __log2f((fast_exp2(l0 - M) + fast_exp2(l1 - M)) +
+                                                      (fast_exp2(l2 - M) + fast_exp2(l3 - M)))
+                                        : -INFINITY;
+                irow[j] = (sp[oi] + sp[LCH + oi]) + (sp[2 * LCH + oi] + sp[3 * LCH + oi]);
+            }
+        }
+    }
+
+    // ------------------------------------------- target, student, KL, dI
+    float mt = -INFINITY, ms = -INFINITY;
+    for (int j = threadIdx.x; j < nv; j += NT) {
+        mt = fmaxf(mt, arow[j]);
+        ms = fmaxf(ms, irow[j]);
+    }
+    mt = block_max(mt, red);
+    ms = block_max(ms, red);
+    float zt = 0.f, zs = 0.f;
+    for (int j = threadIdx.x; j < nv; j += NT) {
+        zt += fast_exp2(arow[j] - mt);
+        zs += __expf(irow[j] - ms);
+    }
+    zt = block_sum(zt, red);
+    zs = block_sum(zs, red);
+    const float lzt = __logf(zt), lzs = __logf(zs), izt = 1.f / zt, izs = 1.f / zs;
+    const float dkl = grads ? p.dkl[row] : 0.f;
+    float klp = 0.f;
+    for (int j = threadIdx.x; j < nv; j += NT) {
+        const float a2 = arow[j], sc = irow[j];
+        const float tg = fast_exp2(a2 - mt) * izt;
+        const float lt = (a2 - mt) * LN2 - lzt;                  // log target
+        const float lp = (sc - ms) - lzs;                        // log student
+        if (tg > 0.f) klp += tg * (lt - lp);
+        arow[j] = dkl * (__expf(sc - ms) * izs - tg);            // dI (read by the keys kernel)
+    }
+    const float kl = block_sum(klp, red);
+    if (p.kl && threadIdx.x == 0) p.kl[row] = nch > 0 ? kl : 0.f;
+    if (!grads) return;
+
+    // ---------------------------------------------- pass 2: student backward
+    const float wv = hh < p.HI ? p.w[row * p.HI + hh] : 0.f;
+    f32x4 o[DTI];
+#pragma unroll
+    for (int dt = 0; dt < DTI; ++dt) o[dt] = f4zero();
+    float dwl = 0.f;
+    // the owners of chunk k hand its dI over to every wave through LDS
+    auto hand = [&](int k) {
+        if (owner == (k & 7)) {
+            const int j = k * LCH + oi;
+            dib[(k & 1) * LCH + oi] = j < nv ? arow[j] : 0.f;
+        }
+    };
+    if (nch > 0) { rows_fetch<T, DI>(kr, kb, 0, jmax); chunk_stash<T, DI>(kr, kt); hand(0); }
+    if (nch > 1) rows_fetch<T, DI>(kr, kb, LCH, jmax);
+    __syncthreads();
+    for (int k = 0; k < nch; ++k) {
+        const T* tile = kt + (size_t)(k & 1) * LCH * DI;
+        const float* dk = dib + (k & 1) * LCH;
+        Frag<T> gb;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            // a^T[r, h] for 16 rows (m) and the wave's 16 heads (n)
+            f32x4 a = f4zero();
+#pragma unroll
+            for (int ks = 0; ks < KSI; ++ks) a = mfma16(tile_frag<T, DI>(tile, 16 * rt + n16, ks, g), qif[ks], a);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float gi = dk[16 * rt + 4 * g + i];
+                const bool pos = a[i] > 0.f;
+                dwl += pos ? gi * a[i] : 0.f;
+                gb.v[4 * rt + i] = from_f32<T>(pos ? gi * wv : 0.f);
+            }
+        }
+        // dq_i^T[d, h] += sum_r K[r, d] G^T[r, h]
+#pragma unroll
+        for (int dt = 0; dt < DTI; ++dt) o[dt] = mfma16(rows_operand<T>(tile, DI, 0, 16 * dt, true), gb, o[dt]);
+        if (k + 1 < nch) { chunk_stash<T, DI>(kr, kt + (size_t)((k + 1) & 1) * LCH * DI); hand(k + 1); }
+        if (k + 2 < nch) rows_fetch<T, DI>(kr, kb, LCH * (k + 2), jmax);
+        __syncthreads();
+    }
+    dwl = rows_sum(dwl);
+    if (hh < p.HI) {
+        if (g == 0) p.dw[row * p.HI + hh] = dwl;
+        T* dst = (T*)p.dqi + (row * p.HI + hh) * DI;
+#pragma unroll
+        for (int dt = 0; dt < DTI; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[16 * dt + 4 * g + i] = from_f32<T>(o[dt][i]);
+    }
+}
+
 // ------------------------------------------------------ dk_i, key-stationary
 struct KeysGeom {
     int Qb, nqb, ntiles;
 };
 
-template <typename T, int DI>
+// DENSE: every valid block is the support; the query's dI row (dense_ld
+// floats, chunk-local) is read directly instead of through its index row.
+template <typename T, int DI, bool DENSE>
 __global__ __launch_bounds__(NT) void loss_keys_kernel(LossArgs p, KeysGeom geo, const float* __restrict__ gws,
                                                        float* __restrict__ part)
 {
@@ -309,8 +532,9 @@ __global__ __launch_bounds__(NT) void loss_keys_kernel(LossArgs p, KeysGeom geo,
     if (qbi >= p.b * geo.nqb) return;
     const int bi = qbi / geo.nqb, qb = geo.nqb - 1 - qbi % geo.nqb;
     const int tile_lo = tile * KTR;
-    const int t0 = max(qb * geo.Qb, (tile_lo + 1) * p.r - 1);
-    const int t1 = min(p.S, (qb + 1) * geo.Qb);
+    const int tb = p.t_begin, te = p.t_begin + p.t_count;
+    const int t0 = max(tb + qb * geo.Qb, (tile_lo + 1) * p.r - 1);
+    const int t1 = min(te, tb + (qb + 1) * geo.Qb);
     if (t0 >= t1) return;                                       // no query of the block reaches the tile
     const int hp_n = (p.HI + 31) / 32;                          // 32-head pairs in use
 
@@ -344,11 +568,17 @@ __global__ __launch_bounds__(NT) void loss_keys_kernel(LossArgs p, KeysGeom geo,
                                                  : piece_t{0u, 0u, 0u, 0u};
         }
         if (threadIdx.x < HP) wreg = (int)threadIdx.x < p.HI ? p.w[row * p.HI + threadIdx.x] : 0.f;
+        if constexpr (DENSE) {
+            const int j = tile_lo + (int)threadIdx.x, nvt = min((t + 1) / p.r, p.nc);
+            greg[0] = ((int)threadIdx.x < KTR && j < nvt)
+                          ? gws[((int64_t)bi * p.t_count + (t - tb)) * 2 * p.dense_ld + j] : 0.f;
+        } else {
 #pragma unroll
-        for (int k = 0; k < IPT; ++k) {
-            const int s = (int)threadIdx.x + NT * k;
-            jreg[k] = s < p.kp ? p.idx[row * p.kp + s] : -1;
-            greg[k] = s < p.kp ? gws[row * p.kp + s] : 0.f;
+            for (int k = 0; k < IPT; ++k) {
+                const int s = (int)threadIdx.x + NT * k;
+                jreg[k] = s < p.kp ? p.idx[row * p.kp + s] : -1;
+                greg[k] = s < p.kp ? gws[row * p.kp + s] : 0.f;
+            }
         }
     };
     auto place = [&](int buf, int cb) {
@@ -364,10 +594,14 @@ __global__ __launch_bounds__(NT) void loss_keys_kernel(LossArgs p, KeysGeom geo,
         }
         if (threadIdx.x < HP) wt[buf * HP + threadIdx.x] = wreg;
         float* gtb = gt + cb * KTR;
+        if constexpr (DENSE) {
+            if ((int)threadIdx.x < KTR) gtb[threadIdx.x] = greg[0];
+        } else {
 #pragma unroll
-        for (int k = 0; k < IPT; ++k) {
-            const int j = jreg[k] - tile_lo;
-            if (j >= 0 && j < KTR && greg[k] != 0.f) atomicAdd(&gtb[j], greg[k]);
+            for (int k = 0; k < IPT; ++k) {
+                const int j = jreg[k] - tile_lo;
+                if (j >= 0 && j < KTR && greg[k] != 0.f) atomicAdd(&gtb[j], greg[k]);
+            }
         }
     };
 
@@ -451,24 +685,31 @@ __global__ __launch_bounds__(NT) void loss_reduce_kernel(LossArgs p, KeysGeom ge
         v = (int)(i % v4);
         bj = i / v4;
         const int j = (int)(bj % p.nc), bi = (int)(bj / p.nc);
-        const int qlo = ((j + 1) * p.r - 1) / geo.Qb;
+        const int qlo = max(0, ((j + 1) * p.r - 1 - p.t_begin) / geo.Qb);
         for (int q = qlo + split; q < geo.nqb; q += 4)
             s += *reinterpret_cast<const f32x4*>(part + ((((int64_t)bi * geo.nqb + q) * p.nc) + j) * p.DI + 4 * v);
     }
     red[split][col] = s;
     __syncthreads();
-    if (split == 0 && live)
-        *reinterpret_cast<f32x4*>(p.dki + bj * p.DI + 4 * v) = ((red[0][col] + red[1][col]) + red[2][col]) + red[3][col];
+    if (split == 0 && live) {
+        f32x4* dst = reinterpret_cast<f32x4*>(p.dki + bj * p.DI + 4 * v);
+        const f32x4 sum = ((red[0][col] + red[1][col]) + red[2][col]) + red[3][col];
+        *dst = p.dk_accumulate ? *dst + sum : sum;
+    }
 }
 
-KeysGeom keys_geometry(const LossArgs& p)
+// qb > 0: that query block (the dense plan's); else the smallest power of
+// two from 32 that keeps the partial rows within 1 GiB
+KeysGeom keys_geometry(const LossArgs& p, int qb = 0)
 {
     KeysGeom g{};
-    auto part_bytes = [&](int qb) { return (int64_t)p.b * ((p.S + qb - 1) / qb) * p.nc * p.DI * 4; };
-    int qb = 32;
-    while (qb < 4096 && part_bytes(qb) > ((int64_t)1 << 30)) qb *= 2;
+    auto part_bytes = [&](int q) { return (int64_t)p.b * ((p.t_count + q - 1) / q) * p.nc * p.DI * 4; };
+    if (qb <= 0) {
+        qb = 32;
+        while (qb < 4096 && part_bytes(qb) > ((int64_t)1 << 30)) qb *= 2;
+    }
     g.Qb = qb;
-    g.nqb = (p.S + qb - 1) / qb;
+    g.nqb = (p.t_count + qb - 1) / qb;
     g.ntiles = (p.nc + KTR - 1) / KTR;
     return g;
 }
@@ -494,7 +735,7 @@ hipError_t launch_loss(const LossArgs& p, float* ws, hipStream_t st)
     const KeysGeom geo = keys_geometry(p);
     float* part = ws + gws_floats(p);
     const size_t klds = 2 * (size_t)64 * DI * sizeof(T) + 2 * 64 * 4 + 3 * KTR * 4;
-    auto kk = loss_keys_kernel<T, DI>;
+    auto kk = loss_keys_kernel<T, DI, false>;
     if ((e = hipFuncSetAttribute((const void*)kk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)klds)) != hipSuccess)
         return e;
     const int64_t groups = ((int64_t)p.b * geo.nqb + 7) / 8;
@@ -523,7 +764,119 @@ hipError_t loss_di(const LossArgs& p, float* ws, hipStream_t st)
     }
 }
 
+// ------------------------------------------------ dense warm-up: the plan
+// The queries run in chunks of qc (a multiple of the keys kernel's query
+// block); per chunk the workspace holds each query's two rows (dense_ld
+// floats each: log2 teacher mass, then dI; student scores) and the chunk's
+// dk_i partial rows.  The plan takes the largest chunk whose bytes fit the
+// budget, so memory is O(budget), never O(sq * n_c) unless the budget allows.
+constexpr int DENSE_QB = 32;
+
+int dense_ld(const LossArgs& p) { return (max(p.nc, 1) + LCH - 1) / LCH * LCH; }
+
+int64_t dense_rows_floats(const LossArgs& p, int qc)
+{
+    return ((int64_t)p.b * qc * 2 * dense_ld(p) + 63) / 64 * 64;   // partial rows start 256-byte aligned
+}
+
+int64_t dense_bytes(const LossArgs& p, int qc)
+{
+    const int64_t part = (int64_t)p.b * ((qc + DENSE_QB - 1) / DENSE_QB) * p.nc * p.DI;
+    return (dense_rows_floats(p, qc) + part) * (int64_t)sizeof(float);
+}
+
+int dense_chunk(const LossArgs& p, size_t budget)
+{
+    int lo = 1, hi = (p.S + DENSE_QB - 1) / DENSE_QB;               // chunk sizes in query blocks
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (dense_bytes(p, mid * DENSE_QB) <= (int64_t)budget) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo * DENSE_QB;
+}
+
+template <typename T, int D, int DI>
+hipError_t launch_dense(const LossArgs& p0, float* ws, int qc, hipStream_t st)
+{
+    constexpr int CB = LCH * D * (int)sizeof(T), KB = LCH * DI * (int)sizeof(T);
+    const size_t lds = 2 * (size_t)CB + 2 * (size_t)KB + (2 * 4 * LCH * 2 + 2 * LCH + 4) * sizeof(float);
+    if (lds > (size_t)ATTN_LDS_LIMIT) return hipErrorInvalidValue;
+    auto qk = loss_dense_query_kernel<T, D, DI>;
+    hipError_t e = hipFuncSetAttribute((const void*)qk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    auto kk = loss_keys_kernel<T, DI, true>;
+    const size_t klds = 2 * (size_t)64 * DI * sizeof(T) + 2 * 64 * 4 + 3 * KTR * 4;
+    if ((e = hipFuncSetAttribute((const void*)kk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)klds)) != hipSuccess)
+        return e;
+    const bool grads = p0.dqi != nullptr;
+    float* part = ws + dense_rows_floats(p0, qc);
+    for (int t0 = 0; t0 < p0.S; t0 += qc) {
+        LossArgs p = p0;
+        p.t_begin = t0;
+        p.t_count = min(qc, p0.S - t0);
+        p.dense_ld = dense_ld(p0);
+        p.dk_accumulate = t0 > 0;
+        {
+            TimedLaunch tl(K_LOSS_QUERY, st);
+            hipLaunchKernelGGL(qk, dim3(p.t_count, p.b), dim3(NT), lds, st, p, ws);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        if (!grads || p.nc == 0) continue;
+        const KeysGeom geo = keys_geometry(p, DENSE_QB);
+        const int64_t groups = ((int64_t)p.b * geo.nqb + 7) / 8;
+        {
+            TimedLaunch tl(K_LOSS_KEYS, st);
+            hipLaunchKernelGGL(kk, dim3((unsigned)(groups * 8 * geo.ntiles)), dim3(NT), klds, st, p, geo,
+                               (const float*)ws, part);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        const int64_t cols = (int64_t)p.b * p.nc * (p.DI / 4);
+        {
+            TimedLaunch tl(K_LOSS_REDUCE, st);
+            hipLaunchKernelGGL(loss_reduce_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(NT), 0, st, p, geo, part);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+template <typename T, int D>
+hipError_t dense_di(const LossArgs& p, float* ws, int qc, hipStream_t st)
+{
+    switch (p.DI) {
+    case 32: return launch_dense<T, D, 32>(p, ws, qc, st);
+    case 64: return launch_dense<T, D, 64>(p, ws, qc, st);
+    case 128: return launch_dense<T, D, 128>(p, ws, qc, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
+
+size_t indexer_loss_dense_workspace_bytes(const LossArgs& p, size_t budget)
+{
+    return (size_t)dense_bytes(p, dense_chunk(p, budget));
+}
+
+hipError_t indexer_loss_dense(const LossArgs& p, bool bf16, float* ws, size_t ws_bytes, hipStream_t st)
+{
+    if (p.S == 0) return hipSuccess;
+    const int qc = dense_chunk(p, ws_bytes);
+    if (bf16) {
+        switch (p.D) {
+        case 64: return dense_di<bf16_t, 64>(p, ws, qc, st);
+        case 128: return dense_di<bf16_t, 128>(p, ws, qc, st);
+        case 512: return dense_di<bf16_t, 512>(p, ws, qc, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (p.D) {
+    case 64: return dense_di<float, 64>(p, ws, qc, st);
+    case 128: return dense_di<float, 128>(p, ws, qc, st);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 size_t indexer_loss_workspace_bytes(const LossArgs& p)
 {

@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 7
+#define CSA_ABI_VERSION 8
 
 enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 };
 
@@ -309,6 +309,36 @@ int csa_indexer_loss(const csa_dims* dims, int dtype, const void* q, const void*
                      const int32_t* idx, const float* score, float scale,
                      const float* dkl, float* kl, void* dq_i, float* dw, float* dk_i,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* Dense warm-up form of the indexer distillation loss (Megatron-LM PR #7152,
+ * the commit adding the dense warm-up tile plan: the dense teacher scores
+ * every attention head against all keys, under a planned memory budget).
+ * Same as csa_indexer_loss with the support of row (b, t) every valid block
+ * j < n_valid(t) instead of the selected slots, and the student's logits
+ * I[t, j] = sum_h w[t, h] * relu(<q_i[t, h], k_i[j]>) formed inside the call
+ * (no idx or score input; topk is ignored):
+ *   mass[j]  = sum_h exp(scale * <q[t, h], c[j]> - lse[t, h])
+ *   target   = mass / sum(mass),  predict = softmax_j I[t, j]
+ *   kl[b, t] = sum_j target (log target - log predict)
+ *   dI[j]    = dkl[t] * (predict[j] - target[j])   (rows with blocks)
+ *   dw, dq_i, dk_i as in csa_indexer_loss over every valid block.
+ * lse is the per-head LSE of the warm-up's attention (e.g. csa_sparse_attn_fwd
+ * with idx == NULL, every valid block attended).  No packed documents.
+ * The queries run in chunks; the workspace holds, per chunk, two fp32 rows of
+ * n_c entries per query and the chunk's fp32 partial rows of dk_i.  The call
+ * plans the largest chunk that fits ws_bytes (so memory follows the budget,
+ * not sq * n_c) and needs at least csa_indexer_loss_dense_workspace(dims, 0)
+ * bytes (CSA_ERR_WORKSPACE otherwise), also when only kl is requested.
+ * csa_indexer_loss_dense_workspace(dims, budget) returns the bytes the plan
+ * for that budget uses (at most budget unless budget is below that minimum;
+ * 0 for invalid dims).  dk_i accumulates over the chunks in a fixed order.
+ * Gradient gate, kl, layouts and the 16-byte alignment as in
+ * csa_indexer_loss. */
+size_t csa_indexer_loss_dense_workspace(const csa_dims* dims, size_t budget);
+int csa_indexer_loss_dense(const csa_dims* dims, int dtype, const void* q, const void* c,
+                           const float* lse, const void* q_i, const void* k_i, const float* w,
+                           float scale, const float* dkl, float* kl, void* dq_i, float* dw,
+                           float* dk_i, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------ simplified DSA over GQA
  * Megatron-LM PR #7152 (description and commit messages): a one-head indexer

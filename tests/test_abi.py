@@ -33,7 +33,7 @@ def test_library_exports_every_header_symbol():
     lib = _lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.csa_version() == 7
+    assert lib.csa_version() == 8
 
 
 def test_dims_struct_matches_header():
@@ -384,3 +384,55 @@ def test_strided_binding_checks_stride_agreement():
     assert (st.q_b, st.q_s, st.q_h, st.kv_b, st.kv_s, st.lse_b, st.lse_s) == (256, 512, 64, 64, 128, 4, 8)
     with pytest.raises(ValueError, match="GPU tensor"):
         _abi._strided_ptr(q, (2, 64, 4, 64), torch.bfloat16, "q")
+
+
+def _dense_args(dims, **over):
+    a = dict(q=P, c=P, lse=P, q_i=P, k_i=P, w=P, dkl=N, kl=P, dq_i=N, dw=N, dk_i=N, ws=N, ws_bytes=0)
+    a.update(over)
+    return (ctypes.byref(dims), 1, a["q"], a["c"], a["lse"], a["q_i"], a["k_i"], a["w"], F1, a["dkl"], a["kl"],
+            a["dq_i"], a["dw"], a["dk_i"], a["ws"], a["ws_bytes"], N)
+
+
+def test_dense_loss_workspace_plan_follows_the_budget():
+    lib = _lib()
+    dm = _d(b=1, sq=4096, h=64, d=128, ratio=4, idx_heads=64, idx_dim=128, topk=512)
+    nc = 4096 // 4
+    least = lib.csa_indexer_loss_dense_workspace(ctypes.byref(dm), 0)
+    full = lib.csa_indexer_loss_dense_workspace(ctypes.byref(dm), 1 << 40)
+    assert 0 < least < full
+    assert least >= 2 * nc * 4                 # at least one query's two rows
+    assert full >= 2 * 4096 * nc * 4           # every query's rows at once
+    prev = least
+    for budget in (least, least + 1, 3 * least, 10 << 20, 50 << 20, full - 1, full, 2 * full):
+        got = lib.csa_indexer_loss_dense_workspace(ctypes.byref(dm), budget)
+        assert got <= max(budget, least) and got >= prev
+        prev = got
+    assert lib.csa_indexer_loss_dense_workspace(ctypes.byref(dm), 2 * full) == full
+    # topk plays no part in the dense form
+    dm2 = _d(b=1, sq=4096, h=64, d=128, ratio=4, idx_heads=64, idx_dim=128, topk=0)
+    assert lib.csa_indexer_loss_dense_workspace(ctypes.byref(dm2), 10 << 20) == \
+        lib.csa_indexer_loss_dense_workspace(ctypes.byref(dm), 10 << 20)
+    assert lib.csa_indexer_loss_dense_workspace(None, 0) == 0
+
+
+def test_dense_loss_validation():
+    lib = _lib()
+    dm = _d(topk=0)
+    need = lib.csa_indexer_loss_dense_workspace(ctypes.byref(dm), 0)
+    # nothing requested: a no-op, no workspace needed
+    assert lib.csa_indexer_loss_dense(*_dense_args(dm, kl=N)) == 0
+    # kl alone still needs the workspace rows
+    assert lib.csa_indexer_loss_dense(*_dense_args(dm)) == -5
+    assert lib.csa_indexer_loss_dense(*_dense_args(dm, ws=P, ws_bytes=need - 1)) == -5
+    assert "at least" in lib.csa_last_error().decode()
+    # gradient gate
+    assert lib.csa_indexer_loss_dense(*_dense_args(dm, dkl=P, dq_i=P, ws=P, ws_bytes=need)) == -1
+    assert "gradient gate" in lib.csa_last_error().decode()
+    # inputs of the student are required
+    assert lib.csa_indexer_loss_dense(*_dense_args(dm, q_i=N, ws=P, ws_bytes=need)) == -1
+    assert lib.csa_indexer_loss_dense(*_dense_args(dm, q=M, ws=P, ws_bytes=need)) == -1
+    assert "q is not 16-byte aligned" in lib.csa_last_error().decode()
+    assert lib.csa_indexer_loss_dense(*_dense_args(dm, ws=M, ws_bytes=need)) == -1
+    assert lib.csa_indexer_loss_dense(*_dense_args(_d(idx_dim=48), ws=P, ws_bytes=need)) == -4
+    assert lib.csa_indexer_loss_dense(*_dense_args(dm, ws=P, ws_bytes=need)[:1] + (7,) +
+                                      _dense_args(dm, ws=P, ws_bytes=need)[2:]) == -3

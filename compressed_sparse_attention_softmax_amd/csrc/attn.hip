@@ -260,9 +260,11 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
     // 32-head dQ kernel, have no registers to spare for that)
     constexpr bool EARLY = sizeof(T) == 2 && !(DQ && G == 1 && HT == 2);
     // chunks gathered ahead into registers: two (the gather latency then
-    // spans two rounds) in the bf16 forward at d <= 128 with heads split over
-    // waves, where the registers allow; one elsewhere
-    constexpr int GDEPTH = (!DQ && sizeof(T) == 2 && D <= 128 && !(G == 1 && HT == 2)) ? 2 : 1;
+    // spans two rounds) where the registers allow it (the bf16 forward at
+    // d <= 128 with heads split over waves, both bf16 kernels at d = 512 with
+    // four waves per query); one elsewhere
+    constexpr int GDEPTH = ((!DQ && sizeof(T) == 2 && D <= 128 && !(G == 1 && HT == 2)) ||
+                             (sizeof(T) == 2 && D == 512 && G == 4)) ? 2 : 1;
     f32x4 o[DT][HT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)

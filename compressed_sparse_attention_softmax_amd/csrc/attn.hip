@@ -554,11 +554,21 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
 //                                     accumulators (lane (r, g) holds heads 4g+i
 //                                     of head tiles 2kk, 2kk+1), B = dO / Q
 //                                     from LDS through the transposing read
-// q/dO staging buffers of the key-stationary kernel: two (the next query
+// Heads the key-stationary kernel stages per unit of its query loop: all 64
+// of a query, or 32 (two units per query) when two stagings of 64 heads do
+// not fit in LDS but two of 32 do (bf16 d = 512), so that the next unit
+// always loads while this one computes.
+template <typename T, int D> constexpr int rows_unit_heads()
+{
+    return 4 * 64 * D * (int)sizeof(T) + 8 * 1024 <= ATTN_LDS_LIMIT
+               ? 64
+               : (4 * 32 * D * (int)sizeof(T) + 8 * 1024 <= ATTN_LDS_LIMIT ? 32 : 64);
+}
+// q/dO staging buffers of the key-stationary kernel: two (the next unit
 // loads while this one computes) when they fit in LDS, else one.
 template <typename T, int D> constexpr int rows_stage_buffers()
 {
-    return 4 * 64 * D * (int)sizeof(T) + 8 * 1024 <= ATTN_LDS_LIMIT ? 2 : 1;
+    return 4 * rows_unit_heads<T, D>() * D * (int)sizeof(T) + 8 * 1024 <= ATTN_LDS_LIMIT ? 2 : 1;
 }
 // waves per workgroup and key rows per wave: a workgroup's tile is 256 rows at
 // d <= 128 (64 at d = 512).  bf16 uses 8 waves of 32 rows: two waves per SIMD,
@@ -568,7 +578,7 @@ template <typename T, int D> constexpr int rows_per_wave_t() { return D <= 128 ?
 // LDS bytes of the key-stationary kernel without / with its key-row tile
 template <typename T, int D, int QS = 1> constexpr size_t rows_lds_base()
 {
-    return 2 * (size_t)rows_stage_buffers<T, D>() * 64 * D * sizeof(T) + 4 * 64 * 4 +
+    return 2 * (size_t)rows_stage_buffers<T, D>() * rows_unit_heads<T, D>() * D * sizeof(T) + 4 * 64 * 4 +
            (size_t)3 * QS * rows_waves_t<T, D>() * rows_per_wave_t<T, D>() * 4;
 }
 template <typename T, int D> constexpr size_t rows_lds_tile()
@@ -610,7 +620,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
     constexpr int HS = HP / QS;
     constexpr int CTR = QS * NW * RW;            // multiplicities per count buffer
     static_assert(QS == 1 || HS >= 4, "a lane's four head slots belong to one query");
-    constexpr int QELEMS = HP * D;               // one staged q (or dO) block
+    constexpr int HU = rows_unit_heads<T, D>();  // heads staged per unit of the query loop
+    constexpr int NU = HP / HU;                  // units per query
+    static_assert(HU == HP || QS == 1, "stacked queries stage all head slots at once");
+    constexpr int QELEMS = HU * D;               // one staged q (or dO) block
     constexpr int NBUF = rows_stage_buffers<T, D>();
     constexpr int L16 = QELEMS * (int)sizeof(T) / 16;   // 16-byte pieces per block
     static_assert(L16 % NT == 0, "staging: whole 1 KiB wave loads");
@@ -716,7 +729,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
     constexpr int SEL_REGS = QS > 1 ? CTR / NT : 1;
     [[maybe_unused]] uint32_t sword[SEL_REGS];
     [[maybe_unused]] uint32_t srep = 0u;
-    auto stage = [&](int t, int buf, int cb) {
+    // hu: which HU heads of query t (unit hu of the query); the index row and
+    // dense multiplicities are loaded with the query's first unit only
+    auto stage = [&](int t, int hu, int buf, int cb) {
         const int64_t qrow = (int64_t)bi * p.S + t;
         const int64_t qoff = (int64_t)bi * p.qsb + (int64_t)t * p.qst;
         const T* qsrc = (const T*)p.q + qoff;
@@ -737,7 +752,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
             const T* qp = qsrc;
             const T* dp_ = dsrc;
             if constexpr (QS == 1) {
-                const int hh = h < p.H ? h : 0;           // padded heads read row 0 (masked later)
+                const int gh = hu * HU + h;
+                const int hh = gh < p.H ? gh : 0;         // padded heads read row 0 (masked later)
                 qp += hh * p.qsh + srcel;
                 dp_ += hh * p.qsh + srcel;
             } else {
@@ -752,17 +768,18 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
             __builtin_amdgcn_global_load_lds((const void*)dp_,
                                              (__attribute__((address_space(3))) void*)((char*)ddst + wbase), 16, 0, 0);
         }
-        if (threadIdx.x < HP) {
-            const int h = threadIdx.x;
+        if (threadIdx.x < HU) {
             // initial values of the S and dP accumulators of head h: the logit
             // offset -lse/scale (so that scale*log2e*S' = log2 P) and -Delta
             // (a query with no candidate has LSE = -inf and multiplicity 0 everywhere:
             // any finite offset keeps its P at 0)
             if constexpr (QS == 1) {
+                const int hl = threadIdx.x, h = hu * HU + hl;
                 const float l = h < p.H ? p.lse[(int64_t)bi * p.lsb + (int64_t)t * p.lst + h] : 0.f;
-                lse_lds[buf * HP + h] = h < p.H ? (l > -INFINITY ? -l / p.scale : 0.f) : -INFINITY;
-                dlt_lds[buf * HP + h] = h < p.H ? -delta[qrow * p.H + h] : 0.f;
+                lse_lds[buf * HP + hl] = h < p.H ? (l > -INFINITY ? -l / p.scale : 0.f) : -INFINITY;
+                dlt_lds[buf * HP + hl] = h < p.H ? -delta[qrow * p.H + h] : 0.f;
             } else {
+                const int h = threadIdx.x;
                 const int tq = t + h / HS, hq = h % HS;
                 const bool hv = hq < p.H && tq < tb;
                 const int64_t hrow = (qrow + (tq - t)) * p.H + hq;
@@ -771,7 +788,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
                 dlt_lds[buf * HP + h] = hv ? -delta[hrow] : 0.f;
             }
         }
-        if (!win && QS == 1) {
+        if (!win && QS == 1 && hu == 0) {
             if (p.idx) {
                 // index entries are only loaded here; count() consumes them later
                 const int32_t* irow = p.idx + qrow * p.kp;
@@ -843,7 +860,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
     }
     const float sl2 = p.scale * LOG2E;
     if (NBUF == 2 && ta < tb) {
-        stage(ta, 0, 0);
+        stage(ta, 0, 0, 0);
         count(ta, 0);
     }
     // waves none of whose rows is a key of this tile only stage and synchronise
@@ -855,20 +872,24 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
     live = __any(live);
     auto query_loop = [&](auto compute_tag) {
     constexpr bool COMPUTE = decltype(compute_tag)::value;
-    for (int t = ta; t < tb; t += QS) {
-        const int it = (t - ta) / QS, buf = NBUF == 2 ? (it & 1) : 0, cb = it % 3;
+    // unit u: heads [HU hu, HU hu + HU) of query t = ta + QS (u / NU), hu = u % NU
+    const int nunits = (tb - ta + QS - 1) / QS * NU;
+    for (int u = 0; u < nunits; ++u) {
+        const int it = u / NU, hu = u % NU;
+        const int t = ta + it * QS;
+        const int buf = NBUF == 2 ? (u & 1) : 0, cb = it % 3;
         if constexpr (NBUF == 2) {
             __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();                               // stage(t) visible; compute(t-1) done
-            if (t + QS < tb) stage(t + QS, buf ^ 1, (it + 1) % 3);
+            __syncthreads();                               // stage(u) visible; compute(u-1) done
+            if (u + 1 < nunits) stage(ta + ((u + 1) / NU) * QS, (u + 1) % NU, buf ^ 1, ((u + 1) / NU) % 3);
         } else {
-            __syncthreads();                               // compute(t-1) done with the buffer
-            stage(t, 0, cb);
-            count(t, cb);
+            __syncthreads();                               // compute(u-1) done with the buffer
+            stage(t, hu, 0, cb);
+            if (hu == 0) count(t, cb);
             __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();                               // stage(t) visible
+            __syncthreads();                               // stage(u) visible
         }
-        if (!win) {                                        // buffer of t+2: last read by compute(t-1)
+        if (!win && hu == 0) {                             // buffer of query it+2: last read by query it-1
             unsigned* nxt = cnt_lds + ((it + 2) % 3) * CTR;
             for (int i = threadIdx.x; i < CTR; i += NT) nxt[i] = 0u;
         }
@@ -916,11 +937,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
         }
         if (__any(anyrow)) {
 #pragma unroll
-        for (int kk = 0; kk < HP / 32; ++kk) {
+        for (int kk = 0; kk < HU / 32; ++kk) {
             // a head pair with no head (h <= 32); not in the bf16 d = 128
             // instantiation, where the branch costs more than it saves at h = 64
             if constexpr (!(sizeof(T) == 2 && D == 128) && QS == 1) {
-                if (32 * kk >= p.H) break;
+                if (32 * (hu * (HU / 32) + kk) >= p.H) break;
             }
             Frag<T> pa[RT], sa[RT];
 #pragma unroll
@@ -1016,7 +1037,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
         }
         }
         if constexpr (NBUF == 2) {
-            if (t + QS < tb) count(t + QS, (it + 1) % 3);   // its index loads had compute(t) to land
+            // the next query's index loads (issued with its first unit's staging) had compute(u) to land
+            if (hu == NU - 1 && t + QS < tb) count(t + QS, (it + 1) % 3);
         }
     }
     };

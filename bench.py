@@ -168,12 +168,14 @@ def cpu_baseline(wl, inp, seed, target_rows):
     t_comp = sec["compress"] + sec["compress_bwd"]
     t_total = t_rows + t_comp * frac
     model, threads = host_cpu()
+    what = ("every query row (a full pass)" if len(rows) == wl.b * wl.sq
+            else f"{len(rows)} query rows stratified over t")
     out = {"value": len(rows) / t_total, "unit": "tokens/s", "cores": threads, "cpu_model": model,
            "kind": "oracle",
-           "sample": (f"{len(rows)} query rows stratified over t (indexer + top-k + attention fwd + bwd, "
-                      f"{t_rows:.1f} s) plus compressor fwd+bwd over all rows ({t_comp:.1f} s) "
-                      f"scaled by {frac:.4f}; fp64; every stage runs OpenMP loops on {threads} threads "
-                      f"(the backward deals rows to 16 fixed chunks, summed in chunk order)")}
+           "sample": (f"{what} (indexer + top-k + attention fwd + bwd, {t_rows:.1f} s) plus compressor "
+                      f"fwd+bwd over all rows ({t_comp:.1f} s) scaled by {frac:.4f}; fp64; every stage runs "
+                      f"OpenMP loops on {threads} threads (the backward deals rows to 16 fixed chunks, summed "
+                      f"in chunk order)")}
     rep = os.path.join(ROOT, "profiles", "cpu_oracle_passes.json")
     if os.path.exists(rep):
         rec = json.load(open(rep))
@@ -443,8 +445,9 @@ def main():
                     help="time the step only (skip the indexer loss, compressor epilogue and DSA-over-GQA lines)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step as one HIP graph replay (reported beside the eager headline)")
-    ap.add_argument("--cpu-rows", type=int, default=1536,
-                    help="query rows of the oracle's CPU sample (about 10-30 s of CPU work)")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="query rows of the oracle's CPU sample (default: every row of the bench workload, a "
+                         "full oracle pass of a few seconds on the GPU host; fewer rows are a stratified sample)")
     ap.add_argument("--cpu-oracle-report", type=int, default=0, metavar="MAX_ROWS",
                     help="time full oracle passes of every workload (sampled and extrapolated above MAX_ROWS "
                          "query rows) on the host CPU, print one JSON object and exit (no GPU used)")

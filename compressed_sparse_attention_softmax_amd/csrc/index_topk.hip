@@ -284,6 +284,17 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
         __syncthreads();
         if (j0 >= nv) continue;
         float my = -INFINITY;
+        // bf16: the tile's 4 x KS key fragments are read before the first MFMA
+        // (one LDS round trip per tile instead of one per fragment)
+        constexpr bool EARLY = sizeof(T) == 2;
+        Frag<T> bfs[EARLY ? 4 : 1][KS];
+        if constexpr (EARLY) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) bfs[st][ks] = load_frag(ktile + (16 * st + n16) * ROW + 32 * ks + 8 * g);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             f32x4 acc[HT];
@@ -291,7 +302,9 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
             for (int ht = 0; ht < HT; ++ht) acc[ht] = f4zero();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                Frag<T> bf = load_frag(ktile + (16 * st + n16) * ROW + 32 * ks + 8 * g);
+                Frag<T> bf;
+                if constexpr (EARLY) bf = bfs[st][ks];
+                else bf = load_frag(ktile + (16 * st + n16) * ROW + 32 * ks + 8 * g);
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma16(qa[ht][ks], bf, acc[ht]);
             }

@@ -329,6 +329,10 @@ ATTN_CASES = [
     ("csa4_bf16_docs_window_only_nosink", CSA4_SMALL.replace(sq=400),
      dict(window_only=True, doc_len=40, with_sink=False)),
     ("d512_bf16", D512_SMALL, {}),
+    # d = 512 stages 32 heads per unit of the key-stationary loop: a second
+    # unit that is partly padding (48 heads) or wholly padding (20 heads)
+    ("d512_bf16_h48", D512_SMALL.replace(sq=200, h=48), {}),
+    ("d512_bf16_h20_b2", D512_SMALL.replace(b=2, sq=150, h=20), {}),
     ("hca128_bf16_dense", HCA_SMALL, dict(idx_mode="dense")),
     # degenerate lengths: one token; shorter than the ratio (no compressed
     # row at all, the zero-size tensors arrive as NULL); one compressed row

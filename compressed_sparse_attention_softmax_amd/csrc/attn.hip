@@ -88,19 +88,19 @@ struct Cand {
     }
     // Row code of a slot: u (window row), j | 0x40000000 (compressed row),
     // or -1 (invalid: padding, out of range, not yet valid, or another
-    // document).  With `use_ids` the index row is read from its copy `ids` in
-    // LDS.  Entries of a given index row get no document test (the indexer
-    // already applied it); window slots and dense-mode slots do.
+    // document).  The index row is read from its copy `ids` in LDS.  Entries
+    // of a given index row get no document test (the indexer already applied
+    // it); window slots and dense-mode slots do.
     __device__ __forceinline__ bool ok_bit(int slot) const
     {
         return !okb || ((((const lds_u32*)okb)[slot >> 5] >> (slot & 31)) & 1u);
     }
-    __device__ __forceinline__ int code(int slot, bool use_ids, const int32_t* ids) const
+    __device__ __forceinline__ int code(int slot, const int32_t* ids) const
     {
         if (slot < nwin) return ok_bit(slot) ? u0 + slot : -1;
         if (slot >= nslots) return -1;
         const int s2 = slot - nwin;
-        const int j = use_ids ? ((const lds_i32*)ids)[s2] : (irow ? irow[s2] : s2);
+        const int j = irow ? ((const lds_i32*)ids)[s2] : s2;
         const bool ok = j >= 0 && j < nv && (irow || ok_bit(slot));
         return ok ? (j | 0x40000000) : -1;
     }
@@ -127,18 +127,35 @@ struct Cand {
 // dQ mode: dP^T = R . dO^T, scale*P^T = exp(S^T scale - lse), dS'^T = scale P^T (dP^T - Delta),
 //   dQ^T[d, h] += R^T dS'^T           same operand shapes
 template <typename T, int D> constexpr int chunk_bytes() { return CHUNK * D * (int)sizeof(T); }
+// 32-row chunks a query's waves gather per round: two for the bf16 d <= 128
+// forward whose heads take two waves (half the rounds, barriers and slot
+// lookups per query; the tile pair still leaves room for four workgroups
+// per CU), one elsewhere (the dq kernel has no registers for the larger
+// gather).  The chunks of a round are processed in order.
+template <typename T, int D, int G, bool DQ> constexpr int round_chunks()
+{
+    return (sizeof(T) == 2 && D <= 128 && G == 2 && !DQ) ? 2 : 1;
+}
+template <typename T, int D, int G, bool DQ> constexpr int round_bytes()
+{
+    return round_chunks<T, D, G, DQ>() * chunk_bytes<T, D>();
+}
 
 template <typename T, int D, int HT, int G, bool DQ, int KSP>
 __global__ __launch_bounds__(256, (D <= 128 && HT <= 2) ? 2 : 1)
 void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict__ csink, int idx_lds, int okw)
 {
     constexpr int KS = D / 32, DT = D / 16, QPW = (G == 2 && D <= 128) ? 1 : 4 / G;
-    constexpr int CHB = chunk_bytes<T, D>();
+    constexpr int NSUB = round_chunks<T, D, G, DQ>();   // chunks per round
+    constexpr int RR = NSUB * CHUNK;              // rows per round
+    constexpr int CHB = round_bytes<T, D, G, DQ>();     // one round's tile
     constexpr int PPR = D * (int)sizeof(T) / 16;  // 16-byte pieces per row
     constexpr int E16 = 16 / (int)sizeof(T);      // elements per piece
     constexpr int NPL = CHB / (16 * WAVE * G);    // pieces each lane of the query's waves carries
-    static_assert(NPL * 16 * WAVE * G == CHB, "chunk pieces split evenly over the query's waves");
-    constexpr int LPR = WAVE * G / CHUNK;         // lanes sharing one row of a chunk
+    static_assert(NPL * 16 * WAVE * G == CHB, "round pieces split evenly over the query's waves");
+    static_assert(RR <= WAVE, "one lane resolves each slot of a round");
+    typedef std::conditional_t<(RR > 32), uint64_t, uint32_t> mask_t;   // bit i: slot i of a round
+    constexpr int LPR = WAVE * G / RR;            // lanes sharing one row of a round
     static_assert(LPR * NPL == PPR, "a row's pieces split evenly over its lanes");
     typedef uint32_t piece_t __attribute__((ext_vector_type(4)));
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -165,7 +182,7 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
     // not wait on memory).  Its loads are issued first, into registers, so
     // that they overlap the loads of Q (dO, O) below.
     int32_t* ids = reinterpret_cast<int32_t*>(smem + (size_t)QPW * 2 * CHB) + (size_t)qs * p.kp;
-    const bool use_ids = idx_lds && cand.irow;
+    const bool use_ids = cand.irow != nullptr;    // the host guarantees the LDS copy (idx_lds)
     constexpr int IPL = 2048 / (WAVE * G);        // index entries per lane, K' <= 2048
     const int qlane = sub * WAVE + lane;
     int iv[IPL];
@@ -263,25 +280,26 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
     // spans two rounds) where the registers allow it (the bf16 forward at
     // d <= 128 with heads split over waves, both bf16 kernels at d = 512 with
     // four waves per query); one elsewhere
-    constexpr int GDEPTH = ((!DQ && sizeof(T) == 2 && D <= 128 && !(G == 1 && HT == 2)) ||
-                             (sizeof(T) == 2 && D == 512 && G == 4)) ? 2 : 1;
+    constexpr int GDEPTH = NSUB == 1 && ((!DQ && sizeof(T) == 2 && D <= 128 && !(G == 1 && HT == 2)) ||
+                                         (sizeof(T) == 2 && D == 512 && G == 4)) ? 2 : 1;
     f32x4 o[DT][HT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) o[dt][ht] = OACC ? agpr_zero() : f4zero();
 
-    // Gather chunk c0's rows into registers; returns the chunk's candidate
-    // mask.  Lane q = 64 sub + lane of the query's waves owns row q / LPR of the
-    // chunk and its pieces (q % LPR) + LPR k, k < NPL: it resolves that row's
-    // address itself, and its loads differ by immediate offsets only.
+    // Gather the rows of the round starting at slot c0 into registers; returns
+    // the round's candidate mask (bit i: slot c0 + i).  Lane q = 64 sub + lane
+    // of the query's waves owns row q / LPR of the round and its pieces
+    // (q % LPR) + LPR k, k < NPL: it resolves that row's address itself, and
+    // its loads differ by immediate offsets only.
     const int my_r = (sub * WAVE + lane) / LPR, my_j = (sub * WAVE + lane) % LPR;
     piece_t rg[GDEPTH][NPL];
-    auto fetch = [&](int c0, piece_t (&r)[NPL]) -> uint32_t {
-        // lane l (and l + 32) resolves slot c0 + l % 32; the lanes that load
-        // row my_r take its code from lane my_r
-        const int cl = cand.code(c0 + (lane & 31), use_ids, ids);
-        const uint32_t mask = (uint32_t)__ballot(cl >= 0);
+    auto fetch = [&](int c0, piece_t (&r)[NPL]) -> mask_t {
+        // lane l resolves slot c0 + l % RR; the lanes that load row my_r take
+        // its code from lane my_r
+        const int cl = cand.code(c0 + (lane & (RR - 1)), ids);
+        const mask_t mask = (mask_t)__ballot(cl >= 0);
         const T* rp = cand.row_ptr(__shfl(cl, my_r)) + my_j * E16;
 #pragma unroll
         for (int k = 0; k < NPL; ++k) r[k] = *reinterpret_cast<const piece_t*>(rp + k * LPR * E16);
@@ -451,11 +469,6 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
                 if (iv[k] >= 0 && iv[k] < cand.nv) lastc = max(lastc, s0);
             }
         }
-    } else if (cand.irow) {                       // index row left in global memory
-        for (int s0 = qlane; s0 < p.kp; s0 += WAVE * G) {
-            const int j = cand.irow[s0];
-            if (j >= 0 && j < cand.nv) lastc = max(lastc, s0);
-        }
     } else {
         lastc = cand.nslots - cand.nwin - 1;      // dense mode: every valid block; window only: none
     }
@@ -466,8 +479,10 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
     if constexpr (G > 1) {
         // one barrier: the index row is in LDS, and every wave sees every
         // query's last slot; all waves of the workgroup run the same number of
-        // barrier rounds, for the longest candidate list among its queries
-        __shared__ int last_s[4];
+        // barrier rounds, for the longest candidate list among its queries.
+        // The slots borrow the second tile of query slot 0, first written
+        // after the barrier that ends the prologue below.
+        int* last_s = reinterpret_cast<int*>(smem + CHB);
         if (lane == 0) last_s[wave] = last;
         __syncthreads();
         nloop = 0;
@@ -477,34 +492,45 @@ void attn_query_kernel(AttnArgs p, float* __restrict__ delta, float* __restrict_
 #pragma unroll
             for (int w = 0; w < G; ++w) lq = max(lq, last_s[q * G + w]);
             if (q == qs) last = lq;
-            nloop = max(nloop, (lq + CHUNK) / CHUNK);
+            nloop = max(nloop, (lq + RR) / RR);
         }
     }
-    const int nch = (last + CHUNK) / CHUNK;
+    const int nch = (last + RR) / RR;             // rounds
     if constexpr (G == 1) nloop = nch;
     // every load so far (Q, dO, O, the index row) has landed: the loop below
     // then waits only on its own row gathers
     __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)
-    // Round k computes chunk k from one LDS tile, writes chunk k+1 into the
-    // other and gathers chunk k + 1 + GDEPTH into registers.  G > 1: chunk
-    // k+1 fully written, chunk k read by every wave, before the next round
-    // reads k+1 and refills k's tile.  G == 1: a wave's LDS accesses run in
-    // order, so its own reads of a tile finish before its later writes to it.
-    uint32_t mk[3] = {0u, 0u, 0u};                // masks of chunks k, k+1, k+2
+    // Round k computes the rows of round k from one LDS tile, writes those of
+    // round k+1 into the other and gathers round k + 1 + GDEPTH into
+    // registers.  G > 1: round k+1 fully written, round k read by every wave,
+    // before the next round reads k+1 and refills k's tile.  G == 1: a wave's
+    // LDS accesses run in order, so its own reads of a tile finish before its
+    // later writes to it.
+    mask_t mk[3] = {0u, 0u, 0u};                  // masks of rounds k, k+1, k+2
     if (nch > 0) { mk[0] = fetch(0, rg[0]); stash(0, rg[0]); }
 #pragma unroll
     for (int j = 1; j <= GDEPTH; ++j)
-        if (nch > j) mk[j] = fetch(CHUNK * j, rg[j % GDEPTH]);
+        if (nch > j) mk[j] = fetch(RR * j, rg[j % GDEPTH]);
     if constexpr (G > 1) __syncthreads();
-    // r: the registers holding chunk k+1, which then receive chunk k + 1 + GDEPTH
+    // r: the registers holding round k+1, which then receive round k + 1 + GDEPTH
     auto round = [&](int k, piece_t (&r)[NPL]) {
-        if (G == 1 || k < nch) process(reinterpret_cast<const T*>(tiles + (size_t)(k & 1) * CHB), mk[0]);
+        if constexpr (NSUB == 1) {
+            if (G == 1 || k < nch) process(reinterpret_cast<const T*>(tiles + (size_t)(k & 1) * CHB), mk[0]);
+        } else if (k < nch) {
+            const T* tile = reinterpret_cast<const T*>(tiles + (size_t)(k & 1) * CHB);
+#pragma unroll
+            for (int h = 0; h < NSUB; ++h) {
+                // a chunk with no candidate (past the last one) adds nothing
+                const uint32_t mh = (uint32_t)(mk[0] >> (CHUNK * h));
+                if (mh != 0u) process(tile + h * CHUNK * D, mh);
+            }
+        }
         if (k + 1 < nch) {
             stash((k + 1) & 1, r);
             mk[0] = mk[1];
             mk[1] = mk[2];
         }
-        if (k + 1 + GDEPTH < nch) mk[GDEPTH] = fetch(CHUNK * (k + 1 + GDEPTH), r);
+        if (k + 1 + GDEPTH < nch) mk[GDEPTH] = fetch(RR * (k + 1 + GDEPTH), r);
         if constexpr (G > 1) __syncthreads();
     };
     if constexpr (GDEPTH == 1) {
@@ -1327,11 +1353,16 @@ hipError_t launch_query_k(const AttnArgs& p, bool dq, float* delta, float* csink
     // 128): each chunk barrier then couples only the waves that share the
     // tile, and no workgroup runs extra rounds for a longer neighbour
     const int qpw = (G == 2 && D <= 128) ? 1 : 4 / G;
-    // two chunk tiles per query of the workgroup, then (when they fit) the index rows
-    size_t lds = (size_t)qpw * 2 * chunk_bytes<T, D>();
+    // two round tiles per query of the workgroup, then (when they fit) the index rows
+    const int rbytes = (G == 2 && !dq) ? round_bytes<T, D, 2, false>() : chunk_bytes<T, D>();
+    static_assert(round_chunks<T, D, 1, false>() == 1 && round_chunks<T, D, 4, false>() == 1 &&
+                  round_chunks<T, D, 2, true>() == 1, "two-chunk rounds: the forward with G == 2 only");
+    size_t lds = (size_t)qpw * 2 * rbytes;
     if (lds > (size_t)ATTN_LDS_LIMIT) return hipErrorInvalidValue;
     const size_t with_ids = lds + (size_t)qpw * p.kp * sizeof(int32_t);
     const int idx_lds = (p.idx && p.kp > 0 && with_ids <= (size_t)ATTN_LDS_LIMIT) ? 1 : 0;
+    // the kernels read index rows from their LDS copy only (it always fits: K' <= 2048)
+    if (p.c && p.idx && p.kp > 0 && !idx_lds) return hipErrorInvalidValue;
     if (idx_lds) lds = with_ids;
     // document bits: window slots, plus every block in dense mode
     int okw = 0;

@@ -611,6 +611,8 @@ template <typename T, int D> constexpr size_t rows_lds_tile()
 {
     return (size_t)rows_waves_t<T, D>() * rows_per_wave_t<T, D>() * (D + 16 / sizeof(T)) * sizeof(T);
 }
+// LDS bytes of the next query's index row (one query per unit only; K' <= 2048)
+template <int QS> constexpr size_t rows_lds_index() { return QS == 1 ? 2048 * sizeof(int32_t) : 0; }
 // bf16 rows at d <= 128 stay in registers (64 VGPRs next to the AGPR
 // accumulators): the tile would be re-read from LDS for every head tile.
 template <typename T, int D> constexpr bool rows_tile_in_lds()
@@ -746,8 +748,12 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
     // chosen so that the LDS block holds rows of 8-element units permuted as
     // unit u of row h at u ^ unit_swz(h).  Also lse, Delta (plain loads) and the
     // multiplicities of the tile's rows for query t in cnt buffer `cb`.
+    // The next query's index row goes to LDS (after the other areas) with
+    // asynchronous loads: entry s lands where thread s % NT reads it back in
+    // count(), and no register waits on it while the unit computes.
     constexpr int IDX_REGS = 2048 / NT;           // K' <= 2048
-    int jreg[IDX_REGS];
+    [[maybe_unused]] int32_t* const idx_buf = reinterpret_cast<int32_t*>(
+        smem + rows_lds_base<T, D, QS>() + (rows_tile_in_lds<T, D>() ? rows_lds_tile<T, D>() : 0));
     // stacked queries with a selection bitmap: stage() loads the bitmap words
     // of the stack's (query, tile row) entries and the queries' repeat flags,
     // and the following count() turns them into multiplicities
@@ -757,6 +763,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
     [[maybe_unused]] uint32_t srep = 0u;
     // hu: which HU heads of query t (unit hu of the query); the index row and
     // dense multiplicities are loaded with the query's first unit only
+    float st_l = 0.f, st_d = 0.f;                 // LSE and Delta of the staged unit's head slot
+    bool st_hv = false;
     auto stage = [&](int t, int hu, int buf, int cb) {
         const int64_t qrow = (int64_t)bi * p.S + t;
         const int64_t qoff = (int64_t)bi * p.qsb + (int64_t)t * p.qst;
@@ -795,23 +803,21 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
                                              (__attribute__((address_space(3))) void*)((char*)ddst + wbase), 16, 0, 0);
         }
         if (threadIdx.x < HU) {
-            // initial values of the S and dP accumulators of head h: the logit
-            // offset -lse/scale (so that scale*log2e*S' = log2 P) and -Delta
-            // (a query with no candidate has LSE = -inf and multiplicity 0 everywhere:
-            // any finite offset keeps its P at 0)
+            // the LSE and Delta of head slot threadIdx.x, into registers only:
+            // stage_params() writes them to LDS once they have landed (a wait
+            // here would also wait for the staging loads just issued)
             if constexpr (QS == 1) {
-                const int hl = threadIdx.x, h = hu * HU + hl;
-                const float l = h < p.H ? p.lse[(int64_t)bi * p.lsb + (int64_t)t * p.lst + h] : 0.f;
-                lse_lds[buf * HP + hl] = h < p.H ? (l > -INFINITY ? -l / p.scale : 0.f) : -INFINITY;
-                dlt_lds[buf * HP + hl] = h < p.H ? -delta[qrow * p.H + h] : 0.f;
+                const int h = hu * HU + (int)threadIdx.x;
+                st_hv = h < p.H;
+                st_l = st_hv ? p.lse[(int64_t)bi * p.lsb + (int64_t)t * p.lst + h] : 0.f;
+                st_d = st_hv ? delta[qrow * p.H + h] : 0.f;
             } else {
                 const int h = threadIdx.x;
                 const int tq = t + h / HS, hq = h % HS;
-                const bool hv = hq < p.H && tq < tb;
+                st_hv = hq < p.H && tq < tb;
                 const int64_t hrow = (qrow + (tq - t)) * p.H + hq;
-                const float l = hv ? p.lse[(int64_t)bi * p.lsb + (int64_t)tq * p.lst + hq] : 0.f;
-                lse_lds[buf * HP + h] = hv ? (l > -INFINITY ? -l / p.scale : 0.f) : -INFINITY;
-                dlt_lds[buf * HP + h] = hv ? -delta[hrow] : 0.f;
+                st_l = st_hv ? p.lse[(int64_t)bi * p.lsb + (int64_t)tq * p.lst + hq] : 0.f;
+                st_d = st_hv ? delta[hrow] : 0.f;
             }
         }
         if (!win && QS == 1 && hu == 0) {
@@ -821,16 +827,28 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
 #pragma unroll
                 for (int k = 0; k < IDX_REGS; ++k) {
                     const int s = threadIdx.x + NT * k;
-                    jreg[k] = s < p.kp ? irow[s] : -1;
+                    if (s < p.kp)
+                        __builtin_amdgcn_global_load_lds((const void*)(irow + s),
+                                                         (__attribute__((address_space(3))) void*)(idx_buf + NT * k +
+                                                                                                   WAVE * wave),
+                                                         4, 0, 0);
                 }
             } else {
                 unsigned* cnt = cnt_lds + cb * CTR;
                 const int nv = min((t + 1) / p.r, p.nc);
                 // dense mode: every valid block once (with documents: blocks of t's document)
-                const int32_t* dcol = p.doc ? p.doc + (int64_t)bi * p.S : nullptr;
-                const int dt = dcol ? dcol[t] : 0;
-                for (int j = tile_lo + threadIdx.x; j < min(tile_hi, nv); j += NT)
-                    if (!dcol || dcol[j * p.r] == dt) cnt[j - tile_lo] = 1u;
+                if (p.doc) {
+                    const int32_t* dcol = p.doc + (int64_t)bi * p.S;
+                    const int dt = dcol[t];
+                    for (int j = tile_lo + threadIdx.x; j < min(tile_hi, nv); j += NT)
+                        if (dcol[j * p.r] == dt) cnt[j - tile_lo] = 1u;
+                    // settle these loads on their own path: a later wait for
+                    // their registers would be a wait for every load, the
+                    // staging included, on every path
+                    __builtin_amdgcn_s_waitcnt(0x0F70);
+                } else {
+                    for (int j = tile_lo + threadIdx.x; j < min(tile_hi, nv); j += NT) cnt[j - tile_lo] = 1u;
+                }
             }
         }
         if constexpr (QS > 1) {
@@ -843,6 +861,17 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
                 }
                 srep = (lane < QS && t + lane < tb) ? mrow[(int64_t)(t + lane) * p.selw + p.selw - 1] : 0u;
             }
+        }
+    };
+    // initial values of the S and dP accumulators of each head slot of the
+    // staged unit, into LDS buffer buf: the logit offset -lse/scale (so that
+    // scale*log2e*S' = log2 P) and -Delta (a query with no candidate has
+    // LSE = -inf and multiplicity 0 everywhere: any finite offset keeps its P
+    // at 0)
+    auto stage_params = [&](int buf) {
+        if (threadIdx.x < HU) {
+            lse_lds[buf * HP + threadIdx.x] = st_hv ? (st_l > -INFINITY ? -st_l / p.scale : 0.f) : -INFINITY;
+            dlt_lds[buf * HP + threadIdx.x] = st_hv ? -st_d : 0.f;
         }
     };
     // multiplicities of the tile's rows for query t from the staged index entries
@@ -873,9 +902,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
             return;
         }
         const int nv = min((t + 1) / p.r, p.nc);
+        __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this thread's index entries have landed
 #pragma unroll
         for (int k = 0; k < IDX_REGS; ++k) {
-            const int j = jreg[k];
+            const int s = threadIdx.x + NT * k;
+            const int j = s < p.kp ? idx_buf[s] : -1;
             if (j >= 0 && j < nv && j >= tile_lo && j < tile_hi) atomicAdd(&cnt[j - tile_lo], 1u);
         }
     };
@@ -887,6 +918,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
     const float sl2 = p.scale * LOG2E;
     if (NBUF == 2 && ta < tb) {
         stage(ta, 0, 0, 0);
+        stage_params(0);
         count(ta, 0);
     }
     // waves none of whose rows is a key of this tile only stage and synchronise
@@ -913,6 +945,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
             stage(t, hu, 0, cb);
             if (hu == 0) count(t, cb);
             __builtin_amdgcn_s_waitcnt(0);
+            stage_params(0);
             __syncthreads();                               // stage(u) visible
         }
         if (!win && hu == 0) {                             // buffer of query it+2: last read by query it-1
@@ -924,7 +957,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
         const float* ls_b = lse_lds + buf * HP;
         const float* dl_b = dlt_lds + buf * HP;
         if constexpr (COMPUTE) {
-        [[maybe_unused]] const int dtq = (p.doc && win) ? p.doc[(int64_t)bi * p.S + t] : 0;
+        [[maybe_unused]] int dtq = 0;
+        if (p.doc && win) {
+            dtq = p.doc[(int64_t)bi * p.S + t];
+            __builtin_amdgcn_s_waitcnt(0x0F70);    // settled on its own path, as in stage()
+        }
         // every (head, row) pair of a wave with a candidate of t is computed;
         // its rows that are not candidates get multiplicity 0.  The
         // multiplicity enters the exponent: m P = 2^(scale log2e S' + log2 m).
@@ -1063,7 +1100,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
         }
         }
         if constexpr (NBUF == 2) {
-            // the next query's index loads (issued with its first unit's staging) had compute(u) to land
+            // the next unit's LSE / Delta and the next query's index loads
+            // (issued with the staging) had compute(u) to land
+            if (u + 1 < nunits) stage_params(buf ^ 1);
             if (hu == NU - 1 && t + QS < tb) count(t + QS, (it + 1) % 3);
         }
     }
@@ -1442,7 +1481,8 @@ template <typename T, int D, int QS, int KSP>
 hipError_t launch_rows_qk(const AttnArgs& p, const RowsGeom& geo, float* ws, hipStream_t st)
 {
     constexpr int RW = rows_per_wave_t<T, D>(), NW = rows_waves_t<T, D>();
-    const size_t lds = rows_lds_base<T, D, QS>() + (rows_tile_in_lds<T, D>() ? rows_lds_tile<T, D>() : 0);
+    const size_t lds = rows_lds_base<T, D, QS>() + (rows_tile_in_lds<T, D>() ? rows_lds_tile<T, D>() : 0) +
+                       rows_lds_index<QS>();
     if (lds > (size_t)ATTN_LDS_LIMIT) return hipErrorInvalidValue;
     auto kern = attn_rows_kernel<T, D, RW, NW, QS, KSP>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

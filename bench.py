@@ -7,9 +7,11 @@ input already resident in HBM:
     csa_compress -> csa_index_topk -> csa_sparse_attn_fwd
                  -> csa_sparse_attn_bwd -> csa_compress_bwd
 
-all on the current HIP stream.  W untimed warm-up steps, then exactly K timed
-steps bracketed by device synchronisation.  Per-stage durations come from HIP
-events recorded on that same stream inside the timed region.
+all on the current HIP stream.  W untimed warm-up steps (continued until the
+GPU has been busy SETTLE_S seconds, so that its clocks have settled), then
+exactly K timed steps bracketed by device synchronisation, one HIP event pair
+per step.  A second pass of K steps records per-stage events and times the
+dominant kernel around each launch.
 
 Prints one JSON line (metric, tokens/s, roofline of the dominant kernel, the
 oracle's CPU baseline on a bounded sample).  ``--gpus N`` with N > 1 exits:
@@ -31,6 +33,11 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0
 STAGES = ["compress", "index_topk", "attn_fwd", "attn_bwd", "compress_bwd"]
+# Continuous GPU work before the timed steps: the GPU raises its clocks over
+# some tens of milliseconds of load (after an idle moment a step of the bench
+# workload starts about 15 % slower and settles after about 50 steps), so the
+# warm-up runs until the GPU has been busy this long.
+SETTLE_S = 0.25
 
 
 def log(*a):
@@ -508,11 +515,25 @@ def main():
             if c is not None:
                 c()
 
-    for _ in range(args.warmup):
-        one_step()
+    # the work counts read the step's selection on the host (the GPU idles):
+    # they come before the warm-up
+    one_step()
     torch.cuda.synchronize()
     work = count_work(wl, buf.idx)
     kwork = kernel_work(wl, work)
+
+    # warm-up: W steps, then more until the GPU has been busy SETTLE_S seconds
+    t_w = time.perf_counter()
+    for _ in range(args.warmup):
+        one_step()
+    settle = 0
+    while True:
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_w >= SETTLE_S:
+            break
+        for _ in range(8):
+            one_step()
+        settle += 8
 
     # per-kernel durations (HIP events around each launch, two steps per
     # kernel, outside the timed region): picks the dominant kernel
@@ -611,8 +632,11 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle_steps": settle,
         "ms_per_step": ms_step,
-        "ms_per_step_timing": "median of per-step HIP event pairs on the stream over the K timed steps (eager launches)",
+        "ms_per_step_timing": "median of per-step HIP event pairs on the stream over the K timed steps (eager "
+                              "launches), after the W warm-up steps and settle_steps more (the GPU busy "
+                              f"{SETTLE_S} s before the timed steps)",
         "ms_per_step_wall_mean": elapsed * 1e3 / K,
         "ms_per_step_min_max": [step_ms[0], step_ms[-1]],
         "ms_per_step_graph_median": graph_ms,

@@ -1028,6 +1028,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
                     f32x4 sv = s0, dp = d0;
+                    if constexpr (sizeof(T) == 2 && D == 128 && !ROWS_LDS && KSP == 0) {
+                        mfma16_sd4_arows(sv, dp, qa, da, rb[rt]);
+                    } else {
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
                         Frag<T> bk;
@@ -1035,6 +1038,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
                         else bk = rb[rt][ks];
                         if (KSP == 0 || ks < KSP) sv = mfma16(qa[ks], bk, sv);
                         if (KSP == 0 || ks >= KSP) dp = mfma16(da[ks], bk, dp);
+                    }
                     }
                     // sv = S - lse/scale, dp = dP - Delta:  m P = 2^(sv sl2 + lm),
                     // scaled dS = scale (m P) (dP - Delta)
@@ -1057,15 +1061,26 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_rows_kernel(AttnArgs p, RowsG
             // group of four d tiles lies in one half).
             if constexpr (sizeof(T) == 2 && RT == 2) {
                 static_assert(KSP == 0 && DT % 2 == 0, "two-row-tile blocks");
-#pragma unroll
-                for (int dt = 0; dt < DT; dt += 2) {
-                    Frag<T> dob[2], qbf[2];
+                // the operands of the next two d-tile pairs are in flight while
+                // a pair feeds the matrix cores (scheduling fences keep the
+                // reads ahead of the products)
+                Frag<T> dob[3][2], qbf[3][2];
+                auto ld = [&](int dt, int b) {
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        dob[j] = rows_operand<T>(do_lds, D, 32 * kk, 16 * (dt + j), true);
-                        qbf[j] = rows_operand<T>(q_lds, D, 32 * kk, 16 * (dt + j), true);
+                        dob[b][j] = rows_operand<T>(do_lds, D, 32 * kk, 16 * (dt + j), true);
+                        qbf[b][j] = rows_operand<T>(q_lds, D, 32 * kk, 16 * (dt + j), true);
                     }
-                    mfma16_2x2_acc(acc[0][dt], acc[0][dt + 1], acc[1][dt], acc[1][dt + 1], pa, sa, dob, qbf);
+                };
+                ld(0, 0);
+                ld(2, 1);
+#pragma unroll
+                for (int dt = 0; dt < DT; dt += 2) {
+                    const int b = (dt / 2) % 3;
+                    if (dt + 4 < DT) ld(dt + 4, (dt / 2 + 2) % 3);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfma16_2x2_acc(acc[0][dt], acc[0][dt + 1], acc[1][dt], acc[1][dt + 1], pa, sa, dob[b], qbf[b]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             } else if constexpr (sizeof(T) == 2 && RT == 1) {
                 static_assert(DT % 4 == 0 && (KSP == 0 || (2 * KSP) % 4 == 0), "one-row-tile blocks");

@@ -144,6 +144,27 @@ __device__ __forceinline__ void mfma16_4_acc(f32x4* c, const Frag<bf16_t>* a, co
         : "v"(a[0].v), "v"(a[1].v), "v"(a[2].v), "v"(a[3].v), "v"(b[0].v), "v"(b[1].v), "v"(b[2].v), "v"(b[3].v));
 }
 
+// The two logit products of one row tile against four k steps, S += qa * r
+// and dP += da * r, accumulating in VGPRs, with the row fragments r read
+// from the AGPR file (an MFMA source may be either file): rows that stay
+// resident for a whole kernel then hold no VGPRs.
+__device__ __forceinline__ void mfma16_sd4_arows(f32x4& s, f32x4& d, const Frag<bf16_t>* qa, const Frag<bf16_t>* da,
+                                                 const Frag<bf16_t>* r)
+{
+    asm("s_nop 1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %0, %2, %10, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %6, %10, %1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %0, %3, %11, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %7, %11, %1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %0, %4, %12, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %8, %12, %1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %0, %5, %13, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %9, %13, %1" CSA_MFMA_TAIL
+        : "+v"(s), "+v"(d)
+        : "v"(qa[0].v), "v"(qa[1].v), "v"(qa[2].v), "v"(qa[3].v), "v"(da[0].v), "v"(da[1].v), "v"(da[2].v),
+          "v"(da[3].v), "a"(r[0].v), "a"(r[1].v), "a"(r[2].v), "a"(r[3].v));
+}
+
 // Zero accumulator created in the AGPR file (an MFMA of zero operands), so
 // that a loop-carried accumulator is an AGPR value from its first definition.
 // The trailing 32 wait states let the compiler copy the result right away.

@@ -11,7 +11,9 @@ from ._abi import (CSA_BF16, CSA_F32, CSA_K_ATTN_DQ, CSA_K_ATTN_FWD, CSA_K_ATTN_
                    csa_compress_bwd, csa_compress_bwd_workspace, csa_dims,
                    csa_dsa_gqa_bwd, csa_dsa_gqa_fwd, csa_dsa_gqa_workspace, csa_gqa_dims, csa_index_topk, csa_index_topk_workspace, csa_indexer_loss,
                    csa_indexer_loss_dense, csa_indexer_loss_dense_workspace, csa_indexer_loss_workspace, csa_kernel_name,
-                   csa_last_error, csa_sparse_attn_bwd, csa_sparse_attn_bwd_noalloc, csa_sparse_attn_fwd_strided, csa_sparse_attn_bwd_strided, csa_attn_strides, attn_strides_of, csa_sparse_attn_bwd_query_block, csa_sparse_attn_bwd_workspace,
+                   csa_last_error, csa_sparse_attn_bwd, csa_sparse_attn_bwd_noalloc, csa_sparse_attn_fwd_strided, csa_sparse_attn_bwd_strided, csa_attn_strides, attn_strides_of,
+                   csa_compress_strided, csa_compress_bwd_strided, csa_compress_strides, compress_strides_of,
+                   csa_index_topk_strided, csa_index_strides, index_strides_of, csa_sparse_attn_bwd_query_block, csa_sparse_attn_bwd_workspace,
                    csa_sparse_attn_fwd,
                    csa_timing_enable, csa_timing_read, csa_version, dims_of, kprime, load, make_dims,
                    n_compressed, LIB_PATH)
@@ -22,7 +24,9 @@ __all__ = ["CSA_BF16", "CSA_F32", "CSA_K_ATTN_DQ", "CSA_K_ATTN_FWD", "CSA_K_ATTN
            "csa_compress_bwd", "csa_compress_bwd_workspace", "csa_dims",
            "csa_dsa_gqa_bwd", "csa_dsa_gqa_fwd", "csa_dsa_gqa_workspace", "csa_gqa_dims", "csa_index_topk", "csa_index_topk_workspace", "csa_indexer_loss",
            "csa_indexer_loss_dense", "csa_indexer_loss_dense_workspace", "csa_indexer_loss_workspace", "csa_kernel_name",
-           "csa_last_error", "csa_sparse_attn_bwd", "csa_sparse_attn_bwd_noalloc", "csa_sparse_attn_fwd_strided", "csa_sparse_attn_bwd_strided", "csa_attn_strides", "attn_strides_of", "csa_sparse_attn_bwd_query_block", "csa_sparse_attn_bwd_workspace",
+           "csa_last_error", "csa_sparse_attn_bwd", "csa_sparse_attn_bwd_noalloc", "csa_sparse_attn_fwd_strided", "csa_sparse_attn_bwd_strided", "csa_attn_strides", "attn_strides_of",
+           "csa_compress_strided", "csa_compress_bwd_strided", "csa_compress_strides", "compress_strides_of",
+           "csa_index_topk_strided", "csa_index_strides", "index_strides_of", "csa_sparse_attn_bwd_query_block", "csa_sparse_attn_bwd_workspace",
            "csa_sparse_attn_fwd",
            "csa_timing_enable", "csa_timing_read", "csa_version", "dims_of", "kprime", "load", "make_dims",
            "n_compressed", "LIB_PATH"]

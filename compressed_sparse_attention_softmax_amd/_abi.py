@@ -23,6 +23,7 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_ARG", -2: "CSA_ERR_SHAPE", -3: "CSA_ERR_DTYP
 
 # every symbol include/csa.h declares
 EXPORTS = ["csa_compress", "csa_compress_bwd_workspace", "csa_compress_bwd", "csa_index_topk_workspace", "csa_index_topk",
+           "csa_compress_strided", "csa_compress_bwd_strided", "csa_index_topk_strided",
            "csa_sparse_attn_fwd", "csa_sparse_attn_bwd_workspace", "csa_sparse_attn_bwd_query_block",
            "csa_sparse_attn_bwd", "csa_sparse_attn_bwd_noalloc", "csa_sparse_attn_fwd_strided",
            "csa_sparse_attn_bwd_strided", "csa_indexer_loss_workspace", "csa_indexer_loss", "csa_indexer_loss_dense_workspace",
@@ -49,6 +50,14 @@ class csa_dims(ctypes.Structure):
 
 class csa_attn_strides(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("q_b", "q_s", "q_h", "kv_b", "kv_s", "lse_b", "lse_s")]
+
+
+class csa_compress_strides(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("x_b", "x_s", "z_b", "z_s")]
+
+
+class csa_index_strides(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("qi_b", "qi_s", "qi_h", "ki_b", "ki_s", "w_b", "w_s")]
 
 
 class csa_gqa_dims(ctypes.Structure):
@@ -89,6 +98,11 @@ def load(path: Optional[str] = None):
     lib.csa_sparse_attn_fwd_strided.argtypes = [D, ST, i, vp, vp, vp, vp, vp, vp, f, vp, vp, vp]
     lib.csa_sparse_attn_bwd_strided.argtypes = [D, ST, i, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp,
                                                 sz, vp]
+    CST = ctypes.POINTER(csa_compress_strides)
+    lib.csa_compress_strided.argtypes = [D, CST, i, vp, vp, i, vp, f, i, f, vp, vp, vp]
+    lib.csa_compress_bwd_strided.argtypes = [D, CST, i, vp, vp, i, vp, f, i, f, vp, vp, vp, vp, vp, sz, vp]
+    lib.csa_index_topk_strided.argtypes = [D, ctypes.POINTER(csa_index_strides), i, vp, vp, vp, vp, vp, vp, vp, sz,
+                                           vp]
     lib.csa_indexer_loss_workspace.argtypes = [D]
     lib.csa_indexer_loss_workspace.restype = sz
     lib.csa_indexer_loss.argtypes = [D, i, vp, vp, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -107,7 +121,8 @@ def load(path: Optional[str] = None):
     lib.csa_timing_read.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
     lib.csa_kernel_name.argtypes = [i]
     lib.csa_kernel_name.restype = ctypes.c_char_p
-    for fn in ("csa_compress", "csa_compress_bwd", "csa_index_topk", "csa_sparse_attn_fwd",
+    for fn in ("csa_compress", "csa_compress_bwd", "csa_index_topk", "csa_compress_strided", "csa_compress_bwd_strided",
+               "csa_index_topk_strided", "csa_sparse_attn_fwd",
                "csa_sparse_attn_bwd", "csa_sparse_attn_bwd_noalloc", "csa_sparse_attn_fwd_strided",
                "csa_sparse_attn_bwd_strided", "csa_indexer_loss", "csa_indexer_loss_dense", "csa_dsa_gqa_fwd", "csa_dsa_gqa_bwd", "csa_version", "csa_timing_enable", "csa_timing_read"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -219,6 +234,69 @@ def csa_index_topk(dims: csa_dims, q_i, k_i, w, idx, score=None, ws=None, stream
           _ptr(q_i, shape=(b, S, dims.idx_heads, dims.idx_dim), dtype=dt, name="q_i"),
           _ptr(k_i, shape=(b, nc, dims.idx_dim), dtype=dt, name="k_i"),
           _ptr(w, shape=(b, S, dims.idx_heads), dtype=f32, name="w"), _doc_ptr(dims, doc_ids),
+          _ptr(idx, shape=(b, S, kp), dtype=torch.int32, name="idx"),
+          _ptr(score, shape=(b, S, kp), dtype=f32, name="score"),
+          _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def compress_strides_of(x, z) -> csa_compress_strides:
+    """csa_compress_strides of views x [b, sq, d] and z [b, sq, z_channels]."""
+    return csa_compress_strides(x.stride(0), x.stride(1), z.stride(0), z.stride(1))
+
+
+def csa_compress_strided(dims: csa_dims, x, z, c, c32=None, stream=None, norm_w=None, norm_eps: float = 1e-6,
+                         rope_dim: int = 0, rope_base: float = 40000.0) -> None:
+    """csa_compress over views x [b, sq, d] and z [b, sq, z_channels] whose
+    last axis is contiguous (c and c32 contiguous)."""
+    dt = x.dtype
+    b, S, D = dims.b, dims.sq, dims.d
+    zc = z.shape[-1]
+    nc = n_compressed(dims)
+    st = compress_strides_of(x, z)
+    _call("csa_compress_strided", ctypes.byref(dims), ctypes.byref(st), _dtype_code(x),
+          _strided_ptr(x, (b, S, D), dt, "x"), _strided_ptr(z, (b, S, zc), dt, "z"), zc,
+          _ptr(norm_w, shape=(D,), dtype=torch.float32, name="norm_w"), ctypes.c_float(norm_eps), int(rope_dim),
+          ctypes.c_float(rope_base), _ptr(c, shape=(b, nc, D), dtype=dt, name="c"),
+          _ptr(c32, shape=(b, nc, D), dtype=torch.float32, name="c32"), _stream(stream))
+
+
+def csa_compress_bwd_strided(dims: csa_dims, x, z, dc, dx, dz, stream=None, norm_w=None, norm_eps: float = 1e-6,
+                             rope_dim: int = 0, rope_base: float = 40000.0, dnorm_w=None, ws=None) -> None:
+    """csa_compress_bwd over strided views: dx (fp32) shares x's element
+    strides, dz shares z's; dc is contiguous."""
+    dt = x.dtype
+    b, S, D = dims.b, dims.sq, dims.d
+    zc = z.shape[-1]
+    nc = n_compressed(dims)
+    f32 = torch.float32
+    st = compress_strides_of(x, z)
+    _call("csa_compress_bwd_strided", ctypes.byref(dims), ctypes.byref(st), _dtype_code(x),
+          _strided_ptr(x, (b, S, D), dt, "x"), _strided_ptr(z, (b, S, zc), dt, "z"), zc,
+          _ptr(norm_w, shape=(D,), dtype=f32, name="norm_w"), ctypes.c_float(norm_eps), int(rope_dim),
+          ctypes.c_float(rope_base), _ptr(dc, shape=(b, nc, D), dtype=f32, name="dc"),
+          _strided_ptr(dx, (b, S, D), f32, "dx", like=x), _strided_ptr(dz, (b, S, zc), f32, "dz", like=z),
+          _ptr(dnorm_w, shape=(D,), dtype=f32, name="dnorm_w"), _ptr(ws, name="ws"),
+          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def index_strides_of(q_i, k_i, w) -> csa_index_strides:
+    """csa_index_strides of views q_i [b, sq, hi, di], k_i [b, n_c, di] and w [b, sq, hi] (w may be None)."""
+    return csa_index_strides(q_i.stride(0), q_i.stride(1), q_i.stride(2), k_i.stride(0), k_i.stride(1),
+                             w.stride(0) if w is not None else 0, w.stride(1) if w is not None else 0)
+
+
+def csa_index_topk_strided(dims: csa_dims, q_i, k_i, w, idx, score=None, ws=None, stream=None, doc_ids=None) -> None:
+    """csa_index_topk over views q_i, k_i and w whose last axis is contiguous
+    (idx, score and doc_ids contiguous)."""
+    dt = q_i.dtype
+    b, S = dims.b, dims.sq
+    nc, kp = n_compressed(dims), kprime(dims)
+    f32 = torch.float32
+    st = index_strides_of(q_i, k_i, w)
+    _call("csa_index_topk_strided", ctypes.byref(dims), ctypes.byref(st), _dtype_code(q_i),
+          _strided_ptr(q_i, (b, S, dims.idx_heads, dims.idx_dim), dt, "q_i"),
+          _strided_ptr(k_i, (b, nc, dims.idx_dim), dt, "k_i"),
+          _strided_ptr(w, (b, S, dims.idx_heads), f32, "w"), _doc_ptr(dims, doc_ids),
           _ptr(idx, shape=(b, S, kp), dtype=torch.int32, name="idx"),
           _ptr(score, shape=(b, S, kp), dtype=f32, name="score"),
           _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))

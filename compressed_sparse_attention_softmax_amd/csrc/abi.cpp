@@ -84,6 +84,7 @@ csa::CompressArgs compress_args(const csa_dims* dm, const void* x, const void* z
     a.x = x; a.z = z; a.zc = zc;
     a.b = dm->b; a.S = dm->sq; a.D = dm->d; a.r = dm->ratio; a.L = dm->span;
     a.nc = dm->sq / dm->ratio;
+    a.set_contiguous();
     return a;
 }
 
@@ -174,6 +175,77 @@ void apply_strides(csa::AttnArgs& a, const csa_attn_strides* st)
     a.lsb = st->lse_b; a.lst = st->lse_s;
 }
 
+// One stride of a row-addressed tensor: positive, and a multiple of `mult`
+// elements when its axis has more than one entry.
+struct StrideCheck { int64_t v, n, mult; const char* name; };
+
+int check_stride_list(std::initializer_list<StrideCheck> l, const char* fn)
+{
+    for (const auto& x : l)
+        if (x.n > 1 && (x.v < 1 || x.v % x.mult))
+            return fail(CSA_ERR_ARG, "%s: stride %s = %lld must be a positive multiple of %lld elements", fn, x.name,
+                        (long long)x.v, (long long)x.mult);
+    return CSA_OK;
+}
+
+// x / dx rows of d channels and z / dz rows of z_channels, strided by token
+// and batch; rows that 16-byte loads read (x, and z with z_channels = d) keep
+// 16-byte aligned strides
+int check_compress_strides(const csa_dims* dm, int dtype, int zc, const csa_compress_strides* st, const char* fn)
+{
+    if (!st) return CSA_OK;
+    const int64_t e = dtype == CSA_BF16 ? 8 : 4;
+    const int64_t b = dm->b, s = dm->sq, d = dm->d;
+    int rc = check_stride_list({{st->x_b, b, e, "x_b"}, {st->x_s, s, e, "x_s"},
+                                {st->z_b, b, zc == 1 ? 1 : e, "z_b"}, {st->z_s, s, zc == 1 ? 1 : e, "z_s"}}, fn);
+    if (rc) return rc;
+    if (!no_overlap({{1, d}, {st->x_b, b}, {st->x_s, s}}))
+        return fail(CSA_ERR_ARG, "%s: x strides (%lld, %lld) make rows overlap", fn, (long long)st->x_b,
+                    (long long)st->x_s);
+    if (!no_overlap({{1, zc}, {st->z_b, b}, {st->z_s, s}}))
+        return fail(CSA_ERR_ARG, "%s: z strides (%lld, %lld) make rows overlap", fn, (long long)st->z_b,
+                    (long long)st->z_s);
+    return CSA_OK;
+}
+
+void apply_compress_strides(csa::CompressArgs& a, const csa_compress_strides* st)
+{
+    if (!st) return;
+    a.xsb = st->x_b; a.xss = st->x_s; a.zsb = st->z_b; a.zss = st->z_s;
+}
+
+// q_i rows of idx_dim (by token, head, batch), k_i rows (by block, batch), w
+// rows of idx_heads (by token, batch); q_i and k_i rows are read with 16-byte
+// loads
+int check_index_strides(const csa_dims* dm, int dtype, const csa_index_strides* st, const char* fn)
+{
+    if (!st) return CSA_OK;
+    const int64_t e = dtype == CSA_BF16 ? 8 : 4;
+    const int64_t b = dm->b, s = dm->sq, hi = dm->idx_heads, di = dm->idx_dim, nc = dm->sq / dm->ratio;
+    int rc = check_stride_list({{st->qi_b, b, e, "qi_b"}, {st->qi_s, s, e, "qi_s"}, {st->qi_h, hi, e, "qi_h"},
+                                {st->ki_b, b, e, "ki_b"}, {st->ki_s, nc, e, "ki_s"},
+                                {st->w_b, b, 1, "w_b"}, {st->w_s, s, 1, "w_s"}}, fn);
+    if (rc) return rc;
+    if (!no_overlap({{1, di}, {st->qi_b, b}, {st->qi_s, s}, {st->qi_h, hi}}))
+        return fail(CSA_ERR_ARG, "%s: q_i strides (%lld, %lld, %lld) make rows overlap", fn, (long long)st->qi_b,
+                    (long long)st->qi_s, (long long)st->qi_h);
+    if (!no_overlap({{1, di}, {st->ki_b, b}, {st->ki_s, nc}}))
+        return fail(CSA_ERR_ARG, "%s: k_i strides (%lld, %lld) make rows overlap", fn, (long long)st->ki_b,
+                    (long long)st->ki_s);
+    if (!no_overlap({{1, hi}, {st->w_b, b}, {st->w_s, s}}))
+        return fail(CSA_ERR_ARG, "%s: w strides (%lld, %lld) make rows overlap", fn, (long long)st->w_b,
+                    (long long)st->w_s);
+    return CSA_OK;
+}
+
+void apply_index_strides(csa::IndexArgs& a, const csa_index_strides* st)
+{
+    if (!st) return;
+    a.qsb = st->qi_b; a.qss = st->qi_s; a.qsh = st->qi_h;
+    a.ksb = st->ki_b; a.kss = st->ki_s;
+    a.wsb = st->w_b; a.wss = st->w_s;
+}
+
 int check_epilogue(const csa_dims* dm, const float* norm_w, float eps, int rope_dim, float base, const char* fn)
 {
     if (norm_w && !(std::isfinite(eps) && eps >= 0.f))
@@ -190,6 +262,91 @@ void set_epilogue(csa::CompressArgs& a, const float* norm_w, float eps, int rope
     a.norm_w = norm_w; a.eps = eps; a.rope_dim = rope_dim; a.rope_base = base;
 }
 
+// the compressor and indexer calls, with optional element strides (NULL: contiguous)
+int compress_call(const csa_dims* dm, const csa_compress_strides* st, int dtype, const void* x, const void* z,
+                  int z_channels, const float* norm_w, float norm_eps, int rope_dim, float rope_base, void* c,
+                  float* c32, void* stream, const char* fn)
+{
+    int rc = check_common(dm, dtype, fn);
+    if (rc) return rc;
+    if ((rc = check_compress_dims(dm, z_channels, fn))) return rc;
+    if ((rc = check_epilogue(dm, norm_w, norm_eps, rope_dim, rope_base, fn))) return rc;
+    if (!x || !z || (!c && dm->sq / dm->ratio > 0))
+        return fail(CSA_ERR_ARG, "%s: x, z and c must be non-NULL", fn);
+    if ((rc = check_aligned(fn, {{"x", x}, {"z", z}, {"norm_w", norm_w}, {"c", c}, {"c32", c32}})))
+        return rc;
+    if ((rc = check_compress_strides(dm, dtype, z_channels, st, fn))) return rc;
+    csa::CompressArgs a = compress_args(dm, x, z, z_channels);
+    apply_compress_strides(a, st);
+    a.c = c; a.c32 = c32;
+    set_epilogue(a, norm_w, norm_eps, rope_dim, rope_base);
+    return hip_status(csa::compress_fwd(a, dtype == CSA_BF16, (hipStream_t)stream), fn);
+}
+
+int compress_bwd_call(const csa_dims* dm, const csa_compress_strides* st, int dtype, const void* x, const void* z,
+                      int z_channels, const float* norm_w, float norm_eps, int rope_dim, float rope_base,
+                      const float* dc, float* dx, float* dz, float* dnorm_w, void* ws, size_t ws_bytes, void* stream,
+                      const char* fn)
+{
+    int rc = check_common(dm, dtype, fn);
+    if (rc) return rc;
+    if ((rc = check_compress_dims(dm, z_channels, fn))) return rc;
+    if ((rc = check_epilogue(dm, norm_w, norm_eps, rope_dim, rope_base, fn))) return rc;
+    if (!x || !z || (!dc && dm->sq / dm->ratio > 0) || !dx || !dz)
+        return fail(CSA_ERR_ARG, "%s: x, z, dc, dx and dz must be non-NULL", fn);
+    if (dnorm_w && !norm_w) return fail(CSA_ERR_ARG, "%s: dnorm_w given without norm_w", fn);
+    if ((rc = check_aligned(fn, {{"x", x}, {"z", z}, {"norm_w", norm_w}, {"dc", dc}, {"dx", dx}, {"dz", dz},
+                                 {"dnorm_w", dnorm_w}})))
+        return rc;
+    if ((rc = check_compress_strides(dm, dtype, z_channels, st, fn))) return rc;
+    csa::CompressArgs a = compress_args(dm, x, z, z_channels);
+    apply_compress_strides(a, st);
+    a.dc = dc; a.dx = dx; a.dz = dz;
+    set_epilogue(a, norm_w, norm_eps, rope_dim, rope_base);
+    a.dnorm_w = dnorm_w;
+    const size_t need = csa::compress_bwd_workspace_bytes(a);
+    if (need > 0) {
+        if (!ws || ws_bytes < need)
+            return fail(CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                        ws ? ws_bytes : (size_t)0);
+        if (((uintptr_t)ws) & 15) return fail(CSA_ERR_ARG, "%s: workspace must be 16-byte aligned", fn);
+    }
+    a.ws = (float*)ws;
+    return hip_status(csa::compress_bwd(a, dtype == CSA_BF16, (hipStream_t)stream), fn);
+}
+
+int index_topk_call(const csa_dims* dm, const csa_index_strides* st, int dtype, const void* q_i, const void* k_i,
+                    const float* w, const int32_t* doc_ids, int32_t* idx, float* score, void* stream, const char* fn)
+{
+    int rc = check_common(dm, dtype, fn);
+    if (rc) return rc;
+    if (dm->ratio < 1) return fail(CSA_ERR_ARG, "%s: ratio=%d must be >= 1", fn, dm->ratio);
+    if (dm->topk < 1) return fail(CSA_ERR_ARG, "%s: topk=%d must be >= 1", fn, dm->topk);
+    if (dm->idx_heads < 1) return fail(CSA_ERR_ARG, "%s: idx_heads=%d must be >= 1", fn, dm->idx_heads);
+    if (dm->idx_heads > 64) return fail(CSA_ERR_UNSUPPORTED, "%s: idx_heads=%d > 64", fn, dm->idx_heads);
+    if (dm->idx_dim != 32 && dm->idx_dim != 64 && dm->idx_dim != 128)
+        return fail(CSA_ERR_UNSUPPORTED, "%s: idx_dim=%d not in {32,64,128}", fn, dm->idx_dim);
+    const int kp = kprime(dm);
+    if (!q_i) return fail(CSA_ERR_ARG, "%s: q_i must be non-NULL", fn);
+    // sq < ratio: no block exists, K' = 0, idx / score / k_i have no elements
+    if (kp == 0) return ok();
+    if (!k_i || !idx) return fail(CSA_ERR_ARG, "%s: k_i and idx must be non-NULL", fn);
+    if (kp > 2048) return fail(CSA_ERR_UNSUPPORTED, "%s: K'=%d > 2048", fn, kp);
+    if ((rc = check_aligned(fn, {{"q_i", q_i}, {"k_i", k_i}, {"w", w}, {"doc_ids", doc_ids}, {"idx", idx},
+                                 {"score", score}})))
+        return rc;
+    if ((rc = check_index_strides(dm, dtype, st, fn))) return rc;
+    csa::IndexArgs a{};
+    a.qi = q_i; a.ki = k_i; a.w = w; a.doc = doc_ids; a.idx = idx; a.score = score;
+    a.b = dm->b; a.S = dm->sq; a.HI = dm->idx_heads; a.DI = dm->idx_dim; a.r = dm->ratio;
+    a.nc = dm->sq / dm->ratio; a.kp = kp;
+    a.set_contiguous();
+    apply_index_strides(a, st);
+    if (kp > 0 && csa::index_topk_cap(a, dtype == CSA_BF16) == 0)
+        return fail(CSA_ERR_UNSUPPORTED, "%s: K'=%d does not fit the on-chip candidate buffer", fn, kp);
+    return hip_status(csa::index_topk(a, dtype == CSA_BF16, (hipStream_t)stream), fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -201,18 +358,16 @@ const char* csa_last_error(void) { return g_err.c_str(); }
 int csa_compress(const csa_dims* dm, int dtype, const void* x, const void* z, int z_channels, const float* norm_w,
                  float norm_eps, int rope_dim, float rope_base, void* c, float* c32, void* stream)
 {
-    int rc = check_common(dm, dtype, "csa_compress");
-    if (rc) return rc;
-    if ((rc = check_compress_dims(dm, z_channels, "csa_compress"))) return rc;
-    if ((rc = check_epilogue(dm, norm_w, norm_eps, rope_dim, rope_base, "csa_compress"))) return rc;
-    if (!x || !z || (!c && dm->sq / dm->ratio > 0))
-        return fail(CSA_ERR_ARG, "csa_compress: x, z and c must be non-NULL");
-    if ((rc = check_aligned("csa_compress", {{"x", x}, {"z", z}, {"norm_w", norm_w}, {"c", c}, {"c32", c32}})))
-        return rc;
-    csa::CompressArgs a = compress_args(dm, x, z, z_channels);
-    a.c = c; a.c32 = c32;
-    set_epilogue(a, norm_w, norm_eps, rope_dim, rope_base);
-    return hip_status(csa::compress_fwd(a, dtype == CSA_BF16, (hipStream_t)stream), "csa_compress");
+    return compress_call(dm, nullptr, dtype, x, z, z_channels, norm_w, norm_eps, rope_dim, rope_base, c, c32, stream,
+                         "csa_compress");
+}
+
+int csa_compress_strided(const csa_dims* dm, const csa_compress_strides* strides, int dtype, const void* x,
+                         const void* z, int z_channels, const float* norm_w, float norm_eps, int rope_dim,
+                         float rope_base, void* c, float* c32, void* stream)
+{
+    return compress_call(dm, strides, dtype, x, z, z_channels, norm_w, norm_eps, rope_dim, rope_base, c, c32, stream,
+                         "csa_compress_strided");
 }
 
 size_t csa_compress_bwd_workspace(const csa_dims* dm)
@@ -227,29 +382,17 @@ int csa_compress_bwd(const csa_dims* dm, int dtype, const void* x, const void* z
                      const float* norm_w, float norm_eps, int rope_dim, float rope_base, const float* dc, float* dx,
                      float* dz, float* dnorm_w, void* ws, size_t ws_bytes, void* stream)
 {
-    int rc = check_common(dm, dtype, "csa_compress_bwd");
-    if (rc) return rc;
-    if ((rc = check_compress_dims(dm, z_channels, "csa_compress_bwd"))) return rc;
-    if ((rc = check_epilogue(dm, norm_w, norm_eps, rope_dim, rope_base, "csa_compress_bwd"))) return rc;
-    if (!x || !z || (!dc && dm->sq / dm->ratio > 0) || !dx || !dz)
-        return fail(CSA_ERR_ARG, "csa_compress_bwd: x, z, dc, dx and dz must be non-NULL");
-    if (dnorm_w && !norm_w) return fail(CSA_ERR_ARG, "csa_compress_bwd: dnorm_w given without norm_w");
-    if ((rc = check_aligned("csa_compress_bwd", {{"x", x}, {"z", z}, {"norm_w", norm_w}, {"dc", dc}, {"dx", dx},
-                                                 {"dz", dz}, {"dnorm_w", dnorm_w}})))
-        return rc;
-    csa::CompressArgs a = compress_args(dm, x, z, z_channels);
-    a.dc = dc; a.dx = dx; a.dz = dz;
-    set_epilogue(a, norm_w, norm_eps, rope_dim, rope_base);
-    a.dnorm_w = dnorm_w;
-    const size_t need = csa::compress_bwd_workspace_bytes(a);
-    if (need > 0) {
-        if (!ws || ws_bytes < need)
-            return fail(CSA_ERR_WORKSPACE, "csa_compress_bwd: workspace of %zu bytes needed, %zu given", need,
-                        ws ? ws_bytes : (size_t)0);
-        if (((uintptr_t)ws) & 15) return fail(CSA_ERR_ARG, "csa_compress_bwd: workspace must be 16-byte aligned");
-    }
-    a.ws = (float*)ws;
-    return hip_status(csa::compress_bwd(a, dtype == CSA_BF16, (hipStream_t)stream), "csa_compress_bwd");
+    return compress_bwd_call(dm, nullptr, dtype, x, z, z_channels, norm_w, norm_eps, rope_dim, rope_base, dc, dx, dz,
+                             dnorm_w, ws, ws_bytes, stream, "csa_compress_bwd");
+}
+
+int csa_compress_bwd_strided(const csa_dims* dm, const csa_compress_strides* strides, int dtype, const void* x,
+                             const void* z, int z_channels, const float* norm_w, float norm_eps, int rope_dim,
+                             float rope_base, const float* dc, float* dx, float* dz, float* dnorm_w, void* ws,
+                             size_t ws_bytes, void* stream)
+{
+    return compress_bwd_call(dm, strides, dtype, x, z, z_channels, norm_w, norm_eps, rope_dim, rope_base, dc, dx, dz,
+                             dnorm_w, ws, ws_bytes, stream, "csa_compress_bwd_strided");
 }
 
 size_t csa_index_topk_workspace(const csa_dims* dm)
@@ -263,30 +406,15 @@ int csa_index_topk(const csa_dims* dm, int dtype, const void* q_i, const void* k
                    void* stream)
 {
     (void)ws; (void)ws_bytes;
-    int rc = check_common(dm, dtype, "csa_index_topk");
-    if (rc) return rc;
-    if (dm->ratio < 1) return fail(CSA_ERR_ARG, "csa_index_topk: ratio=%d must be >= 1", dm->ratio);
-    if (dm->topk < 1) return fail(CSA_ERR_ARG, "csa_index_topk: topk=%d must be >= 1", dm->topk);
-    if (dm->idx_heads < 1) return fail(CSA_ERR_ARG, "csa_index_topk: idx_heads=%d must be >= 1", dm->idx_heads);
-    if (dm->idx_heads > 64) return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: idx_heads=%d > 64", dm->idx_heads);
-    if (dm->idx_dim != 32 && dm->idx_dim != 64 && dm->idx_dim != 128)
-        return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: idx_dim=%d not in {32,64,128}", dm->idx_dim);
-    const int kp = kprime(dm);
-    if (!q_i) return fail(CSA_ERR_ARG, "csa_index_topk: q_i must be non-NULL");
-    // sq < ratio: no block exists, K' = 0, idx / score / k_i have no elements
-    if (kp == 0) return ok();
-    if (!k_i || !idx) return fail(CSA_ERR_ARG, "csa_index_topk: k_i and idx must be non-NULL");
-    if (kp > 2048) return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: K'=%d > 2048", kp);
-    if ((rc = check_aligned("csa_index_topk", {{"q_i", q_i}, {"k_i", k_i}, {"w", w}, {"doc_ids", doc_ids},
-                                               {"idx", idx}, {"score", score}})))
-        return rc;
-    csa::IndexArgs a{};
-    a.qi = q_i; a.ki = k_i; a.w = w; a.doc = doc_ids; a.idx = idx; a.score = score;
-    a.b = dm->b; a.S = dm->sq; a.HI = dm->idx_heads; a.DI = dm->idx_dim; a.r = dm->ratio;
-    a.nc = dm->sq / dm->ratio; a.kp = kp;
-    if (kp > 0 && csa::index_topk_cap(a, dtype == CSA_BF16) == 0)
-        return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: K'=%d does not fit the on-chip candidate buffer", kp);
-    return hip_status(csa::index_topk(a, dtype == CSA_BF16, (hipStream_t)stream), "csa_index_topk");
+    return index_topk_call(dm, nullptr, dtype, q_i, k_i, w, doc_ids, idx, score, stream, "csa_index_topk");
+}
+
+int csa_index_topk_strided(const csa_dims* dm, const csa_index_strides* strides, int dtype, const void* q_i,
+                           const void* k_i, const float* w, const int32_t* doc_ids, int32_t* idx, float* score,
+                           void* ws, size_t ws_bytes, void* stream)
+{
+    (void)ws; (void)ws_bytes;
+    return index_topk_call(dm, strides, dtype, q_i, k_i, w, doc_ids, idx, score, stream, "csa_index_topk_strided");
 }
 
 }  // extern "C"

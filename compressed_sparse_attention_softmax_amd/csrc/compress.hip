@@ -43,12 +43,17 @@ template <typename T> __device__ __forceinline__ void load8(const T* p, float* o
 // e^x on the transcendental unit (v_exp_f32 after a multiply by log2 e)
 __device__ __forceinline__ float fexp(float x) { return fast_exp2(x * LOG2E); }
 
+// element strides (batch, token) of x and dx, and of z and dz
+struct RowStrides { int64_t xb, xs, zb, zs; };
+RowStrides row_strides(const CompressArgs& p) { return RowStrides{p.xsb, p.xss, p.zsb, p.zss}; }
+
 // Softmax state (max m, denominator s, weighted sum a) of the 8 channels
 // [8q, 8q+8) over the rows [lo, hi) of one span, split NS ways over
-// consecutive lanes; every lane of the group returns the merged state.
+// consecutive lanes; every lane of the group returns the merged state.  x and
+// z point at the batch's first row; rows are xs and zs elements apart.
 template <typename T, int D, int NS>
-__device__ __forceinline__ void span_state(const T* __restrict__ x, const T* __restrict__ z, int zc,
-                                           int64_t rowbase, int lo, int hi, int q, int sp,
+__device__ __forceinline__ void span_state(const T* __restrict__ x, int64_t xs, const T* __restrict__ z,
+                                           int64_t zs, int zc, int lo, int hi, int q, int sp,
                                            float* m, float* s, float* a)
 {
 #pragma unroll
@@ -59,13 +64,13 @@ __device__ __forceinline__ void span_state(const T* __restrict__ x, const T* __r
         for (int k = 0; k < 8; ++k) {
             const int u = u0 + k * NS;
             if (u < hi) {
-                load8(x + (rowbase + u) * D + 8 * q, xv[k]);
+                load8(x + u * xs + 8 * q, xv[k]);
                 if (zc == 1) {
-                    const float zz = to_f32(z[rowbase + u]);
+                    const float zz = to_f32(z[u * zs]);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) zv[k][e] = zz;
                 } else {
-                    load8(z + (rowbase + u) * D + 8 * q, zv[k]);
+                    load8(z + u * zs + 8 * q, zv[k]);
                 }
             } else {
 #pragma unroll
@@ -110,7 +115,7 @@ template <typename T, int D, int NS>
 __global__ __launch_bounds__(256) void compress_fwd_kernel(const T* __restrict__ x,
                                                            const T* __restrict__ z, int zc,
                                                            T* __restrict__ c, float* __restrict__ c32,
-                                                           int b, int S, int r, int L, int nc)
+                                                           int b, int S, int r, int L, int nc, RowStrides rs)
 {
     constexpr int NCH = D / 8;
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -123,7 +128,7 @@ __global__ __launch_bounds__(256) void compress_fwd_kernel(const T* __restrict__
     const int j = (int)(bj % nc), bi = (int)(bj / nc);
     const int hi = (j + 1) * r, lo = max(0, hi - L);
     float m[8], s[8], a[8];
-    span_state<T, D, NS>(x, z, zc, (int64_t)bi * S, lo, hi, q, sp, m, s, a);
+    span_state<T, D, NS>(x + bi * rs.xb, rs.xs, z + bi * rs.zb, rs.zs, zc, lo, hi, q, sp, m, s, a);
     if (live && sp == 0) {
         const int64_t o = bj * D + 8 * q;
         Frag<T> f;
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(256) void compress_epi_bwd_kernel(const T* __restri
                                                                int rope_dim, float base,
                                                                const float* __restrict__ dc, float* __restrict__ dy,
                                                                float* __restrict__ wpart, int S, int r, int L,
-                                                               int64_t rows, int nc)
+                                                               int64_t rows, int nc, RowStrides rs)
 {
     constexpr int G = D / 8, RPW = 256 / G;
     __shared__ float dws[RPW * D];
@@ -231,7 +236,7 @@ __global__ __launch_bounds__(256) void compress_epi_bwd_kernel(const T* __restri
     const int j = (int)(bj % nc), bi = (int)(bj / nc);
     const int hi = (j + 1) * r, lo = max(0, hi - L);
     float m[8], s[8], a[8], y[8], g[8];
-    span_state<T, D, 1>(x, z, zc, (int64_t)bi * S, lo, hi, q, 0, m, s, a);
+    span_state<T, D, 1>(x + bi * rs.xb, rs.xs, z + bi * rs.zb, rs.zs, zc, lo, hi, q, 0, m, s, a);
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = to_f32(from_f32<T>(a[e] / s[e]));   // the cast pooled row
     const Frag<float> df = load_frag(dc + bj * D + 8 * q);
@@ -306,7 +311,7 @@ __global__ __launch_bounds__(256) void compress_bwd_kernel(const T* __restrict__
                                                            const float* __restrict__ dc,
                                                            float* __restrict__ dx,
                                                            float* __restrict__ dz, int S, int r,
-                                                           int L, int nc, int JB)
+                                                           int L, int nc, int JB, RowStrides rs)
 {
     constexpr int NCH = D / 8;
     extern __shared__ float st[];             // [block][4][D]: max, 1/den, c32, dc
@@ -314,7 +319,11 @@ __global__ __launch_bounds__(256) void compress_bwd_kernel(const T* __restrict__
     const int j0 = blockIdx.x * JB;
     const int halo = (L + r - 1) / r - 1;
     const int jhi = min(nc, j0 + JB + halo);
-    const int64_t rowbase = (int64_t)bi * S;
+    // the batch's first rows of x, z, dx and dz
+    const T* xr = x + bi * rs.xb;
+    const T* zr = z + bi * rs.zb;
+    float* dxr = dx + bi * rs.xb;
+    float* dzr = dz + bi * rs.zb;
     // softmax state of every block the workgroup needs, NS lanes per (block, chunk)
     const int nst = (jhi - j0) * NCH * NS;
     for (int i0 = 0; i0 < nst; i0 += 256) {       // uniform trip count: groups stay whole
@@ -324,7 +333,7 @@ __global__ __launch_bounds__(256) void compress_bwd_kernel(const T* __restrict__
         const int sp = ii % NS, q = ii / NS % NCH, j = j0 + ii / NS / NCH;
         const int hi = (j + 1) * r, lo = max(0, hi - L);
         float m[8], s[8], a[8];
-        span_state<T, D, NS>(x, z, zc, rowbase, lo, hi, q, sp, m, s, a);
+        span_state<T, D, NS>(xr, rs.xs, zr, rs.zs, zc, lo, hi, q, sp, m, s, a);
         if (live && sp == 0) {
             float* sj = st + (size_t)(j - j0) * 4 * D;
             const Frag<float> gf = load_frag(dc + ((int64_t)bi * nc + j) * D + 8 * q);
@@ -351,13 +360,13 @@ __global__ __launch_bounds__(256) void compress_bwd_kernel(const T* __restrict__
 #pragma unroll
         for (int e = 0; e < 8; ++e) { gx[e] = 0.f; gz[e] = 0.f; }
         if (live) {
-            load8(x + (rowbase + u) * D + 8 * qq, xv);
+            load8(xr + u * rs.xs + 8 * qq, xv);
             if (zc == 1) {
-                const float zz = to_f32(z[rowbase + u]);
+                const float zz = to_f32(zr[u * rs.zs]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) zv[e] = zz;
             } else {
-                load8(z + (rowbase + u) * D + 8 * qq, zv);
+                load8(zr + u * rs.zs + 8 * qq, zv);
             }
             const int jlast = min(nc - 1, (u + L) / r - 1);
             for (int j = u / r; j <= jlast; ++j) {
@@ -374,25 +383,25 @@ __global__ __launch_bounds__(256) void compress_bwd_kernel(const T* __restrict__
             Frag<float> fx;
 #pragma unroll
             for (int e = 0; e < 8; ++e) fx.v[e] = gx[e];
-            store_frag(dx + (rowbase + u) * D + 8 * qq, fx);
+            store_frag(dxr + u * rs.xs + 8 * qq, fx);
             if (zc != 1) {
                 Frag<float> fz;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) fz.v[e] = gz[e];
-                store_frag(dz + (rowbase + u) * D + 8 * qq, fz);
+                store_frag(dzr + u * rs.zs + 8 * qq, fz);
             }
         }
         if (zc == 1) {
             // the NCH threads of a row are consecutive lanes of one wave
 #pragma unroll
             for (int o = 1; o < NCH; o <<= 1) gzs += __shfl_xor(gzs, o);
-            if (live && qq == 0) dz[rowbase + u] = gzs;
+            if (live && qq == 0) dzr[u * rs.zs] = gzs;
         }
     }
     // rows past the last block: no block covers them
     if (j0 + JB >= nc) {
-        for (int i = threadIdx.x; i < (S - nc * r) * D; i += 256) dx[(rowbase + nc * r) * D + i] = 0.f;
-        for (int i = threadIdx.x; i < (S - nc * r) * zc; i += 256) dz[(rowbase + nc * r) * zc + i] = 0.f;
+        for (int i = threadIdx.x; i < (S - nc * r) * D; i += 256) dxr[(nc * r + i / D) * rs.xs + i % D] = 0.f;
+        for (int i = threadIdx.x; i < (S - nc * r) * zc; i += 256) dzr[(nc * r + i / zc) * rs.zs + i % zc] = 0.f;
     }
 }
 
@@ -412,7 +421,7 @@ hipError_t launch_compress_fwd_ns(const CompressArgs& p, hipStream_t st)
     dim3 grid((unsigned)((threads + 255) / 256));
     TimedLaunch tl(K_COMPRESS_FWD, st);
     hipLaunchKernelGGL((compress_fwd_kernel<T, D, NS>), grid, dim3(256), 0, st, (const T*)p.x, (const T*)p.z, p.zc,
-                       (T*)p.c, p.c32, p.b, p.S, p.r, p.L, p.nc);
+                       (T*)p.c, p.c32, p.b, p.S, p.r, p.L, p.nc, row_strides(p));
     return hipGetLastError();
 }
 
@@ -443,7 +452,7 @@ hipError_t launch_compress_bwd_ns(const CompressArgs& p, hipStream_t st)
     dim3 grid((p.nc + jb - 1) / jb, p.b);
     TimedLaunch tl(K_COMPRESS_BWD, st);
     hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const T*)p.x, (const T*)p.z, p.zc, p.dc, p.dx,
-                       p.dz, p.S, p.r, p.L, p.nc, jb);
+                       p.dz, p.S, p.r, p.L, p.nc, jb, row_strides(p));
     return hipGetLastError();
 }
 
@@ -493,7 +502,7 @@ hipError_t compress_bwd_d(const CompressArgs& p, hipStream_t st)
         TimedLaunch tl(K_COMPRESS_EPI, st);
         hipLaunchKernelGGL((compress_epi_bwd_kernel<T, D>), dim3((unsigned)parts), dim3(256), 0, st, (const T*)p.x,
                            (const T*)p.z, p.zc, p.norm_w, p.eps, p.rope_dim, p.rope_base, p.dc, dy, wpart, p.S, p.r,
-                           p.L, rows, p.nc);
+                           p.L, rows, p.nc, row_strides(p));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (wpart) {

@@ -26,6 +26,9 @@ struct CompressArgs {
     float rope_base;
     float* dnorm_w;       // [D] weight gradient (backward; nullptr: not wanted)
     float* ws;            // backward workspace when the epilogue is on
+    // element strides (batch, token) of x and dx, and of z and dz
+    int64_t xsb, xss, zsb, zss;
+    void set_contiguous() { xsb = (int64_t)S * D; xss = D; zsb = (int64_t)S * zc; zss = zc; }
 };
 
 struct IndexArgs {
@@ -36,6 +39,14 @@ struct IndexArgs {
     int32_t* idx;
     float* score;
     int b, S, HI, DI, r, nc, kp;
+    // element strides: q_i (batch, token, head), k_i (batch, block), w (batch, token)
+    int64_t qsb, qss, qsh, ksb, kss, wsb, wss;
+    void set_contiguous()
+    {
+        qsh = DI; qss = (int64_t)HI * DI; qsb = (int64_t)S * HI * DI;
+        kss = DI; ksb = (int64_t)nc * DI;
+        wss = HI; wsb = (int64_t)S * HI;
+    }
 };
 
 struct AttnArgs {

@@ -195,6 +195,9 @@ __device__ float select_keep(const WaveBufs& b, int n, int k)
     return T;
 }
 
+// element strides: q_i (batch, token, head), k_i (batch, block), w (batch, token)
+struct IndexStrides { int64_t qb, qs, qh, kb, ks, wb, ws; };
+
 template <typename T, int DI, int HT>
 __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict__ qi,
                                                             const T* __restrict__ ki,
@@ -202,7 +205,8 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
                                                             const int32_t* __restrict__ doc,
                                                             int32_t* __restrict__ idx,
                                                             float* __restrict__ score, int S,
-                                                            int HI, int r, int nc, int kp, int cap)
+                                                            int HI, int r, int nc, int kp, int cap,
+                                                            IndexStrides is)
 {
     constexpr int KS = DI / 32;            // k-steps of 32
     constexpr int ROW = DI + 16 / sizeof(T) * 1;   // LDS row stride (elements), one 16-B pad
@@ -229,6 +233,8 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
     const int t_last = min(qblk * 4 + 3, S - 1);
     const int nv_max = min((t_last + 1) / r, nc);
     const int64_t row = (int64_t)bi * S + (active ? t : 0);
+    const T* qrow = qi + bi * is.qb + (int64_t)(active ? t : 0) * is.qs;
+    const float* wrow = w ? w + bi * is.wb + (int64_t)(active ? t : 0) * is.ws : nullptr;
 
     // query operands (A: m = head, k = dim) and per-head weights in C-row layout
     Frag<T> qa[HT][KS];
@@ -238,16 +244,15 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
         const int h = 16 * ht + n16;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qa[ht][ks] = (active && h < HI) ? load_frag(qi + (row * HI + h) * DI + 32 * ks + 8 * g)
-                                             : zero_frag<T>();
+            qa[ht][ks] = (active && h < HI) ? load_frag(qrow + h * is.qh + 32 * ks + 8 * g) : zero_frag<T>();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int hh = 16 * ht + 4 * g + i;
-            wv[ht][i] = (active && hh < HI) ? (w ? w[row * HI + hh] : 1.f) : 0.f;   // no w: unit weights
+            wv[ht][i] = (active && hh < HI) ? (w ? wrow[hh] : 1.f) : 0.f;   // no w: unit weights
         }
     }
 
-    const T* kb = ki + (int64_t)bi * nc * DI;
+    const T* kb = ki + bi * is.kb;
     float tau = -INFINITY;
     int cnt = 0;
     constexpr int CH = 16 / sizeof(T);               // elements per 16-B chunk
@@ -266,7 +271,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
         for (int k = 0; k < CPT; ++k) {
             const int c = (int)threadIdx.x + 256 * k;
             const int rr = c / (DI / CH), cc = (c % (DI / CH)) * CH;
-            pre[k] = j0 + rr < nc ? *reinterpret_cast<const uint4*>(kb + (int64_t)(j0 + rr) * DI + cc)
+            pre[k] = j0 + rr < nc ? *reinterpret_cast<const uint4*>(kb + (int64_t)(j0 + rr) * is.ks + cc)
                                   : make_uint4(0u, 0u, 0u, 0u);
         }
     };
@@ -364,8 +369,9 @@ hipError_t launch_index(const IndexArgs& p, hipStream_t st)
     if (e != hipSuccess) return e;
     dim3 grid((p.S + 3) / 4, p.b);
     TimedLaunch tl(K_INDEX_TOPK, st);
+    const IndexStrides is{p.qsb, p.qss, p.qsh, p.ksb, p.kss, p.wsb, p.wss};
     hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const T*)p.qi, (const T*)p.ki, p.w, p.doc, p.idx,
-                       p.score, p.S, p.HI, p.r, p.nc, kp, cap);
+                       p.score, p.S, p.HI, p.r, p.nc, kp, cap, is);
     return hipGetLastError();
 }
 

@@ -37,9 +37,12 @@
  *      q_i     [b, sq, idx_heads, idx_dim];  k_i [b, n_c, idx_dim]
  *      w       [b, sq, idx_heads];   lse [b, sq, h];  sink, dsink [h]
  *      idx, score [b, sq, K'],  K' = min(topk, n_c)
- *    The *_strided attention calls take the q-like, kv-like and lse layouts
- *    as element strides instead (csa_attn_strides); every other tensor keeps
- *    the layout above.
+ *    The *_strided calls take the layouts of the tensors they read from the
+ *    caller as element strides instead: q-like, kv-like and lse for the
+ *    attention (csa_attn_strides), x / dx and z / dz for the compressor
+ *    (csa_compress_strides), q_i, k_i and w for the indexer
+ *    (csa_index_strides).  Outputs the library hands to its own calls (c,
+ *    c32, dc, idx, score) and every other tensor keep the layout above.
  *    Base pointers must be 16-byte aligned (the CSA calls return CSA_ERR_ARG,
  *    naming the argument, for any non-NULL tensor that is not; the DSA-over-GQA
  *    calls accept any element-aligned tensor).
@@ -76,7 +79,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 8
+#define CSA_ABI_VERSION 9
 
 enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 };
 
@@ -147,6 +150,35 @@ int csa_compress_bwd(const csa_dims* dims, int dtype, const void* x, const void*
                      float rope_base, const float* dc, float* dx, float* dz, float* dnorm_w,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* Element strides (in elements, not bytes) of the compressor's token rows
+ * for the *_strided compressor calls, so that a sequence-major caller ([sq,
+ * b, d] views) needs no transposed copy.  The channel axis stays contiguous.
+ *   x_b, x_s   x and dx (dx uses the same element strides in fp32)
+ *   z_b, z_s   z and dz (likewise)
+ * Axes of extent > 1 must not overlap (sorted by stride, each stride at least
+ * the previous one times its extent, the contiguous axis first); x strides,
+ * and z strides when z_channels = d, are multiples of 16 bytes of the dtype
+ * (8 bf16 or 4 fp32 elements).  Otherwise CSA_ERR_ARG naming the stride.
+ * Axes of extent 1 are ignored. */
+typedef struct csa_compress_strides {
+    int64_t x_b, x_s;
+    int64_t z_b, z_s;
+} csa_compress_strides;
+
+/* csa_compress over strided x and z (strides == NULL: the contiguous layout,
+ * identical to csa_compress); c and c32 are written contiguously. */
+int csa_compress_strided(const csa_dims* dims, const csa_compress_strides* strides, int dtype, const void* x,
+                         const void* z, int z_channels, const float* norm_w, float norm_eps, int rope_dim,
+                         float rope_base, void* c, float* c32, void* stream);
+
+/* csa_compress_bwd over strided x, z, dx and dz (strides == NULL: identical
+ * to csa_compress_bwd); dc is read contiguously.  Results are bit-identical
+ * to the contiguous call on the same values. */
+int csa_compress_bwd_strided(const csa_dims* dims, const csa_compress_strides* strides, int dtype,
+                             const void* x, const void* z, int z_channels, const float* norm_w,
+                             float norm_eps, int rope_dim, float rope_base, const float* dc, float* dx,
+                             float* dz, float* dnorm_w, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes csa_index_topk needs (0: scores never leave the chip). */
 size_t csa_index_topk_workspace(const csa_dims* dims);
 
@@ -167,6 +199,27 @@ size_t csa_index_topk_workspace(const csa_dims* dims);
 int csa_index_topk(const csa_dims* dims, int dtype, const void* q_i, const void* k_i,
                    const float* w, const int32_t* doc_ids, int32_t* idx, float* score, void* ws,
                    size_t ws_bytes, void* stream);
+
+/* Element strides of the indexer's inputs for csa_index_topk_strided (the
+ * last axis of each stays contiguous):
+ *   qi_b, qi_s, qi_h   q_i [b, sq, idx_heads, idx_dim]
+ *   ki_b, ki_s         k_i [b, n_c, idx_dim]
+ *   w_b, w_s           w   [b, sq, idx_heads] (fp32)
+ * Axes of extent > 1 must not overlap; q_i and k_i strides of such axes are
+ * multiples of 16 bytes of the dtype.  Otherwise CSA_ERR_ARG naming the
+ * stride.  doc_ids, idx and score keep the contiguous layout. */
+typedef struct csa_index_strides {
+    int64_t qi_b, qi_s, qi_h;
+    int64_t ki_b, ki_s;
+    int64_t w_b, w_s;
+} csa_index_strides;
+
+/* csa_index_topk over strided q_i, k_i and w (strides == NULL: identical to
+ * csa_index_topk).  Results are identical to the contiguous call on the same
+ * values. */
+int csa_index_topk_strided(const csa_dims* dims, const csa_index_strides* strides, int dtype,
+                           const void* q_i, const void* k_i, const float* w, const int32_t* doc_ids,
+                           int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream);
 
 /* Sparse attention forward (Megatron-LM PR #6400 gather and sink threads;
  * torchtitan PR #4452 fused operator).  For query (b, t) and head h the

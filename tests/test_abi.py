@@ -33,7 +33,7 @@ def test_library_exports_every_header_symbol():
     lib = _lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.csa_version() == 8
+    assert lib.csa_version() == 9
 
 
 def test_dims_struct_matches_header():
@@ -384,6 +384,108 @@ def test_strided_binding_checks_stride_agreement():
     assert (st.q_b, st.q_s, st.q_h, st.kv_b, st.kv_s, st.lse_b, st.lse_s) == (256, 512, 64, 64, 128, 4, 8)
     with pytest.raises(ValueError, match="GPU tensor"):
         _abi._strided_ptr(q, (2, 64, 4, 64), torch.bfloat16, "q")
+
+
+def _seq_major_compress(b=2, sq=64, d=64, zc=64):
+    """Element strides of sequence-major x [sq, b, d] and z [sq, b, zc]."""
+    return _abi.csa_compress_strides(d, b * d, zc, b * zc)
+
+
+def _compress_strided(st, dims=None, x=P, z=P, zc=64):
+    return (ctypes.byref(dims or _d(b=2)), None if st is None else ctypes.byref(st), 1, x, z, zc, N,
+            ctypes.c_float(1e-6), 0, F4, P, N, N)
+
+
+@pytest.mark.parametrize("name,cls,fields,size", [
+    ("csa_compress_strides", "csa_compress_strides", ("x_b", "x_s", "z_b", "z_s"), 32),
+    ("csa_index_strides", "csa_index_strides", ("qi_b", "qi_s", "qi_h", "ki_b", "ki_s", "w_b", "w_s"), 56),
+])
+def test_compress_and_index_stride_structs_match_header(name, cls, fields, size):
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (name, name), src, re.S).group(1)
+    names = re.findall(r"([a-z_]+)[,;]", body.replace("int64_t", ""))
+    assert names == [f[0] for f in getattr(_abi, cls)._fields_] == list(fields)
+    assert ctypes.sizeof(getattr(_abi, cls)) == size
+
+
+@pytest.mark.parametrize("st", [None, "seq", "contiguous"])
+def test_compress_strided_accepts_valid_strides(st):
+    # valid strides pass validation; the misaligned x is then what is reported
+    lib = _lib()
+    s = {"seq": _seq_major_compress(), "contiguous": _abi.csa_compress_strides(64 * 64, 64, 64 * 64, 64), None: None}[st]
+    rc = lib.csa_compress_strided(*_compress_strided(s, x=M))
+    assert rc == -1 and "x is not 16-byte aligned" in lib.csa_last_error().decode()
+
+
+@pytest.mark.parametrize("field,value,text", [
+    ("x_s", 132, "stride x_s"),          # not a multiple of 8 bf16 elements
+    ("z_b", 0, "stride z_b"),
+    ("x_s", 32, "x strides"),            # tokens overlap rows of 64 channels
+    ("z_b", 64 * 2, "z strides"),        # batch and sequence alias
+])
+def test_compress_strided_rejects_bad_strides(field, value, text):
+    lib = _lib()
+    st = _seq_major_compress()
+    setattr(st, field, value)
+    rc = lib.csa_compress_strided(*_compress_strided(st))
+    assert rc == -1 and text in lib.csa_last_error().decode()
+
+
+def test_compress_strided_scalar_gate_strides_need_no_alignment():
+    # z_channels = 1: the gate is read one element at a time
+    lib = _lib()
+    st = _abi.csa_compress_strides(64, 2 * 64, 1, 2)
+    rc = lib.csa_compress_strided(*_compress_strided(st, x=M, zc=1))
+    assert rc == -1 and "x is not 16-byte aligned" in lib.csa_last_error().decode()
+
+
+def test_compress_bwd_strided_validates_strides():
+    lib = _lib()
+    st = _seq_major_compress()
+    st.x_s = 36
+    rc = lib.csa_compress_bwd_strided(ctypes.byref(_d(b=2)), ctypes.byref(st), 1, P, P, 64, N, ctypes.c_float(1e-6),
+                                      0, F4, P, P, P, N, N, 0, N)
+    assert rc == -1 and "stride x_s" in lib.csa_last_error().decode()
+
+
+def _seq_major_index(b=2, sq=64, hi=2, di=32, nc=16):
+    """Element strides of sequence-major q_i [sq, b, hi, di], k_i [nc, b, di], w [sq, b, hi]."""
+    return _abi.csa_index_strides(hi * di, b * hi * di, di, di, b * di, hi, b * hi)
+
+
+@pytest.mark.parametrize("field,value,text", [
+    ("qi_s", 68, "stride qi_s"),         # not a multiple of 8 bf16 elements
+    ("qi_h", 16, "q_i strides"),         # heads overlap rows of 32
+    ("ki_s", 16, "k_i strides"),
+    ("w_s", 1, "w strides"),             # tokens step inside the 2 heads
+    ("w_b", 0, "stride w_b"),
+])
+def test_index_topk_strided_rejects_bad_strides(field, value, text):
+    lib = _lib()
+    st = _seq_major_index()
+    setattr(st, field, value)
+    rc = lib.csa_index_topk_strided(ctypes.byref(_d(b=2)), ctypes.byref(st), 1, P, P, P, N, P, P, N, 0, N)
+    assert rc == -1 and text in lib.csa_last_error().decode()
+
+
+def test_index_topk_strided_accepts_valid_strides():
+    lib = _lib()
+    rc = lib.csa_index_topk_strided(ctypes.byref(_d(b=2)), ctypes.byref(_seq_major_index()), 1, M, P, P, N, P, P, N,
+                                    0, N)
+    assert rc == -1 and "q_i is not 16-byte aligned" in lib.csa_last_error().decode()
+
+
+def test_compress_and_index_stride_helpers():
+    import torch
+    x = torch.zeros(64, 2, 64, dtype=torch.bfloat16).transpose(0, 1)
+    z = torch.zeros(64, 2, 1, dtype=torch.bfloat16).transpose(0, 1)
+    st = _abi.compress_strides_of(x, z)
+    assert (st.x_b, st.x_s, st.z_b, st.z_s) == (64, 128, 1, 2)
+    q_i = torch.zeros(64, 2, 2, 32, dtype=torch.bfloat16).transpose(0, 1)
+    k_i = torch.zeros(16, 2, 32, dtype=torch.bfloat16).transpose(0, 1)
+    w = torch.zeros(64, 2, 2).transpose(0, 1)
+    si = _abi.index_strides_of(q_i, k_i, w)
+    assert (si.qi_b, si.qi_s, si.qi_h, si.ki_b, si.ki_s, si.w_b, si.w_s) == (64, 128, 32, 32, 64, 2, 4)
 
 
 def _dense_args(dims, **over):

@@ -127,3 +127,88 @@ def test_strided_binding_rejects_mismatched_output_strides(gpu):
     lse = torch.empty(wl.b, wl.sq, wl.h, device="cuda")
     with pytest.raises(ValueError, match="differ"):
         csa.csa_sparse_attn_fwd_strided(dm, q, kv, None, None, inp["sink"], wl.scale, out, lse)
+
+
+COMPRESS_CASES = [
+    ("tiny_f32_sbhd", TINY.replace(b=2), "sbhd", 0, False),
+    ("csa4_bf16_b3_sbhd", CSA4_SMALL.replace(b=3, sq=1030), "sbhd", 0, False),
+    ("csa4_bf16_b2_pad_epilogue", CSA4_SMALL.replace(b=2, sq=517), "pad", 8, True),
+    ("csa4_bf16_b2_gate1_sbhd", CSA4_SMALL.replace(b=2, sq=301, z_channels=1), "sbhd", 0, False),
+    ("d512_bf16_b2_sbhd_epilogue", D512_SMALL.replace(b=2, sq=260), "sbhd", 0, True),
+]
+
+
+@pytest.mark.parametrize("name,wl,layout,pad,epi", COMPRESS_CASES, ids=[c[0] for c in COMPRESS_CASES])
+def test_strided_compressor_matches_contiguous(gpu, name, wl, layout, pad, epi):
+    """Sequence-major or padded x, z, dx and dz through the strided compressor
+    calls: c, c32, dx, dz and dnorm_w equal the contiguous calls' bit for bit
+    (rows past n_c * ratio included, which receive zero)."""
+    import compressed_sparse_attention_softmax_amd as csa
+    say(f"[strided compressor] {name} b={wl.b} sq={wl.sq} d={wl.d} zc={wl.z_channels} layout={layout} epi={epi}")
+    inp = csa_synth.make_inputs(wl, 31, device="cuda", parts=("compress",))
+    dm = csa.dims_of(wl)
+    b, S, D, zc, nc = wl.b, wl.sq, wl.d, wl.z_channels, wl.n_c
+    g = torch.Generator().manual_seed(37)
+    dc = (torch.randn(b, nc, D, generator=g) * 0.5).cuda()
+    ep = {}
+    if epi:
+        ep = dict(norm_w=(1.0 + 0.1 * torch.randn(D, generator=g)).cuda(), rope_dim=min(64, D))
+    ws = torch.empty(max(csa.csa_compress_bwd_workspace(dm), 16), dtype=torch.uint8, device="cuda")
+
+    def run(strided):
+        x, z = inp["x"], inp["z"]
+        mk = (lambda shape: _empty_like_layout(shape, torch.float32, layout, pad)) if strided else \
+            (lambda shape: torch.full(shape, 3.0, device="cuda"))
+        if strided:
+            x, z = _view(x, layout, pad), _view(z, layout, pad)
+        c = torch.full((b, nc, D), 3.0, device="cuda").to(wl.torch_dtype)
+        c32 = torch.full((b, nc, D), 3.0, device="cuda")
+        dx, dz = mk((b, S, D)), mk((b, S, zc))
+        dnw = torch.full((D,), 3.0, device="cuda") if epi else None
+        if strided:
+            csa.csa_compress_strided(dm, x, z, c, c32, **ep)
+            csa.csa_compress_bwd_strided(dm, x, z, dc, dx, dz, dnorm_w=dnw, ws=ws, **ep)
+        else:
+            csa.csa_compress(dm, x, z, c, c32, **ep)
+            csa.csa_compress_bwd(dm, x, z, dc, dx, dz, dnorm_w=dnw, ws=ws, **ep)
+        torch.cuda.synchronize()
+        return dict(c=c, c32=c32, dx=dx.contiguous(), dz=dz.contiguous(), dnw=dnw)
+
+    ref, got = run(False), run(True)
+    for k, v in ref.items():
+        if v is None:
+            continue
+        assert torch.equal(got[k], v), f"{k}: strided compressor call differs from the contiguous call"
+    assert bool((got["dx"][:, nc * wl.ratio:] == 0).all()) and bool((got["dz"][:, nc * wl.ratio:] == 0).all())
+
+
+INDEX_CASES = [
+    ("tiny_f32_sbhd", TINY.replace(b=2), "sbhd", 0),
+    ("csa4_bf16_b2_sbhd", CSA4_SMALL.replace(b=2, sq=1030), "sbhd", 0),
+    ("csa4_bf16_b3_pad", CSA4_SMALL.replace(b=3, sq=700, topk=64), "pad", 8),
+]
+
+
+@pytest.mark.parametrize("name,wl,layout,pad", INDEX_CASES, ids=[c[0] for c in INDEX_CASES])
+def test_strided_indexer_matches_contiguous(gpu, name, wl, layout, pad):
+    """Sequence-major or padded q_i, k_i and w through csa_index_topk_strided:
+    idx and score equal the contiguous call's exactly."""
+    import compressed_sparse_attention_softmax_amd as csa
+    say(f"[strided indexer] {name} b={wl.b} sq={wl.sq} hi={wl.idx_heads} di={wl.idx_dim} layout={layout}")
+    inp = csa_synth.make_inputs(wl, 41, device="cuda", parts=("index",))
+    dm = csa.dims_of(wl)
+    b, S, kp = wl.b, wl.sq, wl.kprime
+    out = {}
+    for strided in (False, True):
+        q_i, k_i, w = inp["q_i"], inp["k_i"], inp["w"]
+        idx = torch.full((b, S, kp), 7, dtype=torch.int32, device="cuda")
+        score = torch.full((b, S, kp), 3.0, device="cuda")
+        if strided:
+            q_i, k_i, w = _view(q_i, layout, pad), _view(k_i, layout, pad), _view(w, layout, 4 if pad else 0)
+            csa.csa_index_topk_strided(dm, q_i, k_i, w, idx, score)
+        else:
+            csa.csa_index_topk(dm, q_i, k_i, w, idx, score)
+        torch.cuda.synchronize()
+        out[strided] = (idx, score)
+    assert torch.equal(out[True][0], out[False][0]), "idx: strided indexer call differs from the contiguous call"
+    assert torch.equal(out[True][1], out[False][1]), "score: strided indexer call differs from the contiguous call"

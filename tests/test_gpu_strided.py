@@ -42,7 +42,7 @@ def _empty_like_layout(shape, dtype, layout, pad=0, fill=3.0):
     return store[..., :shape[-1]]
 
 
-def _run(csa, dm, wl, q, kv, c, idx, sink, do, layout=None, pad=0):
+def _run(csa, dm, wl, q, kv, c, idx, sink, do, layout=None, pad=0, doc=None):
     b, S, H, D = wl.b, wl.sq, wl.h, wl.d
     strided = layout is not None
     mk = (lambda shape, dt: _empty_like_layout(shape, dt, layout, pad)) if strided else \
@@ -59,11 +59,13 @@ def _run(csa, dm, wl, q, kv, c, idx, sink, do, layout=None, pad=0):
     dsink = torch.full((H,), 3.0, device="cuda") if sink is not None else None
     ws = torch.empty(csa.csa_sparse_attn_bwd_workspace(dm), dtype=torch.uint8, device="cuda")
     if strided:
-        csa.csa_sparse_attn_fwd_strided(dm, q, kv, c, idx, sink, wl.scale, out, lse)
-        csa.csa_sparse_attn_bwd_strided(dm, q, kv, c, idx, sink, wl.scale, out, lse, do, dq, dkv, dc, dsink, ws=ws)
+        csa.csa_sparse_attn_fwd_strided(dm, q, kv, c, idx, sink, wl.scale, out, lse, doc_ids=doc)
+        csa.csa_sparse_attn_bwd_strided(dm, q, kv, c, idx, sink, wl.scale, out, lse, do, dq, dkv, dc, dsink, ws=ws,
+                                        doc_ids=doc)
     else:
-        csa.csa_sparse_attn_fwd(dm, q, kv, c, idx, sink, wl.scale, out, lse)
-        csa.csa_sparse_attn_bwd(dm, q, kv, c, idx, sink, wl.scale, out, lse, do, dq, dkv, dc, dsink, ws=ws)
+        csa.csa_sparse_attn_fwd(dm, q, kv, c, idx, sink, wl.scale, out, lse, doc_ids=doc)
+        csa.csa_sparse_attn_bwd(dm, q, kv, c, idx, sink, wl.scale, out, lse, do, dq, dkv, dc, dsink, ws=ws,
+                                doc_ids=doc)
     torch.cuda.synchronize()
     return dict(out=out.contiguous(), lse=lse.contiguous(), dq=dq.contiguous(), dkv=dkv.contiguous(), dc=dc,
                 dsink=dsink)
@@ -78,6 +80,8 @@ STRIDED_CASES = [
     ("csa4_bf16_b2_window_only_sbhd", CSA4_SMALL.replace(b=2, sq=300), "sbhd", 0, "window"),
     ("d512_bf16_b2_sbhd", D512_SMALL.replace(b=2, sq=200), "sbhd", 0, "random"),
     ("bf16_d64_b2_sbhd", CSA4_SMALL.replace(b=2, sq=300, h=16, d=64, z_channels=64, topk=40), "sbhd", 0, "random"),
+    ("csa4_bf16_b2_docs_sbhd", CSA4_SMALL.replace(b=2, sq=400, topk=40), "sbhd", 0, "docs"),
+    ("csa4_bf16_b2_dense_docs_pad", CSA4_SMALL.replace(b=2, sq=333), "pad", 16, "dense_docs"),
 ]
 
 
@@ -90,10 +94,11 @@ def test_strided_attention_matches_contiguous(gpu, name, wl, layout, pad, mode):
     c = None
     if mode != "window":
         c = (torch.randn(wl.b, wl.n_c, wl.d, generator=g) * 0.5).to(wl.torch_dtype).cuda()
-    idx = csa_synth.random_topk_indices(wl, 24).cuda() if mode == "random" else None
+    idx = csa_synth.random_topk_indices(wl, 24).cuda() if mode in ("random", "docs") else None
+    doc = csa_synth.packed_doc_ids(wl.b, wl.sq, 90.0, 25).cuda() if mode in ("docs", "dense_docs") else None
     dm = csa.dims_of(wl)
-    ref = _run(csa, dm, wl, inp["q"], inp["kv"], c, idx, inp["sink"], inp["do"])
-    got = _run(csa, dm, wl, inp["q"], inp["kv"], c, idx, inp["sink"], inp["do"], layout=layout, pad=pad)
+    ref = _run(csa, dm, wl, inp["q"], inp["kv"], c, idx, inp["sink"], inp["do"], doc=doc)
+    got = _run(csa, dm, wl, inp["q"], inp["kv"], c, idx, inp["sink"], inp["do"], layout=layout, pad=pad, doc=doc)
     for k in ("out", "lse", "dq", "dkv", "dc", "dsink"):
         if ref[k] is None:
             continue
@@ -183,21 +188,24 @@ def test_strided_compressor_matches_contiguous(gpu, name, wl, layout, pad, epi):
 
 
 INDEX_CASES = [
-    ("tiny_f32_sbhd", TINY.replace(b=2), "sbhd", 0),
-    ("csa4_bf16_b2_sbhd", CSA4_SMALL.replace(b=2, sq=1030), "sbhd", 0),
-    ("csa4_bf16_b3_pad", CSA4_SMALL.replace(b=3, sq=700, topk=64), "pad", 8),
+    ("tiny_f32_sbhd", TINY.replace(b=2), "sbhd", 0, False),
+    ("csa4_bf16_b2_sbhd", CSA4_SMALL.replace(b=2, sq=1030), "sbhd", 0, False),
+    ("csa4_bf16_b3_pad", CSA4_SMALL.replace(b=3, sq=700, topk=64), "pad", 8, False),
+    ("csa4_bf16_b2_sbhd_docs", CSA4_SMALL.replace(b=2, sq=900, topk=64), "sbhd", 0, True),
 ]
 
 
-@pytest.mark.parametrize("name,wl,layout,pad", INDEX_CASES, ids=[c[0] for c in INDEX_CASES])
-def test_strided_indexer_matches_contiguous(gpu, name, wl, layout, pad):
-    """Sequence-major or padded q_i, k_i and w through csa_index_topk_strided:
-    idx and score equal the contiguous call's exactly."""
+@pytest.mark.parametrize("name,wl,layout,pad,docs", INDEX_CASES, ids=[c[0] for c in INDEX_CASES])
+def test_strided_indexer_matches_contiguous(gpu, name, wl, layout, pad, docs):
+    """Sequence-major or padded q_i, k_i and w through csa_index_topk_strided
+    (with and without packed documents): idx and score equal the contiguous
+    call's exactly."""
     import compressed_sparse_attention_softmax_amd as csa
     say(f"[strided indexer] {name} b={wl.b} sq={wl.sq} hi={wl.idx_heads} di={wl.idx_dim} layout={layout}")
     inp = csa_synth.make_inputs(wl, 41, device="cuda", parts=("index",))
     dm = csa.dims_of(wl)
     b, S, kp = wl.b, wl.sq, wl.kprime
+    doc = csa_synth.packed_doc_ids(b, S, 150.0, 43).cuda() if docs else None
     out = {}
     for strided in (False, True):
         q_i, k_i, w = inp["q_i"], inp["k_i"], inp["w"]
@@ -205,9 +213,9 @@ def test_strided_indexer_matches_contiguous(gpu, name, wl, layout, pad):
         score = torch.full((b, S, kp), 3.0, device="cuda")
         if strided:
             q_i, k_i, w = _view(q_i, layout, pad), _view(k_i, layout, pad), _view(w, layout, 4 if pad else 0)
-            csa.csa_index_topk_strided(dm, q_i, k_i, w, idx, score)
+            csa.csa_index_topk_strided(dm, q_i, k_i, w, idx, score, doc_ids=doc)
         else:
-            csa.csa_index_topk(dm, q_i, k_i, w, idx, score)
+            csa.csa_index_topk(dm, q_i, k_i, w, idx, score, doc_ids=doc)
         torch.cuda.synchronize()
         out[strided] = (idx, score)
     assert torch.equal(out[True][0], out[False][0]), "idx: strided indexer call differs from the contiguous call"

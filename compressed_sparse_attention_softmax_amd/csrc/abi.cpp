@@ -215,16 +215,16 @@ void apply_compress_strides(csa::CompressArgs& a, const csa_compress_strides* st
 }
 
 // q_i rows of idx_dim (by token, head, batch), k_i rows (by block, batch), w
-// rows of idx_heads (by token, batch); q_i and k_i rows are read with 16-byte
-// loads
-int check_index_strides(const csa_dims* dm, int dtype, const csa_index_strides* st, const char* fn)
+// rows of idx_heads (by token, batch; ignored when there is no w); q_i and k_i
+// rows are read with 16-byte loads
+int check_index_strides(const csa_dims* dm, int dtype, const csa_index_strides* st, bool has_w, const char* fn)
 {
     if (!st) return CSA_OK;
     const int64_t e = dtype == CSA_BF16 ? 8 : 4;
     const int64_t b = dm->b, s = dm->sq, hi = dm->idx_heads, di = dm->idx_dim, nc = dm->sq / dm->ratio;
     int rc = check_stride_list({{st->qi_b, b, e, "qi_b"}, {st->qi_s, s, e, "qi_s"}, {st->qi_h, hi, e, "qi_h"},
                                 {st->ki_b, b, e, "ki_b"}, {st->ki_s, nc, e, "ki_s"},
-                                {st->w_b, b, 1, "w_b"}, {st->w_s, s, 1, "w_s"}}, fn);
+                                {st->w_b, has_w ? b : 1, 1, "w_b"}, {st->w_s, has_w ? s : 1, 1, "w_s"}}, fn);
     if (rc) return rc;
     if (!no_overlap({{1, di}, {st->qi_b, b}, {st->qi_s, s}, {st->qi_h, hi}}))
         return fail(CSA_ERR_ARG, "%s: q_i strides (%lld, %lld, %lld) make rows overlap", fn, (long long)st->qi_b,
@@ -232,7 +232,7 @@ int check_index_strides(const csa_dims* dm, int dtype, const csa_index_strides* 
     if (!no_overlap({{1, di}, {st->ki_b, b}, {st->ki_s, nc}}))
         return fail(CSA_ERR_ARG, "%s: k_i strides (%lld, %lld) make rows overlap", fn, (long long)st->ki_b,
                     (long long)st->ki_s);
-    if (!no_overlap({{1, hi}, {st->w_b, b}, {st->w_s, s}}))
+    if (has_w && !no_overlap({{1, hi}, {st->w_b, b}, {st->w_s, s}}))
         return fail(CSA_ERR_ARG, "%s: w strides (%lld, %lld) make rows overlap", fn, (long long)st->w_b,
                     (long long)st->w_s);
     return CSA_OK;
@@ -335,7 +335,7 @@ int index_topk_call(const csa_dims* dm, const csa_index_strides* st, int dtype, 
     if ((rc = check_aligned(fn, {{"q_i", q_i}, {"k_i", k_i}, {"w", w}, {"doc_ids", doc_ids}, {"idx", idx},
                                  {"score", score}})))
         return rc;
-    if ((rc = check_index_strides(dm, dtype, st, fn))) return rc;
+    if ((rc = check_index_strides(dm, dtype, st, w != nullptr, fn))) return rc;
     csa::IndexArgs a{};
     a.qi = q_i; a.ki = k_i; a.w = w; a.doc = doc_ids; a.idx = idx; a.score = score;
     a.b = dm->b; a.S = dm->sq; a.HI = dm->idx_heads; a.DI = dm->idx_dim; a.r = dm->ratio;

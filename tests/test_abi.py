@@ -475,6 +475,15 @@ def test_index_topk_strided_accepts_valid_strides():
     assert rc == -1 and "q_i is not 16-byte aligned" in lib.csa_last_error().decode()
 
 
+def test_index_topk_strided_ignores_w_strides_without_w():
+    # w == NULL (unit weights): its strides are never used and not checked
+    lib = _lib()
+    st = _seq_major_index()
+    st.w_b = st.w_s = 0
+    rc = lib.csa_index_topk_strided(ctypes.byref(_d(b=2)), ctypes.byref(st), 1, M, P, N, N, P, P, N, 0, N)
+    assert rc == -1 and "q_i is not 16-byte aligned" in lib.csa_last_error().decode()
+
+
 def test_compress_and_index_stride_helpers():
     import torch
     x = torch.zeros(64, 2, 64, dtype=torch.bfloat16).transpose(0, 1)

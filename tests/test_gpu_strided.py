@@ -192,6 +192,7 @@ INDEX_CASES = [
     ("csa4_bf16_b2_sbhd", CSA4_SMALL.replace(b=2, sq=1030), "sbhd", 0, False),
     ("csa4_bf16_b3_pad", CSA4_SMALL.replace(b=3, sq=700, topk=64), "pad", 8, False),
     ("csa4_bf16_b2_sbhd_docs", CSA4_SMALL.replace(b=2, sq=900, topk=64), "sbhd", 0, True),
+    ("one_head_unit_w_b2_sbhd", CSA4_SMALL.replace(b=2, sq=600, topk=64, idx_heads=1), "sbhd", 0, False),
 ]
 
 
@@ -207,12 +208,14 @@ def test_strided_indexer_matches_contiguous(gpu, name, wl, layout, pad, docs):
     b, S, kp = wl.b, wl.sq, wl.kprime
     doc = csa_synth.packed_doc_ids(b, S, 150.0, 43).cuda() if docs else None
     out = {}
+    unit_w = name.startswith("one_head_unit_w")          # no w: unit weights
     for strided in (False, True):
-        q_i, k_i, w = inp["q_i"], inp["k_i"], inp["w"]
+        q_i, k_i, w = inp["q_i"], inp["k_i"], None if unit_w else inp["w"]
         idx = torch.full((b, S, kp), 7, dtype=torch.int32, device="cuda")
         score = torch.full((b, S, kp), 3.0, device="cuda")
         if strided:
-            q_i, k_i, w = _view(q_i, layout, pad), _view(k_i, layout, pad), _view(w, layout, 4 if pad else 0)
+            q_i, k_i = _view(q_i, layout, pad), _view(k_i, layout, pad)
+            w = None if w is None else _view(w, layout, 4 if pad else 0)
             csa.csa_index_topk_strided(dm, q_i, k_i, w, idx, score, doc_ids=doc)
         else:
             csa.csa_index_topk(dm, q_i, k_i, w, idx, score, doc_ids=doc)

@@ -25,6 +25,8 @@
 // hands the gradient of the pooled rows to the pooling backward through the
 // workspace; the weight gradient is summed per workgroup and then over
 // workgroups, in a fixed order.
+#include <algorithm>
+
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
 #include "timing.hpp"
@@ -534,11 +536,35 @@ hipError_t compress_fwd(const CompressArgs& p, bool bf16, hipStream_t st)
     }
 }
 
+namespace {
+
+// rows [0, S) of a [b, S, W] fp32 tensor with element strides (sb, ss) set
+// to zero (a strided view: elements between its rows are not touched)
+__global__ __launch_bounds__(256) void zero_rows_kernel(float* __restrict__ p, int S, int W, int64_t n, int64_t sb,
+                                                        int64_t ss)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int64_t row = i / W;
+        p[(row / S) * sb + (row % S) * ss + i % W] = 0.f;
+    }
+}
+
+hipError_t zero_rows(float* p, int b, int S, int W, int64_t sb, int64_t ss, hipStream_t st)
+{
+    const int64_t n = (int64_t)b * S * W;
+    if (n == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, S, W, n, sb, ss);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t compress_bwd(const CompressArgs& p, bool bf16, hipStream_t st)
 {
     if (p.nc == 0) {     // no block: every gradient row is zero, and so is the weight gradient
-        hipError_t e = zero_fill(p.dx, (size_t)p.b * p.S * p.D, st);
-        if (e == hipSuccess) e = zero_fill(p.dz, (size_t)p.b * p.S * p.zc, st);
+        hipError_t e = zero_rows(p.dx, p.b, p.S, p.D, p.xsb, p.xss, st);
+        if (e == hipSuccess) e = zero_rows(p.dz, p.b, p.S, p.zc, p.zsb, p.zss, st);
         if (e == hipSuccess && p.dnorm_w) e = zero_fill(p.dnorm_w, (size_t)p.D, st);
         return e;
     }

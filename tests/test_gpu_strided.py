@@ -223,3 +223,27 @@ def test_strided_indexer_matches_contiguous(gpu, name, wl, layout, pad, docs):
         out[strided] = (idx, score)
     assert torch.equal(out[True][0], out[False][0]), "idx: strided indexer call differs from the contiguous call"
     assert torch.equal(out[True][1], out[False][1]), "score: strided indexer call differs from the contiguous call"
+
+
+@pytest.mark.parametrize("layout", ["pad", "sbhd"])
+def test_strided_compressor_bwd_without_blocks_leaves_padding(gpu, layout):
+    """sq < ratio (no compressed block): dx and dz are zero on every row of
+    the view, and elements outside the view (padding) keep their values."""
+    import compressed_sparse_attention_softmax_amd as csa
+    wl = CSA4_SMALL.replace(b=2, sq=3)
+    assert wl.n_c == 0
+    say(f"[strided compressor, no block] layout={layout}")
+    inp = csa_synth.make_inputs(wl, 47, device="cuda", parts=("compress",))
+    dm = csa.dims_of(wl)
+    b, S, D, zc = wl.b, wl.sq, wl.d, wl.z_channels
+    x, z = _view(inp["x"], layout, 8), _view(inp["z"], layout, 8)
+    dx = _empty_like_layout((b, S, D), torch.float32, layout, 8, fill=5.0)
+    dz = _empty_like_layout((b, S, zc), torch.float32, layout, 8, fill=5.0)
+    dc = torch.empty(b, 0, D, device="cuda")
+    csa.csa_compress_bwd_strided(dm, x, z, dc, dx, dz)
+    torch.cuda.synchronize()
+    assert bool((dx == 0).all()) and bool((dz == 0).all())
+    if layout == "pad":
+        # the storage behind the views: the 8 padding columns of every row keep 5.0
+        assert bool((dx.as_strided((b, S, D + 8), dx.stride())[..., D:] == 5.0).all())
+        assert bool((dz.as_strided((b, S, zc + 8), dz.stride())[..., zc:] == 5.0).all())

@@ -67,17 +67,51 @@ __device__ __forceinline__ int bin_of(float s, float lo, float scale)
     return (int)f;
 }
 
+// Each pass over the buffer reads SB entries per lane before it uses any of
+// them, so that one pass waits for LDS about n / (64 SB) times, not n / 64
+// (the kernels use SB = 8 in bf16, fewer in fp32, whose registers are fuller).
+
+// s[u] (and j[u]) = entry i0 + 64 u + lane of the buffer, where it is < n
+template <int SB>
+__device__ __forceinline__ void read_batch(const WaveBufs& b, int i0, int n, float (&s)[SB])
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+        const int i = i0 + u * WAVE + lane;
+        s[u] = i < n ? b.s[i] : -INFINITY;
+    }
+}
+template <int SB>
+__device__ __forceinline__ void read_batch(const WaveBufs& b, int i0, int n, float (&s)[SB], int (&j)[SB])
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+        const int i = i0 + u * WAVE + lane;
+        s[u] = i < n ? b.s[i] : -INFINITY;
+        j[u] = i < n ? b.j[i] : 0;
+    }
+}
+
 // Keep the k best of b.s/b.j[0..n) by (score desc, index asc), preserving
 // buffer order.  Requires 1 <= k < n.  Returns the threshold score T (the
 // k-th best score).  Wave-uniform control flow.
+template <int SB>
 __device__ float select_keep(const WaveBufs& b, int n, int k)
 {
     const int lane = lane_id();
     float lo = INFINITY, hi = -INFINITY;
-    for (int i = lane; i < n; i += WAVE) {
-        float s = b.s[i];
-        lo = fminf(lo, s);
-        hi = fmaxf(hi, s);
+    for (int i0 = 0; i0 < n; i0 += SB * WAVE) {
+        float s[SB];
+        read_batch(b, i0, n, s);
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            if (i0 + u * WAVE + lane < n) {
+                lo = fminf(lo, s[u]);
+                hi = fmaxf(hi, s[u]);
+            }
+        }
     }
     lo = wave_min(lo);
     hi = wave_max(hi);
@@ -91,9 +125,12 @@ __device__ float select_keep(const WaveBufs& b, int n, int k)
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         const float scale = (float)HBINS / (hi - lo);
-        for (int i = lane; i < n; i += WAVE) {
-            float s = b.s[i];
-            if (s >= lo && s <= hi) atomicAdd(&b.hist[bin_of(s, lo, scale)], 1u);
+        for (int i0 = 0; i0 < n; i0 += SB * WAVE) {
+            float s[SB];
+            read_batch(b, i0, n, s);
+#pragma unroll
+            for (int u = 0; u < SB; ++u)
+                if (i0 + u * WAVE + lane < n && s[u] >= lo && s[u] <= hi) atomicAdd(&b.hist[bin_of(s[u], lo, scale)], 1u);
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -121,29 +158,37 @@ __device__ float select_keep(const WaveBufs& b, int n, int k)
         kk -= above_b;
         // range of the chosen bin
         float lo2 = INFINITY, hi2 = -INFINITY;
-        for (int i = lane; i < n; i += WAVE) {
-            float s = b.s[i];
-            if (s >= lo && s <= hi && bin_of(s, lo, scale) == bstar) {
-                lo2 = fminf(lo2, s);
-                hi2 = fmaxf(hi2, s);
+        for (int i0 = 0; i0 < n; i0 += SB * WAVE) {
+            float s[SB];
+            read_batch(b, i0, n, s);
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+                if (i0 + u * WAVE + lane < n && s[u] >= lo && s[u] <= hi && bin_of(s[u], lo, scale) == bstar) {
+                    lo2 = fminf(lo2, s[u]);
+                    hi2 = fmaxf(hi2, s[u]);
+                }
             }
         }
         lo2 = wave_min(lo2);
         hi2 = wave_max(hi2);
         if (cnt_b <= WAVE) {
-            // gather the bin's entries into lanes and rank them exactly
+            // gather the bin's entries into lanes (in buffer order) and rank them exactly
             int base = 0;
-            for (int i0 = 0; i0 < n; i0 += WAVE) {
-                int i = i0 + lane;
-                float s = i < n ? b.s[i] : -INFINITY;
-                bool in = i < n && s >= lo2 && s <= hi2;
-                uint64_t m = __ballot(in);
-                if (in) {
-                    int p = base + (int)mbcnt(m);
-                    b.xs[p] = s;
-                    b.xj[p] = b.j[i];
+            for (int i0 = 0; i0 < n; i0 += SB * WAVE) {
+                float s[SB];
+                int jj[SB];
+                read_batch(b, i0, n, s, jj);
+#pragma unroll
+                for (int u = 0; u < SB; ++u) {
+                    const bool in = i0 + u * WAVE + lane < n && s[u] >= lo2 && s[u] <= hi2;
+                    const uint64_t m = __ballot(in);
+                    if (in) {
+                        const int p = base + (int)mbcnt(m);
+                        b.xs[p] = s[u];
+                        b.xj[p] = jj[u];
+                    }
+                    base += __popcll(m);
                 }
-                base += __popcll(m);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -167,27 +212,31 @@ __device__ float select_keep(const WaveBufs& b, int n, int k)
         lo = lo2;
         hi = hi2;
     }
-    // in-order compaction
+    // in-order compaction: a batch is read whole before any of it is written,
+    // and an entry only moves down, so no write lands on an unread entry
     int out = 0, ties = 0;
-    for (int i0 = 0; i0 < n; i0 += WAVE) {
-        int i = i0 + lane;
-        bool in = i < n;
-        float s = in ? b.s[i] : -INFINITY;
-        int j = in ? b.j[i] : 0;
-        bool eq = in && s == T;
-        uint64_t em = __ballot(eq);
-        int tr = ties + (int)mbcnt(em);
-        ties += __popcll(em);
-        bool keep = in && (s > T || (eq && tr < need));
-        uint64_t km = __ballot(keep);
+    for (int i0 = 0; i0 < n; i0 += SB * WAVE) {
+        float s[SB];
+        int jj[SB];
+        read_batch(b, i0, n, s, jj);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        if (keep) {
-            int p = out + (int)mbcnt(km);
-            b.s[p] = s;
-            b.j[p] = j;
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            const bool in = i0 + u * WAVE + lane < n;
+            const bool eq = in && s[u] == T;
+            const uint64_t em = __ballot(eq);
+            const int tr = ties + (int)mbcnt(em);
+            ties += __popcll(em);
+            const bool keep = in && (s[u] > T || (eq && tr < need));
+            const uint64_t km = __ballot(keep);
+            if (keep) {
+                const int p = out + (int)mbcnt(km);
+                b.s[p] = s[u];
+                b.j[p] = jj[u];
+            }
+            out += __popcll(km);
         }
-        out += __popcll(km);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -209,6 +258,9 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
                                                             IndexStrides is)
 {
     constexpr int KS = DI / 32;            // k-steps of 32
+    // buffer entries per lane per read batch (fp32 at d_i = 128 with four head
+    // tiles has no registers to spare)
+    constexpr int SB = sizeof(T) == 2 ? 8 : (DI == 128 && HT == 4 ? 1 : 4);
     constexpr int ROW = DI + 16 / sizeof(T) * 1;   // LDS row stride (elements), one 16-B pad
     extern __shared__ __attribute__((aligned(16))) char smem[];
     T* ktile = reinterpret_cast<T*>(smem);
@@ -327,7 +379,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
         const bool valid = j < nv && (!dcol || dcur == dt);
         const int ntile = min(KT, nv - j0);
         if (cnt + ntile > cap) {
-            tau = select_keep(bufs, cnt, kp);
+            tau = select_keep<SB>(bufs, cnt, kp);
             cnt = kp;
         }
         const bool take = valid && my > tau;
@@ -345,7 +397,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int kk = min(kp, nv);
     if (cnt > kk) {
-        select_keep(bufs, cnt, kk);
+        select_keep<SB>(bufs, cnt, kk);
         cnt = kk;
     }
     int32_t* orow = idx + row * kp;

@@ -158,7 +158,14 @@ INDEX_CASES = [
     ("csa4_bf16_b2_ragged", CSA4_SMALL.replace(b=2, sq=1027, topk=50), None),
     ("streaming_cuts", CSA4_SMALL.replace(sq=32768, topk=100), 384),
     ("streaming_cuts_b2_ragged", CSA4_SMALL.replace(b=2, sq=32771, topk=130), 256),
+    # large candidate buffers: n_c = 2048 held whole (no cut), and K' = 2048,
+    # the largest, over n_c = 5003 with its 4096-entry buffer cut
+    ("nc2048_whole_buffer", CSA4_SMALL.replace(sq=8192, topk=512), 384),
+    ("kprime2048_cuts_b2_ragged", CSA4_SMALL.replace(b=2, sq=20013, topk=2048), 256),
     ("idx_dim64_heads40", CSA4_SMALL.replace(idx_heads=40, idx_dim=64, sq=900, topk=70), None),
+    # fp32 at d_i = 128 (the cut reads its buffer one entry per lane at a time)
+    ("f32_idx_dim128_heads20", TINY.replace(idx_heads=20, idx_dim=128, sq=700, topk=40), None),
+    ("f32_idx_dim128_cuts", TINY.replace(idx_heads=20, idx_dim=128, sq=16001, topk=30), 256),
     ("one_block", CSA4_SMALL.replace(sq=5, topk=40), None),
     ("b3_sq9", CSA4_SMALL.replace(b=3, sq=9, topk=1), None),
 ]
@@ -180,17 +187,20 @@ def test_index_topk(gpu, name, wl, nrows):
     say(f"  rows identical to the oracle: {exact}/{len(rows)}")
 
 
-def test_index_topk_exact_integer_scores_and_ties(gpu):
+@pytest.mark.parametrize("heads,topk", [(8, 40), (64, 1024)])
+def test_index_topk_exact_integer_scores_and_ties(gpu, heads, topk):
     # small integer inputs make every fp32 score exact, so the GPU must match
     # the oracle bit for bit, including the lowest-index rule on exact ties;
-    # n_c = 8192 blocks drive the streaming cut path
-    wl = CSA4_SMALL.replace(sq=32768, topk=40, idx_heads=8)
+    # n_c = 8192 blocks drive the streaming cut path (with 64 heads and
+    # K' = 1024, 2048-entry buffers)
+    say(f"[index_topk exact] heads={heads} K={topk}")
+    wl = CSA4_SMALL.replace(sq=32768, topk=topk, idx_heads=heads)
     g = torch.Generator().manual_seed(5)
-    qi = torch.randint(-2, 3, (1, wl.sq, 8, 128), generator=g).to(torch.bfloat16)
+    qi = torch.randint(-2, 3, (1, wl.sq, heads, 128), generator=g).to(torch.bfloat16)
     ki = torch.randint(-1, 2, (1, wl.n_c, 128), generator=g).to(torch.bfloat16)
     ki[0, 100:140] = ki[0, 7]                                   # many identical keys
     ki[0, 5000:5100] = ki[0, 4000]
-    w = (torch.randint(-2, 5, (1, wl.sq, 8), generator=g).float() / 4)
+    w = (torch.randint(-2, 5, (1, wl.sq, heads), generator=g).float() / 4)
     rows = _edge_rows(wl, 512, 0)
     gi, gs, oidx, dense, rows = _index_case(wl, 0, rows=rows, q_i=qi.cuda(), k_i=ki.cuda(), w=w.cuda())
     np.testing.assert_array_equal(gi, oidx)
@@ -202,6 +212,7 @@ DOC_INDEX_CASES = [
     ("csa4_bf16_b2", CSA4_SMALL.replace(b=2, sq=1500, topk=60), 300, None),
     ("csa4_bf16_short_docs", CSA4_SMALL.replace(sq=1200, topk=40), 30, None),
     ("csa4_bf16_streaming_cuts", CSA4_SMALL.replace(sq=32768, topk=64), 2000, 256),
+    ("csa4_bf16_nc2048", CSA4_SMALL.replace(sq=8192, topk=300), 1500, 256),
 ]
 
 

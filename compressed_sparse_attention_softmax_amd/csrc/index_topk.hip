@@ -244,6 +244,84 @@ __device__ float select_keep(const WaveBufs& b, int n, int k)
     return T;
 }
 
+// A cut that only makes room (before the stream ends): keep every entry whose
+// histogram bin over [lo, hi] (the buffer's score range) is at or above the
+// bin holding the k-th best, if that keeps at most `limit` entries.  Every
+// dropped entry then scores below every kept one, of which there are at least
+// k, so none of them can reach the final k best; and a later key whose score
+// is at most the smallest kept score (returned in tau) ranks below at least k
+// kept entries with that score or more and lower indices, so it may be
+// rejected too.  The exact selection at the end of the stream is unchanged.
+// Returns the number kept, or 0 (buffer untouched) when the bin of the k-th
+// best holds too many entries for the limit, or the range is empty.
+template <int SB>
+__device__ int select_room(const WaveBufs& b, int n, int k, int limit, float lo, float hi, float& tau)
+{
+    const int lane = lane_id();
+    if (!(hi > lo)) return 0;
+    for (int i = lane; i < HBINS; i += WAVE) b.hist[i] = 0u;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    const float scale = (float)HBINS / (hi - lo);
+    // every entry gets a bin (bin_of clamps), and bins are monotonic in the score
+    for (int i0 = 0; i0 < n; i0 += SB * WAVE) {
+        float s[SB];
+        read_batch(b, i0, n, s);
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+            if (i0 + u * WAVE + lane < n) atomicAdd(&b.hist[bin_of(s[u], lo, scale)], 1u);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const unsigned c0 = b.hist[4 * lane], c1 = b.hist[4 * lane + 1], c2 = b.hist[4 * lane + 2],
+                   c3 = b.hist[4 * lane + 3];
+    const int mine = (int)(c0 + c1 + c2 + c3);
+    int suf = mine;
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const int v = __shfl_down(suf, o);
+        if (lane + o < WAVE) suf += v;
+    }
+    const int ls = 63 - __clzll((long long)__ballot(suf >= k));
+    const int above_lane = __shfl(suf - mine, ls);
+    const int cb[4] = {(int)__shfl((int)c0, ls), (int)__shfl((int)c1, ls), (int)__shfl((int)c2, ls),
+                       (int)__shfl((int)c3, ls)};
+    int cum = above_lane, bstar = 4 * ls, keep_n = 0;
+#pragma unroll
+    for (int q = 3; q >= 0; --q) {
+        if (cum < k && cum + cb[q] >= k) { bstar = 4 * ls + q; keep_n = cum + cb[q]; }
+        cum += cb[q];
+    }
+    if (keep_n > limit) return 0;
+    // in-order compaction, as in select_keep
+    int out = 0;
+    float mn = INFINITY;
+    for (int i0 = 0; i0 < n; i0 += SB * WAVE) {
+        float s[SB];
+        int jj[SB];
+        read_batch(b, i0, n, s, jj);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            const bool keep = i0 + u * WAVE + lane < n && bin_of(s[u], lo, scale) >= bstar;
+            const uint64_t km = __ballot(keep);
+            if (keep) {
+                const int p = out + (int)mbcnt(km);
+                b.s[p] = s[u];
+                b.j[p] = jj[u];
+                mn = fminf(mn, s[u]);
+            }
+            out += __popcll(km);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    tau = wave_min(mn);
+    return out;
+}
+
 // element strides: q_i (batch, token, head), k_i (batch, block), w (batch, token)
 struct IndexStrides { int64_t qb, qs, qh, kb, ks, wb, ws; };
 
@@ -261,6 +339,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
     // buffer entries per lane per read batch (fp32 at d_i = 128 with four head
     // tiles has no registers to spare)
     constexpr int SB = sizeof(T) == 2 ? 8 : (DI == 128 && HT == 4 ? 1 : 4);
+    constexpr bool ROOM = !(sizeof(T) == 4 && DI == 128 && HT == 4);   // the loose cut (same registers)
     constexpr int ROW = DI + 16 / sizeof(T) * 1;   // LDS row stride (elements), one 16-B pad
     extern __shared__ __attribute__((aligned(16))) char smem[];
     T* ktile = reinterpret_cast<T*>(smem);
@@ -307,6 +386,11 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
     const T* kb = ki + bi * is.kb;
     float tau = -INFINITY;
     int cnt = 0;
+    float rlo = INFINITY, rhi = -INFINITY;           // this lane's share of the buffer's score range
+    // the loose cut may keep up to half the headroom above K' (tried only
+    // when that leaves at least a tile's worth of slack)
+    const int room_limit = kp + (cap - kp) / 2 - KT;
+    const bool try_room = ROOM && room_limit >= kp + KT;
     constexpr int CH = 16 / sizeof(T);               // elements per 16-B chunk
     constexpr int CHUNKS = KT * DI / CH;
     constexpr int CPT = CHUNKS / 256;                // chunks per thread
@@ -379,8 +463,20 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
         const bool valid = j < nv && (!dcol || dcur == dt);
         const int ntile = min(KT, nv - j0);
         if (cnt + ntile > cap) {
-            tau = select_keep<SB>(bufs, cnt, kp);
-            cnt = kp;
+            // make room: the loose cut when its bin allows, else the exact one
+            const float hi = wave_max(rhi);
+            int kept = 0;
+            if constexpr (ROOM) {
+                if (try_room) kept = select_room<SB>(bufs, cnt, kp, room_limit, wave_min(rlo), hi, tau);
+            }
+            if (kept > 0) {
+                cnt = kept;
+            } else {
+                tau = select_keep<SB>(bufs, cnt, kp);
+                cnt = kp;
+            }
+            rlo = tau;                                // the kept entries span [tau, hi]
+            rhi = hi;
         }
         const bool take = valid && my > tau;
         const uint64_t m = __ballot(take);
@@ -388,6 +484,10 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(const T* __restrict_
             const int p = cnt + (int)mbcnt(m);
             bufs.s[p] = my;
             bufs.j[p] = j;
+            if constexpr (ROOM) {
+                rlo = fminf(rlo, my);
+                rhi = fmaxf(rhi, my);
+            }
         }
         cnt += __popcll(m);
     }

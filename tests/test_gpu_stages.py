@@ -162,6 +162,9 @@ INDEX_CASES = [
     # the largest, over n_c = 5003 with its 4096-entry buffer cut
     ("nc2048_whole_buffer", CSA4_SMALL.replace(sq=8192, topk=512), 384),
     ("kprime2048_cuts_b2_ragged", CSA4_SMALL.replace(b=2, sq=20013, topk=2048), 256),
+    # K' >= ~200 leaves headroom for the loose cut (keep the K'-th best's bin
+    # and above) before the exact one at the end
+    ("kprime512_cuts", CSA4_SMALL.replace(sq=32768, topk=512), 384),
     ("idx_dim64_heads40", CSA4_SMALL.replace(idx_heads=40, idx_dim=64, sq=900, topk=70), None),
     # fp32 at d_i = 128 (the cut reads its buffer one entry per lane at a time)
     ("f32_idx_dim128_heads20", TINY.replace(idx_heads=20, idx_dim=128, sq=700, topk=40), None),
@@ -213,6 +216,7 @@ DOC_INDEX_CASES = [
     ("csa4_bf16_short_docs", CSA4_SMALL.replace(sq=1200, topk=40), 30, None),
     ("csa4_bf16_streaming_cuts", CSA4_SMALL.replace(sq=32768, topk=64), 2000, 256),
     ("csa4_bf16_nc2048", CSA4_SMALL.replace(sq=8192, topk=300), 1500, 256),
+    ("csa4_bf16_kprime512_cuts", CSA4_SMALL.replace(sq=32768, topk=512), 2000, 256),
 ]
 
 

@@ -20,14 +20,18 @@
 // Streaming top-k: each wave keeps a candidate buffer in LDS.  Keys arrive
 // in ascending index, and a key is appended (ballot + mbcnt compaction) iff
 // its score beats the current threshold tau; the buffer therefore stays
-// sorted by index.  When the next tile could overflow it, the buffer is cut
-// to exactly the K' best entries and tau becomes the K'-th score: a later key
-// with an equal score has a larger index and loses the tie, so it is rejected.
-// The cut is an exact wave-level selection: value histograms over the current
-// [lo, hi] range narrow down to one bin, which is ranked exactly; ties at the
-// threshold are kept in buffer order, i.e. lowest index first.  At the end
-// the same selection keeps min(K', n_valid) entries and the buffer is written
-// out as is: already in ascending index.
+// sorted by index.  When the next tile could overflow it, the buffer is cut:
+// first by keeping the value-histogram bin that holds the K'-th best and every
+// bin above it (tau becomes the smallest kept score), or, when that bin holds
+// too many entries, to exactly the K' best (tau becomes the K'-th score).
+// Either way at least K' kept entries beat every dropped entry and every later
+// key scoring at most tau (equal scores lose on their larger index), so
+// nothing of the final top K' is lost.  The exact cut is a wave-level
+// selection: value histograms over the current [lo, hi] range narrow down to
+// one bin, which is ranked exactly; ties at the threshold are kept in buffer
+// order, i.e. lowest index first.  At the end the exact selection keeps
+// min(K', n_valid) entries and the buffer is written out as is: already in
+// ascending index.
 #include <cstdlib>
 
 #include "csa_device.hpp"

@@ -553,13 +553,19 @@ hipError_t index_topk(const IndexArgs& p, bool bf16, hipStream_t st)
 
 // Candidate-buffer capacity per query (entries): the whole valid prefix when
 // it fits on chip (no cut ever happens), else twice K' rounded up to a tile,
-// which leaves room for a full tile after every cut.  0 = does not fit.
+// which leaves room for a full tile after every cut; the smaller size also
+// when it lets two workgroups share a CU and the whole prefix does not (the
+// cuts cost less than the lost occupancy).  0 = does not fit.
 int index_topk_cap(const IndexArgs& p, bool bf16)
 {
     const int elem = bf16 ? 2 : 4;
     const int nc64 = (p.nc + 63) / 64 * 64, kp64 = (p.kp + 63) / 64 * 64;
     int cap = nc64;
-    if (topk_lds_bytes(p.DI, elem, cap) > (size_t)INDEX_LDS_LIMIT) cap = 2 * kp64;
+    const int small = 2 * kp64;
+    const size_t lim = INDEX_LDS_LIMIT;
+    if (small < cap && (topk_lds_bytes(p.DI, elem, cap) > lim ||
+                        (2 * topk_lds_bytes(p.DI, elem, small) <= lim && 2 * topk_lds_bytes(p.DI, elem, cap) > lim)))
+        cap = small;
     if (topk_lds_bytes(p.DI, elem, cap) > (size_t)INDEX_LDS_LIMIT) return 0;
     return cap;
 }

@@ -158,9 +158,10 @@ INDEX_CASES = [
     ("csa4_bf16_b2_ragged", CSA4_SMALL.replace(b=2, sq=1027, topk=50), None),
     ("streaming_cuts", CSA4_SMALL.replace(sq=32768, topk=100), 384),
     ("streaming_cuts_b2_ragged", CSA4_SMALL.replace(b=2, sq=32771, topk=130), 256),
-    # large candidate buffers: n_c = 2048 held whole (no cut), and K' = 2048,
-    # the largest, over n_c = 5003 with its 4096-entry buffer cut
-    ("nc2048_whole_buffer", CSA4_SMALL.replace(sq=8192, topk=512), 384),
+    # n_c = 2048 with K' = 512: a 1024-entry buffer (two workgroups per CU)
+    # rather than the whole prefix; K' = 2048, the largest, over n_c = 5003
+    # with its 4096-entry buffer cut
+    ("nc2048_kprime512", CSA4_SMALL.replace(sq=8192, topk=512), 384),
     ("kprime2048_cuts_b2_ragged", CSA4_SMALL.replace(b=2, sq=20013, topk=2048), 256),
     # K' >= ~200 leaves headroom for the loose cut (keep the K'-th best's bin
     # and above) before the exact one at the end

@@ -232,10 +232,16 @@ def test_index_topk_packed_documents(gpu, name, wl, mean, nrows):
     say(f"  rows identical to the oracle: {exact}/{len(rows)}")
 
 
-def test_index_topk_all_zero_keys(gpu):
-    wl = CSA4_SMALL.replace(sq=600, topk=30)
+@pytest.mark.parametrize("sq,topk,nrows", [(600, 30, None), (32768, 512, 256)])
+def test_index_topk_all_zero_keys(gpu, sq, topk, nrows):
+    # every score 0: the lowest indices win; at sq 32768 with K' = 512 every
+    # mid-stream cut finds an empty score range, so the room-making cut gives
+    # way to the exact one
+    say(f"[index_topk zero keys] sq={sq} K={topk}")
+    wl = CSA4_SMALL.replace(sq=sq, topk=topk)
     ki = torch.zeros(1, wl.n_c, 128, dtype=torch.bfloat16, device="cuda")
-    gi, gs, oidx, dense, rows = _index_case(wl, 3, k_i=ki)
+    rows = None if nrows is None else _edge_rows(wl, nrows, 3)
+    gi, gs, oidx, dense, rows = _index_case(wl, 3, rows=rows, k_i=ki)
     np.testing.assert_array_equal(gi, oidx)
     assert np.all(gs[gi >= 0] == 0.0) and not np.any(np.signbit(gs[gi >= 0]))
 
